@@ -1,0 +1,217 @@
+"""Plain float64 CPU definition of scaled-dot-product attention forward.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring): the product path never
+imports this module.
+
+What is computed
+----------------
+``O = softmax(scale * Q K^T + mask) V`` per batch and query head, with
+
+* grouped-query attention: query head ``h`` reads key/value head
+  ``h // (Hq // Hkv)``, i.e. consecutive query heads share one KV head
+  ("gqa_factor" query heads per KV head; mlx issue #3826 "2.3-2.8x latency
+  jump from L=8 to L=12 queries", first maintainer comment, item 1).  This is
+  the same as repeating every KV head ``Hq // Hkv`` times in place.
+* causal masking aligned bottom-right: query row ``i`` sits at key position
+  ``p = i + (Lk - Lq)`` and sees keys ``j <= p`` (K-relative coordinates with
+  ``qL_off = kL - qL``; mlx PR #3552 "feat(fast): add sliding-window SDPA
+  kernel path", Implementation).  ``Lq > Lk`` with a causal mask is an error
+  (mlx PR #4185 "Add force_fused option to scaled_dot_product_attention",
+  Validation).
+* sliding window: each query sees only the last ``window`` key positions up to
+  and including its own, combined with causal masking, i.e. ``p - W < j <= p``
+  (mlx PR #3552, Summary and the per-element rule "row_pos - col_pos >= W is
+  masked" in Implementation).  ``window >= 1`` is required.
+* the log-sum-exp of the visible scaled scores, natural log, per query row
+  (the output that training needs; mlx PR #4185, API).
+
+Everything is evaluated in float64 after an exact upcast of the inputs, with
+the full score rows materialised, which is the unfused "matmul -> softmax ->
+matmul" shape the fused kernels avoid (mlx PR #4185, Background).
+"""
+
+from __future__ import annotations
+
+import math
+from typing import Iterable, Sequence, Tuple
+
+import numpy as np
+
+MASK_KINDS = ("none", "causal", "window")
+
+
+def _as_f64(x) -> np.ndarray:
+    """Exact upcast of a numpy array or a CPU torch tensor to float64."""
+    if hasattr(x, "detach"):  # torch tensor: float16/bfloat16/float32 -> float64 is exact
+        x = x.detach().to("cpu")
+        import torch  # local: the oracle does not otherwise need torch
+
+        x = x.to(torch.float64).numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def _check_mask(lq: int, lk: int, mask: str, window: int) -> None:
+    if mask not in MASK_KINDS:
+        raise ValueError(f"unknown mask kind {mask!r}")
+    if mask != "none" and lq > lk:
+        raise ValueError("causal masking needs Lq <= Lk (queries align to the last Lq keys)")
+    if mask == "window" and window < 1:
+        raise ValueError("a sliding window needs window >= 1")
+
+
+def visible_mask(lq: int, lk: int, mask: str = "none", window: int = 0) -> np.ndarray:
+    """Boolean ``[lq, lk]`` visibility: True where query row i may attend key j."""
+    _check_mask(lq, lk, mask, window)
+    if mask == "none":
+        return np.ones((lq, lk), dtype=bool)
+    pos = np.arange(lq, dtype=np.int64)[:, None] + (lk - lq)  # absolute key position of row i
+    key = np.arange(lk, dtype=np.int64)[None, :]
+    vis = key <= pos
+    if mask == "window":
+        vis &= key > pos - window
+    return vis
+
+
+def _visible_row(i: int, lq: int, lk: int, mask: str, window: int) -> np.ndarray:
+    """Visibility of one query row, the same rule as ``visible_mask`` row by row."""
+    key = np.arange(lk, dtype=np.int64)
+    if mask == "none":
+        return np.ones(lk, dtype=bool)
+    pos = i + (lk - lq)
+    vis = key <= pos
+    if mask == "window":
+        vis &= key > pos - window
+    return vis
+
+
+def visible_pairs(lq: int, lk: int, mask: str = "none", window: int = 0) -> int:
+    """Number of visible (query, key) pairs of one head (counted, not derived)."""
+    return int(visible_mask(lq, lk, mask, window).sum())
+
+
+def _dims(q, k, v) -> Tuple[int, int, int, int, int, int, int]:
+    if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
+        raise ValueError("q, k, v must be [B, H, L, D]")
+    b, hq, lq, dqk = q.shape
+    bk, hkv, lk, dk = k.shape
+    bv, hv, lv, dv = v.shape
+    if bk != b or bv != b or hv != hkv or lv != lk or dk != dqk:
+        raise ValueError("inconsistent q/k/v shapes")
+    if hq % hkv != 0:
+        raise ValueError("Hq must be a multiple of Hkv")
+    return b, hq, hkv, lq, lk, dqk, dv
+
+
+def sdpa_ref(q, k, v, scale: float, mask: str = "none", window: int = 0, chunk: int = 512):
+    """Reference forward.  Returns ``(o, lse)`` in float64.
+
+    ``o`` is ``[B, Hq, Lq, Dv]``, ``lse`` is ``[B, Hq, Lq]``.  ``scale`` is
+    used as given (pass the same float32 value the GPU receives).
+    """
+    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    b, hq, hkv, lq, lk, dqk, dv = _dims(q, k, v)
+    vis = visible_mask(lq, lk, mask, window)
+    group = hq // hkv
+    scale = float(scale)
+    o = np.zeros((b, hq, lq, dv), dtype=np.float64)
+    lse = np.zeros((b, hq, lq), dtype=np.float64)
+    for bi in range(b):
+        for h in range(hq):
+            kvh = h // group
+            kt = k[bi, kvh].T
+            vv = v[bi, kvh]
+            for r0 in range(0, lq, chunk):
+                r1 = min(lq, r0 + chunk)
+                s = scale * (q[bi, h, r0:r1] @ kt)  # [rows, Lk] scaled scores
+                s = np.where(vis[r0:r1], s, -np.inf)
+                m = s.max(axis=1, keepdims=True)  # every row has a visible key
+                p = np.exp(s - m)  # exp(-inf) = 0 on masked entries
+                den = p.sum(axis=1, keepdims=True)
+                o[bi, h, r0:r1] = (p @ vv) / den
+                lse[bi, h, r0:r1] = (m + np.log(den))[:, 0]
+    return o, lse
+
+
+def sdpa_probs(q, k, scale: float, mask: str = "none", window: int = 0) -> np.ndarray:
+    """Attention probabilities ``[B, Hq, Lq, Lk]`` (tiny shapes only)."""
+    q, k = _as_f64(q), _as_f64(k)
+    b, hq, lq, _ = q.shape
+    hkv, lk = k.shape[1], k.shape[2]
+    vis = visible_mask(lq, lk, mask, window)
+    group = hq // hkv
+    out = np.zeros((b, hq, lq, lk), dtype=np.float64)
+    for bi in range(b):
+        for h in range(hq):
+            s = float(scale) * (q[bi, h] @ k[bi, h // group].T)
+            s = np.where(vis, s, -np.inf)
+            p = np.exp(s - s.max(axis=1, keepdims=True))
+            out[bi, h] = p / p.sum(axis=1, keepdims=True)
+    return out
+
+
+def sdpa_ref_rows(q, k, v, scale: float, mask: str, window: int,
+                  picks: Iterable[Sequence[int]]):
+    """Reference output for selected rows only, for full-size sampled checks.
+
+    ``picks`` holds ``(b, h, i)`` triples.  Returns ``(o_rows [n, Dv],
+    lse_rows [n])`` in float64, with the same definition as ``sdpa_ref``.
+    ``q``, ``k`` and ``v`` may be torch CPU tensors; only the rows touched are
+    upcast.
+    """
+    picks = [tuple(int(t) for t in p) for p in picks]
+    b, hq, lq, _ = q.shape
+    hkv, lk = k.shape[1], k.shape[2]
+    dv = v.shape[3]
+    _check_mask(lq, lk, mask, window)
+    group = hq // hkv
+    o = np.zeros((len(picks), dv), dtype=np.float64)
+    lse = np.zeros(len(picks), dtype=np.float64)
+    cache = {}
+    for n, (bi, h, i) in enumerate(picks):
+        kvh = h // group
+        if (bi, kvh) not in cache:
+            cache = {(bi, kvh): (_as_f64(k[bi, kvh]), _as_f64(v[bi, kvh]))}
+        kk, vv = cache[(bi, kvh)]
+        vis = _visible_row(i, lq, lk, mask, window)
+        s = float(scale) * (kk[vis] @ _as_f64(q[bi, h, i]))
+        m = s.max()
+        p = np.exp(s - m)
+        den = p.sum()
+        o[n] = (p @ vv[vis]) / den
+        lse[n] = m + math.log(den)
+    return o, lse
+
+
+def sdpa_loop(q, k, v, scale: float, mask: str = "none", window: int = 0):
+    """Second formulation in pure Python loops (tiny shapes only).
+
+    Walks each query row over the explicit key index range it may see and
+    forms the softmax from ``exp(s - max)`` sums with ``math.fsum``.
+    """
+    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    b, hq, hkv, lq, lk, dqk, dv = _dims(q, k, v)
+    _check_mask(lq, lk, mask, window)
+    group = hq // hkv
+    o = np.zeros((b, hq, lq, dv))
+    lse = np.zeros((b, hq, lq))
+    for bi in range(b):
+        for h in range(hq):
+            kvh = h // group
+            for i in range(lq):
+                pos = i + lk - lq
+                if mask == "none":
+                    lo, hi = 0, lk - 1
+                elif mask == "causal":
+                    lo, hi = 0, pos
+                else:
+                    lo, hi = max(0, pos - window + 1), pos
+                keys = list(range(lo, hi + 1))
+                s = [float(scale) * math.fsum(q[bi, h, i, d] * k[bi, kvh, j, d] for d in range(dqk))
+                     for j in keys]
+                mx = max(s)
+                w = [math.exp(x - mx) for x in s]
+                den = math.fsum(w)
+                for c in range(dv):
+                    o[bi, h, i, c] = math.fsum(w[t] * v[bi, kvh, j, c] for t, j in enumerate(keys)) / den
+                lse[bi, h, i] = mx + math.log(den)
+    return o, lse

@@ -1,0 +1,290 @@
+"""Pins for the CPU oracle (no GPU).
+
+The oracle is checked against things other than itself: a pure-Python loop
+formulation on tiny inputs, closed forms, invariants, a library special case
+(torch's CPU float64 attention with an explicit boolean mask) and the K-block
+skip ratios printed in mlx PR #3552 "feat(fast): add sliding-window SDPA kernel
+path" (Performance table), stored under ``tests/golden/``.
+"""
+
+import itertools
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import (sdpa_loop, sdpa_probs, sdpa_ref, sdpa_ref_rows, visible_mask,
+                    visible_pairs)
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def _case(b, hq, hkv, lq, lk, dqk, dv, seed):
+    return (_rand((b, hq, lq, dqk), seed), _rand((b, hkv, lk, dqk), seed + 1),
+            _rand((b, hkv, lk, dv), seed + 2))
+
+
+TINY = [
+    # b, hq, hkv, lq, lk, dqk, dv, mask, window
+    (1, 2, 2, 3, 5, 4, 4, "none", 0),
+    (2, 4, 2, 5, 5, 3, 6, "none", 0),
+    (1, 4, 1, 1, 7, 5, 2, "none", 0),
+    (1, 2, 1, 4, 4, 4, 4, "causal", 0),
+    (2, 4, 2, 3, 7, 6, 3, "causal", 0),
+    (1, 3, 3, 1, 6, 2, 5, "causal", 0),
+    (1, 2, 1, 6, 6, 4, 4, "window", 1),
+    (1, 4, 2, 5, 9, 3, 4, "window", 3),
+    (2, 2, 2, 4, 4, 4, 2, "window", 2),
+    (1, 2, 1, 3, 8, 5, 5, "window", 20),
+]
+
+
+@pytest.mark.parametrize("case", TINY)
+def test_ref_matches_loop_brute_force(case):
+    b, hq, hkv, lq, lk, dqk, dv, mask, w = case
+    q, k, v = _case(b, hq, hkv, lq, lk, dqk, dv, seed=sum(case[:7]))
+    o, lse = sdpa_ref(q, k, v, 0.7, mask, w)
+    o2, lse2 = sdpa_loop(q, k, v, 0.7, mask, w)
+    np.testing.assert_allclose(o, o2, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, lse2, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("case", TINY)
+def test_ref_rows_matches_ref(case):
+    b, hq, hkv, lq, lk, dqk, dv, mask, w = case
+    q, k, v = _case(b, hq, hkv, lq, lk, dqk, dv, seed=3 + sum(case[:7]))
+    o, lse = sdpa_ref(q, k, v, 1.3, mask, w)
+    picks = list(itertools.product(range(b), range(hq), range(lq)))
+    orow, lrow = sdpa_ref_rows(q, k, v, 1.3, mask, w, picks)
+    for n, (bi, h, i) in enumerate(picks):
+        np.testing.assert_allclose(orow[n], o[bi, h, i], rtol=0, atol=1e-12)
+        assert abs(lrow[n] - lse[bi, h, i]) < 1e-12
+
+
+@pytest.mark.parametrize("case", TINY)
+def test_torch_cpu_sdpa_special_case(case):
+    """Library special case: torch's float64 CPU attention, explicit bool mask, KV heads repeated."""
+    b, hq, hkv, lq, lk, dqk, dv, mask, w = case
+    q, k, v = _case(b, hq, hkv, lq, lk, dqk, dv, seed=11 + sum(case[:7]))
+    o, _ = sdpa_ref(q, k, v, 0.45, mask, w)
+    g = hq // hkv
+    tq = torch.from_numpy(q)
+    tk = torch.from_numpy(k).repeat_interleave(g, dim=1)
+    tv = torch.from_numpy(v).repeat_interleave(g, dim=1)
+    m = torch.from_numpy(visible_mask(lq, lk, mask, w))
+    ot = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=m, scale=0.45)
+    np.testing.assert_allclose(o, ot.numpy(), rtol=0, atol=1e-12)
+
+
+def _expected_visible_set(i, lq, lk, mask, w):
+    """Textbook statement of the visible key set of query row i (bottom-right aligned)."""
+    last = lk - lq + i  # the key position the query occupies
+    if mask == "none":
+        return set(range(lk))
+    if mask == "causal":
+        return set(range(0, last + 1))
+    return set(range(max(0, last - w + 1), last + 1))
+
+
+@pytest.mark.parametrize("lq,lk,mask,w", [
+    (1, 9, "causal", 0), (4, 9, "causal", 0), (9, 9, "causal", 0), (5, 9, "none", 0),
+    (9, 9, "window", 1), (9, 9, "window", 4), (3, 11, "window", 5), (6, 6, "window", 6),
+    (2, 7, "window", 100),
+])
+def test_zero_query_identity_values_reveal_visible_set(lq, lk, mask, w):
+    """Q = 0 makes every visible key equally likely: with V = I the output row is
+    the indicator of the visible set over its size, and lse = ln(size)."""
+    q = np.zeros((1, 1, lq, 3))
+    k = _rand((1, 1, lk, 3), 5)
+    v = np.eye(lk)[None, None]
+    o, lse = sdpa_ref(q, k, v, 1.0, mask, w)
+    for i in range(lq):
+        vis = _expected_visible_set(i, lq, lk, mask, w)
+        exp = np.array([1.0 / len(vis) if j in vis else 0.0 for j in range(lk)])
+        np.testing.assert_allclose(o[0, 0, i], exp, rtol=0, atol=1e-15)
+        assert abs(lse[0, 0, i] - math.log(len(vis))) < 1e-14
+
+
+def test_scale_zero_gives_mean_of_values():
+    q, k, v = _case(1, 2, 1, 4, 6, 5, 3, seed=21)
+    o, lse = sdpa_ref(q, k, v, 0.0, "causal", 0)
+    for i in range(4):
+        n = i + 2 + 1
+        np.testing.assert_allclose(o[0, 0, i], v[0, 0, :n].mean(axis=0), atol=1e-14)
+        assert abs(lse[0, 1, i] - math.log(n)) < 1e-14
+
+
+def test_single_key_closed_form():
+    q, k, v = _case(1, 3, 1, 1, 1, 4, 5, seed=31)
+    o, lse = sdpa_ref(q, k, v, 0.37, "none", 0)
+    for h in range(3):
+        np.testing.assert_allclose(o[0, h, 0], v[0, 0, 0], atol=1e-15)
+        assert abs(lse[0, h, 0] - 0.37 * float(q[0, h, 0] @ k[0, 0, 0])) < 1e-13
+
+
+def test_two_keys_sigmoid_closed_form():
+    q, k, v = _case(1, 1, 1, 3, 2, 4, 3, seed=41)
+    o, lse = sdpa_ref(q, k, v, 0.8, "none", 0)
+    for i in range(3):
+        s0 = 0.8 * float(q[0, 0, i] @ k[0, 0, 0])
+        s1 = 0.8 * float(q[0, 0, i] @ k[0, 0, 1])
+        sig = 1.0 / (1.0 + math.exp(-(s0 - s1)))
+        np.testing.assert_allclose(o[0, 0, i], sig * v[0, 0, 0] + (1 - sig) * v[0, 0, 1], atol=1e-14)
+        assert abs(lse[0, 0, i] - (max(s0, s1) + math.log1p(math.exp(-abs(s0 - s1))))) < 1e-13
+
+
+def test_window_one_selects_own_position():
+    q, k, v = _case(1, 2, 2, 4, 7, 3, 4, seed=51)
+    o, lse = sdpa_ref(q, k, v, 2.0, "window", 1)
+    for h in range(2):
+        for i in range(4):
+            p = i + 3
+            np.testing.assert_allclose(o[0, h, i], v[0, h, p], atol=1e-15)
+            assert abs(lse[0, h, i] - 2.0 * float(q[0, h, i] @ k[0, h, p])) < 1e-13
+
+
+def test_large_scale_limit_picks_argmax():
+    q, k, v = _case(1, 1, 1, 4, 16, 8, 4, seed=61)
+    o, _ = sdpa_ref(q, k, v, 1e4, "none", 0)
+    s = q[0, 0] @ k[0, 0].T
+    for i in range(4):
+        np.testing.assert_allclose(o[0, 0, i], v[0, 0, int(np.argmax(s[i]))], atol=1e-9)
+
+
+@pytest.mark.parametrize("mask,w", [("none", 0), ("causal", 0), ("window", 3)])
+def test_probabilities_sum_to_one_and_reproduce_output(mask, w):
+    q, k, v = _case(2, 4, 2, 5, 8, 6, 3, seed=71)
+    p = sdpa_probs(q, k, 0.5, mask, w)
+    np.testing.assert_allclose(p.sum(axis=-1), 1.0, atol=1e-14)
+    assert (p[..., ~visible_mask(5, 8, mask, w)] == 0).all()
+    o, _ = sdpa_ref(q, k, v, 0.5, mask, w)
+    g = 2
+    for b in range(2):
+        for h in range(4):
+            np.testing.assert_allclose(p[b, h] @ v[b, h // g], o[b, h], atol=1e-13)
+
+
+def test_output_linear_in_values():
+    q, k, v1 = _case(1, 2, 1, 4, 6, 4, 3, seed=81)
+    v2 = _rand(v1.shape, 82)
+    a, c = 0.3, -1.7
+    o1, _ = sdpa_ref(q, k, v1, 0.9, "causal", 0)
+    o2, _ = sdpa_ref(q, k, v2, 0.9, "causal", 0)
+    o3, _ = sdpa_ref(q, k, a * v1 + c * v2, 0.9, "causal", 0)
+    np.testing.assert_allclose(o3, a * o1 + c * o2, atol=1e-13)
+
+
+def test_unmasked_invariant_to_key_permutation():
+    q, k, v = _case(1, 2, 2, 3, 9, 4, 4, seed=91)
+    perm = np.random.default_rng(0).permutation(9)
+    o, lse = sdpa_ref(q, k, v, 0.6, "none", 0)
+    o2, lse2 = sdpa_ref(q, k[:, :, perm], v[:, :, perm], 0.6, "none", 0)
+    np.testing.assert_allclose(o, o2, atol=1e-13)
+    np.testing.assert_allclose(lse, lse2, atol=1e-13)
+
+
+def test_causal_single_query_equals_no_mask():
+    q, k, v = _case(1, 4, 2, 1, 10, 5, 3, seed=101)
+    np.testing.assert_array_equal(sdpa_ref(q, k, v, 0.4, "causal")[0], sdpa_ref(q, k, v, 0.4, "none")[0])
+
+
+@pytest.mark.parametrize("w", [9, 10, 1000])
+def test_window_at_least_lk_equals_causal(w):
+    q, k, v = _case(1, 2, 1, 6, 9, 4, 4, seed=111)
+    a = sdpa_ref(q, k, v, 0.5, "causal")
+    b = sdpa_ref(q, k, v, 0.5, "window", w)
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
+
+
+def test_gqa_equals_repeated_kv_heads_bitwise():
+    q, k, v = _case(2, 6, 2, 4, 7, 5, 3, seed=121)
+    o, lse = sdpa_ref(q, k, v, 0.5, "causal")
+    o2, lse2 = sdpa_ref(q, np.repeat(k, 3, axis=1), np.repeat(v, 3, axis=1), 0.5, "causal")
+    np.testing.assert_array_equal(o, o2)
+    np.testing.assert_array_equal(lse, lse2)
+
+
+def test_gqa_uses_consecutive_heads():
+    """Query heads 0..G-1 read KV head 0: zeroing KV head 1 leaves them unchanged."""
+    q, k, v = _case(1, 4, 2, 3, 5, 4, 4, seed=131)
+    o, _ = sdpa_ref(q, k, v, 0.5, "none")
+    k2, v2 = k.copy(), v.copy()
+    k2[:, 1] = 0
+    v2[:, 1] = 0
+    o2, _ = sdpa_ref(q, k2, v2, 0.5, "none")
+    np.testing.assert_array_equal(o[:, :2], o2[:, :2])
+    assert not np.allclose(o[:, 2:], o2[:, 2:])
+
+
+def test_zero_padding_head_dims():
+    q, k, v = _case(1, 2, 1, 4, 6, 5, 3, seed=141)
+    o, lse = sdpa_ref(q, k, v, 0.5, "causal")
+    pad = ((0, 0), (0, 0), (0, 0), (0, 3))
+    o2, lse2 = sdpa_ref(np.pad(q, pad), np.pad(k, pad), np.pad(v, pad), 0.5, "causal")
+    np.testing.assert_allclose(o2[..., :3], o, atol=1e-14)
+    np.testing.assert_array_equal(o2[..., 3:], 0.0)
+    np.testing.assert_allclose(lse2, lse, atol=1e-14)
+
+
+@pytest.mark.parametrize("lq,lk,mask,w", [(7, 7, "none", 0), (7, 7, "causal", 0), (3, 10, "causal", 0),
+                                         (10, 10, "window", 4), (4, 12, "window", 3), (5, 5, "window", 9)])
+def test_visible_pair_counts_closed_form(lq, lk, mask, w):
+    off = lk - lq
+    if mask == "none":
+        exp = lq * lk
+    elif mask == "causal":
+        exp = lq * (lq + 1) // 2 + lq * off
+    else:
+        exp = sum(min(w, i + off + 1) for i in range(lq))
+    assert visible_pairs(lq, lk, mask, w) == exp
+
+
+def _load_golden(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append(line.split())
+    return rows
+
+
+def test_window_skip_ratio_matches_printed_table():
+    """The K-block skip ratio printed for W=1024 at 2K/4K/8K is the fraction of the
+    key range lying below the last query's window: (L - W) / L."""
+    rows = _load_golden("window_skip_ratio.txt")
+    assert len(rows) == 3
+    for ctx, w, pct in rows:
+        L, W = int(ctx), int(w)
+        vis_last = visible_mask(4, L, "window", W)[-1]  # last query sits at position L-1
+        below = int(np.argmax(vis_last))  # first visible key
+        assert abs(100.0 * below / L - float(pct)) < 1e-9
+
+
+@pytest.mark.parametrize("bad", [
+    dict(lq=5, lk=4, mask="causal", w=0), dict(lq=5, lk=4, mask="window", w=2),
+    dict(lq=2, lk=4, mask="window", w=0), dict(lq=2, lk=4, mask="bogus", w=0),
+])
+def test_invalid_masks_raise(bad):
+    with pytest.raises(ValueError):
+        visible_mask(bad["lq"], bad["lk"], bad["mask"], bad["w"])
+
+
+def test_no_visible_keys_never_happens():
+    for lq, lk in [(1, 1), (3, 3), (2, 9)]:
+        for mask, w in [("causal", 0), ("window", 1), ("window", 2)]:
+            assert visible_mask(lq, lk, mask, w).any(axis=1).all()
+
+
+def test_oracle_reads_torch_low_precision_exactly():
+    t = torch.tensor([1.0 + 2 ** -7, 3.140625, -0.0078125], dtype=torch.bfloat16)
+    q = t.reshape(1, 1, 1, 3)
+    o, lse = sdpa_ref(q, q, q, 1.0, "none")
+    np.testing.assert_array_equal(o[0, 0, 0], np.array([1.0 + 2 ** -7, 3.140625, -0.0078125]))
