@@ -1,0 +1,125 @@
+/*
+ * sdpa.h - C ABI of the MI355X (gfx950) fused scaled-dot-product attention
+ * forward library (libsdpa_fwd.so).
+ *
+ * Operation (mlx PR #4185 "Add force_fused option to
+ * scaled_dot_product_attention", API and Background; mlx PR #3552
+ * "feat(fast): add sliding-window SDPA kernel path", Summary and Public API):
+ *
+ *     O[b,h] = softmax(scale * Q[b,h] K[b,kv]^T + mask) V[b,kv],
+ *     kv = h / (Hq / Hkv)                      (grouped-query attention)
+ *
+ * computed tile by tile with an online softmax, so the Lq x Lk score matrix
+ * never exists in memory.  Masks:
+ *   SDPA_MASK_NONE    every key is visible;
+ *   SDPA_MASK_CAUSAL  query row i sits at key position p = i + Lk - Lq (rows
+ *                     aligned to the last Lq keys) and sees keys j <= p;
+ *   SDPA_MASK_WINDOW  causal and additionally p - window < j, i.e. the last
+ *                     `window` key positions up to and including p.
+ * The optional log-sum-exp output is lse[b,h,i] = ln sum_j exp(scale*q.k_j)
+ * over the visible keys (natural log, float32).
+ *
+ * Tensors (element strides; the head-dim stride is always 1):
+ *   q [B, Hq,  Lq, Dqk]   k [B, Hkv, Lk, Dqk]   v [B, Hkv, Lk, Dv]
+ *   o [B, Hq,  Lq, Dv]    lse [B, Hq, Lq] contiguous float32 (optional)
+ * q, k, v and o share one element type (float32, float16 or bfloat16).
+ * Accumulation is float32; o is rounded once, to nearest even.
+ *
+ * Ownership: the caller owns every buffer.  The library keeps no pointer
+ * after a call returns and allocates no device memory: a split plan needs a
+ * caller workspace of sdpa_workspace_bytes() bytes (0 for an unsplit plan).
+ * All pointers are device pointers of the current HIP device.
+ *
+ * Errors: every entry point returns SDPA_OK (0) or a negative sdpa_status_t.
+ * Validation runs on the host before anything is launched; on any error
+ * nothing is launched and o / lse are left untouched.  sdpa_last_error()
+ * returns a thread-local message naming the violated constraint.  Calls are
+ * asynchronous on `stream` and reentrant.
+ */
+#ifndef SDPA_FWD_H
+#define SDPA_FWD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SDPA_F32 = 0,
+  SDPA_F16 = 1,
+  SDPA_BF16 = 2
+} sdpa_dtype_t;
+
+typedef enum {
+  SDPA_MASK_NONE = 0,
+  SDPA_MASK_CAUSAL = 1,
+  SDPA_MASK_WINDOW = 2
+} sdpa_mask_t;
+
+typedef enum {
+  SDPA_OK = 0,
+  SDPA_E_NULL = -1,      /* a required pointer is NULL */
+  SDPA_E_SHAPE = -2,     /* a size < 1, Hq not a multiple of Hkv, size overflow */
+  SDPA_E_HEAD_DIM = -3,  /* head dim outside the instantiated set (e.g. 512) */
+  SDPA_E_DTYPE = -4,     /* unknown element type */
+  SDPA_E_MASK = -5,      /* unknown mask, causal/window with Lq > Lk, bad window */
+  SDPA_E_STRIDE = -6,    /* stride or pointer alignment (16-byte rows) violated */
+  SDPA_E_WORKSPACE = -7, /* workspace missing or smaller than required */
+  SDPA_E_SCALE = -8,     /* scale is not finite */
+  SDPA_E_DEVICE = -9,    /* no usable gfx950 device */
+  SDPA_E_HIP = -10,      /* a HIP runtime call or kernel launch failed */
+  SDPA_E_PLAN = -11      /* a plan override cannot be honoured */
+} sdpa_status_t;
+
+/* A HIP stream (hipStream_t); NULL selects the null stream. */
+typedef void* sdpa_stream_t;
+
+typedef struct {
+  int64_t batch, heads_q, heads_kv, len_q, len_k, dim_qk, dim_v;
+  /* element strides of the (batch, head, position) dims of each tensor */
+  int64_t q_stride[3], k_stride[3], v_stride[3], o_stride[3];
+  int32_t dtype;   /* sdpa_dtype_t */
+  int32_t mask;    /* sdpa_mask_t */
+  int32_t window;  /* >= 1 iff mask == SDPA_MASK_WINDOW, else 0 */
+  float scale;     /* finite; any sign; 0 allowed */
+  /* Plan overrides (0 = let the planner choose).  They select among the same
+   * kernels, never a different code path.  num_splits forces the number of
+   * key splits (>= 1); row_tile forces the query rows per workgroup (32, 64
+   * or 128). */
+  int32_t num_splits;
+  int32_t row_tile;
+} sdpa_desc_t;
+
+/* Fills *desc with contiguous [B,H,L,D] strides for the given sizes, no mask,
+ * scale = 1/sqrt(dim_qk), no overrides.  Returns SDPA_OK or SDPA_E_NULL. */
+int sdpa_desc_init(sdpa_desc_t* desc, int64_t batch, int64_t heads_q, int64_t heads_kv,
+                   int64_t len_q, int64_t len_k, int64_t dim_qk, int64_t dim_v,
+                   int32_t dtype);
+
+/* Workspace bytes the plan for *desc needs (0 when the plan does not split
+ * the key range).  Validates *desc; host only, launches nothing. */
+int sdpa_workspace_bytes(const sdpa_desc_t* desc, size_t* bytes);
+
+/* Forward pass.  q, k, v, o: device pointers, 16-byte aligned, laid out as
+ * described above.  lse: NULL or a contiguous [B,Hq,Lq] float32 buffer.
+ * workspace: at least sdpa_workspace_bytes() bytes (may be NULL when that is
+ * 0).  Enqueues one kernel (unsplit) or a split kernel plus a combine kernel
+ * on `stream` and returns without synchronising. */
+int sdpa_forward(const sdpa_desc_t* desc, const void* q, const void* k, const void* v,
+                 void* o, float* lse, void* workspace, size_t workspace_bytes,
+                 sdpa_stream_t stream);
+
+/* Writes a one-line, NUL-terminated description of the plan (kernel family,
+ * tile, splits, grid, workspace) into buf.  Host only. */
+int sdpa_describe_plan(const sdpa_desc_t* desc, char* buf, size_t len);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* sdpa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SDPA_FWD_H */

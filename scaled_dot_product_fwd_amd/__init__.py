@@ -1,0 +1,137 @@
+"""MI355X (gfx950) fused scaled-dot-product attention forward.
+
+``forward(q, k, v, ...)`` computes ``softmax(scale * q k^T + mask) v`` with the
+HIP kernels of ``libsdpa_fwd.so`` (see ``include/sdpa.h``).  PyTorch supplies
+device memory and the current stream only; there is no CPU or PyTorch
+fallback, and a missing library raises.
+
+Python mirrors the Python API described in mlx PR #4185 "Add force_fused
+option to scaled_dot_product_attention" (API) and the ``window_size`` keyword
+of mlx PR #3552 "feat(fast): add sliding-window SDPA kernel path" (Public
+API).
+"""
+
+from __future__ import annotations
+
+import math
+from typing import Optional, Tuple, Union
+
+from ._lib import (SDPA_BF16, SDPA_F16, SDPA_F32, SDPA_MASK_CAUSAL, SDPA_MASK_NONE,  # noqa: F401
+                   SDPA_MASK_WINDOW, SdpaError, SdpaRuntimeError, SdpaValueError, load,
+                   sdpa_desc_init, sdpa_desc_t, sdpa_describe_plan, sdpa_forward,
+                   sdpa_last_error, sdpa_workspace_bytes)
+
+__all__ = ["forward", "make_desc", "plan_for", "workspace_for", "sdpa_forward",
+           "sdpa_workspace_bytes", "sdpa_describe_plan", "sdpa_last_error", "sdpa_desc_init",
+           "SdpaError", "SdpaValueError", "SdpaRuntimeError"]
+
+_MASKS = {"none": SDPA_MASK_NONE, "causal": SDPA_MASK_CAUSAL, "window": SDPA_MASK_WINDOW}
+
+
+def _dtype_code(dtype) -> int:
+    import torch
+
+    codes = {torch.float32: SDPA_F32, torch.float16: SDPA_F16, torch.bfloat16: SDPA_BF16}
+    if dtype not in codes:
+        raise SdpaValueError(f"SDPA_E_DTYPE: unsupported dtype {dtype}")
+    return codes[dtype]
+
+
+def make_desc(q_shape, k_shape, v_shape, dtype: int, *, scale: Optional[float] = None,
+              mask: str = "none", window_size: int = 0, q_stride=None, k_stride=None,
+              v_stride=None, o_stride=None, num_splits: int = 0, row_tile: int = 0) -> sdpa_desc_t:
+    """Build a descriptor from shapes ``[B,H,L,D]`` (contiguous unless strides are given)."""
+    if mask not in _MASKS:
+        raise SdpaValueError(f"SDPA_E_MASK: mask must be one of {sorted(_MASKS)} (got {mask!r})")
+    b, hq, lq, dqk = (int(x) for x in q_shape)
+    _, hkv, lk, _ = (int(x) for x in k_shape)
+    dv = int(v_shape[3])
+    d = sdpa_desc_t()
+    d.batch, d.heads_q, d.heads_kv, d.len_q, d.len_k, d.dim_qk, d.dim_v = b, hq, hkv, lq, lk, dqk, dv
+
+    def contig(h, l, dd):
+        return (h * l * dd, l * dd, dd)
+
+    for name, given, dflt in (("q_stride", q_stride, contig(hq, lq, dqk)),
+                              ("k_stride", k_stride, contig(hkv, lk, dqk)),
+                              ("v_stride", v_stride, contig(hkv, lk, dv)),
+                              ("o_stride", o_stride, contig(hq, lq, dv))):
+        arr = getattr(d, name)
+        for j, s in enumerate(given if given is not None else dflt):
+            arr[j] = int(s)
+    d.dtype = int(dtype)
+    d.mask = _MASKS[mask]
+    d.window = int(window_size) if mask == "window" else int(window_size or 0)
+    d.scale = float(1.0 / math.sqrt(dqk)) if scale is None else float(scale)
+    d.num_splits = int(num_splits)
+    d.row_tile = int(row_tile)
+    return d
+
+
+def plan_for(desc: sdpa_desc_t) -> str:
+    return sdpa_describe_plan(desc)
+
+
+def workspace_for(desc: sdpa_desc_t) -> int:
+    return sdpa_workspace_bytes(desc)
+
+
+def forward(q, k, v, *, scale: Optional[float] = None, mask: str = "none", window_size: int = 0,
+            return_lse: bool = False, num_splits: int = 0, row_tile: int = 0,
+            out=None, lse_out=None, workspace=None, stream=None
+            ) -> Union["torch.Tensor", Tuple["torch.Tensor", "torch.Tensor"]]:  # noqa: F821
+    """Fused attention forward on the current HIP device.
+
+    q ``[B,Hq,Lq,Dqk]``, k ``[B,Hkv,Lk,Dqk]``, v ``[B,Hkv,Lk,Dv]`` on one GPU, one
+    dtype (float32/float16/bfloat16), unit stride in the head dim.  ``scale``
+    defaults to ``1/sqrt(Dqk)``.  ``mask`` is ``"none"``, ``"causal"`` (query
+    rows aligned to the last Lq keys) or ``"window"`` (causal plus the last
+    ``window_size`` keys).  Returns ``o`` (and the float32 log-sum-exp
+    ``[B,Hq,Lq]`` when ``return_lse``).  Validation errors raise
+    ``SdpaValueError`` (a ``ValueError``) naming the constraint.
+    """
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or t.dim() != 4:
+            raise SdpaValueError(f"SDPA_E_SHAPE: {name} must be a 4-D tensor [B, H, L, D]")
+        if not t.is_cuda:
+            raise SdpaValueError(f"SDPA_E_DEVICE: {name} must be on a GPU; there is no CPU path")
+        if t.stride(3) != 1:
+            raise SdpaValueError(f"SDPA_E_STRIDE: {name} must have unit stride in the head dim")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise SdpaValueError("SDPA_E_DTYPE: q, k and v must share one dtype")
+    if not (q.device == k.device == v.device):
+        raise SdpaValueError("SDPA_E_DEVICE: q, k and v must be on one device")
+    dt = _dtype_code(q.dtype)
+    b, hq, lq, _ = q.shape
+    dv = v.shape[3]
+    if out is None:
+        out = torch.empty((b, hq, lq, dv), dtype=q.dtype, device=q.device)
+    elif out.shape != (b, hq, lq, dv) or out.dtype != q.dtype or out.stride(3) != 1:
+        raise SdpaValueError("SDPA_E_SHAPE: out must be [B, Hq, Lq, Dv] in the input dtype")
+    desc = make_desc(q.shape, k.shape, v.shape, dt, scale=scale, mask=mask, window_size=window_size,
+                     q_stride=q.stride()[:3], k_stride=k.stride()[:3], v_stride=v.stride()[:3],
+                     o_stride=out.stride()[:3], num_splits=num_splits, row_tile=row_tile)
+    lse = None
+    if return_lse:
+        lse = lse_out if lse_out is not None else torch.empty((b, hq, lq), dtype=torch.float32,
+                                                              device=q.device)
+        if lse.shape != (b, hq, lq) or lse.dtype != torch.float32 or not lse.is_contiguous():
+            raise SdpaValueError("SDPA_E_SHAPE: lse_out must be contiguous float32 [B, Hq, Lq]")
+    nbytes = sdpa_workspace_bytes(desc)
+    if nbytes > 0 and (workspace is None or workspace.numel() * workspace.element_size() < nbytes):
+        if stream is not None:
+            # A workspace allocated here is stream-ordered on torch's current
+            # stream only; a caller-chosen stream must bring its own.
+            raise SdpaValueError(f"SDPA_E_WORKSPACE: a split plan on an explicit stream needs a "
+                                 f"caller workspace of {nbytes} bytes")
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if (workspace is not None and nbytes > 0) else 0
+    ws_len = workspace.numel() * workspace.element_size() if ws_ptr else 0
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    with torch.cuda.device(q.device):
+        sdpa_forward(desc, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                     lse.data_ptr() if lse is not None else 0, ws_ptr, ws_len, stream)
+    return (out, lse) if return_lse else out

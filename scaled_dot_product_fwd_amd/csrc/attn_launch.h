@@ -1,0 +1,77 @@
+// Launch glue shared by the per-(element type, family) instantiation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <string>
+
+#include "attn_kernel.h"
+
+namespace sdpa {
+
+template <class E, int DQK, int DV, int NWQ, int NWK, int BKW>
+int launch_one(const Plan& p, const AttnArgs& a, void* stream, std::string* err) {
+  using S = dev::Shape<E, DQK, DV, NWQ, NWK, BKW>;
+  auto kern = dev::attn_fwd_kernel<E, DQK, DV, NWQ, NWK, BKW>;
+  // Check the compiled kernel can run the workgroup size it is launched with,
+  // once per instance: an oversized launch must fail loudly, never return
+  // silently unwritten output (mlx PR #4185 "Add force_fused option to
+  // scaled_dot_product_attention", Kernel support: pipeline size check).
+  static int checked = 0;  // 0 unknown, 1 ok, -1 unusable
+  if (checked == 0) {
+    hipFuncAttributes attr;
+    if (hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(kern)) != hipSuccess) {
+      *err = "hipFuncGetAttributes failed for the attention kernel";
+      return SDPA_E_HIP;
+    }
+    checked = (attr.maxThreadsPerBlock >= S::NT && attr.sharedSizeBytes <= 160 * 1024) ? 1 : -1;
+    if (checked < 0) {
+      *err = "attention kernel cannot run " + std::to_string(S::NT) + " threads per workgroup (max " +
+             std::to_string(attr.maxThreadsPerBlock) + ", lds " + std::to_string(attr.sharedSizeBytes) + ")";
+      return SDPA_E_HIP;
+    }
+  } else if (checked < 0) {
+    *err = "attention kernel cannot run its workgroup size on this device";
+    return SDPA_E_HIP;
+  }
+  hipLaunchKernelGGL(kern, dim3((unsigned)p.grid), dim3(S::NT), 0, (hipStream_t)stream, a);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    *err = std::string("attention kernel launch failed: ") + hipGetErrorString(e);
+    return SDPA_E_HIP;
+  }
+  return SDPA_OK;
+}
+
+}  // namespace sdpa
+
+// One dispatch case: padded dims and wave arrangement must match the plan.
+#define SDPA_CASE(E, DQK, DV, NWQ, NWK, BKW)                                              \
+  if (p.dqk_pad == DQK && p.dv_pad == DV && p.fam.nwq == NWQ && p.fam.nwk == NWK &&       \
+      p.fam.bkw == BKW)                                                                   \
+    return launch_one<dev::E, DQK, DV, NWQ, NWK, BKW>(p, a, stream, err);
+
+// Head-dim pairs of the 16-bit types: equal padded dims plus (192, 128).
+#define SDPA_PAIRS16(E, NWQ, NWK, BKW_SMALL, BKW_BIG) \
+  SDPA_CASE(E, 32, 32, NWQ, NWK, BKW_SMALL)           \
+  SDPA_CASE(E, 64, 64, NWQ, NWK, BKW_SMALL)           \
+  SDPA_CASE(E, 96, 96, NWQ, NWK, BKW_SMALL)           \
+  SDPA_CASE(E, 128, 128, NWQ, NWK, BKW_SMALL)         \
+  SDPA_CASE(E, 160, 160, NWQ, NWK, BKW_BIG)           \
+  SDPA_CASE(E, 192, 192, NWQ, NWK, BKW_BIG)           \
+  SDPA_CASE(E, 224, 224, NWQ, NWK, BKW_BIG)           \
+  SDPA_CASE(E, 256, 256, NWQ, NWK, BKW_BIG)           \
+  SDPA_CASE(E, 192, 128, NWQ, NWK, BKW_BIG)
+
+// float32 stops at 128.
+#define SDPA_PAIRS32(E, NWQ, NWK, BKW) \
+  SDPA_CASE(E, 32, 32, NWQ, NWK, BKW)  \
+  SDPA_CASE(E, 64, 64, NWQ, NWK, BKW)  \
+  SDPA_CASE(E, 96, 96, NWQ, NWK, BKW)  \
+  SDPA_CASE(E, 128, 128, NWQ, NWK, BKW)
+
+#define SDPA_NO_INSTANCE()                                                                \
+  *err = "no kernel instance for dqk_pad=" + std::to_string(p.dqk_pad) +                  \
+         " dv_pad=" + std::to_string(p.dv_pad) + " waves=" + std::to_string(p.fam.nwq) +  \
+         "x" + std::to_string(p.fam.nwk) + " bkw=" + std::to_string(p.fam.bkw);           \
+  return SDPA_E_HEAD_DIM;

@@ -1,0 +1,9 @@
+// bf16 attention kernels, prefill family.
+#include "attn_launch.h"
+
+namespace sdpa {
+int launch_attn_bf16_prefill(const Plan& p, const AttnArgs& a, void* stream, std::string* err) {
+  SDPA_PAIRS16(BF16, 4, 1, 64, 32)
+  SDPA_NO_INSTANCE()
+}
+}  // namespace sdpa

@@ -1,0 +1,9 @@
+// bf16 attention kernels, short family.
+#include "attn_launch.h"
+
+namespace sdpa {
+int launch_attn_bf16_short(const Plan& p, const AttnArgs& a, void* stream, std::string* err) {
+  SDPA_PAIRS16(BF16, 2, 2, 32, 32)
+  SDPA_NO_INSTANCE()
+}
+}  // namespace sdpa

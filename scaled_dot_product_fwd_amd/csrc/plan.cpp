@@ -1,0 +1,233 @@
+// Host-side validation and planning for libsdpa_fwd.  Pure C++: no HIP calls,
+// nothing launched, so every error path can be exercised without a GPU.
+//
+// Validation follows the force-fused contract of mlx PR #4185 "Add
+// force_fused option to scaled_dot_product_attention" (API, Validation): a
+// shape no fused kernel covers raises with the violated constraint named
+// (unsupported head dims such as 512, causal with qL > kL), instead of
+// silently falling back.
+//
+// Planning picks the kernel family from the packed row count R = G * Lq and
+// the number of key splits from the occupancy the row tiles alone would give,
+// so that short query tiles still spread the key range over the whole chip
+// (mlx issue #3826 "2.3-2.8x latency jump from L=8 to L=12 queries": a launch
+// of one workgroup per head that streams all keys serially is the cliff).
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <sstream>
+#include <string>
+
+#include "sdpa_internal.h"
+
+namespace sdpa {
+
+namespace {
+
+constexpr int kTargetCUs = 256;        // gfx950 compute units (MI355X)
+constexpr int kWgsPerCU = 2;           // aim for two resident workgroups per CU
+constexpr int64_t kMaxLen = 1 << 30;   // keeps every in-kernel index in int32
+constexpr int kMaxSplits = 1024;
+constexpr int kMaxDim = 256;
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int fail(std::string* err, int code, const std::string& msg) {
+  if (err) *err = msg;
+  return code;
+}
+
+const char* dtype_name(int dt) {
+  switch (dt) {
+    case SDPA_F32: return "float32";
+    case SDPA_F16: return "float16";
+    case SDPA_BF16: return "bfloat16";
+    default: return "?";
+  }
+}
+
+const char* mask_name(int m) {
+  switch (m) {
+    case MASK_NONE: return "none";
+    case MASK_CAUSAL: return "causal";
+    case MASK_WINDOW: return "window";
+    default: return "?";
+  }
+}
+
+}  // namespace
+
+// Kernel families (rows per workgroup -> wave arrangement).  The same list is
+// instantiated in the element-type units.
+Family family_for(int rows_per_wg, int dqk_pad, int dv_pad) {
+  const int dmax = dqk_pad > dv_pad ? dqk_pad : dv_pad;
+  if (rows_per_wg == 32) return Family{1, 4, 32};    // decode: 4 waves split each key block
+  if (rows_per_wg == 64) return Family{2, 2, 32};    // short queries: 2 x 2 waves
+  return Family{4, 1, dmax <= 128 ? 64 : 32};        // prefill: 4 waves stacked on rows
+}
+
+size_t attn_lds_bytes(int dtype, int dqk_pad, int dv_pad, const Family& f) {
+  // Mirrors Shape<> in attn_kernel.h.
+  const int es = dtype == SDPA_F32 ? 4 : 2;
+  const int bk = f.nwk * f.bkw;
+  const int kbytes = bk * (dqk_pad * es + 16);
+  const int vbytes = dv_pad * (bk * es + 16);
+  const int buf = kbytes + vbytes;
+  const bool db = 2 * buf <= 80 * 1024;
+  const int tiles = (db ? 2 : 1) * buf;
+  const int merge = f.nwk > 1 ? f.nwq * f.nwk * 32 * (dv_pad + 4) * 4 + f.nwq * f.nwk * 32 * 8 : 0;
+  return (size_t)(tiles > merge ? tiles : merge);
+}
+
+int make_plan(const sdpa_desc_t* d, Plan* p, std::string* err) {
+  if (!d) return fail(err, SDPA_E_NULL, "desc is NULL");
+  if (!p) return fail(err, SDPA_E_NULL, "plan is NULL");
+  const int64_t B = d->batch, Hq = d->heads_q, Hkv = d->heads_kv, Lq = d->len_q, Lk = d->len_k;
+  const int64_t Dqk = d->dim_qk, Dv = d->dim_v;
+  if (B < 1 || Hq < 1 || Hkv < 1 || Lq < 1 || Lk < 1 || Dqk < 1 || Dv < 1) {
+    std::ostringstream s;
+    s << "every size must be >= 1 (got B=" << B << " Hq=" << Hq << " Hkv=" << Hkv << " Lq=" << Lq
+      << " Lk=" << Lk << " Dqk=" << Dqk << " Dv=" << Dv << ")";
+    return fail(err, SDPA_E_SHAPE, s.str());
+  }
+  if (Hq % Hkv != 0) {
+    std::ostringstream s;
+    s << "grouped-query attention needs heads_q to be a multiple of heads_kv (got Hq=" << Hq
+      << ", Hkv=" << Hkv << ")";
+    return fail(err, SDPA_E_SHAPE, s.str());
+  }
+  if (Lq > kMaxLen || Lk > kMaxLen || (Hq / Hkv) * Lq > kMaxLen || B * Hkv > kMaxLen) {
+    return fail(err, SDPA_E_SHAPE, "sizes exceed the supported range (Lq, Lk, G*Lq and B*Hkv must be <= 2^30)");
+  }
+  if (d->dtype != SDPA_F32 && d->dtype != SDPA_F16 && d->dtype != SDPA_BF16) {
+    return fail(err, SDPA_E_DTYPE, "dtype must be SDPA_F32, SDPA_F16 or SDPA_BF16 (got " +
+                                       std::to_string(d->dtype) + ")");
+  }
+  if (Dqk % 8 || Dv % 8 || Dqk > kMaxDim || Dv > kMaxDim) {
+    std::ostringstream s;
+    s << "no fused kernel for head dims (Dqk=" << Dqk << ", Dv=" << Dv
+      << "): supported head dims are multiples of 8 from 8 to " << kMaxDim;
+    return fail(err, SDPA_E_HEAD_DIM, s.str());
+  }
+  int dqk_pad = (int)ceil_div(Dqk, 32) * 32;
+  int dv_pad = (int)ceil_div(Dv, 32) * 32;
+  if (dqk_pad == 192 && dv_pad <= 128) {
+    dv_pad = 128;  // the asymmetric (192, 128) instance
+  } else {
+    const int m = dqk_pad > dv_pad ? dqk_pad : dv_pad;
+    dqk_pad = dv_pad = m;  // zero padding in-kernel: no host copy
+  }
+  if (d->dtype == SDPA_F32 && (dqk_pad > 128 || dv_pad > 128)) {
+    std::ostringstream s;
+    s << "no fused float32 kernel for head dims (Dqk=" << Dqk << ", Dv=" << Dv
+      << "): float32 supports head dims up to 128";
+    return fail(err, SDPA_E_HEAD_DIM, s.str());
+  }
+  if (d->mask != SDPA_MASK_NONE && d->mask != SDPA_MASK_CAUSAL && d->mask != SDPA_MASK_WINDOW) {
+    return fail(err, SDPA_E_MASK, "mask must be SDPA_MASK_NONE, SDPA_MASK_CAUSAL or SDPA_MASK_WINDOW (got " +
+                                      std::to_string(d->mask) + ")");
+  }
+  if (d->mask != SDPA_MASK_NONE && Lq > Lk) {
+    std::ostringstream s;
+    s << "causal masking requires Lq <= Lk: queries align to the last Lq keys (got Lq=" << Lq
+      << ", Lk=" << Lk << ")";
+    return fail(err, SDPA_E_MASK, s.str());
+  }
+  if (d->mask == SDPA_MASK_WINDOW && d->window < 1) {
+    return fail(err, SDPA_E_MASK, "a sliding window needs window >= 1 (got " + std::to_string(d->window) + ")");
+  }
+  if (d->mask != SDPA_MASK_WINDOW && d->window != 0) {
+    return fail(err, SDPA_E_MASK, "window must be 0 unless mask is SDPA_MASK_WINDOW (got " +
+                                      std::to_string(d->window) + ")");
+  }
+  if (!std::isfinite(d->scale)) return fail(err, SDPA_E_SCALE, "scale must be finite");
+  const int es = d->dtype == SDPA_F32 ? 4 : 2;
+  const int64_t* strides[4] = {d->q_stride, d->k_stride, d->v_stride, d->o_stride};
+  const char* names[4] = {"q", "k", "v", "o"};
+  for (int t = 0; t < 4; ++t) {
+    for (int j = 0; j < 3; ++j) {
+      if (strides[t][j] < 0 || (strides[t][j] * es) % 16 != 0) {
+        std::ostringstream s;
+        s << names[t] << "_stride[" << j << "] = " << strides[t][j]
+          << " must be >= 0 and a multiple of 16 bytes (rows are read with 16-byte loads)";
+        return fail(err, SDPA_E_STRIDE, s.str());
+      }
+    }
+  }
+  if (d->num_splits < 0 || d->num_splits > kMaxSplits) {
+    return fail(err, SDPA_E_PLAN, "num_splits must be 0 (auto) or 1.." + std::to_string(kMaxSplits));
+  }
+  if (d->row_tile != 0 && d->row_tile != 32 && d->row_tile != 64 && d->row_tile != 128) {
+    return fail(err, SDPA_E_PLAN, "row_tile must be 0 (auto), 32, 64 or 128 (got " +
+                                      std::to_string(d->row_tile) + ")");
+  }
+
+  // ---- canonical mask ----
+  int mask = d->mask, window = d->window;
+  if (mask == MASK_WINDOW && window >= Lk) { mask = MASK_CAUSAL; window = 0; }  // window covers every key <= p
+  if (mask == MASK_CAUSAL && Lq == 1) mask = MASK_NONE;                        // the single query sees every key
+
+  const int64_t G = Hq / Hkv;
+  const int64_t R = G * Lq;
+  int rows = d->row_tile ? d->row_tile : (R <= 32 ? 32 : (R <= 64 ? 64 : 128));
+  const Family fam = family_for(rows, dqk_pad, dv_pad);
+  const int64_t row_tiles = ceil_div(R, rows);
+  const int64_t base = B * Hkv * row_tiles;
+  const int64_t bk = (int64_t)fam.nwk * fam.bkw;
+
+  // Key blocks a row tile visits (the longest tile; every tile for `none`).
+  int64_t keys = Lk;
+  if (mask == MASK_WINDOW) keys = std::min<int64_t>(Lk, window + rows);  // window plus one tile of rows
+  const int64_t nblocks = ceil_div(keys, bk);
+
+  int64_t splits = 1;
+  if (d->num_splits > 0) {
+    splits = d->num_splits;
+  } else {
+    // Split the key range when the row tiles alone leave the chip idle.  A
+    // full-size prefill tile (128 rows) is only split when very few tiles
+    // exist: its partial outputs would cost HBM traffic comparable to the
+    // K/V it reads, while an unsplit wave of large tiles already keeps the
+    // MFMA units busy.
+    const int64_t target = (int64_t)kTargetCUs * kWgsPerCU;
+    const bool starved = rows < 128 ? base < target : base < kTargetCUs / 4;
+    if (starved) splits = std::min<int64_t>(ceil_div(target, base), nblocks);
+    splits = std::max<int64_t>(1, std::min<int64_t>(splits, kMaxSplits));
+  }
+  if (base * splits > 0x7fffffffLL) return fail(err, SDPA_E_SHAPE, "grid too large");
+
+  p->dtype = d->dtype;
+  p->dqk_pad = dqk_pad;
+  p->dv_pad = dv_pad;
+  p->fam = fam;
+  p->rows_per_wg = rows;
+  p->row_tiles = (int)row_tiles;
+  p->splits = (int)splits;
+  p->mask = mask;
+  p->window = window;
+  p->grid = base * splits;
+  p->combine_grid = splits > 1 ? B * Hkv * R : 0;
+  p->workspace = 0;
+  if (splits > 1) {
+    const size_t rows_total = (size_t)(B * Hkv * R * splits);
+    const size_t o_bytes = (rows_total * (size_t)Dv * 4 + 255) / 256 * 256;
+    p->workspace = o_bytes + rows_total * 8;
+  }
+  p->lds_bytes = attn_lds_bytes(d->dtype, dqk_pad, dv_pad, fam);
+  return SDPA_OK;
+}
+
+std::string describe(const sdpa_desc_t* d, const Plan& p) {
+  std::ostringstream s;
+  const char* fam = p.fam.nwk > 1 ? (p.fam.nwq > 1 ? "short" : "decode") : "prefill";
+  s << "family=" << fam << " dtype=" << dtype_name(p.dtype) << " dqk=" << d->dim_qk << "->" << p.dqk_pad
+    << " dv=" << d->dim_v << "->" << p.dv_pad << " rows_per_wg=" << p.rows_per_wg
+    << " waves=" << p.fam.nwq << "x" << p.fam.nwk << " block_keys=" << p.fam.nwk * p.fam.bkw
+    << " row_tiles=" << p.row_tiles << " splits=" << p.splits << " mask=" << mask_name(p.mask);
+  if (p.mask == MASK_WINDOW) s << "(" << p.window << ")";
+  s << " grid=" << p.grid << " combine_grid=" << p.combine_grid << " lds=" << p.lds_bytes
+    << " workspace=" << p.workspace;
+  return s.str();
+}
+
+}  // namespace sdpa

@@ -1,0 +1,203 @@
+// C entry points of libsdpa_fwd (declared in include/sdpa.h).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "sdpa_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int set_error(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return SDPA_OK;
+}
+
+// gfx950 check of the current device, cached per device ordinal.
+int check_device(std::string* err) {
+  static std::mutex mu;
+  static signed char state[64] = {0};  // 0 unknown, 1 gfx950, -1 other
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    *err = "no HIP device is available";
+    return SDPA_E_DEVICE;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (dev < 64 && state[dev] != 0) {
+    if (state[dev] > 0) return SDPA_OK;
+    *err = "the current HIP device is not a gfx950 (MI355X-class) GPU";
+    return SDPA_E_DEVICE;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+    *err = "hipGetDeviceProperties failed";
+    return SDPA_E_DEVICE;
+  }
+  const bool is950 = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < 64) state[dev] = is950 ? 1 : -1;
+  if (!is950) {
+    *err = std::string("the current HIP device is ") + prop.gcnArchName + ", not gfx950";
+    return SDPA_E_DEVICE;
+  }
+  return SDPA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+int sdpa_desc_init(sdpa_desc_t* d, int64_t batch, int64_t heads_q, int64_t heads_kv, int64_t len_q,
+                   int64_t len_k, int64_t dim_qk, int64_t dim_v, int32_t dtype) {
+  if (!d) return set_error(SDPA_E_NULL, "desc is NULL");
+  std::memset(d, 0, sizeof(*d));
+  d->batch = batch;
+  d->heads_q = heads_q;
+  d->heads_kv = heads_kv;
+  d->len_q = len_q;
+  d->len_k = len_k;
+  d->dim_qk = dim_qk;
+  d->dim_v = dim_v;
+  d->q_stride[2] = dim_qk;
+  d->q_stride[1] = len_q * dim_qk;
+  d->q_stride[0] = heads_q * len_q * dim_qk;
+  d->k_stride[2] = dim_qk;
+  d->k_stride[1] = len_k * dim_qk;
+  d->k_stride[0] = heads_kv * len_k * dim_qk;
+  d->v_stride[2] = dim_v;
+  d->v_stride[1] = len_k * dim_v;
+  d->v_stride[0] = heads_kv * len_k * dim_v;
+  d->o_stride[2] = dim_v;
+  d->o_stride[1] = len_q * dim_v;
+  d->o_stride[0] = heads_q * len_q * dim_v;
+  d->dtype = dtype;
+  d->mask = SDPA_MASK_NONE;
+  d->window = 0;
+  d->scale = dim_qk > 0 ? (float)(1.0 / std::sqrt((double)dim_qk)) : 1.0f;
+  return ok();
+}
+
+int sdpa_workspace_bytes(const sdpa_desc_t* d, size_t* bytes) {
+  if (!bytes) return set_error(SDPA_E_NULL, "bytes is NULL");
+  sdpa::Plan p;
+  std::string err;
+  const int rc = sdpa::make_plan(d, &p, &err);
+  if (rc != SDPA_OK) return set_error(rc, err);
+  *bytes = p.workspace;
+  return ok();
+}
+
+int sdpa_describe_plan(const sdpa_desc_t* d, char* buf, size_t len) {
+  if (!buf || len == 0) return set_error(SDPA_E_NULL, "buf is NULL or empty");
+  sdpa::Plan p;
+  std::string err;
+  const int rc = sdpa::make_plan(d, &p, &err);
+  if (rc != SDPA_OK) return set_error(rc, err);
+  const std::string s = sdpa::describe(d, p);
+  const size_t n = s.size() < len - 1 ? s.size() : len - 1;
+  std::memcpy(buf, s.data(), n);
+  buf[n] = '\0';
+  return ok();
+}
+
+int sdpa_forward(const sdpa_desc_t* d, const void* q, const void* k, const void* v, void* o, float* lse,
+                 void* workspace, size_t workspace_bytes, sdpa_stream_t stream) {
+  if (!q || !k || !v || !o) return set_error(SDPA_E_NULL, "q, k, v and o must be non-NULL device pointers");
+  sdpa::Plan p;
+  std::string err;
+  int rc = sdpa::make_plan(d, &p, &err);
+  if (rc != SDPA_OK) return set_error(rc, err);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return set_error(SDPA_E_STRIDE, "q, k, v and o must be 16-byte aligned");
+  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u))
+    return set_error(SDPA_E_STRIDE, "lse must be 4-byte aligned");
+  if (p.workspace > 0) {
+    if (!workspace || workspace_bytes < p.workspace)
+      return set_error(SDPA_E_WORKSPACE, "the plan needs a workspace of " + std::to_string(p.workspace) +
+                                             " bytes (got " + std::to_string(workspace_bytes) + ")");
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+      return set_error(SDPA_E_WORKSPACE, "workspace must be 256-byte aligned");
+  }
+  rc = check_device(&err);
+  if (rc != SDPA_OK) return set_error(rc, err);
+
+  sdpa::AttnArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  for (int j = 0; j < 3; ++j) {
+    a.qs[j] = d->q_stride[j];
+    a.ks[j] = d->k_stride[j];
+    a.vs[j] = d->v_stride[j];
+    a.os[j] = d->o_stride[j];
+  }
+  a.B = (int)d->batch;
+  a.Hq = (int)d->heads_q;
+  a.Hkv = (int)d->heads_kv;
+  a.Lq = (int)d->len_q;
+  a.Lk = (int)d->len_k;
+  a.dqk = (int)d->dim_qk;
+  a.dv = (int)d->dim_v;
+  a.G = (int)(d->heads_q / d->heads_kv);
+  a.R = a.G * a.Lq;
+  a.off = a.Lk - a.Lq;
+  a.mask = p.mask;
+  a.window = p.window;
+  a.c = (float)((double)d->scale * 1.4426950408889634074);  // log2(e)
+  a.splits = p.splits;
+  a.row_tiles = p.row_tiles;
+  a.heavy_first = p.mask != sdpa::MASK_NONE && p.row_tiles > 1;
+  if (p.splits > 1) {
+    const size_t rows_total = (size_t)d->batch * d->heads_kv * a.R * p.splits;
+    const size_t o_bytes = (rows_total * (size_t)d->dim_v * 4 + 255) / 256 * 256;
+    a.ws_o = static_cast<float*>(workspace);
+    a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes);
+  }
+
+  const int fam = p.rows_per_wg == 32 ? 2 : (p.rows_per_wg == 64 ? 1 : 0);
+  using L = int (*)(const sdpa::Plan&, const sdpa::AttnArgs&, void*, std::string*);
+  static const L table[3][3] = {
+      {sdpa::launch_attn_f32_prefill, sdpa::launch_attn_f32_short, sdpa::launch_attn_f32_decode},
+      {sdpa::launch_attn_f16_prefill, sdpa::launch_attn_f16_short, sdpa::launch_attn_f16_decode},
+      {sdpa::launch_attn_bf16_prefill, sdpa::launch_attn_bf16_short, sdpa::launch_attn_bf16_decode},
+  };
+  rc = table[p.dtype][fam](p, a, stream, &err);
+  if (rc != SDPA_OK) return set_error(rc, err);
+  if (p.splits > 1) {
+    sdpa::CombineArgs c;
+    c.ws_o = a.ws_o;
+    c.ws_ml = a.ws_ml;
+    c.o = o;
+    c.lse = lse;
+    for (int j = 0; j < 3; ++j) c.os[j] = d->o_stride[j];
+    c.B = a.B;
+    c.Hq = a.Hq;
+    c.Hkv = a.Hkv;
+    c.Lq = a.Lq;
+    c.dv = a.dv;
+    c.G = a.G;
+    c.R = a.R;
+    c.splits = p.splits;
+    rc = sdpa::launch_combine(p, c, stream, &err);
+    if (rc != SDPA_OK) return set_error(rc, err);
+  }
+  return ok();
+}
+
+const char* sdpa_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

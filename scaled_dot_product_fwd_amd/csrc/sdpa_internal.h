@@ -1,0 +1,97 @@
+// Internal host/device interface of libsdpa_fwd: kernel arguments, the plan
+// the host builds for a call, and the launchers the instantiation units export.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+
+#include "../../include/sdpa.h"
+
+namespace sdpa {
+
+// Mask kinds after canonicalisation (see plan.cpp).
+enum : int { MASK_NONE = 0, MASK_CAUSAL = 1, MASK_WINDOW = 2 };
+
+// Arguments of the split / unsplit attention kernel.  Passed by value.
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;          // nullable
+  float* ws_o;         // split partial outputs [z][r][split][dv] (unnormalised)
+  float* ws_ml;        // split partial (m, l) pairs [z][r][split][2], m in log2 units
+  int64_t qs[3], ks[3], vs[3], os[3];  // element strides of (batch, head, position)
+  int B, Hq, Hkv, Lq, Lk, dqk, dv, G;
+  int R;               // packed rows per KV head = G * Lq; row r -> (g = r % G, i = r / G)
+  int off;             // Lk - Lq: absolute key position of query row i is i + off
+  int mask;            // canonical mask kind
+  int window;          // window size when mask == MASK_WINDOW
+  float c;             // scale * log2(e): scores live in log2 units on the device
+  int splits;          // key splits per row tile (1: normalise in place)
+  int row_tiles;       // ceil(R / rows per workgroup)
+  int heavy_first;     // causal/window prefill: visit the longest row tiles first
+};
+
+// Arguments of the split combine kernel.
+struct CombineArgs {
+  const float* ws_o;
+  const float* ws_ml;
+  void* o;
+  float* lse;
+  int64_t os[3];
+  int B, Hq, Hkv, Lq, dv, G, R, splits;
+};
+
+// Kernel family = how the waves of a workgroup divide the work.
+struct Family {
+  int nwq;   // waves stacked along query rows (32 rows each)
+  int nwk;   // waves splitting each key block between them
+  int bkw;   // keys per wave per iteration (multiple of 32)
+};
+
+struct Plan {
+  int dtype;
+  int dqk_pad, dv_pad;   // head dims rounded up to the instantiated tile dims
+  Family fam;
+  int rows_per_wg;       // 32 * nwq
+  int row_tiles;
+  int splits;
+  int mask, window;      // canonical mask
+  int64_t grid;          // workgroups of the attention kernel
+  int64_t combine_grid;  // workgroups of the combine kernel (0 when unsplit)
+  size_t workspace;      // bytes
+  size_t lds_bytes;      // static LDS of the chosen attention kernel
+};
+
+// Validation + planning (plan.cpp).  Returns SDPA_OK or an error status and
+// fills *err with the violated constraint.
+int make_plan(const sdpa_desc_t* d, Plan* plan, std::string* err);
+std::string describe(const sdpa_desc_t* d, const Plan& p);
+
+// Launchers, one per (element type, kernel family) instantiation unit.
+// Return SDPA_OK, SDPA_E_HEAD_DIM when no kernel is instantiated for the plan,
+// or SDPA_E_HIP with *err set when the launch fails.
+#define SDPA_DECLARE_LAUNCH(NAME) \
+  int NAME(const Plan& p, const AttnArgs& a, void* stream, std::string* err);
+SDPA_DECLARE_LAUNCH(launch_attn_bf16_prefill)
+SDPA_DECLARE_LAUNCH(launch_attn_bf16_short)
+SDPA_DECLARE_LAUNCH(launch_attn_bf16_decode)
+SDPA_DECLARE_LAUNCH(launch_attn_f16_prefill)
+SDPA_DECLARE_LAUNCH(launch_attn_f16_short)
+SDPA_DECLARE_LAUNCH(launch_attn_f16_decode)
+SDPA_DECLARE_LAUNCH(launch_attn_f32_prefill)
+SDPA_DECLARE_LAUNCH(launch_attn_f32_short)
+SDPA_DECLARE_LAUNCH(launch_attn_f32_decode)
+#undef SDPA_DECLARE_LAUNCH
+int launch_combine(const Plan& p, const CombineArgs& a, void* stream, std::string* err);
+
+// Kernel family for a row tile of `rows_per_wg` rows (32, 64 or 128).
+Family family_for(int rows_per_wg, int dqk_pad, int dv_pad);
+
+// LDS bytes of an attention kernel instance (host mirror of the kernel's
+// static layout, used by the planner's capacity check).
+size_t attn_lds_bytes(int dtype, int dqk_pad, int dv_pad, const Family& f);
+
+}  // namespace sdpa

@@ -1,0 +1,172 @@
+"""C-ABI boundary on the host (no GPU): exports, validation, planning.
+
+Every validation error is forced from the CPU; none of these calls reaches a
+kernel launch (validation runs before any HIP call, and the device check comes
+last).  Error messages must name the violated constraint, as the force-fused
+contract of mlx PR #4185 "Add force_fused option to
+scaled_dot_product_attention" (Validation) asks.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import scaled_dot_product_fwd_amd as sdpa
+from scaled_dot_product_fwd_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "sdpa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sdpa_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    declared = _declared_functions()
+    assert set(declared) == set(_lib.EXPORTED)
+    for name in declared:
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_desc_init_contiguous_strides():
+    d = sdpa.sdpa_desc_init(2, 8, 2, 5, 7, 64, 32, _lib.SDPA_BF16)
+    assert list(d.q_stride) == [8 * 5 * 64, 5 * 64, 64]
+    assert list(d.k_stride) == [2 * 7 * 64, 7 * 64, 64]
+    assert list(d.v_stride) == [2 * 7 * 32, 7 * 32, 32]
+    assert list(d.o_stride) == [8 * 5 * 32, 5 * 32, 32]
+    assert d.mask == 0 and d.window == 0 and d.num_splits == 0
+    assert abs(d.scale - 0.125) < 1e-9
+
+
+def _desc(b=1, hq=4, hkv=2, lq=8, lk=16, dqk=64, dv=64, dtype=_lib.SDPA_BF16, **kw):
+    return sdpa.make_desc((b, hq, lq, dqk), (b, hkv, lk, dqk), (b, hkv, lk, dv), dtype, **kw)
+
+
+def _status(fn, *args):
+    with pytest.raises(sdpa.SdpaError) as ei:
+        fn(*args)
+    return str(ei.value)
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(lq=0), "SDPA_E_SHAPE", "every size must be >= 1"),
+    (dict(hq=6, hkv=4), "SDPA_E_SHAPE", "multiple of heads_kv"),
+    (dict(dqk=512, dv=512), "SDPA_E_HEAD_DIM", "Dqk=512"),
+    (dict(dqk=72, dv=76), "SDPA_E_HEAD_DIM", "multiples of 8"),
+    (dict(dqk=160, dv=160, dtype=_lib.SDPA_F32), "SDPA_E_HEAD_DIM", "float32 supports head dims up to 128"),
+    (dict(dtype=7), "SDPA_E_DTYPE", "dtype"),
+    (dict(lq=17, lk=16, mask="causal"), "SDPA_E_MASK", "causal masking requires Lq <= Lk"),
+    (dict(lq=17, lk=16, mask="window", window_size=4), "SDPA_E_MASK", "Lq <= Lk"),
+    (dict(mask="window", window_size=0), "SDPA_E_MASK", "window >= 1"),
+    (dict(mask="causal", window_size=3), "SDPA_E_MASK", "window must be 0"),
+    (dict(scale=float("inf")), "SDPA_E_SCALE", "finite"),
+    (dict(scale=float("nan")), "SDPA_E_SCALE", "finite"),
+    (dict(q_stride=(8 * 8 * 64, 8 * 64, 60)), "SDPA_E_STRIDE", "q_stride[2]"),
+    (dict(num_splits=-1), "SDPA_E_PLAN", "num_splits"),
+    (dict(row_tile=48), "SDPA_E_PLAN", "row_tile"),
+])
+def test_validation_errors_name_the_constraint(kw, code, needle):
+    d = _desc(**kw)
+    msg = _status(sdpa.sdpa_workspace_bytes, d)
+    assert msg.startswith(code), msg
+    assert needle in msg, msg
+    msg2 = _status(sdpa.sdpa_describe_plan, d)
+    assert msg2.startswith(code)
+    # forward validates before touching the device: same error, nothing launched
+    msg3 = _status(sdpa.sdpa_forward, d, 16, 16, 16, 16, None, None, 0, None)
+    assert msg3.startswith(code)
+
+
+def test_validation_errors_are_value_errors():
+    with pytest.raises(ValueError):
+        sdpa.sdpa_workspace_bytes(_desc(dqk=512, dv=512))
+
+
+def test_forward_null_pointers():
+    msg = _status(sdpa.sdpa_forward, _desc(), 0, 16, 16, 16, None, None, 0, None)
+    assert msg.startswith("SDPA_E_NULL")
+
+
+def test_forward_unaligned_pointer():
+    msg = _status(sdpa.sdpa_forward, _desc(), 16 + 8, 16, 16, 16, None, None, 0, None)
+    assert msg.startswith("SDPA_E_STRIDE") and "16-byte aligned" in msg
+
+
+def test_forward_missing_workspace():
+    d = _desc(hq=64, hkv=4, lq=1, lk=32768, dqk=192, dv=128, mask="causal")
+    need = sdpa.sdpa_workspace_bytes(d)
+    assert need > 0
+    msg = _status(sdpa.sdpa_forward, d, 16, 16, 16, 16, None, None, 0, None)
+    assert msg.startswith("SDPA_E_WORKSPACE") and str(need) in msg
+    msg = _status(sdpa.sdpa_forward, d, 16, 16, 16, 16, None, 256, need - 1, None)
+    assert msg.startswith("SDPA_E_WORKSPACE")
+
+
+def test_last_error_is_cleared_by_success():
+    _status(sdpa.sdpa_workspace_bytes, _desc(dqk=512, dv=512))
+    assert sdpa.sdpa_last_error() != ""
+    sdpa.sdpa_workspace_bytes(_desc())
+    assert sdpa.sdpa_last_error() == ""
+
+
+def _plan(**kw):
+    s = sdpa.sdpa_describe_plan(_desc(**kw))
+    return dict(tok.split("=", 1) for tok in s.split())
+
+
+def test_plan_decode_config_splits_keys():
+    for hkv in (4, 8):
+        for lk in (256, 1024, 4096, 8192, 16384, 32768):
+            p = _plan(hq=64, hkv=hkv, lq=1, lk=lk, dqk=192, dv=128, mask="causal")
+            assert p["family"] == "decode"
+            assert p["mask"] == "none"  # causal with one query sees every key
+            assert p["dqk"] == "192->192" and p["dv"] == "128->128"
+            splits = int(p["splits"])
+            assert splits >= 1 and splits <= (lk + 127) // 128
+            if lk >= 8192:
+                assert int(p["grid"]) >= 256  # the whole chip streams the keys
+            assert (int(p["workspace"]) > 0) == (splits > 1)
+
+
+@pytest.mark.parametrize("lq,fam", [(1, "decode"), (8, "decode"), (12, "short"), (16, "short"),
+                                    (24, "prefill"), (64, "prefill")])
+def test_plan_verify_window_family(lq, fam):
+    p = _plan(hq=32, hkv=8, lq=lq, lk=16384, dqk=128, dv=128, dtype=_lib.SDPA_F16)
+    assert p["family"] == fam
+    assert int(p["grid"]) >= 256
+
+
+def test_plan_prefill_configs_do_not_split():
+    p = _plan(hq=20, hkv=20, lq=1500, lk=1500, dqk=64, dv=64)
+    assert p["family"] == "prefill" and p["splits"] == "1" and p["workspace"] == "0"
+    p = _plan(hq=16, hkv=16, lq=4096, lk=4096, dqk=72, dv=72)
+    assert p["dqk"] == "72->96" and p["dv"] == "72->96"
+    p = _plan(hq=16, hkv=2, lq=32768, lk=32768, dqk=256, dv=256, mask="causal")
+    assert p["splits"] == "1" and p["mask"] == "causal"
+
+
+def test_plan_canonical_masks():
+    assert _plan(lq=8, lk=16, mask="window", window_size=16)["mask"] == "causal"
+    assert _plan(lq=8, lk=16, mask="window", window_size=100)["mask"] == "causal"
+    assert _plan(lq=8, lk=16, mask="window", window_size=15)["mask"] == "window(15)"
+    assert _plan(lq=1, lk=16, mask="causal")["mask"] == "none"
+
+
+def test_plan_overrides():
+    p = _plan(hq=32, hkv=8, lq=4, lk=4096, num_splits=3, row_tile=128)
+    assert p["splits"] == "3" and p["rows_per_wg"] == "128" and p["family"] == "prefill"
+    p = _plan(hq=32, hkv=8, lq=4, lk=4096, num_splits=1)
+    assert p["splits"] == "1" and p["workspace"] == "0"
+
+
+def test_forward_without_gpu_tensors_raises():
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(1, 1, 4, 64)
+    with pytest.raises(ValueError, match="there is no CPU path"):
+        sdpa.forward(q, q, q)

@@ -1,0 +1,199 @@
+"""GPU parity of the fused forward against the float64 oracle, whole outputs.
+
+Sizes are small enough for the oracle to finish in seconds but span several
+row tiles and key blocks with ragged tails.  Every case prints its parameters
+before touching the GPU.
+"""
+
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import scaled_dot_product_fwd_amd as sdpa
+from gpu_cases import TOL_O, check_full, run_gpu
+from scaled_dot_product_fwd_amd.synth import default_scale, make_qkv
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print("CASE", *a, flush=True)
+
+
+def test_tiny_fp32_config():
+    """B=1, Hq=Hkv=4, Lq=Lk=128, D=64, float32, no mask, scale 1/sqrt(64)."""
+    _say("tiny fp32 config")
+    check_full(1, 4, 4, 128, 128, 64, 64, "f32", "none", 0, seed=1000)
+
+
+CASES = [
+    # b, hq, hkv, lq, lk, dqk, dv, dtype, mask, window
+    (1, 4, 2, 200, 200, 64, 64, "bf16", "causal", 0),
+    (2, 4, 1, 77, 300, 128, 128, "f16", "causal", 0),
+    (1, 2, 2, 300, 300, 72, 72, "bf16", "none", 0),
+    (1, 2, 1, 150, 333, 96, 96, "bf16", "window", 37),
+    (1, 2, 2, 257, 257, 8, 8, "bf16", "none", 0),
+    (1, 2, 2, 130, 130, 80, 80, "f16", "causal", 0),
+    (1, 2, 1, 140, 140, 256, 256, "bf16", "causal", 0),
+    (1, 2, 2, 129, 129, 160, 160, "f16", "window", 64),
+    (1, 2, 2, 100, 100, 224, 224, "bf16", "none", 0),
+    (1, 32, 2, 1, 1000, 192, 128, "bf16", "none", 0),
+    (1, 16, 1, 3, 777, 192, 128, "bf16", "causal", 0),
+    (1, 8, 8, 5, 400, 192, 192, "f16", "causal", 0),
+    (1, 4, 1, 12, 2000, 128, 128, "f16", "none", 0),
+    (1, 4, 1, 8, 2000, 128, 128, "f16", "none", 0),
+    (1, 4, 1, 24, 1500, 128, 128, "f16", "causal", 0),
+    (1, 4, 2, 64, 64, 64, 64, "f32", "causal", 0),
+    (2, 4, 2, 70, 190, 128, 128, "f32", "window", 50),
+    (1, 4, 4, 33, 33, 96, 96, "f32", "none", 0),
+    (1, 8, 2, 1, 4096, 32, 64, "f32", "none", 0),
+    (1, 3, 1, 40, 500, 64, 32, "bf16", "none", 0),
+    (1, 2, 2, 96, 96, 16, 48, "f16", "causal", 0),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "-".join(str(x) for x in c))
+def test_small_cases(case):
+    b, hq, hkv, lq, lk, dqk, dv, dt, mask, w = case
+    _say(case)
+    check_full(b, hq, hkv, lq, lk, dqk, dv, dt, mask, w, seed=zlib.crc32(repr(case).encode()) % 10000)
+
+
+@pytest.mark.parametrize("lk", [1, 2, 63, 64, 65, 127, 129])
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_short_key_lengths(lk, dt):
+    _say("short lk", lk, dt)
+    check_full(1, 4, 2, 1, lk, 64, 64, dt, "none", 0, seed=lk)
+    lq = min(lk, 5)
+    check_full(1, 4, 2, lq, lk, 64, 64, dt, "causal", 0, seed=lk + 1)
+
+
+@pytest.mark.parametrize("w", [1, 2, 63, 64, 65, 127, 128, 129, 1000])
+def test_window_edges(w):
+    """Unaligned and aligned window edges, including a window of one key."""
+    _say("window", w)
+    check_full(1, 2, 1, 260, 300, 64, 64, "bf16", "window", w, seed=w)
+
+
+def test_window_1000_unaligned_prefill():
+    """A window whose lower edge is not block aligned (W=1000) over several tiles."""
+    _say("window 1000 prefill")
+    check_full(1, 2, 2, 2100, 2100, 64, 64, "bf16", "window", 1000, seed=5)
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 5, 8, 16])
+def test_forced_splits_agree(splits):
+    _say("splits", splits)
+    check_full(1, 8, 2, 4, 3000, 128, 128, "bf16", "causal", 0, seed=77, num_splits=splits)
+
+
+@pytest.mark.parametrize("row_tile", [32, 64, 128])
+@pytest.mark.parametrize("mask,w", [("none", 0), ("causal", 0), ("window", 100)])
+def test_forced_row_tiles_agree(row_tile, mask, w):
+    _say("row tile", row_tile, mask, w)
+    check_full(1, 4, 2, 90, 700, 64, 64, "f16", mask, w, seed=row_tile, row_tile=row_tile)
+
+
+def test_strided_kv_cache_view():
+    """K/V are views into a cache with capacity beyond Lk (non-contiguous head stride)."""
+    _say("strided kv cache")
+    from oracle import sdpa_ref
+    cap, lk, lq = 512, 300, 7
+    q, kc, vc = make_qkv(1, 8, 2, lq, cap, 128, 128, torch.bfloat16, 42)
+    k, v = kc[:, :, :lk], vc[:, :, :lk]
+    dev = torch.device("cuda", 0)
+    kd, vd = kc.to(dev)[:, :, :lk], vc.to(dev)[:, :, :lk]
+    assert not kd.is_contiguous()
+    o, lse = sdpa.forward(q.to(dev), kd, vd, mask="causal", return_lse=True)
+    ro, rl = sdpa_ref(q, k, v, default_scale(128), "causal", 0)
+    assert float(np.abs(o.double().cpu().numpy() - ro).max()) <= TOL_O[torch.bfloat16]
+    assert float(np.abs(lse.double().cpu().numpy() - rl).max()) <= 1e-4
+
+
+def test_batch_two_gqa_eight():
+    _say("batch 2, G=8")
+    check_full(2, 16, 2, 33, 257, 64, 64, "bf16", "causal", 0, seed=9)
+
+
+def test_large_magnitude_queries_stay_finite():
+    _say("large q")
+    q, k, v = make_qkv(1, 4, 2, 64, 500, 64, 64, torch.bfloat16, 3)
+    q = (q.float() * 30).to(torch.bfloat16)
+    o, lse = run_gpu(q, k, v, default_scale(64), "causal", 0)
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    from oracle import sdpa_ref
+    ro, rl = sdpa_ref(q, k, v, default_scale(64), "causal", 0)
+    assert float(np.abs(o - ro).max()) <= 2e-2
+    assert float(np.abs(lse - rl).max() / max(1.0, np.abs(rl).max())) <= 1e-5
+
+
+def test_monotone_scores_running_max_changes_every_block():
+    """Keys ordered so the running max rises (then falls) block after block."""
+    _say("monotone scores")
+    from oracle import sdpa_ref
+    lk, d = 1024, 64
+    q = torch.ones(1, 1, 2, d)
+    ramp = torch.linspace(-4, 4, lk)[:, None].repeat(1, d) / d
+    for sign in (1.0, -1.0):
+        k = (sign * ramp)[None, None].to(torch.float16)
+        v = torch.randn(1, 1, lk, d, generator=torch.Generator().manual_seed(1)).to(torch.float16)
+        qq = q.to(torch.float16)
+        o, lse = run_gpu(qq, k, v, 1.0, "none", 0)
+        ro, rl = sdpa_ref(qq, k, v, 1.0, "none", 0)
+        assert float(np.abs(o - ro).max()) <= 5e-3
+        assert float(np.abs(lse - rl).max()) <= 1e-4
+
+
+def test_single_spike_key_in_last_split():
+    _say("spike in last split")
+    from oracle import sdpa_ref
+    q, k, v = make_qkv(1, 8, 1, 1, 4000, 128, 128, torch.bfloat16, 11)
+    k[0, 0, 3990] = (q[0, 0, 0].float() * 3).to(torch.bfloat16)
+    o, lse = run_gpu(q, k, v, default_scale(128), "none", 0, num_splits=8)
+    ro, rl = sdpa_ref(q, k, v, default_scale(128), "none", 0)
+    assert float(np.abs(o - ro).max()) <= 2e-2
+    assert float(np.abs(lse - rl).max()) <= 1e-4
+
+
+def test_fixed_plan_is_bitwise_deterministic():
+    _say("determinism")
+    q, k, v = make_qkv(1, 8, 2, 16, 3000, 128, 128, torch.bfloat16, 21)
+    a = run_gpu(q, k, v, default_scale(128), "none", 0)
+    b = run_gpu(q, k, v, default_scale(128), "none", 0)
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
+
+
+def test_negative_and_zero_scale():
+    _say("scale sign")
+    from oracle import sdpa_ref
+    q, k, v = make_qkv(1, 2, 1, 20, 200, 64, 64, torch.float16, 31)
+    for scale in (-0.3, 0.0):
+        o, lse = run_gpu(q, k, v, scale, "causal", 0)
+        ro, rl = sdpa_ref(q, k, v, scale, "causal", 0)
+        assert float(np.abs(o - ro).max()) <= 5e-3
+        assert float(np.abs(lse - rl).max()) <= 1e-4
+
+
+def test_output_without_lse():
+    _say("no lse")
+    q, k, v = make_qkv(1, 4, 4, 50, 60, 64, 64, torch.bfloat16, 2)
+    dev = torch.device("cuda", 0)
+    o = sdpa.forward(q.to(dev), k.to(dev), v.to(dev), mask="causal")
+    from oracle import sdpa_ref
+    ro, _ = sdpa_ref(q, k, v, default_scale(64), "causal", 0)
+    assert float(np.abs(o.double().cpu().numpy() - ro).max()) <= 2e-2
+
+
+def test_error_leaves_output_untouched():
+    _say("error path")
+    dev = torch.device("cuda", 0)
+    q = torch.randn(1, 2, 9, 64, device=dev, dtype=torch.bfloat16)
+    k = torch.randn(1, 2, 8, 64, device=dev, dtype=torch.bfloat16)
+    out = torch.full((1, 2, 9, 64), 7.0, device=dev, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="Lq <= Lk"):
+        sdpa.forward(q, k, k, mask="causal", out=out)
+    torch.cuda.synchronize()
+    assert bool((out == 7.0).all())
