@@ -1,0 +1,410 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused SDPA forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--sweep]
+
+A step is one ``sdpa_forward`` call (validate + plan on the host, the
+attention kernel, and the split combine when the plan splits) over one batch
+of seeded synthetic N(0, 1) inputs already resident in HBM.  The default
+workload is the GQA decode with asymmetric head dims at its largest KV set:
+B=1, Hq=64, Hkv=8, Lq=1, Lk=32768, Dqk=192, Dv=128, bfloat16, causal (the
+query at the last position).  Its metric is the algorithmic KV bandwidth:
+bytes of Q + K + V + O per step over the step time.
+
+The KV set (168 MB) fits in the 256 MB Infinity Cache, so consecutive steps
+rotate over enough identical copies of K/V (> 2 x 256 MB in total) that every
+step streams its K/V from HBM, not from the cache.
+
+Printed: ONE JSON line with the metric, plus ``roofline`` (the attention
+kernel's algorithmic bytes per launch over its average duration, measured with
+HIP events recorded on the launch stream by the library's profiling hook) and
+``cpu_baseline`` (the float64 oracle timed on the host cores).
+
+``--sweep`` additionally times every shape of the five workloads and writes a
+table (stderr) and JSON (``--sweep-out``).
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "SDPA prefill TFLOP/s & decode KV GB/s on 1 MI355X, % of roofline"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+MFMA16_PEAK_TFLOPS = 2500.0  # dense bf16 / fp16 MFMA
+FP32_PEAK_TFLOPS = 157.3     # fp32 matrix
+INFINITY_CACHE = 256 << 20
+ES = {"f32": 4, "f16": 2, "bf16": 2}
+
+# Fused decode on the pages: 64 query / 8 KV heads, Lk=32768, bf16, 728 us on
+# Apple M3 Ultra (mlx PR #3637 "Enable fused SDPA vector kernel for asymmetric
+# Q/V head dims (192, 128)", second benchmark table).  Context, not a target.
+PAGES_DECODE_US = {(4, 256): 218, (4, 1024): 217, (4, 4096): 255, (4, 8192): 305, (4, 16384): 382,
+                   (4, 32768): 599, (8, 256): 207, (8, 1024): 222, (8, 4096): 288, (8, 8192): 358,
+                   (8, 16384): 444, (8, 32768): 728}
+
+
+def shape(name, b, hq, hkv, lq, lk, dqk, dv, dtype, mask, window, seed):
+    return dict(name=name, b=b, hq=hq, hkv=hkv, lq=lq, lk=lk, dqk=dqk, dv=dv, dtype=dtype,
+                mask=mask, window=window, seed=seed)
+
+
+def all_shapes():
+    """Every shape of the five workloads; seeds are 1000 * workload + index."""
+    out = [shape("tiny_f32", 1, 4, 4, 128, 128, 64, 64, "f32", "none", 0, 1000)]
+    lks = [256, 1024, 4096, 8192, 16384, 32768]
+    for j, hkv in enumerate((4, 8)):
+        for i, lk in enumerate(lks):
+            out.append(shape(f"decode_hkv{hkv}_lk{lk}", 1, 64, hkv, 1, lk, 192, 128, "bf16", "causal", 0,
+                             2000 + i + j * len(lks)))
+    lqs = [1, 2, 4, 8, 12, 16, 24, 32, 48, 64]
+    for j, lk in enumerate((16384, 32768)):
+        for i, lq in enumerate(lqs):
+            out.append(shape(f"verify_lk{lk}_lq{lq}", 1, 32, 8, lq, lk, 128, 128, "f16", "none", 0,
+                             3000 + i + j * len(lqs)))
+    out.append(shape("encoder_h20_l1500_d64", 1, 20, 20, 1500, 1500, 64, 64, "bf16", "none", 0, 4000))
+    out.append(shape("vision_h16_l1024_d72", 1, 16, 16, 1024, 1024, 72, 72, "bf16", "none", 0, 4001))
+    out.append(shape("vision_h16_l4096_d72", 1, 16, 16, 4096, 4096, 72, 72, "bf16", "none", 0, 4002))
+    for i, L in enumerate((2048, 4096, 8192)):
+        out.append(shape(f"window_l{L}_d256", 1, 16, 8, L, L, 256, 256, "bf16", "window", 1024, 5000 + i))
+    out.append(shape("causal_l32768_d256", 1, 16, 2, 32768, 32768, 256, 256, "bf16", "causal", 0, 5003))
+    return out
+
+
+SHAPES = {s["name"]: s for s in all_shapes()}
+DEFAULT = "decode_hkv8_lk32768"
+
+
+def visible_pairs(lq, lk, mask, window):
+    """Visible (query, key) pairs of one head, closed form (bottom-right aligned masks)."""
+    off = lk - lq
+    if mask == "none":
+        return lq * lk
+    if mask == "causal":
+        return lq * (lq + 1) // 2 + lq * off
+    w = window
+    # row i sees min(w, i + off + 1) keys
+    first_full = max(0, w - 1 - off)  # rows i >= first_full see w keys
+    if first_full >= lq:
+        return lq * (lq + 1) // 2 + lq * off
+    partial = first_full * (first_full + 1) // 2 + first_full * off
+    return partial + (lq - first_full) * w
+
+
+def row_visible(i, s):
+    """Keys visible to query row i (bottom-right aligned masks)."""
+    pos = s["lk"] - s["lq"] + i
+    if s["mask"] == "none":
+        return s["lk"]
+    if s["mask"] == "causal":
+        return pos + 1
+    return min(s["window"], pos + 1)
+
+
+def work(s):
+    """(algorithmic flops, algorithmic bytes) of one call."""
+    pairs = visible_pairs(s["lq"], s["lk"], s["mask"], s["window"])
+    flops = 2 * s["b"] * s["hq"] * (s["dqk"] + s["dv"]) * pairs
+    es = ES[s["dtype"]]
+    nbytes = es * s["b"] * (s["hq"] * s["lq"] * (s["dqk"] + s["dv"]) + s["hkv"] * s["lk"] * (s["dqk"] + s["dv"]))
+    return flops, nbytes
+
+
+def bound(s):
+    """'hbm' for decode-shaped calls (arithmetic intensity below the ridge), else 'mfma'."""
+    flops, nbytes = work(s)
+    peak = FP32_PEAK_TFLOPS if s["dtype"] == "f32" else MFMA16_PEAK_TFLOPS
+    ridge = peak * 1e12 / (HBM_PEAK_GBS * 1e9)
+    return "hbm" if flops / nbytes < ridge else "mfma"
+
+
+class HipEvents:
+    """hipEvent_t pairs through the HIP runtime torch already loaded."""
+
+    def __init__(self, n):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.start, self.stop = [], []
+        for _ in range(n):
+            a, b = ctypes.c_void_p(), ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(a)) or self.hip.hipEventCreate(ctypes.byref(b)):
+                raise RuntimeError("hipEventCreate failed")
+            self.start.append(a.value)
+            self.stop.append(b.value)
+
+    def elapsed_ms(self, i):
+        ms = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), self.start[i], self.stop[i]):
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def close(self):
+        for e in self.start + self.stop:
+            self.hip.hipEventDestroy(e)
+
+
+class Runner:
+    """Pre-built descriptor, buffers and workspace for repeated raw C calls."""
+
+    def __init__(self, s, kv_bytes_floor=0):
+        import torch
+
+        import scaled_dot_product_fwd_amd as sdpa
+        from scaled_dot_product_fwd_amd.synth import DTYPES, default_scale, make_qkv
+
+        self.s = s
+        self.sdpa = sdpa
+        dt = DTYPES[s["dtype"]]
+        dev = torch.device("cuda", 0)
+        q, k, v = make_qkv(s["b"], s["hq"], s["hkv"], s["lq"], s["lk"], s["dqk"], s["dv"], dt, s["seed"])
+        self.cpu = (q, k, v)
+        self.scale = default_scale(s["dqk"])
+        self.q = q.to(dev)
+        kd, vd = k.to(dev), v.to(dev)
+        set_bytes = (kd.numel() + vd.numel()) * kd.element_size()
+        nsets = 1
+        if kv_bytes_floor:
+            nsets = max(1, min(64, math.ceil(kv_bytes_floor / set_bytes)))
+        self.kv = [(kd, vd)] + [(kd.clone(), vd.clone()) for _ in range(nsets - 1)]
+        self.nsets = nsets
+        self.o = torch.empty((s["b"], s["hq"], s["lq"], s["dv"]), dtype=dt, device=dev)
+        self.lse = torch.empty((s["b"], s["hq"], s["lq"]), dtype=torch.float32, device=dev)
+        self.desc = sdpa.make_desc(self.q.shape, kd.shape, vd.shape, sdpa._dtype_code(dt), scale=self.scale,
+                                   mask=s["mask"], window_size=s["window"])
+        self.plan = sdpa.sdpa_describe_plan(self.desc)
+        self.ws_bytes = sdpa.sdpa_workspace_bytes(self.desc)
+        self.ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=dev)
+        self.stream = torch.cuda.current_stream(dev).cuda_stream
+        lib = sdpa.load()
+        self._fwd = lib.sdpa_forward
+        self._prof = lib.sdpa_set_profile_events
+        self._descref = ctypes.byref(self.desc)
+        self._args = [(self.q.data_ptr(), k_.data_ptr(), v_.data_ptr(), self.o.data_ptr(), self.lse.data_ptr(),
+                       self.ws.data_ptr() if self.ws_bytes else None, self.ws_bytes, self.stream)
+                      for k_, v_ in self.kv]
+
+    def step(self, i, events=None, j=None):
+        if events is not None:
+            self._prof(events.start[j], events.stop[j])
+        rc = self._fwd(self._descref, *self._args[i % self.nsets])
+        if rc:
+            self.sdpa._lib.check(rc)
+
+    def output(self):
+        return self.o, self.lse
+
+
+def time_steps(r, steps, warmup):
+    """Warm up, then time exactly `steps` steps; returns (ms_per_step, kernel_ms list)."""
+    import torch
+
+    ev = HipEvents(steps)
+    for i in range(warmup):
+        r.step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        r.step(i, ev, i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kms = [ev.elapsed_ms(i) for i in range(steps)]
+    ev.close()
+    return (t1 - t0) * 1e3 / steps, kms
+
+
+def cpu_baseline(s, runner, budget_s=12.0):
+    """The float64 oracle on the host cores, on a bounded sample of the workload.
+
+    Whole KV groups (all query heads sharing one KV head) are run one after
+    another until the time budget is spent; when even one group would blow the
+    budget, evenly spaced query rows are recomputed one by one instead.  The
+    work done is scaled to the metric's unit.
+    """
+    from oracle import sdpa_ref, sdpa_ref_rows
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    q, k, v = runner.cpu
+    g = s["hq"] // s["hkv"]
+    flops, nbytes = work(s)
+    group_flops = flops / s["hkv"]
+    t_total, frac, sample = 0.0, 0.0, ""
+    if group_flops < 20e9 * budget_s:  # one group fits the budget at a modest 20 GFLOP/s
+        heads = 0
+        t_start = time.perf_counter()
+        while time.perf_counter() - t_start < budget_s and heads < 50 * s["hq"]:
+            kvh = (heads // g) % s["hkv"]
+            hs = slice(kvh * g, (kvh + 1) * g)
+            t0 = time.perf_counter()
+            sdpa_ref(q[:, hs], k[:, kvh:kvh + 1], v[:, kvh:kvh + 1], runner.scale, s["mask"], s["window"])
+            t_total += time.perf_counter() - t0
+            heads += g
+        frac = heads / s["hq"]
+        sample = f"{heads} query heads in whole KV groups ({frac:.2f} of one step)"
+    else:
+        rows_per_head = s["lq"]
+        picks, n = [], 0
+        stride = max(1, (s["hq"] * rows_per_head) // 4096)
+        for t in range(0, s["hq"] * rows_per_head, stride):
+            picks.append((0, t // rows_per_head, t % rows_per_head))
+        done_flops = 0
+        t_start = time.perf_counter()
+        for n0 in range(0, len(picks), 64):
+            chunk = picks[n0:n0 + 64]
+            t0 = time.perf_counter()
+            sdpa_ref_rows(q, k, v, runner.scale, s["mask"], s["window"], chunk)
+            t_total += time.perf_counter() - t0
+            for (_, _, i) in chunk:
+                done_flops += 2 * (s["dqk"] + s["dv"]) * row_visible(i, s)
+            n += len(chunk)
+            if time.perf_counter() - t_start > budget_s:
+                break
+        frac = done_flops / flops
+        sample = f"{n} evenly spaced query rows recomputed one by one ({frac:.2e} of one step)"
+    sec_per_step = t_total / frac
+    if bound(s) == "hbm":
+        value, unit = nbytes / sec_per_step / 1e9, "GB/s"
+    else:
+        value, unit = flops / sec_per_step / 1e12, "TFLOP/s"
+    return {"value": round(value, 6), "unit": unit, "cores": int(cores), "kind": "oracle",
+            "sample": f"{sample} of the same workload, float64 numpy, {t_total:.1f} s"}
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "scaled_dot_product_fwd_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(name):
+    """HBM bytes per launch from the committed counter summary, if it matches the sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def measure(s, steps, warmup):
+    import torch
+
+    floor = 3 * INFINITY_CACHE if bound(s) == "hbm" else 0
+    r = Runner(s, floor)
+    ms, kms = time_steps(r, steps, warmup)
+    flops, nbytes = work(s)
+    kmean = sum(kms) / len(kms)
+    kms_sorted = sorted(kms)
+    res = dict(s)
+    res.update(plan=r.plan, kv_sets=r.nsets, ms_per_step=ms, kernel_ms_mean=kmean,
+               kernel_ms_p10=kms_sorted[len(kms) // 10], kernel_ms_p50=kms_sorted[len(kms) // 2],
+               kernel_ms_p90=kms_sorted[(9 * len(kms)) // 10], flops=flops, bytes=nbytes, bound=bound(s))
+    if res["bound"] == "hbm":
+        res["achieved"] = nbytes / (kmean * 1e-3) / 1e9
+        res["peak"] = HBM_PEAK_GBS
+        res["unit"] = "GB/s"
+        res["step_value"] = nbytes / (ms * 1e-3) / 1e9
+    else:
+        res["achieved"] = flops / (kmean * 1e-3) / 1e12
+        res["peak"] = FP32_PEAK_TFLOPS if s["dtype"] == "f32" else MFMA16_PEAK_TFLOPS
+        res["unit"] = "TFLOP/s"
+        res["step_value"] = flops / (ms * 1e-3) / 1e12
+    res["frac"] = res["achieved"] / res["peak"]
+    torch.cuda.synchronize()
+    return res, r
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT, choices=sorted(SHAPES))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", action="store_true", help="also time every shape of the five workloads")
+    ap.add_argument("--sweep-out", default=os.path.join("gpurun_out", "sweep.json"))
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU (got --gpus {args.gpus}); this build has no multi-GPU path",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    import scaled_dot_product_fwd_amd as sdpa
+
+    sdpa.load()
+    s = SHAPES[args.workload]
+    res, runner = measure(s, args.steps, args.warmup)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(s, runner)
+    vs = None
+    if s["name"].startswith("decode_"):
+        pages_us = PAGES_DECODE_US[(s["hkv"], s["lk"])]
+        vs = res["step_value"] / (res["bytes"] / (pages_us * 1e-6) / 1e9)
+    line = {
+        "metric": METRIC,
+        "value": round(res["step_value"], 3),
+        "unit": res["unit"],
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None if vs is None else round(vs, 3),
+        "dtype": s["dtype"],
+        "data": "synthetic",
+        "config": {"workload": s["name"], "B": s["b"], "Hq": s["hq"], "Hkv": s["hkv"], "Lq": s["lq"],
+                   "Lk": s["lk"], "Dqk": s["dqk"], "Dv": s["dv"], "mask": s["mask"], "window": s["window"],
+                   "kv_sets": res["kv_sets"], "plan": res["plan"]},
+        "roofline": {"bound": res["bound"], "achieved": round(res["achieved"], 3), "peak": res["peak"],
+                     "unit": res["unit"], "frac": round(res["frac"], 4),
+                     "traffic": traffic_from_profiles(s["name"]),
+                     "kernel_us_mean": round(res["kernel_ms_mean"] * 1e3, 3)},
+        "cpu_baseline": cpu,
+    }
+    if args.sweep:
+        rows = []
+        for sh in all_shapes():
+            print(f"sweep {sh['name']}", file=sys.stderr, flush=True)
+            r, rr = measure(sh, 20, 5)
+            del rr
+            torch.cuda.empty_cache()
+            rows.append({k: r[k] for k in ("name", "plan", "kv_sets", "ms_per_step", "kernel_ms_mean",
+                                           "kernel_ms_p10", "kernel_ms_p50", "kernel_ms_p90", "flops",
+                                           "bytes", "bound", "achieved", "peak", "unit", "frac",
+                                           "step_value")})
+            print(f"  {sh['name']:28s} kernel {r['kernel_ms_mean'] * 1e3:9.2f} us  step {r['ms_per_step'] * 1e3:9.2f} us"
+                  f"  {r['achieved']:9.2f} {r['unit']:8s} {100 * r['frac']:6.2f}% of {r['bound']}",
+                  file=sys.stderr, flush=True)
+        os.makedirs(os.path.dirname(args.sweep_out) or ".", exist_ok=True)
+        with open(args.sweep_out, "w") as f:
+            json.dump(rows, f, indent=1)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

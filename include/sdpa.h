@@ -115,6 +115,13 @@ int sdpa_forward(const sdpa_desc_t* desc, const void* q, const void* k, const vo
  * tile, splits, grid, workspace) into buf.  Host only. */
 int sdpa_describe_plan(const sdpa_desc_t* desc, char* buf, size_t len);
 
+/* Measurement hook: the next sdpa_forward call on this thread records the
+ * two hipEvent_t `start` and `stop` on its stream immediately before and
+ * after the launch of its attention kernel (the split combine, when present,
+ * comes after `stop`), then forgets them.  Passing NULL for both cancels a
+ * pending pair.  The events stay owned by the caller. */
+int sdpa_set_profile_events(void* start, void* stop);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char* sdpa_last_error(void);
 

@@ -19,10 +19,11 @@ from typing import Optional, Tuple, Union
 from ._lib import (SDPA_BF16, SDPA_F16, SDPA_F32, SDPA_MASK_CAUSAL, SDPA_MASK_NONE,  # noqa: F401
                    SDPA_MASK_WINDOW, SdpaError, SdpaRuntimeError, SdpaValueError, load,
                    sdpa_desc_init, sdpa_desc_t, sdpa_describe_plan, sdpa_forward,
-                   sdpa_last_error, sdpa_workspace_bytes)
+                   sdpa_last_error, sdpa_set_profile_events, sdpa_workspace_bytes)
 
 __all__ = ["forward", "make_desc", "plan_for", "workspace_for", "sdpa_forward",
            "sdpa_workspace_bytes", "sdpa_describe_plan", "sdpa_last_error", "sdpa_desc_init",
+           "sdpa_set_profile_events",
            "SdpaError", "SdpaValueError", "SdpaRuntimeError"]
 
 _MASKS = {"none": SDPA_MASK_NONE, "causal": SDPA_MASK_CAUSAL, "window": SDPA_MASK_WINDOW}

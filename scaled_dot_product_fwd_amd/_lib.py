@@ -32,7 +32,7 @@ STATUS = {
 STATUS_CODE = {v: k for k, v in STATUS.items()}
 
 EXPORTED = ("sdpa_desc_init", "sdpa_workspace_bytes", "sdpa_forward", "sdpa_describe_plan",
-            "sdpa_last_error")
+            "sdpa_set_profile_events", "sdpa_last_error")
 
 
 class sdpa_desc_t(ctypes.Structure):
@@ -80,6 +80,13 @@ def load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
                           "`python -m scaled_dot_product_fwd_amd.build_lib`")
+    try:
+        # PyTorch ships its own HIP runtime (SONAME libamdhip64.so.7).  Loading
+        # torch first makes the library bind to that same runtime instead of
+        # bringing a second copy into the process.
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(LIB_PATH)
     P = ctypes.POINTER
     lib.sdpa_desc_init.argtypes = [P(sdpa_desc_t)] + [ctypes.c_int64] * 7 + [ctypes.c_int32]
@@ -92,6 +99,8 @@ def load() -> ctypes.CDLL:
     lib.sdpa_forward.restype = ctypes.c_int
     lib.sdpa_describe_plan.argtypes = [P(sdpa_desc_t), ctypes.c_char_p, ctypes.c_size_t]
     lib.sdpa_describe_plan.restype = ctypes.c_int
+    lib.sdpa_set_profile_events.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    lib.sdpa_set_profile_events.restype = ctypes.c_int
     lib.sdpa_last_error.argtypes = []
     lib.sdpa_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -131,6 +140,11 @@ def sdpa_describe_plan(desc: sdpa_desc_t) -> str:
     buf = ctypes.create_string_buffer(512)
     check(load().sdpa_describe_plan(ctypes.byref(desc), buf, len(buf)))
     return buf.value.decode()
+
+
+def sdpa_set_profile_events(start: int | None, stop: int | None) -> None:
+    """Record two hipEvent_t handles around the next call's attention kernel."""
+    check(load().sdpa_set_profile_events(start or None, stop or None))
 
 
 def sdpa_forward(desc: sdpa_desc_t, q: int, k: int, v: int, o: int, lse: int | None,

@@ -12,6 +12,8 @@
 namespace {
 
 thread_local std::string g_last_error;
+thread_local hipEvent_t g_prof_start = nullptr;
+thread_local hipEvent_t g_prof_stop = nullptr;
 
 int set_error(int code, const std::string& msg) {
   g_last_error = msg;
@@ -113,6 +115,8 @@ int sdpa_describe_plan(const sdpa_desc_t* d, char* buf, size_t len) {
 
 int sdpa_forward(const sdpa_desc_t* d, const void* q, const void* k, const void* v, void* o, float* lse,
                  void* workspace, size_t workspace_bytes, sdpa_stream_t stream) {
+  hipEvent_t ev_start = g_prof_start, ev_stop = g_prof_stop;  // consumed by this call
+  g_prof_start = g_prof_stop = nullptr;
   if (!q || !k || !v || !o) return set_error(SDPA_E_NULL, "q, k, v and o must be non-NULL device pointers");
   sdpa::Plan p;
   std::string err;
@@ -175,8 +179,12 @@ int sdpa_forward(const sdpa_desc_t* d, const void* q, const void* k, const void*
       {sdpa::launch_attn_f16_prefill, sdpa::launch_attn_f16_short, sdpa::launch_attn_f16_decode},
       {sdpa::launch_attn_bf16_prefill, sdpa::launch_attn_bf16_short, sdpa::launch_attn_bf16_decode},
   };
+  if (ev_start && hipEventRecord(ev_start, (hipStream_t)stream) != hipSuccess)
+    return set_error(SDPA_E_HIP, "hipEventRecord(start) failed");
   rc = table[p.dtype][fam](p, a, stream, &err);
   if (rc != SDPA_OK) return set_error(rc, err);
+  if (ev_stop && hipEventRecord(ev_stop, (hipStream_t)stream) != hipSuccess)
+    return set_error(SDPA_E_HIP, "hipEventRecord(stop) failed");
   if (p.splits > 1) {
     sdpa::CombineArgs c;
     c.ws_o = a.ws_o;
@@ -195,6 +203,14 @@ int sdpa_forward(const sdpa_desc_t* d, const void* q, const void* k, const void*
     rc = sdpa::launch_combine(p, c, stream, &err);
     if (rc != SDPA_OK) return set_error(rc, err);
   }
+  return ok();
+}
+
+int sdpa_set_profile_events(void* start, void* stop) {
+  if ((start == nullptr) != (stop == nullptr))
+    return set_error(SDPA_E_NULL, "start and stop must both be set or both be NULL");
+  g_prof_start = static_cast<hipEvent_t>(start);
+  g_prof_stop = static_cast<hipEvent_t>(stop);
   return ok();
 }
 

@@ -61,6 +61,7 @@ def check_full(b, hq, hkv, lq, lk, dqk, dv, dtype, mask="none", window=0, seed=0
 def pick_rows(b, hq, lq, n, seed, window=0):
     """Sampled (b, h, i) rows: random ones plus the first/last rows and window edges."""
     rng = np.random.default_rng(seed)
+    n = min(n, b * hq * lq)  # never ask for more distinct rows than exist
     rows = {(0, 0, 0), (b - 1, hq - 1, lq - 1), (0, hq - 1, lq // 2)}
     for i in (1, 2, 63, 64, 65, 127, 128, window - 1, window, window + 1, lq - 2):
         if 0 <= i < lq:

@@ -1,0 +1,60 @@
+"""Host-side checks of the bench's work accounting (no GPU)."""
+
+import pytest
+
+import bench
+from oracle import visible_mask, visible_pairs
+
+
+@pytest.mark.parametrize("lq,lk,mask,w", [
+    (7, 7, "none", 0), (7, 7, "causal", 0), (3, 10, "causal", 0), (1, 10, "causal", 0),
+    (10, 10, "window", 4), (4, 12, "window", 3), (5, 5, "window", 9), (8, 8, "window", 1),
+    (64, 200, "window", 100), (300, 300, "window", 1024), (40, 40, "window", 40),
+])
+def test_visible_pairs_closed_form_matches_oracle_count(lq, lk, mask, w):
+    assert bench.visible_pairs(lq, lk, mask, w) == visible_pairs(lq, lk, mask, w)
+    s = dict(lq=lq, lk=lk, mask=mask, window=w)
+    vm = visible_mask(lq, lk, mask, w)
+    for i in range(lq):
+        assert bench.row_visible(i, s) == int(vm[i].sum())
+
+
+def test_workload_table_matches_the_five_workloads():
+    names = [s["name"] for s in bench.all_shapes()]
+    assert len(names) == 1 + 12 + 20 + 3 + 4
+    assert bench.DEFAULT in names
+    s = bench.SHAPES[bench.DEFAULT]
+    assert (s["hq"], s["hkv"], s["lq"], s["lk"], s["dqk"], s["dv"], s["dtype"]) == (64, 8, 1, 32768, 192, 128, "bf16")
+    assert bench.bound(s) == "hbm"
+    assert bench.bound(bench.SHAPES["causal_l32768_d256"]) == "mfma"
+    assert bench.bound(bench.SHAPES["verify_lk32768_lq64"]) == "hbm"
+
+
+def test_window_prefill_flops_and_skip():
+    # W=1024 windowed prefill at L=8192, Hq=16, D=256: pairs = W(W+1)/2 + (L-W)W
+    s = bench.SHAPES["window_l8192_d256"]
+    flops, _ = bench.work(s)
+    pairs = 1024 * 1025 // 2 + (8192 - 1024) * 1024
+    assert flops == 2 * 16 * 512 * pairs
+
+
+def test_decode_bytes():
+    s = bench.SHAPES["decode_hkv8_lk32768"]
+    _, nbytes = bench.work(s)
+    assert nbytes == 2 * (64 * 1 * 320 + 8 * 32768 * 320)
+
+
+def test_multi_gpu_request_exits(monkeypatch, capsys):
+    monkeypatch.setattr("sys.argv", ["bench.py", "--gpus", "2"])
+    with pytest.raises(SystemExit) as e:
+        bench.main()
+    assert e.value.code == 2
+    assert "one GPU" in capsys.readouterr().err
+
+
+def test_row_sampler_terminates_when_few_rows_exist():
+    from gpu_cases import pick_rows
+    assert len(pick_rows(1, 32, 1, 64, 3)) == 32
+    assert len(pick_rows(1, 64, 1, 64, 3)) == 64
+    rows = pick_rows(1, 16, 8192, 64, 5, window=1024)
+    assert len(rows) == 64 and all(0 <= i < 8192 for _, _, i in rows)
