@@ -8,15 +8,20 @@
 // bounded regardless of kL).
 //
 // Data flow per key block (BK = NWK * BKW keys):
-//   HBM/L2 --16-byte loads--> registers --> LDS  K tile   [key][d]   (row padded)
-//                                          --> LDS V^T tile [dv][key] (transposed
-//                                              on the way in, row padded)
-//   S^T = K Q^T   MFMA 32x32 (keys x queries), Q kept in registers
-//   mask edge blocks only, online softmax in log2 units (exp2 is native)
-//   O^T += V^T P^T MFMA 32x32 (dv x queries), P rounded to the input type
+//   HBM/L2 --LDS DMA (global_load_lds, 16 B per lane)--> LDS K tile [key][d]
+//                                                    --> LDS V tile [key][dv]
+//   Both tiles keep the global row-major layout; 16-byte chunks are XOR
+//   swizzled per row so the MFMA operand reads below hit distinct banks.  The
+//   next block's DMA is in flight while the current block is computed (two
+//   LDS buffers), and no register is spent on staging.
+//   S^T = K Q^T    MFMA 32x32 (keys x queries), Q kept in registers
+//   mask edge blocks only; online softmax in log2 units (exp2 is native)
+//   O^T += V^T P^T MFMA 32x32 (dv x queries), P rounded to the input type;
+//   the V^T operand comes straight from the row-major V tile through the
+//   gfx950 transposing LDS read (ds_read_b64_tr_b16).
 // Working on S^T rather than S puts one query row in each lane (plus its
-// partner lane l^32), so the row max / row sum need a single cross-lane step
-// and the rescale of O is a per-lane scalar.
+// partner lane l^32), so the row max needs a single cross-lane step and the
+// rescale of O is a per-lane scalar.
 //
 // Packed rows: row r of a KV head is query head g = r % G of the group and
 // query position i = r / G.  This packs the G query heads that share a KV head
@@ -31,12 +36,19 @@
 // window are never loaded.  Only blocks that straddle an edge (the diagonal,
 // any row's window edge, or the Lk tail) apply a per-element mask; every block
 // whose first key lies below the last row's window edge is masked, which is
-// exact for unaligned windows too.
+// exact for unaligned windows too.  Inside a block, a wave whose rows see none
+// of its keys skips the block's arithmetic.
 //
 // Split-K (mlx issue #3826, second and third comments: the block-parallel
 // reduction over S): the block range may be cut into `splits` parts handled by
 // different workgroups; each writes its unnormalised O with (m, l) and a
 // combine kernel merges them by log-sum-exp.
+//
+// Lazy rescaling: the reference max m of a row only moves when a block's max
+// exceeds it by more than kRescale (log2 units); otherwise the block is
+// accumulated against the old reference, so probabilities stay <= 2^kRescale
+// and the O/l rescale (Dv multiplies per row) is skipped for most blocks.  The
+// result is the same softmax: O, l and m stay mutually consistent.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -49,11 +61,15 @@ namespace dev {
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
+#define SDPA_LDS __attribute__((address_space(3)))
+
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kRescale = 8.0f;  // lazy-rescale threshold, log2 units
 
 // ---------------------------------------------------------------------------
 // Element types.  `frag` is what one lane feeds one MFMA operand.
@@ -114,18 +130,9 @@ struct F32 {
   }
 };
 
-// Position of key `kk` (0..BK-1) inside a V^T LDS row.  For the 16-bit types
-// the 4-key groups are swizzled inside each 16-key step so that the 8 keys a
-// lane feeds one PV MFMA (keys 16s + 8i' + 4h + j, i'=0..1, j=0..3, taken from
-// accumulator registers 8s..8s+7) sit contiguously at 16s + 8h + 4i' + j.
-template <class E>
-__device__ __forceinline__ int vt_pos(int kk) {
-  if constexpr (E::ES == 2) {
-    return (kk & ~12) | ((kk & 4) << 1) | ((kk & 8) >> 1);
-  } else {
-    return kk;
-  }
-}
+constexpr int low_pow2(int x) { return x & -x; }
+constexpr int cmin(int a, int b) { return a < b ? a : b; }
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
 // Static shape of one kernel instance.
 template <class E, int DQK, int DV, int NWQ, int NWK, int BKW>
@@ -137,39 +144,45 @@ struct Shape {
   static constexpr int NKT = BKW / 32;         // 32-key tiles per wave
   static constexpr int NDT = DV / 32;          // 32-wide dv tiles
   static constexpr int NQS = DQK / E::KQK;     // QK MFMAs per key tile
-  static constexpr int CH = 16 / E::ES;        // elements per 16-byte chunk
-  static constexpr int KROW = DQK * E::ES + 16;  // K tile row bytes (padded)
-  static constexpr int VROW = BK * E::ES + 16;   // V^T tile row bytes (padded)
+  static constexpr int KCH = DQK * E::ES / 16; // 16-byte chunks per K row
+  static constexpr int VCH = DV * E::ES / 16;  // 16-byte chunks per V row
+  static constexpr int KROW = DQK * E::ES;
+  static constexpr int VROW = DV * E::ES;
   static constexpr int KBYTES = BK * KROW;
-  static constexpr int VBYTES = DV * VROW;
+  static constexpr int VBYTES = BK * VROW;
   static constexpr int BUF = KBYTES + VBYTES;
-  // Double-buffer the tiles when that still leaves room for two workgroups.
-  static constexpr bool DB = 2 * BUF <= 80 * 1024;
-  static constexpr int TILE_BYTES = (DB ? 2 : 1) * BUF;
+  static constexpr int KDMA = KBYTES / 1024;   // 1 KB DMA instructions per tile
+  static constexpr int VDMA = VBYTES / 1024;
+  // Chunk swizzles.  K: chunk ^ (row % KSW) spreads the 8 rows a 16-byte
+  // read serves per cycle over 8 slots.  V: chunk ^ 2*(row % VSW) spreads
+  // the 4 rows of a transposing read group over 4 slots of 32 bytes.
+  static constexpr int KSW = cmin(8, low_pow2(KCH));
+  static constexpr int VSW = cmax(1, cmin(4, low_pow2(VCH) / 2));
+  // Double-buffered tiles.
+  static constexpr int TILE_BYTES = 2 * BUF;
   // Cross-wave merge scratch (NWK > 1): O[slot][q][DV+4] and (m, l)[slot][q].
   static constexpr int MROW = DV + 4;
   static constexpr int MERGE_BYTES = NWK > 1 ? NWQ * NWK * 32 * MROW * 4 + NWQ * NWK * 32 * 8 : 0;
   static constexpr int LDS = TILE_BYTES > MERGE_BYTES ? TILE_BYTES : MERGE_BYTES;
-  // Global -> LDS staging work per thread.
-  static constexpr int KCHUNKS = BK * DQK / CH;
-  static constexpr int KPT = (KCHUNKS + NT - 1) / NT;
-  static constexpr int VUNITS = (BK / 4) * (DV / CH);  // 4 keys x one chunk of dv
-  static constexpr int VPT = (VUNITS + NT - 1) / NT;
   static_assert(BKW % 32 == 0, "BKW must be a multiple of 32");
   static_assert(DQK % E::KQK == 0 && DV % 32 == 0, "bad head-dim tile");
-  static_assert(DQK % CH == 0 && DV % CH == 0, "bad chunking");
+  static_assert(KBYTES % 1024 == 0 && VBYTES % 1024 == 0, "tiles must be whole DMA instructions");
+  static_assert(LDS <= 160 * 1024, "LDS budget of one workgroup exceeded");
 };
 
 __device__ __forceinline__ float wave_max32(float x) {  // combine lanes l and l^32
   return fmaxf(x, __shfl_xor(x, 32));
 }
-__device__ __forceinline__ float wave_sum32(float x) { return x + __shfl_xor(x, 32); }
+
+// Wait until every outstanding vector-memory operation of this wave (the
+// LDS DMA of the next block, the Q loads) has completed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
 template <class E, int DQK, int DV, int NWQ, int NWK, int BKW>
 __global__ __launch_bounds__(NWQ * NWK * 64) void attn_fwd_kernel(AttnArgs a) {
   using S = Shape<E, DQK, DV, NWQ, NWK, BKW>;
   using frag = typename E::frag;
-  __shared__ __attribute__((aligned(16))) char smem[S::LDS];
+  __shared__ __attribute__((aligned(1024))) char smem[S::LDS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -215,6 +228,44 @@ __global__ __launch_bounds__(NWQ * NWK * 64) void attn_fwd_kernel(AttnArgs a) {
   const int nb = kb_end - kb_first;
   const int sb0 = kb_first + (int)(((long long)nb * split) / a.splits);
   const int sb1 = kb_first + (int)(((long long)nb * (split + 1)) / a.splits);
+  const int nblk = sb1 - sb0;
+
+  // ---- LDS DMA of one key block into buffer `buf` ----
+  const char* kbase = (const char*)a.k + ((int64_t)b * a.ks[0] + (int64_t)kvh * a.ks[1]) * E::ES;
+  const char* vbase = (const char*)a.v + ((int64_t)b * a.vs[0] + (int64_t)kvh * a.vs[1]) * E::ES;
+  const int64_t kstr = a.ks[2] * E::ES;
+  const int64_t vstr = a.vs[2] * E::ES;
+  const int kch_valid = a.dqk * E::ES / 16;  // chunks of real data per row
+  const int vch_valid = a.dv * E::ES / 16;
+
+  auto dma_block = [&](int blk, int buf) {
+    const int k0 = blk * S::BK;
+    char* kl = smem + buf * S::BUF;
+    char* vl = kl + S::KBYTES;
+    // Every lane fetches one 16-byte chunk per instruction; rows past Lk and
+    // chunks past the real head dim re-read valid data (masked or multiplied
+    // by zero later), so no access leaves the tensors.
+#pragma unroll
+    for (int i = wave; i < S::KDMA; i += S::NW) {
+      const int slot = i * 64 + lane;
+      const int row = slot / S::KCH;
+      const int c = (slot % S::KCH) ^ (row & (S::KSW - 1));
+      const int grow = min(k0 + row, a.Lk - 1);
+      const char* src = kbase + (int64_t)grow * kstr + min(c, kch_valid - 1) * 16;
+      __builtin_amdgcn_global_load_lds((const void*)src, (SDPA_LDS void*)(kl + i * 1024), 16, 0, 0);
+    }
+#pragma unroll
+    for (int i = wave; i < S::VDMA; i += S::NW) {
+      const int slot = i * 64 + lane;
+      const int row = slot / S::VCH;
+      const int c = (slot % S::VCH) ^ (2 * (row & (S::VSW - 1)));
+      const int grow = min(k0 + row, a.Lk - 1);
+      const char* src = vbase + (int64_t)grow * vstr + min(c, vch_valid - 1) * 16;
+      __builtin_amdgcn_global_load_lds((const void*)src, (SDPA_LDS void*)(vl + i * 1024), 16, 0, 0);
+    }
+  };
+
+  if (nblk > 0) dma_block(sb0, 0);
 
   // ---- Q fragments (B operand of S^T = K Q^T), kept in registers ----
   frag qf[S::NQS];
@@ -239,221 +290,173 @@ __global__ __launch_bounds__(NWQ * NWK * 64) void attn_fwd_kernel(AttnArgs a) {
   f32x16 oacc[S::NDT];
 #pragma unroll
   for (int t = 0; t < S::NDT; ++t) oacc[t] = f32x16{};
-  float m_run = kNegInf;  // running max, log2 units
-  float l_run = 0.f;      // running sum
+  float m_ref = kNegInf;  // reference max of this row, log2 units (same in both lane halves)
+  float l_run = 0.f;      // this lane's share of the row sum (halves add up at the end)
+  const bool pos_scale = a.c > 0.f;
 
-  // ---- global -> register staging of one key block ----
-  const char* kbase = (const char*)a.k + ((int64_t)b * a.ks[0] + (int64_t)kvh * a.ks[1]) * E::ES;
-  const char* vbase = (const char*)a.v + ((int64_t)b * a.vs[0] + (int64_t)kvh * a.vs[1]) * E::ES;
-  const int64_t kstr = a.ks[2] * E::ES;
-  const int64_t vstr = a.vs[2] * E::ES;
-  u32x4 kreg[S::KPT];
-  u32x4 vreg[S::VPT][4];
-
-  auto load_block = [&](int blk) {
-    const int k0 = blk * S::BK;
-#pragma unroll
-    for (int i = 0; i < S::KPT; ++i) {
-      const int c = tid + i * S::NT;
-      const int row = c / (DQK / S::CH);
-      const int cc = c % (DQK / S::CH);
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (c < S::KCHUNKS && k0 + row < a.Lk && cc * S::CH < a.dqk)
-        v = *(const u32x4*)(kbase + (int64_t)(k0 + row) * kstr + cc * 16);
-      kreg[i] = v;
-    }
-#pragma unroll
-    for (int i = 0; i < S::VPT; ++i) {
-      const int u = tid + i * S::NT;
-      const int kg = u % (S::BK / 4);
-      const int dg = u / (S::BK / 4);
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        u32x4 v = {0u, 0u, 0u, 0u};
-        const int key = k0 + kg * 4 + kk;
-        if (u < S::VUNITS && key < a.Lk && dg * S::CH < a.dv)
-          v = *(const u32x4*)(vbase + (int64_t)key * vstr + dg * 16);
-        vreg[i][kk] = v;
-      }
-    }
-  };
-
-  auto store_block = [&](int buf) {
-    char* kl = smem + buf * S::BUF;
-    char* vl = kl + S::KBYTES;
-#pragma unroll
-    for (int i = 0; i < S::KPT; ++i) {
-      const int c = tid + i * S::NT;
-      if (c < S::KCHUNKS) {
-        const int row = c / (DQK / S::CH);
-        const int cc = c % (DQK / S::CH);
-        *(u32x4*)(kl + row * S::KROW + cc * 16) = kreg[i];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < S::VPT; ++i) {
-      const int u = tid + i * S::NT;
-      if (u < S::VUNITS) {
-        const int kg = u % (S::BK / 4);
-        const int dg = u / (S::BK / 4);
-        const int p0 = vt_pos<E>(kg * 4);
-        if constexpr (E::ES == 2) {
-          // 4 keys x 8 dv  ->  8 rows of V^T, 4 keys (8 bytes) each.
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {  // dv pair 2w, 2w+1
-            const unsigned x0 = vreg[i][0][w], x1 = vreg[i][1][w];
-            const unsigned x2 = vreg[i][2][w], x3 = vreg[i][3][w];
-            u32x2 lo, hi;
-            lo[0] = (x0 & 0xffffu) | (x1 << 16);
-            lo[1] = (x2 & 0xffffu) | (x3 << 16);
-            hi[0] = (x0 >> 16) | (x1 & 0xffff0000u);
-            hi[1] = (x2 >> 16) | (x3 & 0xffff0000u);
-            const int dvr = dg * S::CH + 2 * w;
-            *(u32x2*)(vl + dvr * S::VROW + p0 * 2) = lo;
-            *(u32x2*)(vl + (dvr + 1) * S::VROW + p0 * 2) = hi;
-          }
-        } else {
-          // 4 keys x 4 dv  ->  4 rows of V^T, 4 keys (16 bytes) each.
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            u32x4 t;
-            t[0] = vreg[i][0][e];
-            t[1] = vreg[i][1][e];
-            t[2] = vreg[i][2][e];
-            t[3] = vreg[i][3][e];
-            *(u32x4*)(vl + (dg * S::CH + e) * S::VROW + p0 * 4) = t;
-          }
-        }
-      }
-    }
-  };
-
-  const int nblk = sb1 - sb0;
-  if (nblk > 0) {
-    load_block(sb0);
-    store_block(0);
-  }
+  wait_vmem();
   __syncthreads();
 
   for (int j = 0; j < nblk; ++j) {
     const int blk = sb0 + j;
-    const int buf = S::DB ? (j & 1) : 0;
-    const bool more = j + 1 < nblk;
-    if (more) load_block(blk + 1);
+    const int buf = j & 1;
+    if (j + 1 < nblk) dma_block(blk + 1, buf ^ 1);
 
     const char* kl = smem + buf * S::BUF;
     const char* vl = kl + S::KBYTES;
     const int kw = blk * S::BK + wk * BKW;  // first key of this wave's slice
 
-    // ---- S^T = K Q^T for this wave's BKW keys ----
-    f32x16 sacc[S::NKT];
+    // A wave whose rows see none of its keys skips the arithmetic.
+    const bool skip = kw >= a.Lk || (a.mask != MASK_NONE && kw > pmax_w) ||
+                      (a.mask == MASK_WINDOW && kw + BKW - 1 <= pmin_w - a.window);
+    if (!skip) {
+      // ---- S^T = K Q^T for this wave's BKW keys ----
+      f32x16 sacc[S::NKT];
 #pragma unroll
-    for (int kt = 0; kt < S::NKT; ++kt) {
-      sacc[kt] = f32x16{};
-      const char* krow = kl + (wk * BKW + kt * 32 + col) * S::KROW;
+      for (int kt = 0; kt < S::NKT; ++kt) {
+        sacc[kt] = f32x16{};
+        const int row = wk * BKW + kt * 32 + col;
+        const char* krow = kl + row * S::KROW;
+        const int sw = row & (S::KSW - 1);
 #pragma unroll
-      for (int s = 0; s < S::NQS; ++s) {
-        const int d = s * E::KQK + hl * E::EPL;
-        frag af;
-        if constexpr (E::ES == 2) af = *(const u32x4*)(krow + d * 2);
-        else af = *(const float*)(krow + d * 4);
-        sacc[kt] = E::mma(af, qf[s], sacc[kt]);
-      }
-    }
-
-    // ---- scale into log2 units, mask edge blocks ----
-    // Edge test for this wave's rows: diagonal, window edge or Lk tail.
-    const bool edge = (kw + BKW > a.Lk) ||
-                      (a.mask != MASK_NONE && kw + BKW - 1 > pmin_w) ||
-                      (a.mask == MASK_WINDOW && kw < pmax_w - a.window + 1);
-    float mx = kNegInf;
-#pragma unroll
-    for (int kt = 0; kt < S::NKT; ++kt) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        float t = sacc[kt][e] * a.c;
-        if (edge) {
-          const int key = kw + kt * 32 + 8 * (e >> 2) + 4 * hl + (e & 3);
-          bool vis = key < a.Lk;
-          if (a.mask != MASK_NONE) vis = vis && key <= pos;
-          if (a.mask == MASK_WINDOW) vis = vis && key > pos - a.window;
-          t = vis ? t : kNegInf;
-        }
-        sacc[kt][e] = t;
-        mx = fmaxf(mx, t);
-      }
-    }
-
-    // ---- online softmax ----
-    mx = wave_max32(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = (m_new == kNegInf) ? 0.f : m_new;  // fully masked rows stay at 0
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    float rs = 0.f;
-#pragma unroll
-    for (int kt = 0; kt < S::NKT; ++kt) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float p = __builtin_amdgcn_exp2f(sacc[kt][e] - m_use);
-        sacc[kt][e] = p;
-        rs += p;
-      }
-    }
-    rs = wave_sum32(rs);
-    l_run = l_run * alpha + rs;
-    m_run = m_new;
-#pragma unroll
-    for (int t = 0; t < S::NDT; ++t) oacc[t] *= alpha;
-
-    // ---- O^T += V^T P^T ----
-#pragma unroll
-    for (int kt = 0; kt < S::NKT; ++kt) {
-      const int kcol = wk * BKW + kt * 32;  // first key of this tile inside the block
-#pragma unroll
-      for (int s2 = 0; s2 < 32 / E::KPV; ++s2) {
-        frag bf;
-        if constexpr (E::ES == 2) {
-          u32x4 pk;
-#pragma unroll
-          for (int w = 0; w < 4; ++w)
-            pk[w] = E::pack2(sacc[kt][8 * s2 + 2 * w], sacc[kt][8 * s2 + 2 * w + 1]);
-          bf = pk;
-        } else {
-          bf = sacc[kt][s2];
-        }
-#pragma unroll
-        for (int t = 0; t < S::NDT; ++t) {
-          const char* vrow = vl + (t * 32 + col) * S::VROW;
+        for (int s = 0; s < S::NQS; ++s) {
           frag af;
           if constexpr (E::ES == 2) {
-            af = *(const u32x4*)(vrow + (kcol + 16 * s2 + 8 * hl) * 2);
+            const int c = (2 * s + hl) ^ sw;  // 8 elements = one chunk
+            af = *(const u32x4*)(krow + c * 16);
           } else {
-            const int kk = kcol + 8 * (s2 >> 2) + 4 * hl + (s2 & 3);
-            af = *(const float*)(vrow + kk * 4);
+            const int d = 2 * s + hl;
+            af = *(const float*)(krow + (((d >> 2) ^ sw) << 4) + (d & 3) * 4);
           }
-          oacc[t] = E::mma(af, bf, oacc[t]);
+          sacc[kt] = E::mma(af, qf[s], sacc[kt]);
+        }
+      }
+
+      // ---- mask edge blocks (diagonal, window edge, Lk tail) ----
+      const bool edge = (kw + BKW > a.Lk) || (a.mask != MASK_NONE && kw + BKW - 1 > pmin_w) ||
+                        (a.mask == MASK_WINDOW && kw <= pmax_w - a.window);
+      if (edge) {
+#pragma unroll
+        for (int kt = 0; kt < S::NKT; ++kt) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int key = kw + kt * 32 + 8 * (e >> 2) + 4 * hl + (e & 3);
+            bool vis = key < a.Lk;
+            if (a.mask != MASK_NONE) vis = vis && key <= pos;
+            if (a.mask == MASK_WINDOW) vis = vis && key > pos - a.window;
+            // masked scores become -inf in log2 units whatever the scale's sign
+            if (!vis) sacc[kt][e] = pos_scale ? kNegInf : __builtin_inff();
+          }
+        }
+      }
+
+      // ---- online softmax with lazy rescaling ----
+      float mx;
+      if (pos_scale) {
+        mx = kNegInf;
+#pragma unroll
+        for (int kt = 0; kt < S::NKT; ++kt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kt][e]);
+      } else {  // scale <= 0: the largest scaled score is the smallest raw one
+        mx = __builtin_inff();
+#pragma unroll
+        for (int kt = 0; kt < S::NKT; ++kt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) mx = fminf(mx, sacc[kt][e]);
+      }
+      mx = pos_scale ? wave_max32(mx) : -wave_max32(-mx);
+      // block max in log2 units; an all-masked block gives -inf (or NaN for
+      // a zero scale times +inf, treated as -inf by the comparison below)
+      const float mxs = (mx == kNegInf || mx == __builtin_inff()) ? kNegInf : mx * a.c;
+      const bool need = mxs > m_ref + kRescale;
+      if (__builtin_amdgcn_ballot_w64(need)) {
+        const float m_new = need ? mxs : m_ref;
+        const float alpha = need ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.0f;
+        l_run *= alpha;
+#pragma unroll
+        for (int t = 0; t < S::NDT; ++t) oacc[t] *= alpha;
+        m_ref = m_new;
+      }
+      const float msub = (m_ref == kNegInf) ? 0.f : m_ref;
+#pragma unroll
+      for (int kt = 0; kt < S::NKT; ++kt) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float x = sacc[kt][e];
+          const float t = pos_scale ? __builtin_fmaf(x, a.c, -msub)
+                                    : ((x == __builtin_inff()) ? kNegInf : x * a.c - msub);
+          const float p = __builtin_amdgcn_exp2f(t);
+          sacc[kt][e] = p;
+          l_run += p;
+        }
+      }
+
+      // ---- O^T += V^T P^T ----
+#pragma unroll
+      for (int kt = 0; kt < S::NKT; ++kt) {
+        const int kbase_t = wk * BKW + kt * 32;  // first key of this tile inside the block
+#pragma unroll
+        for (int s2 = 0; s2 < 32 / E::KPV; ++s2) {
+          frag bf;
+          if constexpr (E::ES == 2) {
+            u32x4 pk;
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+              pk[w] = E::pack2(sacc[kt][8 * s2 + 2 * w], sacc[kt][8 * s2 + 2 * w + 1]);
+            bf = pk;
+          } else {
+            bf = sacc[kt][s2];
+          }
+#pragma unroll
+          for (int t = 0; t < S::NDT; ++t) {
+            frag af;
+            if constexpr (E::ES == 2) {
+              // Transposing read: lane t16 of group g supplies the address of
+              // 4 dv values of one key; the hardware hands lane i of the group
+              // element i%4 of the chunk addressed by lane 4j + i/4, i.e. the
+              // 4 keys (j = 0..3) of dv column 16*(g%2) + i.
+              const int g = lane >> 4, t16 = lane & 15;
+              const int dv0 = 32 * t + 16 * (g & 1) + 4 * (t16 & 3);
+              u32x2 half[2];
+#pragma unroll
+              for (int rr = 0; rr < 2; ++rr) {
+                const int row = kbase_t + 16 * s2 + 8 * rr + 4 * (g >> 1) + (t16 >> 2);
+                const int c = (dv0 >> 3) ^ (2 * (row & (S::VSW - 1)));
+                const char* p = vl + row * S::VROW + c * 16 + (dv0 & 7) * 2;
+                const i16x4 v4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SDPA_LDS i16x4*)p);
+                half[rr] = __builtin_bit_cast(u32x2, v4);
+              }
+              u32x4 f;
+              f[0] = half[0][0];
+              f[1] = half[0][1];
+              f[2] = half[1][0];
+              f[3] = half[1][1];
+              af = f;
+            } else {
+              const int row = kbase_t + 8 * (s2 >> 2) + 4 * hl + (s2 & 3);
+              const int dv = 32 * t + col;
+              const int c = (dv >> 2) ^ (2 * (row & (S::VSW - 1)));
+              af = *(const float*)(vl + row * S::VROW + c * 16 + (dv & 3) * 4);
+            }
+            oacc[t] = E::mma(af, bf, oacc[t]);
+          }
         }
       }
     }
 
-    if (more) {
-      if constexpr (S::DB) {
-        store_block(buf ^ 1);
-      } else {
-        __syncthreads();
-        store_block(0);
-      }
-    }
+    wait_vmem();
     __syncthreads();
   }
 
   // ---- epilogue ----
+  const float l_row = l_run + __shfl_xor(l_run, 32);  // both halves' keys
   const int64_t ws_row = ((int64_t)z * a.R + r) * a.splits + split;
 
   if constexpr (NWK == 1) {
     if (!row_ok) return;
     if (a.splits == 1) {
-      const float inv = 1.0f / l_run;
+      const float inv = 1.0f / l_row;
       char* orow = (char*)a.o + ((int64_t)b * a.os[0] + (int64_t)hq * a.os[1] + (int64_t)iq * a.os[2]) * E::ES;
 #pragma unroll
       for (int t = 0; t < S::NDT; ++t) {
@@ -475,7 +478,7 @@ __global__ __launch_bounds__(NWQ * NWK * 64) void attn_fwd_kernel(AttnArgs a) {
         }
       }
       if (a.lse && hl == 0)
-        a.lse[((int64_t)b * a.Hq + hq) * a.Lq + iq] = (m_run + log2f(l_run)) * kLn2;
+        a.lse[((int64_t)b * a.Hq + hq) * a.Lq + iq] = (m_ref + log2f(l_row)) * kLn2;
     } else {
       float* wo = a.ws_o + ws_row * a.dv;
 #pragma unroll
@@ -488,7 +491,7 @@ __global__ __launch_bounds__(NWQ * NWK * 64) void attn_fwd_kernel(AttnArgs a) {
                                              oacc[t][4 * i4 + 2], oacc[t][4 * i4 + 3]);
         }
       }
-      if (hl == 0) *(float2*)(a.ws_ml + ws_row * 2) = make_float2(m_run, l_run);
+      if (hl == 0) *(float2*)(a.ws_ml + ws_row * 2) = make_float2(m_ref, l_row);
     }
   } else {
     // Merge the NWK key slices of the same rows through LDS.  The tile
@@ -508,8 +511,8 @@ __global__ __launch_bounds__(NWQ * NWK * 64) void attn_fwd_kernel(AttnArgs a) {
         }
       }
       if (hl == 0) {
-        mml[(slot * 32 + col) * 2 + 0] = m_run;
-        mml[(slot * 32 + col) * 2 + 1] = l_run;
+        mml[(slot * 32 + col) * 2 + 0] = m_ref;
+        mml[(slot * 32 + col) * 2 + 1] = l_row;
       }
     }
     __syncthreads();

@@ -45,33 +45,38 @@ int launch_one(const Plan& p, const AttnArgs& a, void* stream, std::string* err)
 
 }  // namespace sdpa
 
-// One dispatch case: padded dims and wave arrangement must match the plan.
-#define SDPA_CASE(E, DQK, DV, NWQ, NWK, BKW)                                              \
-  if (p.dqk_pad == DQK && p.dv_pad == DV && p.fam.nwq == NWQ && p.fam.nwk == NWK &&       \
-      p.fam.bkw == BKW)                                                                   \
-    return launch_one<dev::E, DQK, DV, NWQ, NWK, BKW>(p, a, stream, err);
+// One dispatch case: the plan's padded dims select the instance; the wave
+// arrangement follows from the kind exactly as in the planner.
+#define SDPA_CASE(E, KIND, DQK, DV)                                                            \
+  if (p.dqk_pad == DQK && p.dv_pad == DV) {                                                    \
+    constexpr Family f_ = family_for(KIND, dev::E::ES, DQK, DV);                               \
+    if (p.fam.nwq != f_.nwq || p.fam.nwk != f_.nwk || p.fam.bkw != f_.bkw) {                   \
+      *err = "plan and kernel instance disagree on the wave arrangement";                      \
+      return SDPA_E_PLAN;                                                                      \
+    }                                                                                          \
+    return launch_one<dev::E, DQK, DV, f_.nwq, f_.nwk, f_.bkw>(p, a, stream, err);             \
+  }
 
 // Head-dim pairs of the 16-bit types: equal padded dims plus (192, 128).
-#define SDPA_PAIRS16(E, NWQ, NWK, BKW_SMALL, BKW_BIG) \
-  SDPA_CASE(E, 32, 32, NWQ, NWK, BKW_SMALL)           \
-  SDPA_CASE(E, 64, 64, NWQ, NWK, BKW_SMALL)           \
-  SDPA_CASE(E, 96, 96, NWQ, NWK, BKW_SMALL)           \
-  SDPA_CASE(E, 128, 128, NWQ, NWK, BKW_SMALL)         \
-  SDPA_CASE(E, 160, 160, NWQ, NWK, BKW_BIG)           \
-  SDPA_CASE(E, 192, 192, NWQ, NWK, BKW_BIG)           \
-  SDPA_CASE(E, 224, 224, NWQ, NWK, BKW_BIG)           \
-  SDPA_CASE(E, 256, 256, NWQ, NWK, BKW_BIG)           \
-  SDPA_CASE(E, 192, 128, NWQ, NWK, BKW_BIG)
+#define SDPA_PAIRS16(E, KIND) \
+  SDPA_CASE(E, KIND, 32, 32)   \
+  SDPA_CASE(E, KIND, 64, 64)   \
+  SDPA_CASE(E, KIND, 96, 96)   \
+  SDPA_CASE(E, KIND, 128, 128) \
+  SDPA_CASE(E, KIND, 160, 160) \
+  SDPA_CASE(E, KIND, 192, 192) \
+  SDPA_CASE(E, KIND, 224, 224) \
+  SDPA_CASE(E, KIND, 256, 256) \
+  SDPA_CASE(E, KIND, 192, 128)
 
 // float32 stops at 128.
-#define SDPA_PAIRS32(E, NWQ, NWK, BKW) \
-  SDPA_CASE(E, 32, 32, NWQ, NWK, BKW)  \
-  SDPA_CASE(E, 64, 64, NWQ, NWK, BKW)  \
-  SDPA_CASE(E, 96, 96, NWQ, NWK, BKW)  \
-  SDPA_CASE(E, 128, 128, NWQ, NWK, BKW)
+#define SDPA_PAIRS32(E, KIND)  \
+  SDPA_CASE(E, KIND, 32, 32)   \
+  SDPA_CASE(E, KIND, 64, 64)   \
+  SDPA_CASE(E, KIND, 96, 96)   \
+  SDPA_CASE(E, KIND, 128, 128)
 
-#define SDPA_NO_INSTANCE()                                                                \
-  *err = "no kernel instance for dqk_pad=" + std::to_string(p.dqk_pad) +                  \
-         " dv_pad=" + std::to_string(p.dv_pad) + " waves=" + std::to_string(p.fam.nwq) +  \
-         "x" + std::to_string(p.fam.nwk) + " bkw=" + std::to_string(p.fam.bkw);           \
+#define SDPA_NO_INSTANCE()                                                               \
+  *err = "no kernel instance for dqk_pad=" + std::to_string(p.dqk_pad) +                 \
+         " dv_pad=" + std::to_string(p.dv_pad);                                          \
   return SDPA_E_HEAD_DIM;

@@ -1,9 +1,9 @@
-// float32 attention kernels, decode family.
+// f32 attention kernels, decode family.
 #include "attn_launch.h"
 
 namespace sdpa {
 int launch_attn_f32_decode(const Plan& p, const AttnArgs& a, void* stream, std::string* err) {
-  SDPA_PAIRS32(F32, 1, 4, 32)
+  SDPA_PAIRS32(F32, KIND_DECODE)
   SDPA_NO_INSTANCE()
 }
 }  // namespace sdpa

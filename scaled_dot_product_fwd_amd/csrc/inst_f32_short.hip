@@ -1,9 +1,9 @@
-// float32 attention kernels, short family.
+// f32 attention kernels, short family.
 #include "attn_launch.h"
 
 namespace sdpa {
 int launch_attn_f32_short(const Plan& p, const AttnArgs& a, void* stream, std::string* err) {
-  SDPA_PAIRS32(F32, 2, 2, 32)
+  SDPA_PAIRS32(F32, KIND_SHORT)
   SDPA_NO_INSTANCE()
 }
 }  // namespace sdpa

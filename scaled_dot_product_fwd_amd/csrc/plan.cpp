@@ -57,24 +57,11 @@ const char* mask_name(int m) {
 
 }  // namespace
 
-// Kernel families (rows per workgroup -> wave arrangement).  The same list is
-// instantiated in the element-type units.
-Family family_for(int rows_per_wg, int dqk_pad, int dv_pad) {
-  const int dmax = dqk_pad > dv_pad ? dqk_pad : dv_pad;
-  if (rows_per_wg == 32) return Family{1, 4, 32};    // decode: 4 waves split each key block
-  if (rows_per_wg == 64) return Family{2, 2, 32};    // short queries: 2 x 2 waves
-  return Family{4, 1, dmax <= 128 ? 64 : 32};        // prefill: 4 waves stacked on rows
-}
-
 size_t attn_lds_bytes(int dtype, int dqk_pad, int dv_pad, const Family& f) {
   // Mirrors Shape<> in attn_kernel.h.
   const int es = dtype == SDPA_F32 ? 4 : 2;
   const int bk = f.nwk * f.bkw;
-  const int kbytes = bk * (dqk_pad * es + 16);
-  const int vbytes = dv_pad * (bk * es + 16);
-  const int buf = kbytes + vbytes;
-  const bool db = 2 * buf <= 80 * 1024;
-  const int tiles = (db ? 2 : 1) * buf;
+  const int tiles = 2 * bk * (dqk_pad + dv_pad) * es;
   const int merge = f.nwk > 1 ? f.nwq * f.nwk * 32 * (dv_pad + 4) * 4 + f.nwq * f.nwk * 32 * 8 : 0;
   return (size_t)(tiles > merge ? tiles : merge);
 }
@@ -170,7 +157,8 @@ int make_plan(const sdpa_desc_t* d, Plan* p, std::string* err) {
   const int64_t G = Hq / Hkv;
   const int64_t R = G * Lq;
   int rows = d->row_tile ? d->row_tile : (R <= 32 ? 32 : (R <= 64 ? 64 : 128));
-  const Family fam = family_for(rows, dqk_pad, dv_pad);
+  const int kind = rows == 32 ? KIND_DECODE : (rows == 64 ? KIND_SHORT : KIND_PREFILL);
+  const Family fam = family_for(kind, d->dtype == SDPA_F32 ? 4 : 2, dqk_pad, dv_pad);
   const int64_t row_tiles = ceil_div(R, rows);
   const int64_t base = B * Hkv * row_tiles;
   const int64_t bk = (int64_t)fam.nwk * fam.bkw;
@@ -197,6 +185,7 @@ int make_plan(const sdpa_desc_t* d, Plan* p, std::string* err) {
   if (base * splits > 0x7fffffffLL) return fail(err, SDPA_E_SHAPE, "grid too large");
 
   p->dtype = d->dtype;
+  p->kind = kind;
   p->dqk_pad = dqk_pad;
   p->dv_pad = dv_pad;
   p->fam = fam;
@@ -219,7 +208,7 @@ int make_plan(const sdpa_desc_t* d, Plan* p, std::string* err) {
 
 std::string describe(const sdpa_desc_t* d, const Plan& p) {
   std::ostringstream s;
-  const char* fam = p.fam.nwk > 1 ? (p.fam.nwq > 1 ? "short" : "decode") : "prefill";
+  const char* fam = p.kind == KIND_DECODE ? "decode" : (p.kind == KIND_SHORT ? "short" : "prefill");
   s << "family=" << fam << " dtype=" << dtype_name(p.dtype) << " dqk=" << d->dim_qk << "->" << p.dqk_pad
     << " dv=" << d->dim_v << "->" << p.dv_pad << " rows_per_wg=" << p.rows_per_wg
     << " waves=" << p.fam.nwq << "x" << p.fam.nwk << " block_keys=" << p.fam.nwk * p.fam.bkw

@@ -172,7 +172,7 @@ int sdpa_forward(const sdpa_desc_t* d, const void* q, const void* k, const void*
     a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes);
   }
 
-  const int fam = p.rows_per_wg == 32 ? 2 : (p.rows_per_wg == 64 ? 1 : 0);
+  const int fam = p.kind;  // KIND_PREFILL=0, KIND_SHORT=1, KIND_DECODE=2
   using L = int (*)(const sdpa::Plan&, const sdpa::AttnArgs&, void*, std::string*);
   static const L table[3][3] = {
       {sdpa::launch_attn_f32_prefill, sdpa::launch_attn_f32_short, sdpa::launch_attn_f32_decode},

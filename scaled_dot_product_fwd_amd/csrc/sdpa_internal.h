@@ -51,8 +51,22 @@ struct Family {
   int bkw;   // keys per wave per iteration (multiple of 32)
 };
 
+enum : int { KIND_PREFILL = 0, KIND_SHORT = 1, KIND_DECODE = 2 };
+
+// The wave arrangement of each kind, sized so that the two LDS buffers of K
+// and V tiles fit: prefill keeps two workgroups per CU (<= 80 KB), decode
+// takes the largest key block that fits one workgroup's 160 KB.  Shared by
+// the planner and the kernel instantiation units.
+constexpr Family family_for(int kind, int elem_bytes, int dqk_pad, int dv_pad) {
+  const int key_bytes = (dqk_pad + dv_pad) * elem_bytes;  // one key of K plus V
+  if (kind == KIND_DECODE) return key_bytes * 128 * 2 <= 160 * 1024 ? Family{1, 4, 32} : Family{1, 2, 32};
+  if (kind == KIND_SHORT) return Family{2, 2, 32};
+  return key_bytes * 64 * 2 <= 80 * 1024 ? Family{4, 1, 64} : Family{4, 1, 32};
+}
+
 struct Plan {
   int dtype;
+  int kind;              // KIND_PREFILL / KIND_SHORT / KIND_DECODE
   int dqk_pad, dv_pad;   // head dims rounded up to the instantiated tile dims
   Family fam;
   int rows_per_wg;       // 32 * nwq
@@ -86,9 +100,6 @@ SDPA_DECLARE_LAUNCH(launch_attn_f32_short)
 SDPA_DECLARE_LAUNCH(launch_attn_f32_decode)
 #undef SDPA_DECLARE_LAUNCH
 int launch_combine(const Plan& p, const CombineArgs& a, void* stream, std::string* err);
-
-// Kernel family for a row tile of `rows_per_wg` rows (32, 64 or 128).
-Family family_for(int rows_per_wg, int dqk_pad, int dv_pad);
 
 // LDS bytes of an attention kernel instance (host mirror of the kernel's
 // static layout, used by the planner's capacity check).
