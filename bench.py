@@ -344,6 +344,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true", help="also time every shape of the five workloads")
     ap.add_argument("--sweep-out", default=os.path.join("gpurun_out", "sweep.json"))
+    ap.add_argument("--sweep-only", default="", help="comma-separated name prefixes to sweep")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (got --gpus {args.gpus}); this build has no multi-GPU path",
@@ -388,7 +389,10 @@ def main():
     }
     if args.sweep:
         rows = []
+        prefixes = [p for p in args.sweep_only.split(",") if p]
         for sh in all_shapes():
+            if prefixes and not any(sh["name"].startswith(p) for p in prefixes):
+                continue
             print(f"sweep {sh['name']}", file=sys.stderr, flush=True)
             r, rr = measure(sh, 20, 5)
             del rr

@@ -38,6 +38,10 @@ def _hipcc() -> str:
 # -packed-fp32-ops keeps the compiler from forming packed fp32 VALU ops.
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             # keep MFMA accumulators in ordinary VGPRs: the softmax rescales
+             # them with VALU ops, which would otherwise copy them out of and
+             # back into the accumulation registers every block
+             "-mllvm", "-amdgpu-mfma-vgpr-form=1",
              "-I", os.path.join(ROOT, "include")]
 
 

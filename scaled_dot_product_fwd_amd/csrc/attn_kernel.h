@@ -64,6 +64,7 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 #define SDPA_LDS __attribute__((address_space(3)))
 
@@ -90,9 +91,10 @@ struct BF16 {
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
   }
   static __device__ __forceinline__ unsigned pack2(float x, float y) {
-    __bf16 a = (__bf16)x, b = (__bf16)y;  // round to nearest even
-    return (unsigned)__builtin_bit_cast(unsigned short, a) |
-           ((unsigned)__builtin_bit_cast(unsigned short, b) << 16);
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    const f32x2 v = {x, y};  // one v_cvt_pk_bf16_f32, round to nearest even
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2));
   }
   static __device__ __forceinline__ unsigned short to_store(float x) {
     return __builtin_bit_cast(unsigned short, (__bf16)x);
@@ -110,9 +112,10 @@ struct F16 {
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
   }
   static __device__ __forceinline__ unsigned pack2(float x, float y) {
-    _Float16 a = (_Float16)x, b = (_Float16)y;  // round to nearest even
-    return (unsigned)__builtin_bit_cast(unsigned short, a) |
-           ((unsigned)__builtin_bit_cast(unsigned short, b) << 16);
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    const f32x2 v = {x, y};  // one v_cvt_pk_f16_f32, round to nearest even
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(v, f16x2));
   }
   static __device__ __forceinline__ unsigned short to_store(float x) {
     return __builtin_bit_cast(unsigned short, (_Float16)x);
@@ -153,17 +156,34 @@ struct Shape {
   static constexpr int BUF = KBYTES + VBYTES;
   static constexpr int KDMA = KBYTES / 1024;   // 1 KB DMA instructions per tile
   static constexpr int VDMA = VBYTES / 1024;
-  // Chunk swizzles.  K: chunk ^ (row % KSW) spreads the 8 rows a 16-byte
-  // read serves per cycle over 8 slots.  V: chunk ^ 2*(row % VSW) spreads
-  // the 4 rows of a transposing read group over 4 slots of 32 bytes.
-  static constexpr int KSW = cmin(8, low_pow2(KCH));
-  static constexpr int VSW = cmax(1, cmin(4, low_pow2(VCH) / 2));
-  // Double-buffered tiles.
-  static constexpr int TILE_BYTES = 2 * BUF;
-  // Cross-wave merge scratch (NWK > 1): O[slot][q][DV+4] and (m, l)[slot][q].
-  static constexpr int MROW = DV + 4;
-  static constexpr int MERGE_BYTES = NWK > 1 ? NWQ * NWK * 32 * MROW * 4 + NWQ * NWK * 32 * 8 : 0;
-  static constexpr int LDS = TILE_BYTES > MERGE_BYTES ? TILE_BYTES : MERGE_BYTES;
+  // Chunk swizzles (16-byte chunks; the LDS serves 256 bytes per cycle).
+  // K: the QK operand read has 16 lanes of consecutive rows reading the same
+  // logical chunk per cycle; chunk ^ kx(row) puts them in 16 distinct slots
+  // of the 256-byte bank window.  V: a transposing read group covers 4
+  // consecutive rows (32 bytes each); chunk ^ vy(row) spreads them over the
+  // window.  Each swizzle permutes chunks inside aligned groups (KG, VG
+  // chunks), so it never leaves the row.
+  static constexpr int KG = (KCH % 16 == 0) ? 16 : (KCH % 8 == 0) ? 8 : 4;
+  static constexpr int KSH = (KG == 16) ? 0 : (KG == 8) ? 1 : 2;
+  static constexpr int VG = (VCH % 16 == 0) ? 16 : (VCH % 8 == 0) ? 8 : 4;
+  static __device__ __forceinline__ int kx(int row) { return (row >> KSH) & (KG - 1); }
+  static __device__ __forceinline__ int vy(int row) {
+    return VG == 16 ? 4 * (row & 3) : (VG == 8 ? 2 * (row & 3) : 2 * (row & 1));
+  }
+  // Pipeline depth: three LDS buffers (two blocks in flight while one is
+  // computed) when they fit the occupancy target of the kind, else two.
+  static constexpr int NSTAGE = (3 * BUF <= (NWQ > 1 ? 80 : 160) * 1024) ? 3 : 2;
+  static constexpr int LDS = NSTAGE * BUF;
+  // Cross-wave merge (NWK > 1): the waves with wk > 0 leave O in buffer 0 as
+  // [slot][q][MROW] and (m, l) in buffer 1; MROW is padded when that fits.
+  static constexpr int MSLOTS = NWQ * (NWK - 1);
+  static constexpr int MROW = (MSLOTS * 32 * (DV + 4) * 4 <= BUF) ? DV + 4 : DV;
+  static_assert(MSLOTS * 32 * MROW * 4 <= BUF && MSLOTS * 32 * 8 <= BUF, "merge scratch must fit a buffer");
+  // DMA instructions one wave issues per block (the fewest, when the tile
+  // does not divide evenly between the waves).
+  static constexpr int KDMA_MIN = KDMA / NW, VDMA_MIN = VDMA / NW;
+  static constexpr int DMA_MIN = KDMA_MIN + VDMA_MIN;
+  static_assert(DMA_MIN >= 1 && (KDMA + VDMA + NW - 1) / NW <= 63, "vmcnt range");
   static_assert(BKW % 32 == 0, "BKW must be a multiple of 32");
   static_assert(DQK % E::KQK == 0 && DV % 32 == 0, "bad head-dim tile");
   static_assert(KBYTES % 1024 == 0 && VBYTES % 1024 == 0, "tiles must be whole DMA instructions");
@@ -174,15 +194,34 @@ __device__ __forceinline__ float wave_max32(float x) {  // combine lanes l and l
   return fmaxf(x, __shfl_xor(x, 32));
 }
 
-// Wait until every outstanding vector-memory operation of this wave (the
-// LDS DMA of the next block, the Q loads) has completed.
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+// LDS DMA of 16 bytes per lane: lane l's chunk at `src` lands at LDS byte
+// address lds + 16 l.  Issued as a single instruction the compiler does not
+// track, so it inserts no wait for it anywhere; the kernel waits itself with
+// wait_vmcnt.  The instruction has no register result; its address registers
+// are consumed at issue.
+__device__ __forceinline__ void lds_dma16(const void* src, unsigned lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(lds)
+               : "memory", "m0");
+}
 
-template <class E, int DQK, int DV, int NWQ, int NWK, int BKW>
-__global__ __launch_bounds__(NWQ * NWK * 64) void attn_fwd_kernel(AttnArgs a) {
+// Wait until at most N vector-memory operations of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);  // expcnt, lgkmcnt: no wait
+}
+
+template <class E, int DQK, int DV, int NWQ, int NWK, int BKW, int WPE>
+__global__ __launch_bounds__(NWQ * NWK * 64) __attribute__((amdgpu_waves_per_eu(WPE)))
+void attn_fwd_kernel(AttnArgs a) {
   using S = Shape<E, DQK, DV, NWQ, NWK, BKW>;
   using frag = typename E::frag;
-  __shared__ __attribute__((aligned(1024))) char smem[S::LDS];
+  __shared__ __attribute__((aligned(1024))) char smem_[S::LDS];
+  // All LDS addressing goes through an LDS-typed pointer, so addresses stay
+  // 32-bit and loop-invariant parts fold into the instructions' offsets.
+  SDPA_LDS char* const smem = (SDPA_LDS char*)smem_;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -231,41 +270,85 @@ __global__ __launch_bounds__(NWQ * NWK * 64) void attn_fwd_kernel(AttnArgs a) {
   const int nblk = sb1 - sb0;
 
   // ---- LDS DMA of one key block into buffer `buf` ----
+  // Each wave issues KPW + VPW DMA instructions per block; lane l of
+  // instruction i fills LDS slot 64 i + l (16 bytes) with the chunk that the
+  // swizzle puts there.  The per-lane byte offset inside a block is fixed, so
+  // it is computed once; only the tail block (rows past Lk) recomputes it,
+  // re-reading the last key (masked later) instead of leaving the tensor.
+  // Chunks past the real head dim re-read the row's last real chunk; they
+  // meet zero Q columns or land in discarded output columns.
   const char* kbase = (const char*)a.k + ((int64_t)b * a.ks[0] + (int64_t)kvh * a.ks[1]) * E::ES;
   const char* vbase = (const char*)a.v + ((int64_t)b * a.vs[0] + (int64_t)kvh * a.vs[1]) * E::ES;
   const int64_t kstr = a.ks[2] * E::ES;
   const int64_t vstr = a.vs[2] * E::ES;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  constexpr int KPW = (S::KDMA + S::NW - 1) / S::NW;  // the last round may leave waves idle
+  constexpr int VPW = (S::VDMA + S::NW - 1) / S::NW;
   const int kch_valid = a.dqk * E::ES / 16;  // chunks of real data per row
   const int vch_valid = a.dv * E::ES / 16;
+  // (row, byte column) of LDS slot `slot` of a K or V tile
+  auto kslot = [&](int slot, int& row, int& colb) {
+    row = slot / S::KCH;
+    colb = min((slot % S::KCH) ^ S::kx(row), kch_valid - 1) * 16;
+  };
+  auto vslot = [&](int slot, int& row, int& colb) {
+    row = slot / S::VCH;
+    colb = min((slot % S::VCH) ^ S::vy(row), vch_valid - 1) * 16;
+  };
+  unsigned koff[KPW], voff[VPW];
+#pragma unroll
+  for (int ii = 0; ii < KPW; ++ii) {
+    int row, colb;
+    kslot((ii * S::NW + wave_u) * 64 + lane, row, colb);
+    koff[ii] = (unsigned)(row * kstr) + colb;
+  }
+#pragma unroll
+  for (int ii = 0; ii < VPW; ++ii) {
+    int row, colb;
+    vslot((ii * S::NW + wave_u) * 64 + lane, row, colb);
+    voff[ii] = (unsigned)(row * vstr) + colb;
+  }
 
-  auto dma_block = [&](int blk, int buf) {
+  const unsigned lds_base = (unsigned)(uintptr_t)smem;
+  auto dma_block = [&](int blk, int buf) __attribute__((always_inline)) {
     const int k0 = blk * S::BK;
-    char* kl = smem + buf * S::BUF;
-    char* vl = kl + S::KBYTES;
-    // Every lane fetches one 16-byte chunk per instruction; rows past Lk and
-    // chunks past the real head dim re-read valid data (masked or multiplied
-    // by zero later), so no access leaves the tensors.
+    const unsigned kl = lds_base + buf * S::BUF;
+    const unsigned vl = kl + S::KBYTES;
+    if (k0 + S::BK <= a.Lk) {
+      const char* kb = kbase + (int64_t)k0 * kstr;
+      const char* vb = vbase + (int64_t)k0 * vstr;
 #pragma unroll
-    for (int i = wave; i < S::KDMA; i += S::NW) {
-      const int slot = i * 64 + lane;
-      const int row = slot / S::KCH;
-      const int c = (slot % S::KCH) ^ (row & (S::KSW - 1));
-      const int grow = min(k0 + row, a.Lk - 1);
-      const char* src = kbase + (int64_t)grow * kstr + min(c, kch_valid - 1) * 16;
-      __builtin_amdgcn_global_load_lds((const void*)src, (SDPA_LDS void*)(kl + i * 1024), 16, 0, 0);
-    }
+      for (int ii = 0; ii < KPW; ++ii)
+        if ((ii + 1) * S::NW <= S::KDMA || ii * S::NW + wave_u < S::KDMA)
+          lds_dma16(kb + koff[ii], kl + (ii * S::NW + wave_u) * 1024);
 #pragma unroll
-    for (int i = wave; i < S::VDMA; i += S::NW) {
-      const int slot = i * 64 + lane;
-      const int row = slot / S::VCH;
-      const int c = (slot % S::VCH) ^ (2 * (row & (S::VSW - 1)));
-      const int grow = min(k0 + row, a.Lk - 1);
-      const char* src = vbase + (int64_t)grow * vstr + min(c, vch_valid - 1) * 16;
-      __builtin_amdgcn_global_load_lds((const void*)src, (SDPA_LDS void*)(vl + i * 1024), 16, 0, 0);
+      for (int ii = 0; ii < VPW; ++ii)
+        if ((ii + 1) * S::NW <= S::VDMA || ii * S::NW + wave_u < S::VDMA)
+          lds_dma16(vb + voff[ii], vl + (ii * S::NW + wave_u) * 1024);
+    } else {
+#pragma unroll
+      for (int ii = 0; ii < KPW; ++ii) {
+        if ((ii + 1) * S::NW > S::KDMA && ii * S::NW + wave_u >= S::KDMA) continue;
+        int row, colb;
+        kslot((ii * S::NW + wave_u) * 64 + lane, row, colb);
+        const int grow = min(k0 + row, a.Lk - 1);
+        lds_dma16(kbase + (int64_t)grow * kstr + colb, kl + (ii * S::NW + wave_u) * 1024);
+      }
+#pragma unroll
+      for (int ii = 0; ii < VPW; ++ii) {
+        if ((ii + 1) * S::NW > S::VDMA && ii * S::NW + wave_u >= S::VDMA) continue;
+        int row, colb;
+        vslot((ii * S::NW + wave_u) * 64 + lane, row, colb);
+        const int grow = min(k0 + row, a.Lk - 1);
+        lds_dma16(vbase + (int64_t)grow * vstr + colb, vl + (ii * S::NW + wave_u) * 1024);
+      }
     }
   };
 
-  if (nblk > 0) dma_block(sb0, 0);
+  // Prologue: the first NSTAGE-1 blocks go in flight.
+#pragma unroll
+  for (int st = 0; st < S::NSTAGE - 1; ++st)
+    if (st < nblk) dma_block(sb0 + st, st);
 
   // ---- Q fragments (B operand of S^T = K Q^T), kept in registers ----
   frag qf[S::NQS];
@@ -287,23 +370,68 @@ __global__ __launch_bounds__(NWQ * NWK * 64) void attn_fwd_kernel(AttnArgs a) {
     }
   }
 
+  // The loop below assumes a positive scale.  A negative one is folded into
+  // Q (negating a rounded value is exact): s * c = (-s) * (-c).  A zero scale
+  // makes every visible key equally likely: Q = 0 with scale 1 gives exactly
+  // that, and masked keys still reach -inf.
+  float c = a.c;
+  if (c < 0.f) {
+    c = -c;
+#pragma unroll
+    for (int s = 0; s < S::NQS; ++s) {
+      if constexpr (E::ES == 2) qf[s] ^= 0x80008000u;
+      else qf[s] = -qf[s];
+    }
+  } else if (c == 0.f) {
+    c = 1.f;
+#pragma unroll
+    for (int s = 0; s < S::NQS; ++s) {
+      if constexpr (E::ES == 2) qf[s] = u32x4{0u, 0u, 0u, 0u};
+      else qf[s] = 0.f;
+    }
+  }
+
+  // Loop-invariant parts of the LDS operand addresses (16-bit types).  The
+  // K swizzle only involves the lane's row inside a 32-key tile and the V
+  // swizzle only the lane bits of the row, so per block every read is one
+  // register plus a constant.
+  constexpr int SPG = S::KG / 2;  // head-dim steps per K swizzle group
+  constexpr int TPG = S::VG / 4;  // dv tiles per V swizzle group
+  int koffl[SPG], voffl[TPG];
+  if constexpr (E::ES == 2) {
+    const int xk = S::kx(col);
+#pragma unroll
+    for (int sl = 0; sl < SPG; ++sl) koffl[sl] = col * S::KROW + 16 * ((2 * sl + hl) ^ xk);
+    const int g = lane >> 4, t16 = lane & 15;
+    const int x = 2 * (g & 1) + ((t16 & 3) >> 1);
+    const int y = S::vy(t16 >> 2);
+#pragma unroll
+    for (int tl = 0; tl < TPG; ++tl)
+      voffl[tl] = (4 * (g >> 1) + (t16 >> 2)) * S::VROW + 16 * ((4 * tl + x) ^ y) + 8 * (t16 & 1);
+  }
+
   f32x16 oacc[S::NDT];
 #pragma unroll
   for (int t = 0; t < S::NDT; ++t) oacc[t] = f32x16{};
   float m_ref = kNegInf;  // reference max of this row, log2 units (same in both lane halves)
   float l_run = 0.f;      // this lane's share of the row sum (halves add up at the end)
-  const bool pos_scale = a.c > 0.f;
 
-  wait_vmem();
+  // Everything issued so far (the prologue blocks and the Q loads) must have
+  // landed.  Waiting for all of it here also tells the compiler the Q loads
+  // are complete, so it puts no load wait inside the loop (where it would
+  // also stall on the DMA in flight).
+  wait_vmcnt<0>();
   __syncthreads();
 
   for (int j = 0; j < nblk; ++j) {
     const int blk = sb0 + j;
-    const int buf = j & 1;
-    if (j + 1 < nblk) dma_block(blk + 1, buf ^ 1);
-
-    const char* kl = smem + buf * S::BUF;
-    const char* vl = kl + S::KBYTES;
+    const int buf = j % S::NSTAGE;
+    // The buffer of block j + NSTAGE - 1 last held block j - 1, which every
+    // wave finished before the barrier that closed the previous iteration.
+    const bool issued = j + S::NSTAGE - 1 < nblk;
+    if (issued) dma_block(blk + S::NSTAGE - 1, (j + S::NSTAGE - 1) % S::NSTAGE);
+    const SDPA_LDS char* kl = smem + buf * S::BUF;
+    const SDPA_LDS char* vl = kl + S::KBYTES;
     const int kw = blk * S::BK + wk * BKW;  // first key of this wave's slice
 
     // A wave whose rows see none of its keys skips the arithmetic.
@@ -315,18 +443,16 @@ __global__ __launch_bounds__(NWQ * NWK * 64) void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
       for (int kt = 0; kt < S::NKT; ++kt) {
         sacc[kt] = f32x16{};
-        const int row = wk * BKW + kt * 32 + col;
-        const char* krow = kl + row * S::KROW;
-        const int sw = row & (S::KSW - 1);
+        const SDPA_LDS char* ktile = kl + (wk * BKW + kt * 32) * S::KROW;
 #pragma unroll
         for (int s = 0; s < S::NQS; ++s) {
           frag af;
           if constexpr (E::ES == 2) {
-            const int c = (2 * s + hl) ^ sw;  // 8 elements = one chunk
-            af = *(const u32x4*)(krow + c * 16);
+            // chunk (2 s + hl) ^ kx(row) of row col: 8 elements
+            af = *(const SDPA_LDS u32x4*)(ktile + koffl[s % SPG] + 16 * S::KG * (s / SPG));
           } else {
             const int d = 2 * s + hl;
-            af = *(const float*)(krow + (((d >> 2) ^ sw) << 4) + (d & 3) * 4);
+            af = *(const SDPA_LDS float*)(ktile + col * S::KROW + (((d >> 2) ^ S::kx(col)) << 4) + (d & 3) * 4);
           }
           sacc[kt] = E::mma(af, qf[s], sacc[kt]);
         }
@@ -336,41 +462,34 @@ __global__ __launch_bounds__(NWQ * NWK * 64) void attn_fwd_kernel(AttnArgs a) {
       const bool edge = (kw + BKW > a.Lk) || (a.mask != MASK_NONE && kw + BKW - 1 > pmin_w) ||
                         (a.mask == MASK_WINDOW && kw <= pmax_w - a.window);
       if (edge) {
+        // Visible keys of this row form [lo, hi]; key of register e in tile
+        // kt is kw + 32 kt + 4 hl + off(e) with off(e) = 8 (e / 4) + e % 4.
+        int hi = a.Lk - 1, lo = 0;
+        if (a.mask != MASK_NONE) hi = min(hi, pos);
+        if (a.mask == MASK_WINDOW) lo = max(lo, pos - a.window + 1);
 #pragma unroll
         for (int kt = 0; kt < S::NKT; ++kt) {
+          const int base = kw + kt * 32 + 4 * hl;
+          const unsigned span = (unsigned)(hi - lo);  // visible iff 0 <= key - lo <= span
+          const int first = lo - base;
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
-            const int key = kw + kt * 32 + 8 * (e >> 2) + 4 * hl + (e & 3);
-            bool vis = key < a.Lk;
-            if (a.mask != MASK_NONE) vis = vis && key <= pos;
-            if (a.mask == MASK_WINDOW) vis = vis && key > pos - a.window;
-            // masked scores become -inf in log2 units whatever the scale's sign
-            if (!vis) sacc[kt][e] = pos_scale ? kNegInf : __builtin_inff();
+            const int off = 8 * (e >> 2) + (e & 3);
+            if ((unsigned)(off - first) > span || hi < lo) sacc[kt][e] = kNegInf;
           }
         }
       }
 
-      // ---- online softmax with lazy rescaling ----
-      float mx;
-      if (pos_scale) {
-        mx = kNegInf;
+      // ---- online softmax with lazy rescaling (scale c > 0) ----
+      float mx = kNegInf;
 #pragma unroll
-        for (int kt = 0; kt < S::NKT; ++kt)
+      for (int kt = 0; kt < S::NKT; ++kt)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kt][e]);
-      } else {  // scale <= 0: the largest scaled score is the smallest raw one
-        mx = __builtin_inff();
-#pragma unroll
-        for (int kt = 0; kt < S::NKT; ++kt)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) mx = fminf(mx, sacc[kt][e]);
-      }
-      mx = pos_scale ? wave_max32(mx) : -wave_max32(-mx);
-      // block max in log2 units; an all-masked block gives -inf (or NaN for
-      // a zero scale times +inf, treated as -inf by the comparison below)
-      const float mxs = (mx == kNegInf || mx == __builtin_inff()) ? kNegInf : mx * a.c;
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kt][e]);
+      mx = wave_max32(mx);
+      const float mxs = mx * c;  // block max in log2 units (-inf if all masked)
       const bool need = mxs > m_ref + kRescale;
-      if (__builtin_amdgcn_ballot_w64(need)) {
+      if (__builtin_expect(__builtin_amdgcn_ballot_w64(need) != 0, 0)) [[unlikely]] {
         const float m_new = need ? mxs : m_ref;
         const float alpha = need ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.0f;
         l_run *= alpha;
@@ -383,10 +502,7 @@ __global__ __launch_bounds__(NWQ * NWK * 64) void attn_fwd_kernel(AttnArgs a) {
       for (int kt = 0; kt < S::NKT; ++kt) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const float x = sacc[kt][e];
-          const float t = pos_scale ? __builtin_fmaf(x, a.c, -msub)
-                                    : ((x == __builtin_inff()) ? kNegInf : x * a.c - msub);
-          const float p = __builtin_amdgcn_exp2f(t);
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][e], c, -msub));
           sacc[kt][e] = p;
           l_run += p;
         }
@@ -416,28 +532,21 @@ __global__ __launch_bounds__(NWQ * NWK * 64) void attn_fwd_kernel(AttnArgs a) {
               // 4 dv values of one key; the hardware hands lane i of the group
               // element i%4 of the chunk addressed by lane 4j + i/4, i.e. the
               // 4 keys (j = 0..3) of dv column 16*(g%2) + i.
-              const int g = lane >> 4, t16 = lane & 15;
-              const int dv0 = 32 * t + 16 * (g & 1) + 4 * (t16 & 3);
-              u32x2 half[2];
-#pragma unroll
-              for (int rr = 0; rr < 2; ++rr) {
-                const int row = kbase_t + 16 * s2 + 8 * rr + 4 * (g >> 1) + (t16 >> 2);
-                const int c = (dv0 >> 3) ^ (2 * (row & (S::VSW - 1)));
-                const char* p = vl + row * S::VROW + c * 16 + (dv0 & 7) * 2;
-                const i16x4 v4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SDPA_LDS i16x4*)p);
-                half[rr] = __builtin_bit_cast(u32x2, v4);
-              }
+              const SDPA_LDS char* vb = vl + (kbase_t + 16 * s2) * S::VROW + voffl[t % TPG] + 16 * S::VG * (t / TPG);
+              const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SDPA_LDS i16x4*)vb);
+              const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SDPA_LDS i16x4*)(vb + 8 * S::VROW));
+              const u32x2 h0 = __builtin_bit_cast(u32x2, v0), h1 = __builtin_bit_cast(u32x2, v1);
               u32x4 f;
-              f[0] = half[0][0];
-              f[1] = half[0][1];
-              f[2] = half[1][0];
-              f[3] = half[1][1];
+              f[0] = h0[0];
+              f[1] = h0[1];
+              f[2] = h1[0];
+              f[3] = h1[1];
               af = f;
             } else {
               const int row = kbase_t + 8 * (s2 >> 2) + 4 * hl + (s2 & 3);
               const int dv = 32 * t + col;
-              const int c = (dv >> 2) ^ (2 * (row & (S::VSW - 1)));
-              af = *(const float*)(vl + row * S::VROW + c * 16 + (dv & 3) * 4);
+              const int cc = (dv >> 2) ^ S::vy(row);
+              af = *(const SDPA_LDS float*)(vl + row * S::VROW + cc * 16 + (dv & 3) * 4);
             }
             oacc[t] = E::mma(af, bf, oacc[t]);
           }
@@ -445,69 +554,32 @@ __global__ __launch_bounds__(NWQ * NWK * 64) void attn_fwd_kernel(AttnArgs a) {
       }
     }
 
-    wait_vmem();
+    // Block j + 1 must have landed before the barrier; the one issued in
+    // this iteration (three stages) may stay in flight.
+    if (S::NSTAGE == 3 && issued) wait_vmcnt<S::DMA_MIN>();
+    else wait_vmcnt<0>();
     __syncthreads();
   }
 
   // ---- epilogue ----
-  const float l_row = l_run + __shfl_xor(l_run, 32);  // both halves' keys
-  const int64_t ws_row = ((int64_t)z * a.R + r) * a.splits + split;
+  float l_row = l_run + __shfl_xor(l_run, 32);  // both halves' keys
 
-  if constexpr (NWK == 1) {
-    if (!row_ok) return;
-    if (a.splits == 1) {
-      const float inv = 1.0f / l_row;
-      char* orow = (char*)a.o + ((int64_t)b * a.os[0] + (int64_t)hq * a.os[1] + (int64_t)iq * a.os[2]) * E::ES;
+  if constexpr (NWK > 1) {
+    // Merge the NWK key slices of the same rows: waves wk > 0 leave their
+    // partial (m, l, O) in LDS (the loop ended with a barrier, so both buffers
+    // are free); wave wk == 0 folds them into its own registers.
+    SDPA_LDS float* mo = (SDPA_LDS float*)smem;               // [MSLOTS][32][MROW]
+    SDPA_LDS float* mml = (SDPA_LDS float*)(smem + S::BUF);  // [MSLOTS][32][2]
+    if (wk > 0) {
+      const int slot = wq * (NWK - 1) + (wk - 1);
+      SDPA_LDS float* myo = mo + (slot * 32 + col) * S::MROW;
 #pragma unroll
       for (int t = 0; t < S::NDT; ++t) {
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
           const int d = t * 32 + 8 * i4 + 4 * hl;
-          if (d < a.dv) {
-            if constexpr (E::ES == 2) {
-              u32x2 w;
-              w[0] = E::pack2(oacc[t][4 * i4 + 0] * inv, oacc[t][4 * i4 + 1] * inv);
-              w[1] = E::pack2(oacc[t][4 * i4 + 2] * inv, oacc[t][4 * i4 + 3] * inv);
-              *(u32x2*)(orow + d * 2) = w;
-            } else {
-              float4 w = make_float4(oacc[t][4 * i4 + 0] * inv, oacc[t][4 * i4 + 1] * inv,
-                                     oacc[t][4 * i4 + 2] * inv, oacc[t][4 * i4 + 3] * inv);
-              *(float4*)(orow + d * 4) = w;
-            }
-          }
-        }
-      }
-      if (a.lse && hl == 0)
-        a.lse[((int64_t)b * a.Hq + hq) * a.Lq + iq] = (m_ref + log2f(l_row)) * kLn2;
-    } else {
-      float* wo = a.ws_o + ws_row * a.dv;
-#pragma unroll
-      for (int t = 0; t < S::NDT; ++t) {
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const int d = t * 32 + 8 * i4 + 4 * hl;
-          if (d < a.dv)
-            *(float4*)(wo + d) = make_float4(oacc[t][4 * i4 + 0], oacc[t][4 * i4 + 1],
-                                             oacc[t][4 * i4 + 2], oacc[t][4 * i4 + 3]);
-        }
-      }
-      if (hl == 0) *(float2*)(a.ws_ml + ws_row * 2) = make_float2(m_ref, l_row);
-    }
-  } else {
-    // Merge the NWK key slices of the same rows through LDS.  The tile
-    // buffers are free: the loop ended with a barrier.
-    float* mo = (float*)smem;                                    // [NWQ*NWK][32][MROW]
-    float* mml = (float*)(smem + NWQ * NWK * 32 * S::MROW * 4);  // [NWQ*NWK][32][2]
-    {
-      const int slot = wq * NWK + wk;
-      float* myo = mo + (slot * 32 + col) * S::MROW;
-#pragma unroll
-      for (int t = 0; t < S::NDT; ++t) {
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const int d = t * 32 + 8 * i4 + 4 * hl;
-          *(float4*)(myo + d) = make_float4(oacc[t][4 * i4 + 0], oacc[t][4 * i4 + 1],
-                                            oacc[t][4 * i4 + 2], oacc[t][4 * i4 + 3]);
+          *(SDPA_LDS f32x4*)(myo + d) = f32x4{oacc[t][4 * i4 + 0], oacc[t][4 * i4 + 1],
+                                              oacc[t][4 * i4 + 2], oacc[t][4 * i4 + 3]};
         }
       }
       if (hl == 0) {
@@ -516,38 +588,75 @@ __global__ __launch_bounds__(NWQ * NWK * 64) void attn_fwd_kernel(AttnArgs a) {
       }
     }
     __syncthreads();
-    const int rows_here = min(S::BM, a.R - r_wg);
-    for (int e = tid; e < S::BM * DV; e += S::NT) {
-      const int q = e / DV;  // row inside the workgroup tile
-      const int d = e % DV;
-      if (q >= rows_here || d >= a.dv) continue;
-      const int qw = q >> 5, qc = q & 31;
-      float M = kNegInf;
+    if (wk > 0) return;
+    float M = m_ref;
 #pragma unroll
-      for (int w = 0; w < NWK; ++w) M = fmaxf(M, mml[((qw * NWK + w) * 32 + qc) * 2]);
-      const float Mu = (M == kNegInf) ? 0.f : M;
-      float L = 0.f, acc = 0.f;
+    for (int w = 1; w < NWK; ++w) M = fmaxf(M, mml[((wq * (NWK - 1) + w - 1) * 32 + col) * 2]);
+    const float Mu = (M == kNegInf) ? 0.f : M;
+    const float own = __builtin_amdgcn_exp2f(m_ref - Mu);
+    l_row *= own;
 #pragma unroll
-      for (int w = 0; w < NWK; ++w) {
-        const int sl = (qw * NWK + w) * 32 + qc;
-        const float sc = __builtin_amdgcn_exp2f(mml[sl * 2] - Mu);
-        L += sc * mml[sl * 2 + 1];
-        acc += sc * mo[sl * S::MROW + d];
-      }
-      const int rr = r_wg + q;
-      const int g2 = rr % a.G, i2 = rr / a.G, h2 = kvh * a.G + g2;
-      if (a.splits == 1) {
-        const float val = acc / L;
-        char* orow = (char*)a.o + ((int64_t)b * a.os[0] + (int64_t)h2 * a.os[1] + (int64_t)i2 * a.os[2]) * E::ES;
-        if constexpr (E::ES == 2) *(unsigned short*)(orow + d * 2) = E::to_store(val);
-        else *(float*)(orow + d * 4) = val;
-        if (d == 0 && a.lse) a.lse[((int64_t)b * a.Hq + h2) * a.Lq + i2] = (Mu + log2f(L)) * kLn2;
-      } else {
-        const int64_t wr = ((int64_t)z * a.R + rr) * a.splits + split;
-        a.ws_o[wr * a.dv + d] = acc;
-        if (d == 0) *(float2*)(a.ws_ml + wr * 2) = make_float2(M, L);
+    for (int t = 0; t < S::NDT; ++t) oacc[t] *= own;
+#pragma unroll
+    for (int w = 1; w < NWK; ++w) {
+      const int sl = (wq * (NWK - 1) + w - 1) * 32 + col;
+      const float sc = __builtin_amdgcn_exp2f(mml[sl * 2] - Mu);
+      l_row += sc * mml[sl * 2 + 1];
+      const SDPA_LDS float* po = mo + sl * S::MROW;
+#pragma unroll
+      for (int t = 0; t < S::NDT; ++t) {
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const f32x4 v4 = *(const SDPA_LDS f32x4*)(po + t * 32 + 8 * i4 + 4 * hl);
+          oacc[t][4 * i4 + 0] += sc * v4[0];
+          oacc[t][4 * i4 + 1] += sc * v4[1];
+          oacc[t][4 * i4 + 2] += sc * v4[2];
+          oacc[t][4 * i4 + 3] += sc * v4[3];
+        }
       }
     }
+    m_ref = M;
+  }
+
+  if (!row_ok) return;
+  if (a.splits == 1) {
+    const float inv = 1.0f / l_row;
+    char* orow = (char*)a.o + ((int64_t)b * a.os[0] + (int64_t)hq * a.os[1] + (int64_t)iq * a.os[2]) * E::ES;
+#pragma unroll
+    for (int t = 0; t < S::NDT; ++t) {
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int d = t * 32 + 8 * i4 + 4 * hl;
+        if (d < a.dv) {
+          if constexpr (E::ES == 2) {
+            u32x2 w;
+            w[0] = E::pack2(oacc[t][4 * i4 + 0] * inv, oacc[t][4 * i4 + 1] * inv);
+            w[1] = E::pack2(oacc[t][4 * i4 + 2] * inv, oacc[t][4 * i4 + 3] * inv);
+            *(u32x2*)(orow + d * 2) = w;
+          } else {
+            float4 w = make_float4(oacc[t][4 * i4 + 0] * inv, oacc[t][4 * i4 + 1] * inv,
+                                   oacc[t][4 * i4 + 2] * inv, oacc[t][4 * i4 + 3] * inv);
+            *(float4*)(orow + d * 4) = w;
+          }
+        }
+      }
+    }
+    if (a.lse && hl == 0)
+      a.lse[((int64_t)b * a.Hq + hq) * a.Lq + iq] = (m_ref + log2f(l_row)) * kLn2;
+  } else {
+    const int64_t ws_row = ((int64_t)z * a.R + r) * a.splits + split;
+    float* wo = a.ws_o + ws_row * a.dv;
+#pragma unroll
+    for (int t = 0; t < S::NDT; ++t) {
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int d = t * 32 + 8 * i4 + 4 * hl;
+        if (d < a.dv)
+          *(float4*)(wo + d) = make_float4(oacc[t][4 * i4 + 0], oacc[t][4 * i4 + 1],
+                                           oacc[t][4 * i4 + 2], oacc[t][4 * i4 + 3]);
+      }
+    }
+    if (hl == 0) *(float2*)(a.ws_ml + ws_row * 2) = make_float2(m_ref, l_row);
   }
 }
 

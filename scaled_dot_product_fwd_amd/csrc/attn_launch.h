@@ -9,10 +9,10 @@
 
 namespace sdpa {
 
-template <class E, int DQK, int DV, int NWQ, int NWK, int BKW>
+template <class E, int DQK, int DV, int NWQ, int NWK, int BKW, int WPE>
 int launch_one(const Plan& p, const AttnArgs& a, void* stream, std::string* err) {
   using S = dev::Shape<E, DQK, DV, NWQ, NWK, BKW>;
-  auto kern = dev::attn_fwd_kernel<E, DQK, DV, NWQ, NWK, BKW>;
+  auto kern = dev::attn_fwd_kernel<E, DQK, DV, NWQ, NWK, BKW, WPE>;
   // Check the compiled kernel can run the workgroup size it is launched with,
   // once per instance: an oversized launch must fail loudly, never return
   // silently unwritten output (mlx PR #4185 "Add force_fused option to
@@ -54,7 +54,8 @@ int launch_one(const Plan& p, const AttnArgs& a, void* stream, std::string* err)
       *err = "plan and kernel instance disagree on the wave arrangement";                      \
       return SDPA_E_PLAN;                                                                      \
     }                                                                                          \
-    return launch_one<dev::E, DQK, DV, f_.nwq, f_.nwk, f_.bkw>(p, a, stream, err);             \
+    return launch_one<dev::E, DQK, DV, f_.nwq, f_.nwk, f_.bkw,                  \
+                      wpe_for(KIND, dev::E::ES, DQK, DV)>(p, a, stream, err);             \
   }
 
 // Head-dim pairs of the 16-bit types: equal padded dims plus (192, 128).

@@ -58,12 +58,12 @@ const char* mask_name(int m) {
 }  // namespace
 
 size_t attn_lds_bytes(int dtype, int dqk_pad, int dv_pad, const Family& f) {
-  // Mirrors Shape<> in attn_kernel.h.
+  // Mirrors Shape<> in attn_kernel.h: two or three K+V tile buffers (the
+  // cross-wave merge reuses them).
   const int es = dtype == SDPA_F32 ? 4 : 2;
-  const int bk = f.nwk * f.bkw;
-  const int tiles = 2 * bk * (dqk_pad + dv_pad) * es;
-  const int merge = f.nwk > 1 ? f.nwq * f.nwk * 32 * (dv_pad + 4) * 4 + f.nwq * f.nwk * 32 * 8 : 0;
-  return (size_t)(tiles > merge ? tiles : merge);
+  const int buf = f.nwk * f.bkw * (dqk_pad + dv_pad) * es;
+  const int stages = 3 * buf <= (f.nwq > 1 ? 80 : 160) * 1024 ? 3 : 2;
+  return (size_t)stages * buf;
 }
 
 int make_plan(const sdpa_desc_t* d, Plan* p, std::string* err) {

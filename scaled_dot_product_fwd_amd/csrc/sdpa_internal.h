@@ -64,6 +64,17 @@ constexpr Family family_for(int kind, int elem_bytes, int dqk_pad, int dv_pad) {
   return key_bytes * 64 * 2 <= 80 * 1024 ? Family{4, 1, 64} : Family{4, 1, 32};
 }
 
+// Waves per SIMD each kernel instance is compiled for: two (so one wave's
+// softmax overlaps the other's MFMA) where the registers of a 32-row tile fit
+// 256 per wave without spilling, else one.
+constexpr int wpe_for(int kind, int elem_bytes, int dqk_pad, int dv_pad) {
+  const int dmax = dqk_pad > dv_pad ? dqk_pad : dv_pad;
+  if (kind == KIND_DECODE) return 1;
+  if (elem_bytes == 4) return dmax <= 96 ? 2 : 1;
+  if (dqk_pad == 192 && dv_pad == 128) return 2;
+  return dmax <= (kind == KIND_PREFILL ? 160 : 128) ? 2 : 1;
+}
+
 struct Plan {
   int dtype;
   int kind;              // KIND_PREFILL / KIND_SHORT / KIND_DECODE
