@@ -170,20 +170,18 @@ struct Shape {
   static __device__ __forceinline__ int vy(int row) {
     return VG == 16 ? 4 * (row & 3) : (VG == 8 ? 2 * (row & 3) : 2 * (row & 1));
   }
-  // Pipeline depth: three LDS buffers (two blocks in flight while one is
-  // computed) when they fit the occupancy target of the kind, else two.
-  static constexpr int NSTAGE = (3 * BUF <= (NWQ > 1 ? 80 : 160) * 1024) ? 3 : 2;
-  static constexpr int LDS = NSTAGE * BUF;
-  // Cross-wave merge (NWK > 1): the waves with wk > 0 leave O in buffer 0 as
-  // [slot][q][MROW] and (m, l) in buffer 1; MROW is padded when that fits.
+  // Two K buffers and two V buffers (see the kernel's block loop).
+  static constexpr int LDS = 2 * BUF;
+  // Overlap the next block's QK with this block's softmax when two blocks of
+  // scores fit the registers next to Q and O.
+  static constexpr bool PIPE = false;
+  // Cross-wave merge (NWK > 1): the waves with wk > 0 leave O at the start of
+  // LDS as [slot][q][MROW] and (m, l) after BUF bytes; MROW is padded when
+  // that fits.
   static constexpr int MSLOTS = NWQ * (NWK - 1);
   static constexpr int MROW = (MSLOTS * 32 * (DV + 4) * 4 <= BUF) ? DV + 4 : DV;
   static_assert(MSLOTS * 32 * MROW * 4 <= BUF && MSLOTS * 32 * 8 <= BUF, "merge scratch must fit a buffer");
-  // DMA instructions one wave issues per block (the fewest, when the tile
-  // does not divide evenly between the waves).
-  static constexpr int KDMA_MIN = KDMA / NW, VDMA_MIN = VDMA / NW;
-  static constexpr int DMA_MIN = KDMA_MIN + VDMA_MIN;
-  static_assert(DMA_MIN >= 1 && (KDMA + VDMA + NW - 1) / NW <= 63, "vmcnt range");
+  static_assert((KDMA + NW - 1) / NW + (VDMA + NW - 1) / NW <= 63, "vmcnt range");
   static_assert(BKW % 32 == 0, "BKW must be a multiple of 32");
   static_assert(DQK % E::KQK == 0 && DV % 32 == 0, "bad head-dim tile");
   static_assert(KBYTES % 1024 == 0 && VBYTES % 1024 == 0, "tiles must be whole DMA instructions");
@@ -309,22 +307,18 @@ void attn_fwd_kernel(AttnArgs a) {
     voff[ii] = (unsigned)(row * vstr) + colb;
   }
 
+  // LDS: K tiles in two buffers, then V tiles in two buffers.  Block j's K
+  // sits in K buffer j % 2 and its V in V buffer j % 2.
   const unsigned lds_base = (unsigned)(uintptr_t)smem;
-  auto dma_block = [&](int blk, int buf) __attribute__((always_inline)) {
+  auto dma_k = [&](int blk, int buf) __attribute__((always_inline)) {
     const int k0 = blk * S::BK;
-    const unsigned kl = lds_base + buf * S::BUF;
-    const unsigned vl = kl + S::KBYTES;
+    const unsigned kl = lds_base + buf * S::KBYTES;
     if (k0 + S::BK <= a.Lk) {
       const char* kb = kbase + (int64_t)k0 * kstr;
-      const char* vb = vbase + (int64_t)k0 * vstr;
 #pragma unroll
       for (int ii = 0; ii < KPW; ++ii)
         if ((ii + 1) * S::NW <= S::KDMA || ii * S::NW + wave_u < S::KDMA)
           lds_dma16(kb + koff[ii], kl + (ii * S::NW + wave_u) * 1024);
-#pragma unroll
-      for (int ii = 0; ii < VPW; ++ii)
-        if ((ii + 1) * S::NW <= S::VDMA || ii * S::NW + wave_u < S::VDMA)
-          lds_dma16(vb + voff[ii], vl + (ii * S::NW + wave_u) * 1024);
     } else {
 #pragma unroll
       for (int ii = 0; ii < KPW; ++ii) {
@@ -334,6 +328,18 @@ void attn_fwd_kernel(AttnArgs a) {
         const int grow = min(k0 + row, a.Lk - 1);
         lds_dma16(kbase + (int64_t)grow * kstr + colb, kl + (ii * S::NW + wave_u) * 1024);
       }
+    }
+  };
+  auto dma_v = [&](int blk, int buf) __attribute__((always_inline)) {
+    const int k0 = blk * S::BK;
+    const unsigned vl = lds_base + 2 * S::KBYTES + buf * S::VBYTES;
+    if (k0 + S::BK <= a.Lk) {
+      const char* vb = vbase + (int64_t)k0 * vstr;
+#pragma unroll
+      for (int ii = 0; ii < VPW; ++ii)
+        if ((ii + 1) * S::NW <= S::VDMA || ii * S::NW + wave_u < S::VDMA)
+          lds_dma16(vb + voff[ii], vl + (ii * S::NW + wave_u) * 1024);
+    } else {
 #pragma unroll
       for (int ii = 0; ii < VPW; ++ii) {
         if ((ii + 1) * S::NW > S::VDMA && ii * S::NW + wave_u >= S::VDMA) continue;
@@ -345,10 +351,13 @@ void attn_fwd_kernel(AttnArgs a) {
     }
   };
 
-  // Prologue: the first NSTAGE-1 blocks go in flight.
-#pragma unroll
-  for (int st = 0; st < S::NSTAGE - 1; ++st)
-    if (st < nblk) dma_block(sb0 + st, st);
+  // Prologue: K of block 0 (and of block 1 when the QK runs a block ahead)
+  // and V of block 0 go in flight.
+  if (nblk > 0) {
+    dma_k(sb0, 0);
+    dma_v(sb0, 0);
+  }
+  if (S::PIPE && nblk > 1) dma_k(sb0 + 1, 1);
 
   // ---- Q fragments (B operand of S^T = K Q^T), kept in registers ----
   frag qf[S::NQS];
@@ -423,142 +432,161 @@ void attn_fwd_kernel(AttnArgs a) {
   wait_vmcnt<0>();
   __syncthreads();
 
-  for (int j = 0; j < nblk; ++j) {
-    const int blk = sb0 + j;
-    const int buf = j % S::NSTAGE;
-    // The buffer of block j + NSTAGE - 1 last held block j - 1, which every
-    // wave finished before the barrier that closed the previous iteration.
-    const bool issued = j + S::NSTAGE - 1 < nblk;
-    if (issued) dma_block(blk + S::NSTAGE - 1, (j + S::NSTAGE - 1) % S::NSTAGE);
-    const SDPA_LDS char* kl = smem + buf * S::BUF;
-    const SDPA_LDS char* vl = kl + S::KBYTES;
-    const int kw = blk * S::BK + wk * BKW;  // first key of this wave's slice
+  // ---- S^T = K Q^T of one block (this wave's BKW keys) ----
+  auto qk = [&](int j, f32x16 (&sacc)[S::NKT]) __attribute__((always_inline)) {
+    const SDPA_LDS char* kl = smem + (j & 1) * S::KBYTES;
+#pragma unroll
+    for (int kt = 0; kt < S::NKT; ++kt) {
+      sacc[kt] = f32x16{};
+      const SDPA_LDS char* ktile = kl + (wk * BKW + kt * 32) * S::KROW;
+#pragma unroll
+      for (int s = 0; s < S::NQS; ++s) {
+        frag af;
+        if constexpr (E::ES == 2) {
+          // chunk (2 s + hl) ^ kx(row) of row col: 8 elements
+          af = *(const SDPA_LDS u32x4*)(ktile + koffl[s % SPG] + 16 * S::KG * (s / SPG));
+        } else {
+          const int d = 2 * s + hl;
+          af = *(const SDPA_LDS float*)(ktile + col * S::KROW + (((d >> 2) ^ S::kx(col)) << 4) + (d & 3) * 4);
+        }
+        sacc[kt] = E::mma(af, qf[s], sacc[kt]);
+      }
+    }
+  };
 
-    // A wave whose rows see none of its keys skips the arithmetic.
-    const bool skip = kw >= a.Lk || (a.mask != MASK_NONE && kw > pmax_w) ||
-                      (a.mask == MASK_WINDOW && kw + BKW - 1 <= pmin_w - a.window);
-    if (!skip) {
-      // ---- S^T = K Q^T for this wave's BKW keys ----
-      f32x16 sacc[S::NKT];
+  // ---- mask, online softmax and O^T += V^T P^T of block j ----
+  // `next` (when given) is the following block's QK, issued between this
+  // block's softmax and its PV product: the MFMAs of the one and the vector
+  // work of the other are independent, so they overlap.
+  auto softmax_pv = [&](int j, f32x16 (&sacc)[S::NKT], f32x16 (*sn)[S::NKT]) __attribute__((always_inline)) {
+    const int kw = (sb0 + j) * S::BK + wk * BKW;  // first key of this wave's slice
+    // ---- mask edge blocks (diagonal, window edge, Lk tail) ----
+    const bool edge = (kw + BKW > a.Lk) || (a.mask != MASK_NONE && kw + BKW - 1 > pmin_w) ||
+                      (a.mask == MASK_WINDOW && kw <= pmax_w - a.window);
+    if (edge) {
+      // Visible keys of this row form [lo, hi]; key of register e in tile
+      // kt is kw + 32 kt + 4 hl + off(e) with off(e) = 8 (e / 4) + e % 4.
+      int hi = a.Lk - 1, lo = 0;
+      if (a.mask != MASK_NONE) hi = min(hi, pos);
+      if (a.mask == MASK_WINDOW) lo = max(lo, pos - a.window + 1);
 #pragma unroll
       for (int kt = 0; kt < S::NKT; ++kt) {
-        sacc[kt] = f32x16{};
-        const SDPA_LDS char* ktile = kl + (wk * BKW + kt * 32) * S::KROW;
-#pragma unroll
-        for (int s = 0; s < S::NQS; ++s) {
-          frag af;
-          if constexpr (E::ES == 2) {
-            // chunk (2 s + hl) ^ kx(row) of row col: 8 elements
-            af = *(const SDPA_LDS u32x4*)(ktile + koffl[s % SPG] + 16 * S::KG * (s / SPG));
-          } else {
-            const int d = 2 * s + hl;
-            af = *(const SDPA_LDS float*)(ktile + col * S::KROW + (((d >> 2) ^ S::kx(col)) << 4) + (d & 3) * 4);
-          }
-          sacc[kt] = E::mma(af, qf[s], sacc[kt]);
-        }
-      }
-
-      // ---- mask edge blocks (diagonal, window edge, Lk tail) ----
-      const bool edge = (kw + BKW > a.Lk) || (a.mask != MASK_NONE && kw + BKW - 1 > pmin_w) ||
-                        (a.mask == MASK_WINDOW && kw <= pmax_w - a.window);
-      if (edge) {
-        // Visible keys of this row form [lo, hi]; key of register e in tile
-        // kt is kw + 32 kt + 4 hl + off(e) with off(e) = 8 (e / 4) + e % 4.
-        int hi = a.Lk - 1, lo = 0;
-        if (a.mask != MASK_NONE) hi = min(hi, pos);
-        if (a.mask == MASK_WINDOW) lo = max(lo, pos - a.window + 1);
-#pragma unroll
-        for (int kt = 0; kt < S::NKT; ++kt) {
-          const int base = kw + kt * 32 + 4 * hl;
-          const unsigned span = (unsigned)(hi - lo);  // visible iff 0 <= key - lo <= span
-          const int first = lo - base;
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int off = 8 * (e >> 2) + (e & 3);
-            if ((unsigned)(off - first) > span || hi < lo) sacc[kt][e] = kNegInf;
-          }
-        }
-      }
-
-      // ---- online softmax with lazy rescaling (scale c > 0) ----
-      float mx = kNegInf;
-#pragma unroll
-      for (int kt = 0; kt < S::NKT; ++kt)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kt][e]);
-      mx = wave_max32(mx);
-      const float mxs = mx * c;  // block max in log2 units (-inf if all masked)
-      const bool need = mxs > m_ref + kRescale;
-      if (__builtin_expect(__builtin_amdgcn_ballot_w64(need) != 0, 0)) [[unlikely]] {
-        const float m_new = need ? mxs : m_ref;
-        const float alpha = need ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.0f;
-        l_run *= alpha;
-#pragma unroll
-        for (int t = 0; t < S::NDT; ++t) oacc[t] *= alpha;
-        m_ref = m_new;
-      }
-      const float msub = (m_ref == kNegInf) ? 0.f : m_ref;
-#pragma unroll
-      for (int kt = 0; kt < S::NKT; ++kt) {
+        const int base = kw + kt * 32 + 4 * hl;
+        const unsigned span = (unsigned)(hi - lo);  // visible iff 0 <= key - lo <= span
+        const int first = lo - base;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][e], c, -msub));
-          sacc[kt][e] = p;
-          l_run += p;
-        }
-      }
-
-      // ---- O^T += V^T P^T ----
-#pragma unroll
-      for (int kt = 0; kt < S::NKT; ++kt) {
-        const int kbase_t = wk * BKW + kt * 32;  // first key of this tile inside the block
-#pragma unroll
-        for (int s2 = 0; s2 < 32 / E::KPV; ++s2) {
-          frag bf;
-          if constexpr (E::ES == 2) {
-            u32x4 pk;
-#pragma unroll
-            for (int w = 0; w < 4; ++w)
-              pk[w] = E::pack2(sacc[kt][8 * s2 + 2 * w], sacc[kt][8 * s2 + 2 * w + 1]);
-            bf = pk;
-          } else {
-            bf = sacc[kt][s2];
-          }
-#pragma unroll
-          for (int t = 0; t < S::NDT; ++t) {
-            frag af;
-            if constexpr (E::ES == 2) {
-              // Transposing read: lane t16 of group g supplies the address of
-              // 4 dv values of one key; the hardware hands lane i of the group
-              // element i%4 of the chunk addressed by lane 4j + i/4, i.e. the
-              // 4 keys (j = 0..3) of dv column 16*(g%2) + i.
-              const SDPA_LDS char* vb = vl + (kbase_t + 16 * s2) * S::VROW + voffl[t % TPG] + 16 * S::VG * (t / TPG);
-              const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SDPA_LDS i16x4*)vb);
-              const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SDPA_LDS i16x4*)(vb + 8 * S::VROW));
-              const u32x2 h0 = __builtin_bit_cast(u32x2, v0), h1 = __builtin_bit_cast(u32x2, v1);
-              u32x4 f;
-              f[0] = h0[0];
-              f[1] = h0[1];
-              f[2] = h1[0];
-              f[3] = h1[1];
-              af = f;
-            } else {
-              const int row = kbase_t + 8 * (s2 >> 2) + 4 * hl + (s2 & 3);
-              const int dv = 32 * t + col;
-              const int cc = (dv >> 2) ^ S::vy(row);
-              af = *(const SDPA_LDS float*)(vl + row * S::VROW + cc * 16 + (dv & 3) * 4);
-            }
-            oacc[t] = E::mma(af, bf, oacc[t]);
-          }
+          const int off = 8 * (e >> 2) + (e & 3);
+          if ((unsigned)(off - first) > span || hi < lo) sacc[kt][e] = kNegInf;
         }
       }
     }
 
-    // Block j + 1 must have landed before the barrier; the one issued in
-    // this iteration (three stages) may stay in flight.
-    if (S::NSTAGE == 3 && issued) wait_vmcnt<S::DMA_MIN>();
-    else wait_vmcnt<0>();
+    // ---- online softmax with lazy rescaling (scale c > 0) ----
+    float mx = kNegInf;
+#pragma unroll
+    for (int kt = 0; kt < S::NKT; ++kt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kt][e]);
+    mx = wave_max32(mx);
+    const float mxs = mx * c;  // block max in log2 units (-inf if all masked)
+    const bool need = mxs > m_ref + kRescale;
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(need) != 0, 0)) [[unlikely]] {
+      const float m_new = need ? mxs : m_ref;
+      const float alpha = need ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.0f;
+      l_run *= alpha;
+#pragma unroll
+      for (int t = 0; t < S::NDT; ++t) oacc[t] *= alpha;
+      m_ref = m_new;
+    }
+    const float msub = (m_ref == kNegInf) ? 0.f : m_ref;
+
+    if (sn) qk(j + 1, *sn);
+
+#pragma unroll
+    for (int kt = 0; kt < S::NKT; ++kt) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][e], c, -msub));
+        sacc[kt][e] = p;
+        l_run += p;
+      }
+    }
+
+    // ---- O^T += V^T P^T ----
+    const SDPA_LDS char* vl = smem + 2 * S::KBYTES + (j & 1) * S::VBYTES;
+#pragma unroll
+    for (int kt = 0; kt < S::NKT; ++kt) {
+      const int kbase_t = wk * BKW + kt * 32;  // first key of this tile inside the block
+#pragma unroll
+      for (int s2 = 0; s2 < 32 / E::KPV; ++s2) {
+        frag bf;
+        if constexpr (E::ES == 2) {
+          u32x4 pk;
+#pragma unroll
+          for (int w = 0; w < 4; ++w)
+            pk[w] = E::pack2(sacc[kt][8 * s2 + 2 * w], sacc[kt][8 * s2 + 2 * w + 1]);
+          bf = pk;
+        } else {
+          bf = sacc[kt][s2];
+        }
+#pragma unroll
+        for (int t = 0; t < S::NDT; ++t) {
+          frag af;
+          if constexpr (E::ES == 2) {
+            // Transposing read: lane t16 of group g supplies the address of
+            // 4 dv values of one key; the hardware hands lane i of the group
+            // element i%4 of the chunk addressed by lane 4j + i/4, i.e. the
+            // 4 keys (j = 0..3) of dv column 16*(g%2) + i.
+            const SDPA_LDS char* vb = vl + (kbase_t + 16 * s2) * S::VROW + voffl[t % TPG] + 16 * S::VG * (t / TPG);
+            const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SDPA_LDS i16x4*)vb);
+            const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SDPA_LDS i16x4*)(vb + 8 * S::VROW));
+            const u32x2 h0 = __builtin_bit_cast(u32x2, v0), h1 = __builtin_bit_cast(u32x2, v1);
+            u32x4 f;
+            f[0] = h0[0];
+            f[1] = h0[1];
+            f[2] = h1[0];
+            f[3] = h1[1];
+            af = f;
+          } else {
+            const int row = kbase_t + 8 * (s2 >> 2) + 4 * hl + (s2 & 3);
+            const int dv = 32 * t + col;
+            const int cc = (dv >> 2) ^ S::vy(row);
+            af = *(const SDPA_LDS float*)(vl + row * S::VROW + cc * 16 + (dv & 3) * 4);
+          }
+          oacc[t] = E::mma(af, bf, oacc[t]);
+        }
+      }
+    }
+  };
+
+  // Iteration j: DMA K of block j + 2 (into the K buffer block j used, whose
+  // QK ran in the previous iteration) and V of block j + 1 (into the V buffer
+  // of block j - 1); softmax + PV of block j with the QK of block j + 1 in
+  // between; then wait for the DMAs and synchronise.  The S^T registers of
+  // two consecutive blocks alternate between sa and sb.
+  // Without the overlap (large head dims, whose registers do not hold two
+  // blocks of scores) K runs one block ahead instead of two and each
+  // iteration computes its own QK.
+  constexpr int KAHEAD = S::PIPE ? 2 : 1;
+  f32x16 sa[S::NKT], sb[S::NKT];
+  if (S::PIPE && nblk > 0) qk(0, sa);
+  auto iter = [&](int j, f32x16 (&cur)[S::NKT], f32x16 (&nxt)[S::NKT]) __attribute__((always_inline)) {
+    if (j + KAHEAD < nblk) dma_k(sb0 + j + KAHEAD, (j + KAHEAD) & 1);
+    if (j + 1 < nblk) dma_v(sb0 + j + 1, (j + 1) & 1);
+    if constexpr (S::PIPE) {
+      if (j + 1 < nblk) softmax_pv(j, cur, &nxt);
+      else softmax_pv(j, cur, nullptr);
+    } else {
+      qk(j, cur);
+      softmax_pv(j, cur, nullptr);
+    }
+    wait_vmcnt<0>();
     __syncthreads();
+  };
+  for (int j = 0; j < nblk; j += 2) {
+    iter(j, sa, sb);
+    if (j + 1 < nblk) iter(j + 1, sb, sa);
   }
 
   // ---- epilogue ----
@@ -588,38 +616,40 @@ void attn_fwd_kernel(AttnArgs a) {
       }
     }
     __syncthreads();
-    if (wk > 0) return;
-    float M = m_ref;
+    if (wk == 0) {
+      float M = m_ref;
 #pragma unroll
-    for (int w = 1; w < NWK; ++w) M = fmaxf(M, mml[((wq * (NWK - 1) + w - 1) * 32 + col) * 2]);
-    const float Mu = (M == kNegInf) ? 0.f : M;
-    const float own = __builtin_amdgcn_exp2f(m_ref - Mu);
-    l_row *= own;
+      for (int w = 1; w < NWK; ++w) M = fmaxf(M, mml[((wq * (NWK - 1) + w - 1) * 32 + col) * 2]);
+      const float Mu = (M == kNegInf) ? 0.f : M;
+      const float own = __builtin_amdgcn_exp2f(m_ref - Mu);
+      l_row *= own;
 #pragma unroll
-    for (int t = 0; t < S::NDT; ++t) oacc[t] *= own;
+      for (int t = 0; t < S::NDT; ++t) oacc[t] *= own;
 #pragma unroll
-    for (int w = 1; w < NWK; ++w) {
-      const int sl = (wq * (NWK - 1) + w - 1) * 32 + col;
-      const float sc = __builtin_amdgcn_exp2f(mml[sl * 2] - Mu);
-      l_row += sc * mml[sl * 2 + 1];
-      const SDPA_LDS float* po = mo + sl * S::MROW;
+      for (int w = 1; w < NWK; ++w) {
+        const int sl = (wq * (NWK - 1) + w - 1) * 32 + col;
+        const float sc = __builtin_amdgcn_exp2f(mml[sl * 2] - Mu);
+        l_row += sc * mml[sl * 2 + 1];
+        const SDPA_LDS float* po = mo + sl * S::MROW;
 #pragma unroll
-      for (int t = 0; t < S::NDT; ++t) {
+        for (int t = 0; t < S::NDT; ++t) {
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const f32x4 v4 = *(const SDPA_LDS f32x4*)(po + t * 32 + 8 * i4 + 4 * hl);
-          oacc[t][4 * i4 + 0] += sc * v4[0];
-          oacc[t][4 * i4 + 1] += sc * v4[1];
-          oacc[t][4 * i4 + 2] += sc * v4[2];
-          oacc[t][4 * i4 + 3] += sc * v4[3];
+          for (int i4 = 0; i4 < 4; ++i4) {
+            const f32x4 v4 = *(const SDPA_LDS f32x4*)(po + t * 32 + 8 * i4 + 4 * hl);
+            oacc[t][4 * i4 + 0] += sc * v4[0];
+            oacc[t][4 * i4 + 1] += sc * v4[1];
+            oacc[t][4 * i4 + 2] += sc * v4[2];
+            oacc[t][4 * i4 + 3] += sc * v4[3];
+          }
         }
       }
+      m_ref = M;
     }
-    m_ref = M;
   }
 
-  if (!row_ok) return;
+  const bool writer = (NWK == 1 || wk == 0) && row_ok;
   if (a.splits == 1) {
+    if (!writer) return;
     const float inv = 1.0f / l_row;
     char* orow = (char*)a.o + ((int64_t)b * a.os[0] + (int64_t)hq * a.os[1] + (int64_t)iq * a.os[2]) * E::ES;
 #pragma unroll
@@ -643,7 +673,11 @@ void attn_fwd_kernel(AttnArgs a) {
     }
     if (a.lse && hl == 0)
       a.lse[((int64_t)b * a.Hq + hq) * a.Lq + iq] = (m_ref + log2f(l_row)) * kLn2;
-  } else {
+    return;
+  }
+
+  // ---- split plan: this split's partial (O, m, l) ----
+  if (writer) {
     const int64_t ws_row = ((int64_t)z * a.R + r) * a.splits + split;
     float* wo = a.ws_o + ws_row * a.dv;
 #pragma unroll

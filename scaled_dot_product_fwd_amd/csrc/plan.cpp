@@ -25,7 +25,7 @@ namespace sdpa {
 namespace {
 
 constexpr int kTargetCUs = 256;        // gfx950 compute units (MI355X)
-constexpr int kWgsPerCU = 2;           // aim for two resident workgroups per CU
+constexpr int kWgsPerCU = 2;           // at most two resident workgroups per CU
 constexpr int64_t kMaxLen = 1 << 30;   // keeps every in-kernel index in int32
 constexpr int kMaxSplits = 1024;
 constexpr int kMaxDim = 256;
@@ -58,12 +58,10 @@ const char* mask_name(int m) {
 }  // namespace
 
 size_t attn_lds_bytes(int dtype, int dqk_pad, int dv_pad, const Family& f) {
-  // Mirrors Shape<> in attn_kernel.h: two or three K+V tile buffers (the
+  // Mirrors Shape<> in attn_kernel.h: two K and two V tile buffers (the
   // cross-wave merge reuses them).
   const int es = dtype == SDPA_F32 ? 4 : 2;
-  const int buf = f.nwk * f.bkw * (dqk_pad + dv_pad) * es;
-  const int stages = 3 * buf <= (f.nwq > 1 ? 80 : 160) * 1024 ? 3 : 2;
-  return (size_t)stages * buf;
+  return (size_t)2 * f.nwk * f.bkw * (dqk_pad + dv_pad) * es;
 }
 
 int make_plan(const sdpa_desc_t* d, Plan* p, std::string* err) {
@@ -172,12 +170,15 @@ int make_plan(const sdpa_desc_t* d, Plan* p, std::string* err) {
   if (d->num_splits > 0) {
     splits = d->num_splits;
   } else {
-    // Split the key range when the row tiles alone leave the chip idle.  A
-    // full-size prefill tile (128 rows) is only split when very few tiles
-    // exist: its partial outputs would cost HBM traffic comparable to the
-    // K/V it reads, while an unsplit wave of large tiles already keeps the
-    // MFMA units busy.
-    const int64_t target = (int64_t)kTargetCUs * kWgsPerCU;
+    // Split the key range when the row tiles alone leave the chip idle: aim
+    // for one full round of resident workgroups (LDS decides how many fit a
+    // CU).  A full-size prefill tile (128 rows) is only split when very few
+    // tiles exist: its partial outputs would cost HBM traffic comparable to
+    // the K/V it reads, while an unsplit wave of large tiles already keeps
+    // the MFMA units busy.
+    const size_t lds_need = attn_lds_bytes(d->dtype, dqk_pad, dv_pad, fam);
+    const int64_t resident = std::max<int64_t>(1, std::min<int64_t>(kWgsPerCU, (160 * 1024) / (int64_t)lds_need));
+    const int64_t target = (int64_t)kTargetCUs * resident;
     const bool starved = rows < 128 ? base < target : base < kTargetCUs / 4;
     if (starved) splits = std::min<int64_t>(ceil_div(target, base), nblocks);
     splits = std::max<int64_t>(1, std::min<int64_t>(splits, kMaxSplits));
@@ -198,6 +199,7 @@ int make_plan(const sdpa_desc_t* d, Plan* p, std::string* err) {
   p->combine_grid = splits > 1 ? B * Hkv * R : 0;
   p->workspace = 0;
   if (splits > 1) {
+    // [partial O][partial (m, l)]
     const size_t rows_total = (size_t)(B * Hkv * R * splits);
     const size_t o_bytes = (rows_total * (size_t)Dv * 4 + 255) / 256 * 256;
     p->workspace = o_bytes + rows_total * 8;

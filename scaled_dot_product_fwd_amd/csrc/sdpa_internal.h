@@ -61,7 +61,12 @@ constexpr Family family_for(int kind, int elem_bytes, int dqk_pad, int dv_pad) {
   const int key_bytes = (dqk_pad + dv_pad) * elem_bytes;  // one key of K plus V
   if (kind == KIND_DECODE) return key_bytes * 128 * 2 <= 160 * 1024 ? Family{1, 4, 32} : Family{1, 2, 32};
   if (kind == KIND_SHORT) return Family{2, 2, 32};
-  return key_bytes * 64 * 2 <= 80 * 1024 ? Family{4, 1, 64} : Family{4, 1, 32};
+  // Prefill: 64-key blocks when two workgroups still fit per CU, or when the
+  // head dims are so large that one workgroup per CU is all the registers
+  // allow anyway (then the longer block halves the per-block overheads).
+  if (key_bytes * 64 * 2 <= 80 * 1024) return Family{4, 1, 64};
+  const int dmax = dqk_pad > dv_pad ? dqk_pad : dv_pad;
+  return dmax >= 192 && key_bytes * 64 * 2 <= 160 * 1024 ? Family{4, 1, 64} : Family{4, 1, 32};
 }
 
 // Waves per SIMD each kernel instance is compiled for: two (so one wave's

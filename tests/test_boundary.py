@@ -170,3 +170,9 @@ def test_forward_without_gpu_tensors_raises():
     q = torch.zeros(1, 1, 4, 64)
     with pytest.raises(ValueError, match="there is no CPU path"):
         sdpa.forward(q, q, q)
+
+
+def test_split_workspace_layout():
+    d = _desc(b=2, hq=16, hkv=4, lq=1, lk=5000, dqk=64, dv=64, num_splits=16)
+    rows = 2 * 16 * 1
+    assert sdpa.sdpa_workspace_bytes(d) >= rows * 16 * (64 * 4 + 8)

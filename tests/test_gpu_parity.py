@@ -197,3 +197,35 @@ def test_error_leaves_output_untouched():
         sdpa.forward(q, k, k, mask="causal", out=out)
     torch.cuda.synchronize()
     assert bool((out == 7.0).all())
+
+
+def test_split_workspace_reused_across_calls():
+    """One caller workspace serves split plans of different shapes in a row."""
+    from oracle import sdpa_ref
+    dev = torch.device("cuda", 0)
+    cases = [(1, 8, 2, 4, 3000, 128, 128, 8), (2, 16, 4, 1, 5000, 64, 64, 16),
+             (1, 8, 2, 4, 3000, 128, 128, 3), (1, 4, 1, 40, 2100, 192, 128, 5)]
+    need = 0
+    for b, hq, hkv, lq, lk, dqk, dv, sp in cases:
+        d = sdpa.make_desc((b, hq, lq, dqk), (b, hkv, lk, dqk), (b, hkv, lk, dv), sdpa.SDPA_BF16,
+                           mask="causal", num_splits=sp)
+        need = max(need, sdpa.sdpa_workspace_bytes(d))
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    for rep in range(2):
+        for n, (b, hq, hkv, lq, lk, dqk, dv, sp) in enumerate(cases):
+            _say("shared workspace", rep, n, b, hq, hkv, lq, lk, dqk, dv, "splits", sp)
+            q, k, v = make_qkv(b, hq, hkv, lq, lk, dqk, dv, torch.bfloat16, 90 + n)
+            o, lse = sdpa.forward(q.to(dev), k.to(dev), v.to(dev), mask="causal", return_lse=True,
+                                  num_splits=sp, workspace=ws)
+            torch.cuda.synchronize()
+            ro, rl = sdpa_ref(q, k, v, default_scale(dqk), "causal", 0)
+            assert float(np.abs(o.double().cpu().numpy() - ro).max()) <= TOL_O[torch.bfloat16]
+            assert float(np.abs(lse.double().cpu().numpy() - rl).max()) <= 1e-4
+
+
+@pytest.mark.parametrize("splits", [7, 16])
+def test_more_splits_than_key_blocks(splits):
+    """Splits left without any key block publish m = -inf, l = 0 and must
+    drop out of the merge."""
+    _say("empty splits", splits)
+    check_full(1, 4, 1, 2, 150, 64, 64, "f16", "none", 0, seed=55, num_splits=splits)
