@@ -129,19 +129,28 @@ def bound(s):
 
 
 class HipEvents:
-    """hipEvent_t pairs through the HIP runtime torch already loaded."""
+    """hipEvent_t pairs through the HIP runtime torch already loaded.
+
+    The events are timing-only (hipEventDisableSystemFence): recording them
+    does not write back and invalidate the caches, which would both inflate
+    the bracketed interval and slow the kernel after them.  They are read
+    only after a full device synchronisation.
+    """
+
+    TIMING_ONLY = 0x20000000  # hipEventDisableSystemFence
 
     def __init__(self, n):
         self.hip = ctypes.CDLL("libamdhip64.so.7")
-        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                  ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
         self.start, self.stop = [], []
         for _ in range(n):
             a, b = ctypes.c_void_p(), ctypes.c_void_p()
-            if self.hip.hipEventCreate(ctypes.byref(a)) or self.hip.hipEventCreate(ctypes.byref(b)):
-                raise RuntimeError("hipEventCreate failed")
+            if (self.hip.hipEventCreateWithFlags(ctypes.byref(a), self.TIMING_ONLY)
+                    or self.hip.hipEventCreateWithFlags(ctypes.byref(b), self.TIMING_ONLY)):
+                raise RuntimeError("hipEventCreateWithFlags failed")
             self.start.append(a.value)
             self.stop.append(b.value)
 
@@ -307,6 +316,74 @@ def traffic_from_profiles(name):
     return t.get("hbm_bytes_per_launch")
 
 
+def calibration_copy(mib):
+    """A plain device copy of known size (float32 ``dst = src * 1``), run three
+    times, so that a counter run over this process can scale its HBM byte
+    counters by what they read for a known number of bytes."""
+    import torch
+
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def summarize_pmc(fetch_dir, write_dir, name, copy_mib, commands):
+    """Reduce two ``rocprofv3 --pmc`` runs (FETCH_SIZE, WRITE_SIZE) of
+    ``bench.py --workload NAME --calibrate-copy-mib M`` to HBM bytes per launch
+    of the attention kernel: each counter's KiB per dispatch, averaged over the
+    attention dispatches, times (known bytes / counter bytes) of the copy."""
+    import csv
+    import glob
+
+    def per_kernel(d, counter):
+        vals = {}
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(f) as fh:
+                for r in csv.DictReader(fh):
+                    if r["Counter_Name"] != counter:
+                        continue
+                    vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return vals
+
+    def pick(vals, needle):
+        rows = [(k, v) for k, v in vals.items() if needle(k)]
+        if not rows:
+            raise SystemExit(f"no dispatch matched in {sorted(vals)[:8]}")
+        k, v = max(rows, key=lambda kv: len(kv[1]))
+        return k, v
+
+    copy_bytes = 2 * copy_mib * (1 << 20)  # read once, written once
+    out = {"workload": name, "kernel_source_hash": kernel_source_hash(), "commands": commands,
+           "copy": {"kernel": "float32 dst = src * 1", "bytes_read": copy_bytes // 2,
+                    "bytes_written": copy_bytes // 2}}
+    total = 0.0
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        vals = per_kernel(d, counter)
+        kname, kv = pick(vals, lambda k: "attn_fwd_kernel" in k)
+        cname, cv = pick(vals, lambda k: "elementwise" in k and "Mul" in k)
+        cv = [x for x in cv if x > 0.25 * copy_bytes / 2 / 1024] or cv
+        k_kib = sum(kv) / len(kv)
+        c_kib = sum(cv) / len(cv)
+        factor = (copy_bytes / 2) / (c_kib * 1024)
+        out[counter] = {"attention_kib_per_dispatch": round(k_kib, 1), "dispatches": len(kv),
+                        "copy_kib_per_dispatch": round(c_kib, 1), "scale": round(factor, 4)}
+        out["kernel"] = kname
+        total += k_kib * 1024 * factor
+    s = SHAPES[name]
+    out["hbm_bytes_per_launch"] = int(total)
+    out["algorithmic_bytes_per_launch"] = work(s)[1]
+    out["ratio_to_algorithmic"] = round(total / work(s)[1], 4)
+    path = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+
+
 def measure(s, steps, warmup):
     import torch
 
@@ -345,7 +422,18 @@ def main():
     ap.add_argument("--sweep", action="store_true", help="also time every shape of the five workloads")
     ap.add_argument("--sweep-out", default=os.path.join("gpurun_out", "sweep.json"))
     ap.add_argument("--sweep-only", default="", help="comma-separated name prefixes to sweep")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="after timing, run a plain copy of this many MiB (counter calibration)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="host only: reduce FETCH_SIZE / WRITE_SIZE counter runs of --workload "
+                         "into profiles/traffic_<workload>.json")
+    ap.add_argument("--pmc-command", action="append", default=[],
+                    help="with --summarize-pmc: the profiling commands, recorded in the summary")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload,
+                      args.calibrate_copy_mib, args.pmc_command)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (got --gpus {args.gpus}); this build has no multi-GPU path",
               file=sys.stderr)
@@ -360,6 +448,8 @@ def main():
     sdpa.load()
     s = SHAPES[args.workload]
     res, runner = measure(s, args.steps, args.warmup)
+    if args.calibrate_copy_mib:
+        calibration_copy(args.calibrate_copy_mib)
     cpu = None if args.no_cpu_baseline else cpu_baseline(s, runner)
     vs = None
     if s["name"].startswith("decode_"):

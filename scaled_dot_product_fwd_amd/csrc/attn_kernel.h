@@ -36,13 +36,12 @@
 // window are never loaded.  Only blocks that straddle an edge (the diagonal,
 // any row's window edge, or the Lk tail) apply a per-element mask; every block
 // whose first key lies below the last row's window edge is masked, which is
-// exact for unaligned windows too.  Inside a block, a wave whose rows see none
-// of its keys skips the block's arithmetic.
+// exact for unaligned windows too.
 //
 // Split-K (mlx issue #3826, second and third comments: the block-parallel
-// reduction over S): the block range may be cut into `splits` parts handled by
-// different workgroups; each writes its unnormalised O with (m, l) and a
-// combine kernel merges them by log-sum-exp.
+// reduction over S): the blocks of the range may be dealt out to `splits`
+// workgroups; each writes its unnormalised O with (m, l) and a combine kernel
+// merges them by log-sum-exp.
 //
 // Lazy rescaling: the reference max m of a row only moves when a block's max
 // exceeds it by more than kRescale (log2 units); otherwise the block is
@@ -172,16 +171,21 @@ struct Shape {
   }
   // Two K buffers and two V buffers (see the kernel's block loop).
   static constexpr int LDS = 2 * BUF;
-  // Overlap the next block's QK with this block's softmax when two blocks of
-  // scores fit the registers next to Q and O.
-  static constexpr bool PIPE = false;
+  // Families that split the keys over waves (decode, short queries) have one
+  // row tile per KV head in practice, so each K/V byte is read once per
+  // launch: stream it past the caches.  Prefill row tiles re-read the same
+  // K/V from L2.
+  static constexpr bool STREAM = NWK > 1;
+  // DMA instructions one block costs the wave that issues the fewest / most.
+  static constexpr int DMA_MIN = KDMA / NW + VDMA / NW;
+  static constexpr int DMA_MAX = (KDMA + NW - 1) / NW + (VDMA + NW - 1) / NW;
   // Cross-wave merge (NWK > 1): the waves with wk > 0 leave O at the start of
   // LDS as [slot][q][MROW] and (m, l) after BUF bytes; MROW is padded when
   // that fits.
   static constexpr int MSLOTS = NWQ * (NWK - 1);
   static constexpr int MROW = (MSLOTS * 32 * (DV + 4) * 4 <= BUF) ? DV + 4 : DV;
   static_assert(MSLOTS * 32 * MROW * 4 <= BUF && MSLOTS * 32 * 8 <= BUF, "merge scratch must fit a buffer");
-  static_assert((KDMA + NW - 1) / NW + (VDMA + NW - 1) / NW <= 63, "vmcnt range");
+  static_assert(DMA_MAX <= 63, "vmcnt range");
   static_assert(BKW % 32 == 0, "BKW must be a multiple of 32");
   static_assert(DQK % E::KQK == 0 && DV % 32 == 0, "bad head-dim tile");
   static_assert(KBYTES % 1024 == 0 && VBYTES % 1024 == 0, "tiles must be whole DMA instructions");
@@ -196,12 +200,20 @@ __device__ __forceinline__ float wave_max32(float x) {  // combine lanes l and l
 // address lds + 16 l.  Issued as a single instruction the compiler does not
 // track, so it inserts no wait for it anywhere; the kernel waits itself with
 // wait_vmcnt.  The instruction has no register result; its address registers
-// are consumed at issue.
+// are consumed at issue.  STREAM marks the load non-temporal: data read once
+// per launch should not displace what the caches hold for re-use.
+template <bool STREAM>
 __device__ __forceinline__ void lds_dma16(const void* src, unsigned lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(src), "s"(lds)
-               : "memory", "m0");
+  if constexpr (STREAM)
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
+                 :
+                 : "v"(src), "s"(lds)
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(src), "s"(lds)
+                 : "memory", "m0");
 }
 
 // Wait until at most N vector-memory operations of this wave are in flight.
@@ -263,9 +275,13 @@ void attn_fwd_kernel(AttnArgs a) {
   const int kb_first = k_lo / S::BK;
   const int kb_end = (k_hi + S::BK - 1) / S::BK;
   const int nb = kb_end - kb_first;
-  const int sb0 = kb_first + (int)(((long long)nb * split) / a.splits);
-  const int sb1 = kb_first + (int)(((long long)nb * (split + 1)) / a.splits);
-  const int nblk = sb1 - sb0;
+  // Split `split` takes every splits-th block of the range, starting at its
+  // own index: at any moment the splits of one head read neighbouring
+  // blocks, so the whole grid streams one region of memory together rather
+  // than `splits` regions far apart (which maps unevenly onto the HBM
+  // channels).  Block j of this workgroup is blk(j).
+  const int nblk = split < nb ? (nb - 1 - split) / a.splits + 1 : 0;
+  auto blk = [&](int j) { return kb_first + split + j * a.splits; };
 
   // ---- LDS DMA of one key block into buffer `buf` ----
   // Each wave issues KPW + VPW DMA instructions per block; lane l of
@@ -318,7 +334,7 @@ void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
       for (int ii = 0; ii < KPW; ++ii)
         if ((ii + 1) * S::NW <= S::KDMA || ii * S::NW + wave_u < S::KDMA)
-          lds_dma16(kb + koff[ii], kl + (ii * S::NW + wave_u) * 1024);
+          lds_dma16<S::STREAM>(kb + koff[ii], kl + (ii * S::NW + wave_u) * 1024);
     } else {
 #pragma unroll
       for (int ii = 0; ii < KPW; ++ii) {
@@ -326,7 +342,7 @@ void attn_fwd_kernel(AttnArgs a) {
         int row, colb;
         kslot((ii * S::NW + wave_u) * 64 + lane, row, colb);
         const int grow = min(k0 + row, a.Lk - 1);
-        lds_dma16(kbase + (int64_t)grow * kstr + colb, kl + (ii * S::NW + wave_u) * 1024);
+        lds_dma16<S::STREAM>(kbase + (int64_t)grow * kstr + colb, kl + (ii * S::NW + wave_u) * 1024);
       }
     }
   };
@@ -338,7 +354,7 @@ void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
       for (int ii = 0; ii < VPW; ++ii)
         if ((ii + 1) * S::NW <= S::VDMA || ii * S::NW + wave_u < S::VDMA)
-          lds_dma16(vb + voff[ii], vl + (ii * S::NW + wave_u) * 1024);
+          lds_dma16<S::STREAM>(vb + voff[ii], vl + (ii * S::NW + wave_u) * 1024);
     } else {
 #pragma unroll
       for (int ii = 0; ii < VPW; ++ii) {
@@ -346,18 +362,17 @@ void attn_fwd_kernel(AttnArgs a) {
         int row, colb;
         vslot((ii * S::NW + wave_u) * 64 + lane, row, colb);
         const int grow = min(k0 + row, a.Lk - 1);
-        lds_dma16(vbase + (int64_t)grow * vstr + colb, vl + (ii * S::NW + wave_u) * 1024);
+        lds_dma16<S::STREAM>(vbase + (int64_t)grow * vstr + colb, vl + (ii * S::NW + wave_u) * 1024);
       }
     }
   };
 
-  // Prologue: K of block 0 (and of block 1 when the QK runs a block ahead)
-  // and V of block 0 go in flight.
+  // Prologue: block 0 goes in flight ahead of the Q loads; block 1 follows
+  // once both have landed (see below).
   if (nblk > 0) {
-    dma_k(sb0, 0);
-    dma_v(sb0, 0);
+    dma_k(blk(0), 0);
+    dma_v(blk(0), 0);
   }
-  if (S::PIPE && nblk > 1) dma_k(sb0 + 1, 1);
 
   // ---- Q fragments (B operand of S^T = K Q^T), kept in registers ----
   frag qf[S::NQS];
@@ -425,12 +440,15 @@ void attn_fwd_kernel(AttnArgs a) {
   float m_ref = kNegInf;  // reference max of this row, log2 units (same in both lane halves)
   float l_run = 0.f;      // this lane's share of the row sum (halves add up at the end)
 
-  // Everything issued so far (the prologue blocks and the Q loads) must have
-  // landed.  Waiting for all of it here also tells the compiler the Q loads
-  // are complete, so it puts no load wait inside the loop (where it would
-  // also stall on the DMA in flight).
+  // Block 0 and the Q loads must have landed.  Waiting for everything here
+  // also tells the compiler the Q loads are complete, so it puts no load
+  // wait of its own inside the loop (which would also stall on the DMA in
+  // flight there).  Block 1 then goes in flight.
   wait_vmcnt<0>();
-  __syncthreads();
+  if (nblk > 1) {
+    dma_k(blk(1), 1);
+    dma_v(blk(1), 1);
+  }
 
   // ---- S^T = K Q^T of one block (this wave's BKW keys) ----
   auto qk = [&](int j, f32x16 (&sacc)[S::NKT]) __attribute__((always_inline)) {
@@ -455,11 +473,8 @@ void attn_fwd_kernel(AttnArgs a) {
   };
 
   // ---- mask, online softmax and O^T += V^T P^T of block j ----
-  // `next` (when given) is the following block's QK, issued between this
-  // block's softmax and its PV product: the MFMAs of the one and the vector
-  // work of the other are independent, so they overlap.
-  auto softmax_pv = [&](int j, f32x16 (&sacc)[S::NKT], f32x16 (*sn)[S::NKT]) __attribute__((always_inline)) {
-    const int kw = (sb0 + j) * S::BK + wk * BKW;  // first key of this wave's slice
+  auto softmax_pv = [&](int j, f32x16 (&sacc)[S::NKT]) __attribute__((always_inline)) {
+    const int kw = blk(j) * S::BK + wk * BKW;  // first key of this wave's slice
     // ---- mask edge blocks (diagonal, window edge, Lk tail) ----
     const bool edge = (kw + BKW > a.Lk) || (a.mask != MASK_NONE && kw + BKW - 1 > pmin_w) ||
                       (a.mask == MASK_WINDOW && kw <= pmax_w - a.window);
@@ -500,8 +515,6 @@ void attn_fwd_kernel(AttnArgs a) {
       m_ref = m_new;
     }
     const float msub = (m_ref == kNegInf) ? 0.f : m_ref;
-
-    if (sn) qk(j + 1, *sn);
 
 #pragma unroll
     for (int kt = 0; kt < S::NKT; ++kt) {
@@ -560,33 +573,26 @@ void attn_fwd_kernel(AttnArgs a) {
     }
   };
 
-  // Iteration j: DMA K of block j + 2 (into the K buffer block j used, whose
-  // QK ran in the previous iteration) and V of block j + 1 (into the V buffer
-  // of block j - 1); softmax + PV of block j with the QK of block j + 1 in
-  // between; then wait for the DMAs and synchronise.  The S^T registers of
-  // two consecutive blocks alternate between sa and sb.
-  // Without the overlap (large head dims, whose registers do not hold two
-  // blocks of scores) K runs one block ahead instead of two and each
-  // iteration computes its own QK.
-  constexpr int KAHEAD = S::PIPE ? 2 : 1;
-  f32x16 sa[S::NKT], sb[S::NKT];
-  if (S::PIPE && nblk > 0) qk(0, sa);
-  auto iter = [&](int j, f32x16 (&cur)[S::NKT], f32x16 (&nxt)[S::NKT]) __attribute__((always_inline)) {
-    if (j + KAHEAD < nblk) dma_k(sb0 + j + KAHEAD, (j + KAHEAD) & 1);
-    if (j + 1 < nblk) dma_v(sb0 + j + 1, (j + 1) & 1);
-    if constexpr (S::PIPE) {
-      if (j + 1 < nblk) softmax_pv(j, cur, &nxt);
-      else softmax_pv(j, cur, nullptr);
-    } else {
-      qk(j, cur);
-      softmax_pv(j, cur, nullptr);
+  // Block j sits in buffer pair j % 2.  Iteration j waits for block j
+  // (block j + 1 stays in flight), computes it, and once every wave is done
+  // with its buffers sends block j + 2 there.  So the next block is always
+  // in flight during the compute and two are while the wave waits: the
+  // stream never drains between blocks.
+  f32x16 sacc[S::NKT];
+  for (int j = 0; j < nblk; ++j) {
+    if (j + 1 < nblk) wait_vmcnt<S::DMA_MIN>();  // only block j + 1 may still be in flight
+    else wait_vmcnt<0>();
+    __syncthreads();  // every wave's share of block j has landed
+    qk(j, sacc);
+    softmax_pv(j, sacc);
+    if (j + 2 < nblk) {
+      // The vector-memory counter holds at most 63 operations: where two
+      // blocks would exceed that, let part of block j + 1 land first.
+      if constexpr (2 * S::DMA_MAX > 63) wait_vmcnt<63 - S::DMA_MAX>();
+      __syncthreads();  // every wave is done reading buffer pair j % 2
+      dma_k(blk(j + 2), j & 1);
+      dma_v(blk(j + 2), j & 1);
     }
-    wait_vmcnt<0>();
-    __syncthreads();
-  };
-  for (int j = 0; j < nblk; j += 2) {
-    iter(j, sa, sb);
-    if (j + 1 < nblk) iter(j + 1, sb, sa);
   }
 
   // ---- epilogue ----
@@ -594,8 +600,9 @@ void attn_fwd_kernel(AttnArgs a) {
 
   if constexpr (NWK > 1) {
     // Merge the NWK key slices of the same rows: waves wk > 0 leave their
-    // partial (m, l, O) in LDS (the loop ended with a barrier, so both buffers
-    // are free); wave wk == 0 folds them into its own registers.
+    // partial (m, l, O) in LDS once every wave is done with the tile
+    // buffers; wave wk == 0 folds them into its own registers.
+    __syncthreads();
     SDPA_LDS float* mo = (SDPA_LDS float*)smem;               // [MSLOTS][32][MROW]
     SDPA_LDS float* mml = (SDPA_LDS float*)(smem + S::BUF);  // [MSLOTS][32][2]
     if (wk > 0) {

@@ -18,30 +18,16 @@ namespace dev {
 constexpr int kCombineThreads = 128;
 constexpr int kCombineMaxSplits = 1024;
 
-__device__ __forceinline__ float block_max(float x, float* red) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
-  __syncthreads();
-  x = fmaxf(red[0], red[1]);
-  __syncthreads();
-  return x;
-}
-
-__device__ __forceinline__ float block_sum(float x, float* red) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
-  __syncthreads();
-  x = red[0] + red[1];
-  __syncthreads();
-  return x;
-}
-
+// One workgroup per packed row.  The (m, l) pairs are read once into LDS;
+// then thread (g, c) sums the weighted partial outputs of 4 head-dim columns
+// c over the splits s = g, g + NG, g + 2 NG, ... with independent 16-byte
+// loads, and the NG group sums are added in LDS.
 template <class E>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a) {
-  __shared__ float wsh[kCombineMaxSplits];
-  __shared__ float red[2];
+  __shared__ float msh[kCombineMaxSplits];
+  __shared__ float lsh[kCombineMaxSplits];
+  __shared__ f32x4 part[kCombineThreads];
+  __shared__ float red[2], red_l[2];
   const int row = blockIdx.x;  // z * R + r
   const int z = row / a.R, r = row % a.R;
   const int b = z / a.Hkv, kvh = z % a.Hkv;
@@ -50,33 +36,69 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a)
   const int tid = threadIdx.x;
 
   float mx = kNegInf;
-  for (int s = tid; s < a.splits; s += kCombineThreads) mx = fmaxf(mx, ml[2 * s]);
-  const float M = block_max(mx, red);
-  const float Mu = (M == kNegInf) ? 0.f : M;
-  float part = 0.f;
   for (int s = tid; s < a.splits; s += kCombineThreads) {
-    const float w = __builtin_amdgcn_exp2f(ml[2 * s] - Mu);
-    wsh[s] = w;
-    part += w * ml[2 * s + 1];
+    const float2 v = *(const float2*)(ml + 2 * s);
+    msh[s] = v.x;
+    lsh[s] = v.y;
+    mx = fmaxf(mx, v.x);
   }
-  const float L = block_sum(part, red);  // its barriers also publish wsh
-  const float inv = 1.0f / L;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  if ((tid & 63) == 0) red[tid >> 6] = mx;
+  __syncthreads();  // also publishes msh / lsh
+  const float M = fmaxf(red[0], red[1]);
+  const float Mu = (M == kNegInf) ? 0.f : M;
 
-  const float* wo = a.ws_o + (int64_t)row * a.splits * a.dv;
-  char* orow = (char*)a.o + ((int64_t)b * a.os[0] + (int64_t)h * a.os[1] + (int64_t)i * a.os[2]) * E::ES;
-  for (int d = tid; d < a.dv; d += kCombineThreads) {
-    float acc = 0.f;
-    for (int s = 0; s < a.splits; ++s) acc += wsh[s] * wo[(int64_t)s * a.dv + d];
-    const float val = acc * inv;
-    if constexpr (E::ES == 2) *(unsigned short*)(orow + d * 2) = E::to_store(val);
-    else *(float*)(orow + d * 4) = val;
+  float lp = 0.f;
+  for (int s = tid; s < a.splits; s += kCombineThreads) lp += __builtin_amdgcn_exp2f(msh[s] - Mu) * lsh[s];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) lp += __shfl_xor(lp, o);
+  if ((tid & 63) == 0) red_l[tid >> 6] = lp;
+
+  const int nc = a.dv / 4;               // 4-column groups: dv % 8 == 0, dv <= 256
+  const int ng = kCombineThreads / nc;   // split groups
+  const int gi = tid / nc, c = tid % nc;
+  const float* wo = a.ws_o + (int64_t)row * a.splits * a.dv + 4 * c;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if (gi < ng) {
+    int s = gi;
+    for (; s + 3 * ng < a.splits; s += 4 * ng) {
+      f32x4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = *(const f32x4*)(wo + (int64_t)(s + u * ng) * a.dv);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc += __builtin_amdgcn_exp2f(msh[s + u * ng] - Mu) * v[u];
+    }
+    for (; s < a.splits; s += ng) acc += __builtin_amdgcn_exp2f(msh[s] - Mu) * *(const f32x4*)(wo + (int64_t)s * a.dv);
   }
-  if (tid == 0 && a.lse) a.lse[((int64_t)b * a.Hq + h) * a.Lq + i] = (Mu + log2f(L)) * kLn2;
+  part[tid] = acc;
+  __syncthreads();  // publishes part and red_l
+  if (tid < nc) {
+    f32x4 sum = part[tid];
+    for (int q = 1; q < ng; ++q) sum += part[q * nc + tid];
+    const float L = red_l[0] + red_l[1];
+    const float inv = 1.0f / L;
+    char* orow = (char*)a.o + ((int64_t)b * a.os[0] + (int64_t)h * a.os[1] + (int64_t)i * a.os[2]) * E::ES;
+    const int d = 4 * tid;
+    if constexpr (E::ES == 2) {
+      u32x2 w;
+      w[0] = E::pack2(sum[0] * inv, sum[1] * inv);
+      w[1] = E::pack2(sum[2] * inv, sum[3] * inv);
+      *(u32x2*)(orow + d * 2) = w;
+    } else {
+      *(f32x4*)(orow + d * 4) = sum * inv;
+    }
+    if (tid == 0 && a.lse) a.lse[((int64_t)b * a.Hq + h) * a.Lq + i] = (Mu + log2f(L)) * kLn2;
+  }
 }
 
 }  // namespace dev
 
 int launch_combine(const Plan& p, const CombineArgs& a, void* stream, std::string* err) {
+  if (a.dv > 4 * dev::kCombineThreads || a.dv % 4 != 0) {
+    *err = "combine supports head dims up to " + std::to_string(4 * dev::kCombineThreads);
+    return SDPA_E_PLAN;
+  }
   if (a.splits > dev::kCombineMaxSplits) {
     *err = "combine supports at most " + std::to_string(dev::kCombineMaxSplits) + " splits";
     return SDPA_E_PLAN;
