@@ -169,22 +169,36 @@ struct Shape {
   static __device__ __forceinline__ int vy(int row) {
     return VG == 16 ? 4 * (row & 3) : (VG == 8 ? 2 * (row & 3) : 2 * (row & 1));
   }
-  // Two K buffers and two V buffers (see the kernel's block loop).
-  static constexpr int LDS = 2 * BUF;
+  // Two K buffers and two V buffers (see the kernel's block loop); the
+  // cross-wave merge below reuses them, and needs a little more than they
+  // hold for the smallest head dims.
+  static constexpr int MSLOTS = NWQ * (NWK - 1);
+  static constexpr int MLB = (MSLOTS * 32 * 8 + 15) / 16 * 16;
+  static constexpr int LDS = cmax(2 * BUF, MLB + MSLOTS * 32 * (32 + 4) * 4);
   // Families that split the keys over waves (decode, short queries) have one
   // row tile per KV head in practice, so each K/V byte is read once per
   // launch: stream it past the caches.  Prefill row tiles re-read the same
   // K/V from L2.
   static constexpr bool STREAM = NWK > 1;
+  // Operand fragments read ahead of their products when the extra registers
+  // (4 per fragment) stay within a budget (16-bit types only).
+  static constexpr bool HOIST_K = E::ES == 2 && NKT * NQS * 4 <= 48;
+  static constexpr bool HOIST_V = E::ES == 2 && NKT * (32 / E::KPV) * NDT * 4 <= 48 && NQS * 4 + NDT * 16 <= 128;
   // DMA instructions one block costs the wave that issues the fewest / most.
   static constexpr int DMA_MIN = KDMA / NW + VDMA / NW;
   static constexpr int DMA_MAX = (KDMA + NW - 1) / NW + (VDMA + NW - 1) / NW;
-  // Cross-wave merge (NWK > 1): the waves with wk > 0 leave O at the start of
-  // LDS as [slot][q][MROW] and (m, l) after BUF bytes; MROW is padded when
-  // that fits.
-  static constexpr int MSLOTS = NWQ * (NWK - 1);
-  static constexpr int MROW = (MSLOTS * 32 * (DV + 4) * 4 <= BUF) ? DV + 4 : DV;
-  static_assert(MSLOTS * 32 * MROW * 4 <= BUF && MSLOTS * 32 * 8 <= BUF, "merge scratch must fit a buffer");
+  // Cross-wave merge (NWK > 1), through the idle tile buffers: (m, l) of
+  // the waves with wk > 0 first, as [slot][q][2]; then their O in rounds of
+  // TPR dv tiles, as [slot][q][MROW] after the (m, l) bytes, TPR as large
+  // as fits.
+  static constexpr int merge_tiles() {
+    for (int t = NDT; t >= 1; --t)
+      if (NDT % t == 0 && MLB + MSLOTS * 32 * (t * 32 + 4) * 4 <= LDS) return t;
+    return 0;
+  }
+  static constexpr int TPR = merge_tiles();
+  static constexpr int MROW = TPR * 32 + 4;  // +4 floats skew the rows across banks
+  static_assert(NWK == 1 || TPR >= 1, "merge scratch must fit the tile buffers");
   static_assert(DMA_MAX <= 63, "vmcnt range");
   static_assert(BKW % 32 == 0, "BKW must be a multiple of 32");
   static_assert(DQK % E::KQK == 0 && DV % 32 == 0, "bad head-dim tile");
@@ -192,8 +206,18 @@ struct Shape {
   static_assert(LDS <= 160 * 1024, "LDS budget of one workgroup exceeded");
 };
 
-__device__ __forceinline__ float wave_max32(float x) {  // combine lanes l and l^32
-  return fmaxf(x, __shfl_xor(x, 32));
+// Combine lanes l and l ^ 32 without a trip through LDS: the lane-half swap
+// leaves {lower half, lower half} in one result and {upper, upper} in the
+// other.
+__device__ __forceinline__ float wave_max32(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
+__device__ __forceinline__ float wave_sum32(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
 }
 
 // LDS DMA of 16 bytes per lane: lane l's chunk at `src` lands at LDS byte
@@ -453,6 +477,26 @@ void attn_fwd_kernel(AttnArgs a) {
   // ---- S^T = K Q^T of one block (this wave's BKW keys) ----
   auto qk = [&](int j, f32x16 (&sacc)[S::NKT]) __attribute__((always_inline)) {
     const SDPA_LDS char* kl = smem + (j & 1) * S::KBYTES;
+    if constexpr (S::HOIST_K) {
+      // Every K fragment of the block is read before the first product, so
+      // the reads overlap each other instead of each product waiting for
+      // its own.
+      frag kf[S::NKT][S::NQS];
+#pragma unroll
+      for (int kt = 0; kt < S::NKT; ++kt) {
+        const SDPA_LDS char* ktile = kl + (wk * BKW + kt * 32) * S::KROW;
+#pragma unroll
+        for (int s = 0; s < S::NQS; ++s)
+          kf[kt][s] = *(const SDPA_LDS u32x4*)(ktile + koffl[s % SPG] + 16 * S::KG * (s / SPG));
+      }
+#pragma unroll
+      for (int kt = 0; kt < S::NKT; ++kt) {
+        sacc[kt] = f32x16{};
+#pragma unroll
+        for (int s = 0; s < S::NQS; ++s) sacc[kt] = E::mma(kf[kt][s], qf[s], sacc[kt]);
+      }
+      return;
+    }
 #pragma unroll
     for (int kt = 0; kt < S::NKT; ++kt) {
       sacc[kt] = f32x16{};
@@ -472,8 +516,46 @@ void attn_fwd_kernel(AttnArgs a) {
     }
   };
 
+  // V operand of the PV product for key tile kt, key step s2, dv tile t.
+  auto vread = [&](int j, int kt, int s2, int t) __attribute__((always_inline)) -> frag {
+    const SDPA_LDS char* vl = smem + 2 * S::KBYTES + (j & 1) * S::VBYTES;
+    const int kbase_t = wk * BKW + kt * 32;  // first key of this tile inside the block
+    if constexpr (E::ES == 2) {
+      // Transposing read: lane t16 of group g supplies the address of 4 dv
+      // values of one key; the hardware hands lane i of the group element
+      // i%4 of the chunk addressed by lane 4j + i/4, i.e. the 4 keys
+      // (j = 0..3) of dv column 16*(g%2) + i.
+      const SDPA_LDS char* vb = vl + (kbase_t + 16 * s2) * S::VROW + voffl[t % TPG] + 16 * S::VG * (t / TPG);
+      const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SDPA_LDS i16x4*)vb);
+      const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SDPA_LDS i16x4*)(vb + 8 * S::VROW));
+      const u32x2 h0 = __builtin_bit_cast(u32x2, v0), h1 = __builtin_bit_cast(u32x2, v1);
+      u32x4 f;
+      f[0] = h0[0];
+      f[1] = h0[1];
+      f[2] = h1[0];
+      f[3] = h1[1];
+      return f;
+    } else {
+      const int row = kbase_t + 8 * (s2 >> 2) + 4 * hl + (s2 & 3);
+      const int dv = 32 * t + col;
+      const int cc = (dv >> 2) ^ S::vy(row);
+      return *(const SDPA_LDS float*)(vl + row * S::VROW + cc * 16 + (dv & 3) * 4);
+    }
+  };
+
   // ---- mask, online softmax and O^T += V^T P^T of block j ----
   auto softmax_pv = [&](int j, f32x16 (&sacc)[S::NKT]) __attribute__((always_inline)) {
+    // Where registers allow, the block's V fragments are read up front so
+    // their latency hides under the softmax.
+    frag vf[S::HOIST_V ? S::NKT : 1][S::HOIST_V ? 32 / E::KPV : 1][S::HOIST_V ? S::NDT : 1];
+    if constexpr (S::HOIST_V) {
+#pragma unroll
+      for (int kt = 0; kt < S::NKT; ++kt)
+#pragma unroll
+        for (int s2 = 0; s2 < 32 / E::KPV; ++s2)
+#pragma unroll
+          for (int t = 0; t < S::NDT; ++t) vf[kt][s2][t] = vread(j, kt, s2, t);
+    }
     const int kw = blk(j) * S::BK + wk * BKW;  // first key of this wave's slice
     // ---- mask edge blocks (diagonal, window edge, Lk tail) ----
     const bool edge = (kw + BKW > a.Lk) || (a.mask != MASK_NONE && kw + BKW - 1 > pmin_w) ||
@@ -527,10 +609,8 @@ void attn_fwd_kernel(AttnArgs a) {
     }
 
     // ---- O^T += V^T P^T ----
-    const SDPA_LDS char* vl = smem + 2 * S::KBYTES + (j & 1) * S::VBYTES;
 #pragma unroll
     for (int kt = 0; kt < S::NKT; ++kt) {
-      const int kbase_t = wk * BKW + kt * 32;  // first key of this tile inside the block
 #pragma unroll
       for (int s2 = 0; s2 < 32 / E::KPV; ++s2) {
         frag bf;
@@ -545,29 +625,8 @@ void attn_fwd_kernel(AttnArgs a) {
         }
 #pragma unroll
         for (int t = 0; t < S::NDT; ++t) {
-          frag af;
-          if constexpr (E::ES == 2) {
-            // Transposing read: lane t16 of group g supplies the address of
-            // 4 dv values of one key; the hardware hands lane i of the group
-            // element i%4 of the chunk addressed by lane 4j + i/4, i.e. the
-            // 4 keys (j = 0..3) of dv column 16*(g%2) + i.
-            const SDPA_LDS char* vb = vl + (kbase_t + 16 * s2) * S::VROW + voffl[t % TPG] + 16 * S::VG * (t / TPG);
-            const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SDPA_LDS i16x4*)vb);
-            const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SDPA_LDS i16x4*)(vb + 8 * S::VROW));
-            const u32x2 h0 = __builtin_bit_cast(u32x2, v0), h1 = __builtin_bit_cast(u32x2, v1);
-            u32x4 f;
-            f[0] = h0[0];
-            f[1] = h0[1];
-            f[2] = h1[0];
-            f[3] = h1[1];
-            af = f;
-          } else {
-            const int row = kbase_t + 8 * (s2 >> 2) + 4 * hl + (s2 & 3);
-            const int dv = 32 * t + col;
-            const int cc = (dv >> 2) ^ S::vy(row);
-            af = *(const SDPA_LDS float*)(vl + row * S::VROW + cc * 16 + (dv & 3) * 4);
-          }
-          oacc[t] = E::mma(af, bf, oacc[t]);
+          if constexpr (S::HOIST_V) oacc[t] = E::mma(vf[kt][s2][t], bf, oacc[t]);
+          else oacc[t] = E::mma(vread(j, kt, s2, t), bf, oacc[t]);
         }
       }
     }
@@ -596,61 +655,72 @@ void attn_fwd_kernel(AttnArgs a) {
   }
 
   // ---- epilogue ----
-  float l_row = l_run + __shfl_xor(l_run, 32);  // both halves' keys
+  float l_row = wave_sum32(l_run);  // both halves' keys
 
   if constexpr (NWK > 1) {
-    // Merge the NWK key slices of the same rows: waves wk > 0 leave their
-    // partial (m, l, O) in LDS once every wave is done with the tile
-    // buffers; wave wk == 0 folds them into its own registers.
+    // Merge the NWK key slices of the same rows once every wave is done with
+    // the tile buffers: waves wk > 0 leave their partial (m, l, O) in LDS,
+    // wave wk == 0 folds them into its own registers.
+    SDPA_LDS float* mml = (SDPA_LDS float*)smem;            // [MSLOTS][32][2]
+    SDPA_LDS float* mo = (SDPA_LDS float*)(smem + S::MLB);  // [MSLOTS][32][MROW]
+    const int slot = wq * (NWK - 1) + (wk - 1);
     __syncthreads();
-    SDPA_LDS float* mo = (SDPA_LDS float*)smem;               // [MSLOTS][32][MROW]
-    SDPA_LDS float* mml = (SDPA_LDS float*)(smem + S::BUF);  // [MSLOTS][32][2]
-    if (wk > 0) {
-      const int slot = wq * (NWK - 1) + (wk - 1);
-      SDPA_LDS float* myo = mo + (slot * 32 + col) * S::MROW;
-#pragma unroll
-      for (int t = 0; t < S::NDT; ++t) {
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const int d = t * 32 + 8 * i4 + 4 * hl;
-          *(SDPA_LDS f32x4*)(myo + d) = f32x4{oacc[t][4 * i4 + 0], oacc[t][4 * i4 + 1],
-                                              oacc[t][4 * i4 + 2], oacc[t][4 * i4 + 3]};
-        }
-      }
-      if (hl == 0) {
-        mml[(slot * 32 + col) * 2 + 0] = m_ref;
-        mml[(slot * 32 + col) * 2 + 1] = l_row;
-      }
+    if (wk > 0 && hl == 0) {
+      mml[(slot * 32 + col) * 2 + 0] = m_ref;
+      mml[(slot * 32 + col) * 2 + 1] = l_row;
     }
     __syncthreads();
+    float sc[NWK];  // weight of each slice's partial in the merged row
     if (wk == 0) {
       float M = m_ref;
 #pragma unroll
       for (int w = 1; w < NWK; ++w) M = fmaxf(M, mml[((wq * (NWK - 1) + w - 1) * 32 + col) * 2]);
       const float Mu = (M == kNegInf) ? 0.f : M;
-      const float own = __builtin_amdgcn_exp2f(m_ref - Mu);
-      l_row *= own;
-#pragma unroll
-      for (int t = 0; t < S::NDT; ++t) oacc[t] *= own;
+      sc[0] = __builtin_amdgcn_exp2f(m_ref - Mu);
+      l_row *= sc[0];
 #pragma unroll
       for (int w = 1; w < NWK; ++w) {
         const int sl = (wq * (NWK - 1) + w - 1) * 32 + col;
-        const float sc = __builtin_amdgcn_exp2f(mml[sl * 2] - Mu);
-        l_row += sc * mml[sl * 2 + 1];
-        const SDPA_LDS float* po = mo + sl * S::MROW;
+        sc[w] = __builtin_amdgcn_exp2f(mml[sl * 2] - Mu);
+        l_row += sc[w] * mml[sl * 2 + 1];
+      }
 #pragma unroll
-        for (int t = 0; t < S::NDT; ++t) {
+      for (int t = 0; t < S::NDT; ++t) oacc[t] *= sc[0];
+      m_ref = M;
+    }
+#pragma unroll
+    for (int t0 = 0; t0 < S::NDT; t0 += S::TPR) {
+      if (t0 > 0) __syncthreads();  // the previous round has been read
+      if (wk > 0) {
+        SDPA_LDS float* myo = mo + (slot * 32 + col) * S::MROW;
+#pragma unroll
+        for (int t = 0; t < S::TPR; ++t) {
 #pragma unroll
           for (int i4 = 0; i4 < 4; ++i4) {
-            const f32x4 v4 = *(const SDPA_LDS f32x4*)(po + t * 32 + 8 * i4 + 4 * hl);
-            oacc[t][4 * i4 + 0] += sc * v4[0];
-            oacc[t][4 * i4 + 1] += sc * v4[1];
-            oacc[t][4 * i4 + 2] += sc * v4[2];
-            oacc[t][4 * i4 + 3] += sc * v4[3];
+            const int d = t * 32 + 8 * i4 + 4 * hl;
+            *(SDPA_LDS f32x4*)(myo + d) = f32x4{oacc[t0 + t][4 * i4 + 0], oacc[t0 + t][4 * i4 + 1],
+                                                oacc[t0 + t][4 * i4 + 2], oacc[t0 + t][4 * i4 + 3]};
           }
         }
       }
-      m_ref = M;
+      __syncthreads();
+      if (wk == 0) {
+#pragma unroll
+        for (int w = 1; w < NWK; ++w) {
+          const SDPA_LDS float* po = mo + ((wq * (NWK - 1) + w - 1) * 32 + col) * S::MROW;
+#pragma unroll
+          for (int t = 0; t < S::TPR; ++t) {
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+              const f32x4 v4 = *(const SDPA_LDS f32x4*)(po + t * 32 + 8 * i4 + 4 * hl);
+              oacc[t0 + t][4 * i4 + 0] += sc[w] * v4[0];
+              oacc[t0 + t][4 * i4 + 1] += sc[w] * v4[1];
+              oacc[t0 + t][4 * i4 + 2] += sc[w] * v4[2];
+              oacc[t0 + t][4 * i4 + 3] += sc[w] * v4[3];
+            }
+          }
+        }
+      }
     }
   }
 

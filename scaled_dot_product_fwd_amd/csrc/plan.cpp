@@ -58,10 +58,13 @@ const char* mask_name(int m) {
 }  // namespace
 
 size_t attn_lds_bytes(int dtype, int dqk_pad, int dv_pad, const Family& f) {
-  // Mirrors Shape<> in attn_kernel.h: two K and two V tile buffers (the
-  // cross-wave merge reuses them).
+  // Mirrors Shape<> in attn_kernel.h: two K and two V tile buffers, which
+  // the cross-wave merge reuses (with a little more for the smallest dims).
   const int es = dtype == SDPA_F32 ? 4 : 2;
-  return (size_t)2 * f.nwk * f.bkw * (dqk_pad + dv_pad) * es;
+  const size_t tiles = (size_t)2 * f.nwk * f.bkw * (dqk_pad + dv_pad) * es;
+  const size_t slots = (size_t)f.nwq * (f.nwk - 1);
+  const size_t merge = (slots * 32 * 8 + 15) / 16 * 16 + slots * 32 * (32 + 4) * 4;
+  return std::max(tiles, merge);
 }
 
 int make_plan(const sdpa_desc_t* d, Plan* p, std::string* err) {
@@ -155,10 +158,10 @@ int make_plan(const sdpa_desc_t* d, Plan* p, std::string* err) {
   const int64_t G = Hq / Hkv;
   const int64_t R = G * Lq;
   int rows = d->row_tile ? d->row_tile : (R <= 32 ? 32 : (R <= 64 ? 64 : 128));
-  const int kind = rows == 32 ? KIND_DECODE : (rows == 64 ? KIND_SHORT : KIND_PREFILL);
-  const Family fam = family_for(kind, d->dtype == SDPA_F32 ? 4 : 2, dqk_pad, dv_pad);
   const int64_t row_tiles = ceil_div(R, rows);
   const int64_t base = B * Hkv * row_tiles;
+  const int kind = rows == 32 ? KIND_DECODE : (rows == 64 ? KIND_SHORT : KIND_PREFILL);
+  const Family fam = family_for(kind, d->dtype == SDPA_F32 ? 4 : 2, dqk_pad, dv_pad);
   const int64_t bk = (int64_t)fam.nwk * fam.bkw;
 
   // Key blocks a row tile visits (the longest tile; every tile for `none`).
@@ -171,13 +174,16 @@ int make_plan(const sdpa_desc_t* d, Plan* p, std::string* err) {
     splits = d->num_splits;
   } else {
     // Split the key range when the row tiles alone leave the chip idle: aim
-    // for one full round of resident workgroups (LDS decides how many fit a
-    // CU).  A full-size prefill tile (128 rows) is only split when very few
+    // for one full round of resident workgroups (LDS and the waves each
+    // instance is compiled for decide how many fit a CU).  A full-size prefill tile (128 rows) is only split when very few
     // tiles exist: its partial outputs would cost HBM traffic comparable to
     // the K/V it reads, while an unsplit wave of large tiles already keeps
     // the MFMA units busy.
     const size_t lds_need = attn_lds_bytes(d->dtype, dqk_pad, dv_pad, fam);
-    const int64_t resident = std::max<int64_t>(1, std::min<int64_t>(kWgsPerCU, (160 * 1024) / (int64_t)lds_need));
+    const int64_t by_waves = 4 * wpe_for(kind, d->dtype == SDPA_F32 ? 4 : 2, dqk_pad, dv_pad) /
+                             (fam.nwq * fam.nwk);
+    const int64_t resident = std::max<int64_t>(
+        1, std::min<int64_t>({(int64_t)kWgsPerCU, (160 * 1024) / (int64_t)lds_need, by_waves}));
     const int64_t target = (int64_t)kTargetCUs * resident;
     const bool starved = rows < 128 ? base < target : base < kTargetCUs / 4;
     if (starved) splits = std::min<int64_t>(ceil_div(target, base), nblocks);

@@ -172,16 +172,17 @@ int sdpa_forward(const sdpa_desc_t* d, const void* q, const void* k, const void*
     a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes);
   }
 
-  const int fam = p.kind;  // KIND_PREFILL=0, KIND_SHORT=1, KIND_DECODE=2
   using L = int (*)(const sdpa::Plan&, const sdpa::AttnArgs&, void*, std::string*);
-  static const L table[3][3] = {
+  // [dtype][kind]
+  static const L table[3][sdpa::kNumKinds] = {
       {sdpa::launch_attn_f32_prefill, sdpa::launch_attn_f32_short, sdpa::launch_attn_f32_decode},
       {sdpa::launch_attn_f16_prefill, sdpa::launch_attn_f16_short, sdpa::launch_attn_f16_decode},
       {sdpa::launch_attn_bf16_prefill, sdpa::launch_attn_bf16_short, sdpa::launch_attn_bf16_decode},
   };
+  const L launch = table[p.dtype][p.kind];
   if (ev_start && hipEventRecord(ev_start, (hipStream_t)stream) != hipSuccess)
     return set_error(SDPA_E_HIP, "hipEventRecord(start) failed");
-  rc = table[p.dtype][fam](p, a, stream, &err);
+  rc = launch(p, a, stream, &err);
   if (rc != SDPA_OK) return set_error(rc, err);
   if (ev_stop && hipEventRecord(ev_stop, (hipStream_t)stream) != hipSuccess)
     return set_error(SDPA_E_HIP, "hipEventRecord(stop) failed");

@@ -52,6 +52,7 @@ struct Family {
 };
 
 enum : int { KIND_PREFILL = 0, KIND_SHORT = 1, KIND_DECODE = 2 };
+constexpr int kNumKinds = 3;
 
 // The wave arrangement of each kind, sized so that the two LDS buffers of K
 // and V tiles fit: prefill keeps two workgroups per CU (<= 80 KB), decode
