@@ -9,10 +9,10 @@
 
 namespace sdpa {
 
-template <class E, int DQK, int DV, int NWQ, int NWK, int BKW, int WPE>
+template <class E, int DQK, int DV, int NWQ, int NWK, int BKW, int QT, int WPE>
 int launch_one(const Plan& p, const AttnArgs& a, void* stream, std::string* err) {
-  using S = dev::Shape<E, DQK, DV, NWQ, NWK, BKW>;
-  auto kern = dev::attn_fwd_kernel<E, DQK, DV, NWQ, NWK, BKW, WPE>;
+  using S = dev::Shape<E, DQK, DV, NWQ, NWK, BKW, QT>;
+  auto kern = dev::attn_fwd_kernel<E, DQK, DV, NWQ, NWK, BKW, QT, WPE>;
   // Check the compiled kernel can run the workgroup size it is launched with,
   // once per instance: an oversized launch must fail loudly, never return
   // silently unwritten output (mlx PR #4185 "Add force_fused option to
@@ -50,25 +50,28 @@ int launch_one(const Plan& p, const AttnArgs& a, void* stream, std::string* err)
 #define SDPA_CASE(E, KIND, DQK, DV)                                                            \
   if (p.dqk_pad == DQK && p.dv_pad == DV) {                                                    \
     constexpr Family f_ = family_for(KIND, dev::E::ES, DQK, DV);                               \
-    if (p.fam.nwq != f_.nwq || p.fam.nwk != f_.nwk || p.fam.bkw != f_.bkw) {                   \
+    if (p.fam.nwq != f_.nwq || p.fam.nwk != f_.nwk || p.fam.bkw != f_.bkw || p.fam.qt != f_.qt) { \
       *err = "plan and kernel instance disagree on the wave arrangement";                      \
       return SDPA_E_PLAN;                                                                      \
     }                                                                                          \
-    return launch_one<dev::E, DQK, DV, f_.nwq, f_.nwk, f_.bkw,                  \
+    return launch_one<dev::E, DQK, DV, f_.nwq, f_.nwk, f_.bkw, f_.qt,           \
                       wpe_for(KIND, dev::E::ES, DQK, DV)>(p, a, stream, err);             \
   }
 
-// Head-dim pairs of the 16-bit types: equal padded dims plus (192, 128).
-#define SDPA_PAIRS16(E, KIND) \
-  SDPA_CASE(E, KIND, 32, 32)   \
-  SDPA_CASE(E, KIND, 64, 64)   \
-  SDPA_CASE(E, KIND, 96, 96)   \
-  SDPA_CASE(E, KIND, 128, 128) \
-  SDPA_CASE(E, KIND, 160, 160) \
-  SDPA_CASE(E, KIND, 192, 192) \
-  SDPA_CASE(E, KIND, 224, 224) \
-  SDPA_CASE(E, KIND, 256, 256) \
+// Head-dim pairs of the 16-bit types: equal padded dims plus (192, 128),
+// split at 192 so that the large ones can live in units of their own.
+#define SDPA_PAIRS16_SMALL(E, KIND) \
+  SDPA_CASE(E, KIND, 32, 32)         \
+  SDPA_CASE(E, KIND, 64, 64)         \
+  SDPA_CASE(E, KIND, 96, 96)         \
+  SDPA_CASE(E, KIND, 128, 128)       \
+  SDPA_CASE(E, KIND, 160, 160)
+#define SDPA_PAIRS16_LARGE(E, KIND) \
+  SDPA_CASE(E, KIND, 192, 192)       \
+  SDPA_CASE(E, KIND, 224, 224)       \
+  SDPA_CASE(E, KIND, 256, 256)       \
   SDPA_CASE(E, KIND, 192, 128)
+#define SDPA_PAIRS16(E, KIND) SDPA_PAIRS16_SMALL(E, KIND) SDPA_PAIRS16_LARGE(E, KIND)
 
 // float32 stops at 128.
 #define SDPA_PAIRS32(E, KIND)  \

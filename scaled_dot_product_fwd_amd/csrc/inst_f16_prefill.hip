@@ -2,8 +2,10 @@
 #include "attn_launch.h"
 
 namespace sdpa {
+int launch_attn_f16_prefill_large(const Plan& p, const AttnArgs& a, void* stream, std::string* err);
+
 int launch_attn_f16_prefill(const Plan& p, const AttnArgs& a, void* stream, std::string* err) {
-  SDPA_PAIRS16(F16, KIND_PREFILL)
-  SDPA_NO_INSTANCE()
+  SDPA_PAIRS16_SMALL(F16, KIND_PREFILL)
+  return launch_attn_f16_prefill_large(p, a, stream, err);
 }
 }  // namespace sdpa

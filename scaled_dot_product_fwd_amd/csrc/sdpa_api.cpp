@@ -165,6 +165,7 @@ int sdpa_forward(const sdpa_desc_t* d, const void* q, const void* k, const void*
   a.splits = p.splits;
   a.row_tiles = p.row_tiles;
   a.heavy_first = p.mask != sdpa::MASK_NONE && p.row_tiles > 1;
+  a.xcd_group = p.xcd_group;
   if (p.splits > 1) {
     const size_t rows_total = (size_t)d->batch * d->heads_kv * a.R * p.splits;
     const size_t o_bytes = (rows_total * (size_t)d->dim_v * 4 + 255) / 256 * 256;

@@ -32,6 +32,7 @@ struct AttnArgs {
   int splits;          // key splits per row tile (1: normalise in place)
   int row_tiles;       // ceil(R / rows per workgroup)
   int heavy_first;     // causal/window prefill: visit the longest row tiles first
+  int xcd_group;       // > 0: consecutive work items run in groups of this many on one XCD
 };
 
 // Arguments of the split combine kernel.
@@ -46,9 +47,10 @@ struct CombineArgs {
 
 // Kernel family = how the waves of a workgroup divide the work.
 struct Family {
-  int nwq;   // waves stacked along query rows (32 rows each)
-  int nwk;   // waves splitting each key block between them
-  int bkw;   // keys per wave per iteration (multiple of 32)
+  int nwq;     // waves stacked along query rows
+  int nwk;     // waves splitting each key block between them
+  int bkw;     // keys per wave per iteration (multiple of 32)
+  int qt = 1;  // groups of 32 query rows per wave
 };
 
 enum : int { KIND_PREFILL = 0, KIND_SHORT = 1, KIND_DECODE = 2 };
@@ -91,6 +93,7 @@ struct Plan {
   int splits;
   int mask, window;      // canonical mask
   int64_t grid;          // workgroups of the attention kernel
+  int xcd_group;         // see AttnArgs::xcd_group
   int64_t combine_grid;  // workgroups of the combine kernel (0 when unsplit)
   size_t workspace;      // bytes
   size_t lds_bytes;      // static LDS of the chosen attention kernel
