@@ -229,3 +229,14 @@ def test_more_splits_than_key_blocks(splits):
     drop out of the merge."""
     _say("empty splits", splits)
     check_full(1, 4, 1, 2, 150, 64, 64, "f16", "none", 0, seed=55, num_splits=splits)
+
+
+@pytest.mark.parametrize("lq", [48, 64])
+def test_split_plan_with_several_row_tiles(lq):
+    """Split plans with more than one row tile per KV head deal their work
+    items to XCDs in groups; every row must still come out exactly once."""
+    _say("split + row tiles", lq)
+    d = sdpa.make_desc((1, 32, lq, 128), (1, 8, 3000, 128), (1, 8, 3000, 128), sdpa.SDPA_F16)
+    plan = dict(t.split("=", 1) for t in sdpa.sdpa_describe_plan(d).split())
+    assert int(plan["row_tiles"]) > 1 and int(plan["splits"]) > 1 and plan["xcd_group"] == "8"
+    check_full(1, 32, 8, lq, 3000, 128, 128, "f16", "none", 0, seed=61)
