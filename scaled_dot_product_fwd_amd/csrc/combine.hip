@@ -15,68 +15,80 @@
 namespace sdpa {
 namespace dev {
 
-constexpr int kCombineThreads = 128;
+constexpr int kCombineThreads = 256;
 constexpr int kCombineMaxSplits = 1024;
+constexpr int kCombineRegs = 8;  // partial outputs a thread holds in registers
 
-// One workgroup per packed row.  The (m, l) pairs are read once into LDS;
-// then thread (g, c) sums the weighted partial outputs of 4 head-dim columns
-// c over the splits s = g, g + NG, g + 2 NG, ... with independent 16-byte
-// loads, and the NG group sums are added in LDS.
+// One workgroup per packed row.  Thread (g, c) owns 4 head-dim columns c of
+// the splits s = g, g + NG, g + 2 NG, ... (NG = threads / (dv / 4)); every
+// load it needs -- its (m, l) pair and up to kCombineRegs partial outputs --
+// is issued before the first wait, so a row costs one memory round trip.
+// The weights follow once the row max is known; the NG group sums are added
+// in LDS.
 template <class E>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a) {
   __shared__ float msh[kCombineMaxSplits];
-  __shared__ float lsh[kCombineMaxSplits];
   __shared__ f32x4 part[kCombineThreads];
-  __shared__ float red[2], red_l[2];
+  __shared__ float red[kCombineThreads / 64], red_l[kCombineThreads / 64];
   const int row = blockIdx.x;  // z * R + r
   const int z = row / a.R, r = row % a.R;
   const int b = z / a.Hkv, kvh = z % a.Hkv;
   const int g = r % a.G, i = r / a.G, h = kvh * a.G + g;
   const float* ml = a.ws_ml + (int64_t)row * a.splits * 2;
   const int tid = threadIdx.x;
+  const int nc = a.dv / 4;              // 4-column groups: dv % 8 == 0, dv <= 4 * threads
+  const int ng = kCombineThreads / nc;  // split groups
+  const int gi = tid / nc, c = tid % nc;
+  const float* wo = a.ws_o + (int64_t)row * a.splits * a.dv + 4 * c;
 
-  float mx = kNegInf;
-  for (int s = tid; s < a.splits; s += kCombineThreads) {
-    const float2 v = *(const float2*)(ml + 2 * s);
-    msh[s] = v.x;
-    lsh[s] = v.y;
-    mx = fmaxf(mx, v.x);
+  f32x4 v[kCombineRegs];
+#pragma unroll
+  for (int u = 0; u < kCombineRegs; ++u) {
+    const int sp = gi + u * ng;
+    v[u] = (gi < ng && sp < a.splits) ? *(const f32x4*)(wo + (int64_t)sp * a.dv) : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  float mx = kNegInf, lp_m = kNegInf, lp_l = 0.f;
+  for (int sp = tid; sp < a.splits; sp += kCombineThreads) {
+    const float2 q = *(const float2*)(ml + 2 * sp);
+    msh[sp] = q.x;
+    if (sp == tid) { lp_m = q.x; lp_l = q.y; }  // first pair of this thread, kept for the sum
+    mx = fmaxf(mx, q.x);
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
   if ((tid & 63) == 0) red[tid >> 6] = mx;
-  __syncthreads();  // also publishes msh / lsh
-  const float M = fmaxf(red[0], red[1]);
+  __syncthreads();  // also publishes msh
+  float M = red[0];
+#pragma unroll
+  for (int w = 1; w < kCombineThreads / 64; ++w) M = fmaxf(M, red[w]);
   const float Mu = (M == kNegInf) ? 0.f : M;
 
-  float lp = 0.f;
-  for (int s = tid; s < a.splits; s += kCombineThreads) lp += __builtin_amdgcn_exp2f(msh[s] - Mu) * lsh[s];
+  // L = sum_s 2^(m_s - M) l_s
+  float lp = tid < a.splits ? __builtin_amdgcn_exp2f(lp_m - Mu) * lp_l : 0.f;
+  for (int sp = tid + kCombineThreads; sp < a.splits; sp += kCombineThreads)
+    lp += __builtin_amdgcn_exp2f(msh[sp] - Mu) * ml[2 * sp + 1];
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) lp += __shfl_xor(lp, o);
   if ((tid & 63) == 0) red_l[tid >> 6] = lp;
 
-  const int nc = a.dv / 4;               // 4-column groups: dv % 8 == 0, dv <= 256
-  const int ng = kCombineThreads / nc;   // split groups
-  const int gi = tid / nc, c = tid % nc;
-  const float* wo = a.ws_o + (int64_t)row * a.splits * a.dv + 4 * c;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   if (gi < ng) {
-    int s = gi;
-    for (; s + 3 * ng < a.splits; s += 4 * ng) {
-      f32x4 v[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = *(const f32x4*)(wo + (int64_t)(s + u * ng) * a.dv);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) acc += __builtin_amdgcn_exp2f(msh[s + u * ng] - Mu) * v[u];
+    for (int u = 0; u < kCombineRegs; ++u) {
+      const int sp = gi + u * ng;
+      if (sp < a.splits) acc += __builtin_amdgcn_exp2f(msh[sp] - Mu) * v[u];
     }
-    for (; s < a.splits; s += ng) acc += __builtin_amdgcn_exp2f(msh[s] - Mu) * *(const f32x4*)(wo + (int64_t)s * a.dv);
+    for (int sp = gi + kCombineRegs * ng; sp < a.splits; sp += ng)
+      acc += __builtin_amdgcn_exp2f(msh[sp] - Mu) * *(const f32x4*)(wo + (int64_t)sp * a.dv);
   }
   part[tid] = acc;
   __syncthreads();  // publishes part and red_l
   if (tid < nc) {
     f32x4 sum = part[tid];
     for (int q = 1; q < ng; ++q) sum += part[q * nc + tid];
-    const float L = red_l[0] + red_l[1];
+    float L = red_l[0];
+#pragma unroll
+    for (int w = 1; w < kCombineThreads / 64; ++w) L += red_l[w];
     const float inv = 1.0f / L;
     char* orow = (char*)a.o + ((int64_t)b * a.os[0] + (int64_t)h * a.os[1] + (int64_t)i * a.os[2]) * E::ES;
     const int d = 4 * tid;
