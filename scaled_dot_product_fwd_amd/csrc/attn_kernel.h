@@ -184,6 +184,10 @@ struct Shape {
   // (4 per fragment) stay within a budget (16-bit types only).
   static constexpr bool HOIST_K = E::ES == 2 && QT == 1 && NKT * NQS * 4 <= 48;
   static constexpr bool HOIST_V = E::ES == 2 && QT == 1 && NKT * (32 / E::KPV) * NDT * 4 <= 48 && NQS * 4 + NDT * 16 <= 128;
+  // Software-pipelined block loop (QK of the next block overlapping this
+  // block's softmax) where two blocks of scores fit next to Q and O:
+  // four-wave prefill tiles of the small head dims, 16-bit types.
+  static constexpr bool PIPE = NWK == 1 && QT == 1 && E::ES == 2 && NQS * 4 + NDT * 16 + 2 * NKT * 16 <= 144;
   // DMA instructions one block costs the wave that issues the fewest / most.
   static constexpr int DMA_MIN = KDMA / NW + VDMA / NW;
   static constexpr int DMA_MAX = (KDMA + NW - 1) / NW + (VDMA + NW - 1) / NW;
@@ -575,21 +579,10 @@ void attn_fwd_kernel(AttnArgs a) {
     }
   };
 
-  // ---- mask, online softmax and O^T += V^T P^T of block j ----
-  auto softmax_pv = [&](int j, f32x16 (&sacc)[QT][S::NKT]) __attribute__((always_inline)) {
-    // Where registers allow, the block's V fragments are read up front so
-    // their latency hides under the softmax.
-    frag vf[S::HOIST_V ? S::NKT : 1][S::HOIST_V ? 32 / E::KPV : 1][S::HOIST_V ? S::NDT : 1];
-    if constexpr (S::HOIST_V) {
-#pragma unroll
-      for (int kt = 0; kt < S::NKT; ++kt)
-#pragma unroll
-        for (int s2 = 0; s2 < 32 / E::KPV; ++s2)
-#pragma unroll
-          for (int t = 0; t < S::NDT; ++t) vf[kt][s2][t] = vread(j, kt, s2, t);
-    }
+  // ---- mask edge blocks and fold the block max into the running max ----
+  auto mask_max = [&](int j, f32x16 (&sacc)[QT][S::NKT]) __attribute__((always_inline)) {
     const int kw = blk(j) * S::BK + wk * BKW;  // first key of this wave's slice
-    // ---- mask edge blocks (diagonal, window edge, Lk tail) ----
+    // edge blocks: the diagonal, a window edge, the Lk tail
     const bool edge = (kw + BKW > a.Lk) || (a.mask != MASK_NONE && kw + BKW - 1 > pmin_w) ||
                       (a.mask == MASK_WINDOW && kw <= pmax_w - a.window);
 #pragma unroll
@@ -612,8 +605,7 @@ void attn_fwd_kernel(AttnArgs a) {
           }
         }
       }
-
-      // ---- online softmax with lazy rescaling (scale c > 0) ----
+      // online softmax with lazy rescaling (scale c > 0)
       float mx = kNegInf;
 #pragma unroll
       for (int kt = 0; kt < S::NKT; ++kt)
@@ -630,8 +622,14 @@ void attn_fwd_kernel(AttnArgs a) {
         for (int t = 0; t < S::NDT; ++t) oacc[q][t] *= alpha;
         m_ref[q] = m_new;
       }
-      const float msub = (m_ref[q] == kNegInf) ? 0.f : m_ref[q];
+    }
+  };
 
+  // ---- probabilities of a block against the reference max ----
+  auto expo = [&](f32x16 (&sacc)[QT][S::NKT]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < QT; ++q) {
+      const float msub = (m_ref[q] == kNegInf) ? 0.f : m_ref[q];
 #pragma unroll
       for (int kt = 0; kt < S::NKT; ++kt) {
 #pragma unroll
@@ -642,8 +640,21 @@ void attn_fwd_kernel(AttnArgs a) {
         }
       }
     }
+  };
 
-    // ---- O^T += V^T P^T ----
+  // ---- O^T += V^T P^T of block j (V fragments optionally read ahead) ----
+  using vfrag_t = frag[S::HOIST_V ? S::NKT : 1][S::HOIST_V ? 32 / E::KPV : 1][S::HOIST_V ? S::NDT : 1];
+  auto vhoist = [&](int j, vfrag_t& vf) __attribute__((always_inline)) {
+    if constexpr (S::HOIST_V) {
+#pragma unroll
+      for (int kt = 0; kt < S::NKT; ++kt)
+#pragma unroll
+        for (int s2 = 0; s2 < 32 / E::KPV; ++s2)
+#pragma unroll
+          for (int t = 0; t < S::NDT; ++t) vf[kt][s2][t] = vread(j, kt, s2, t);
+    }
+  };
+  auto pv = [&](int j, f32x16 (&sacc)[QT][S::NKT], vfrag_t& vf) __attribute__((always_inline)) {
 #pragma unroll
     for (int kt = 0; kt < S::NKT; ++kt) {
 #pragma unroll
@@ -676,25 +687,81 @@ void attn_fwd_kernel(AttnArgs a) {
     }
   };
 
-  // Block j sits in buffer pair j % 2.  Iteration j waits for block j
-  // (block j + 1 stays in flight), computes it, and once every wave is done
-  // with its buffers sends block j + 2 there.  So the next block is always
-  // in flight during the compute and two are while the wave waits: the
-  // stream never drains between blocks.
-  f32x16 sacc[QT][S::NKT];
-  for (int j = 0; j < nblk; ++j) {
-    if (j + 1 < nblk) wait_vmcnt<S::DMA_MIN>();  // only block j + 1 may still be in flight
-    else wait_vmcnt<0>();
-    __syncthreads();  // every wave's share of block j has landed
-    qk(j, sacc);
-    softmax_pv(j, sacc);
-    if (j + 2 < nblk) {
-      // The vector-memory counter holds at most 63 operations: where two
-      // blocks would exceed that, let part of block j + 1 land first.
-      if constexpr (2 * S::DMA_MAX > 63) wait_vmcnt<63 - S::DMA_MAX>();
-      __syncthreads();  // every wave is done reading buffer pair j % 2
-      dma_k(blk(j + 2), j & 1);
-      dma_v(blk(j + 2), j & 1);
+  if constexpr (!S::PIPE) {
+    // Block j sits in buffer pair j % 2.  Iteration j waits for block j
+    // (block j + 1 stays in flight), computes it, and once every wave is
+    // done with its buffers sends block j + 2 there.  So the next block is
+    // always in flight during the compute and two are while the wave waits:
+    // the stream never drains between blocks.
+    f32x16 sacc[QT][S::NKT];
+    for (int j = 0; j < nblk; ++j) {
+      if (j + 1 < nblk) wait_vmcnt<S::DMA_MIN>();  // only block j + 1 may still be in flight
+      else wait_vmcnt<0>();
+      __syncthreads();  // every wave's share of block j has landed
+      qk(j, sacc);
+      vfrag_t vf;
+      vhoist(j, vf);  // in flight during the softmax
+      mask_max(j, sacc);
+      expo(sacc);
+      pv(j, sacc, vf);
+      if (j + 2 < nblk) {
+        // The vector-memory counter holds at most 63 operations: where two
+        // blocks would exceed that, let part of block j + 1 land first.
+        if constexpr (2 * S::DMA_MAX > 63) wait_vmcnt<63 - S::DMA_MAX>();
+        __syncthreads();  // every wave is done reading buffer pair j % 2
+        dma_k(blk(j + 2), j & 1);
+        dma_v(blk(j + 2), j & 1);
+      }
+    }
+  } else {
+    // Software-pipelined loop: the QK products of block j + 1 are issued
+    // between the exponentials of block j and its PV products, so the
+    // matrix cores work while the vector unit computes probabilities (one
+    // wave per SIMD cannot overlap them otherwise).  K runs two blocks
+    // ahead of V: K(j + 1) and V(j) are consumed in step j, after which
+    // their buffers take K(j + 3) and V(j + 2).  Step j waits for K(j + 1)
+    // and V(j); what may still be in flight is K(j + 2) and V(j + 1).
+    f32x16 sa[QT][S::NKT], sb[QT][S::NKT];
+    if (nblk > 0) {
+      __syncthreads();  // block 0 (waited for above) is visible to every wave
+      qk(0, sa);
+      mask_max(0, sa);
+      if (nblk > 2) {
+        __syncthreads();  // every wave is done with K(0)
+        dma_k(blk(2), 0);
+      }
+    }
+    // `more` (block j + 1 exists) is a literal at every call, so the
+    // compute of a step is one branch-free stretch the scheduler can
+    // interleave.
+    auto step = [&](int j, f32x16 (&cur)[QT][S::NKT], f32x16 (&nxt)[QT][S::NKT], const bool more)
+        __attribute__((always_inline)) {
+      if (j + 2 < nblk) wait_vmcnt<S::DMA_MIN>();
+      else if (more) wait_vmcnt<S::VDMA / S::NW>();
+      else wait_vmcnt<0>();
+      __syncthreads();  // K(j + 1) and V(j) have landed for every wave
+      vfrag_t vf;
+      vhoist(j, vf);
+      expo(cur);
+      if (more) qk(j + 1, nxt);
+      pv(j, cur, vf);
+      if (more) mask_max(j + 1, nxt);
+      if (j + 2 < nblk) {
+        __syncthreads();  // every wave is done with K(j + 1) and V(j)
+        if (j + 3 < nblk) dma_k(blk(j + 3), (j + 1) & 1);
+        dma_v(blk(j + 2), j & 1);
+      }
+    };
+    int j = 0;
+    for (; j + 2 < nblk; j += 2) {
+      step(j, sa, sb, true);
+      step(j + 1, sb, sa, true);
+    }
+    if (j + 1 < nblk) {
+      step(j, sa, sb, true);
+      step(j + 1, sb, sa, false);
+    } else if (j < nblk) {
+      step(j, sa, sb, false);
     }
   }
 
