@@ -689,27 +689,35 @@ void attn_fwd_kernel(AttnArgs a) {
 
   if constexpr (!S::PIPE) {
     // Block j sits in buffer pair j % 2.  Iteration j waits for block j
-    // (block j + 1 stays in flight), computes it, and once every wave is
-    // done with its buffers sends block j + 2 there.  So the next block is
+    // (block j + 1 stays in flight), computes it, and sends block j + 2 to
+    // the same pair as soon as every wave is done with each half: K right
+    // after the QK products, V after the PV products.  So the next block is
     // always in flight during the compute and two are while the wave waits:
-    // the stream never drains between blocks.
+    // the stream never drains between blocks.  (Where two blocks would
+    // overflow the 63-entry vector-memory counter, K waits for the end too
+    // and part of block j + 1 lands first.)
+    constexpr bool KEARLY = 2 * S::DMA_MAX <= 63;
     f32x16 sacc[QT][S::NKT];
     for (int j = 0; j < nblk; ++j) {
       if (j + 1 < nblk) wait_vmcnt<S::DMA_MIN>();  // only block j + 1 may still be in flight
       else wait_vmcnt<0>();
       __syncthreads();  // every wave's share of block j has landed
       qk(j, sacc);
+      if constexpr (KEARLY) {
+        if (j + 2 < nblk) {
+          __syncthreads();  // every wave is done with K(j)
+          dma_k(blk(j + 2), j & 1);
+        }
+      }
       vfrag_t vf;
       vhoist(j, vf);  // in flight during the softmax
       mask_max(j, sacc);
       expo(sacc);
       pv(j, sacc, vf);
       if (j + 2 < nblk) {
-        // The vector-memory counter holds at most 63 operations: where two
-        // blocks would exceed that, let part of block j + 1 land first.
-        if constexpr (2 * S::DMA_MAX > 63) wait_vmcnt<63 - S::DMA_MAX>();
-        __syncthreads();  // every wave is done reading buffer pair j % 2
-        dma_k(blk(j + 2), j & 1);
+        if constexpr (!KEARLY) wait_vmcnt<63 - S::DMA_MAX>();
+        __syncthreads();  // every wave is done with V(j)
+        if constexpr (!KEARLY) dma_k(blk(j + 2), j & 1);
         dma_v(blk(j + 2), j & 1);
       }
     }
