@@ -178,10 +178,14 @@ def test_split_workspace_layout():
     assert sdpa.sdpa_workspace_bytes(d) >= rows * 16 * (64 * 4 + 8)
 
 
-def test_plan_xcd_grouping_only_for_multi_tile_splits():
+def test_plan_xcd_grouping():
     p = _plan(hq=32, hkv=8, lq=64, lk=32768, dqk=128, dv=128, dtype=_lib.SDPA_F16)
     assert int(p["row_tiles"]) == 2 and int(p["splits"]) > 1 and p["xcd_group"] == "8"
     p = _plan(hq=64, hkv=8, lq=1, lk=32768, dqk=192, dv=128)
     assert p["xcd_group"] == "0"
     p = _plan(hq=16, hkv=8, lq=4096, lk=4096, dqk=256, dv=256, mask="window", window_size=1024)
-    assert p["splits"] == "1" and p["xcd_group"] == "0"
+    assert p["splits"] == "1" and p["xcd_group"] == "0"  # two rounds of tiles only
+    p = _plan(hq=16, hkv=8, lq=8192, lk=8192, dqk=256, dv=256, mask="window", window_size=1024)
+    assert p["splits"] == "1" and p["xcd_group"] == "8"
+    p = _plan(hq=16, hkv=2, lq=32768, lk=32768, dqk=256, dv=256, mask="causal")
+    assert p["xcd_group"] == "0"
