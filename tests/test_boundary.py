@@ -134,11 +134,11 @@ def test_plan_decode_config_splits_keys():
             assert (int(p["workspace"]) > 0) == (splits > 1)
 
 
-@pytest.mark.parametrize("lq,fam", [(1, "decode"), (8, "decode"), (12, "short"), (16, "short"),
-                                    (24, "prefill"), (64, "prefill")])
-def test_plan_verify_window_family(lq, fam):
+@pytest.mark.parametrize("lq,fam,tiles", [(1, "decode", 1), (8, "decode", 1), (12, "short", 1),
+                                          (16, "decode", 2), (24, "prefill", 1), (64, "prefill", 2)])
+def test_plan_verify_window_family(lq, fam, tiles):
     p = _plan(hq=32, hkv=8, lq=lq, lk=16384, dqk=128, dv=128, dtype=_lib.SDPA_F16)
-    assert p["family"] == fam
+    assert p["family"] == fam and int(p["row_tiles"]) == tiles
     assert int(p["grid"]) >= 256
 
 
