@@ -195,6 +195,12 @@ int make_plan(const sdpa_desc_t* d, Plan* p, std::string* err) {
     splits = std::max<int64_t>(1, std::min<int64_t>(splits, kMaxSplits));
   }
   if (base * splits > 0x7fffffffLL) return fail(err, SDPA_E_SHAPE, "grid too large");
+  // The combine launches one workgroup per packed row.
+  if (splits > 1 && B * Hkv * R > 0x7fffffffLL) {
+    if (d->num_splits > 1)
+      return fail(err, SDPA_E_PLAN, "a split plan needs B*Hq*Lq <= 2^31 - 1 (one combine workgroup per row)");
+    splits = 1;
+  }
 
   p->dtype = d->dtype;
   p->kind = kind;

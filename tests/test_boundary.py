@@ -189,3 +189,12 @@ def test_plan_xcd_grouping():
     assert p["splits"] == "1" and p["xcd_group"] == "8"
     p = _plan(hq=16, hkv=2, lq=32768, lk=32768, dqk=256, dv=256, mask="causal")
     assert p["xcd_group"] == "0"
+
+
+def test_split_rows_beyond_one_grid_fall_back_to_unsplit():
+    # B*Hq*Lq = 2^31 rows would need more combine workgroups than a grid holds
+    kw = dict(b=4, hq=256, hkv=1, lq=1 << 21, lk=1 << 21, dqk=64, dv=64)
+    p = _plan(**kw)
+    assert p["splits"] == "1"
+    msg = _status(sdpa.sdpa_workspace_bytes, _desc(num_splits=2, **kw))
+    assert "SDPA_E_PLAN" in msg and "2^31" in msg
