@@ -137,11 +137,11 @@ constexpr int cmin(int a, int b) { return a < b ? a : b; }
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
 // Static shape of one kernel instance.
-template <class E, int DQK, int DV, int NWQ, int NWK, int BKW, int QT>
+template <class E, int DQK, int DV, int NWQ, int NWK, int BKW>
 struct Shape {
   static constexpr int NW = NWQ * NWK;
   static constexpr int NT = NW * 64;
-  static constexpr int BM = NWQ * 32 * QT;     // rows per workgroup (QT groups of 32 per wave)
+  static constexpr int BM = NWQ * 32;          // rows per workgroup
   static constexpr int BK = NWK * BKW;         // keys per block
   static constexpr int NKT = BKW / 32;         // 32-key tiles per wave
   static constexpr int NDT = DV / 32;          // 32-wide dv tiles
@@ -182,12 +182,12 @@ struct Shape {
   static constexpr bool STREAM = NWK > 1;
   // Operand fragments read ahead of their products when the extra registers
   // (4 per fragment) stay within a budget (16-bit types only).
-  static constexpr bool HOIST_K = E::ES == 2 && QT == 1 && NKT * NQS * 4 <= 48;
-  static constexpr bool HOIST_V = E::ES == 2 && QT == 1 && NKT * (32 / E::KPV) * NDT * 4 <= 48 && NQS * 4 + NDT * 16 <= 128;
+  static constexpr bool HOIST_K = E::ES == 2 && NKT * NQS * 4 <= 48;
+  static constexpr bool HOIST_V = E::ES == 2 && NKT * (32 / E::KPV) * NDT * 4 <= 48 && NQS * 4 + NDT * 16 <= 128;
   // Software-pipelined block loop (QK of the next block overlapping this
   // block's softmax) where two blocks of scores fit next to Q and O:
   // four-wave prefill tiles of the small head dims, 16-bit types.
-  static constexpr bool PIPE = NWK == 1 && QT == 1 && E::ES == 2 && NQS * 4 + NDT * 16 + 2 * NKT * 16 <= 144;
+  static constexpr bool PIPE = NWK == 1 && E::ES == 2 && NQS * 4 + NDT * 16 + 2 * NKT * 16 <= 144;
   // DMA instructions one block costs the wave that issues the fewest / most.
   static constexpr int DMA_MIN = KDMA / NW + VDMA / NW;
   static constexpr int DMA_MAX = (KDMA + NW - 1) / NW + (VDMA + NW - 1) / NW;
@@ -203,7 +203,6 @@ struct Shape {
   static constexpr int TPR = merge_tiles();
   static constexpr int MROW = TPR * 32 + 4;  // +4 floats skew the rows across banks
   static_assert(NWK == 1 || TPR >= 1, "merge scratch must fit the tile buffers");
-  static_assert(QT == 1 || NWK == 1, "row groups per wave only without key slices");
   static_assert(DMA_MAX <= 63, "vmcnt range");
   static_assert(BKW % 32 == 0, "BKW must be a multiple of 32");
   static_assert(DQK % E::KQK == 0 && DV % 32 == 0, "bad head-dim tile");
@@ -216,13 +215,13 @@ struct Shape {
 // other.
 __device__ __forceinline__ float wave_max32(float x) {
   const unsigned u = __builtin_bit_cast(unsigned, x);
-  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+  const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)sw[0]), __builtin_bit_cast(float, (unsigned)sw[1]));
 }
 __device__ __forceinline__ float wave_sum32(float x) {
   const unsigned u = __builtin_bit_cast(unsigned, x);
-  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+  const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (unsigned)sw[0]) + __builtin_bit_cast(float, (unsigned)sw[1]);
 }
 
 // LDS DMA of 16 bytes per lane: lane l's chunk at `src` lands at LDS byte
@@ -252,10 +251,10 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);  // expcnt, lgkmcnt: no wait
 }
 
-template <class E, int DQK, int DV, int NWQ, int NWK, int BKW, int QT, int WPE>
+template <class E, int DQK, int DV, int NWQ, int NWK, int BKW, int WPE>
 __global__ __launch_bounds__(NWQ * NWK * 64) __attribute__((amdgpu_waves_per_eu(WPE)))
 void attn_fwd_kernel(AttnArgs a) {
-  using S = Shape<E, DQK, DV, NWQ, NWK, BKW, QT>;
+  using S = Shape<E, DQK, DV, NWQ, NWK, BKW>;
   using frag = typename E::frag;
   __shared__ __attribute__((aligned(1024))) char smem_[S::LDS];
   // All LDS addressing goes through an LDS-typed pointer, so addresses stay
@@ -267,7 +266,7 @@ void attn_fwd_kernel(AttnArgs a) {
   const int wave = tid >> 6;
   const int wq = wave % NWQ;
   const int wk = wave / NWQ;
-  const int col = lane & 31;  // query column of this lane in S^T / O^T (of each row group)
+  const int col = lane & 31;  // query column of this lane in S^T / O^T
   const int hl = lane >> 5;   // lane half
 
   // ---- workgroup -> (row tile, split, batch * KV head) ----
@@ -294,24 +293,18 @@ void attn_fwd_kernel(AttnArgs a) {
   const int kvh = z % a.Hkv;
 
   // ---- rows of this lane / wave / workgroup ----
-  // A wave holds QT groups of 32 rows; lane `col` of group q has row r[q].
   const int r_wg = rt * S::BM;
-  const int r_wave = r_wg + wq * 32 * QT;
-  int r[QT], iq[QT], pos[QT], hq[QT];
-  bool row_ok[QT];
-#pragma unroll
-  for (int q = 0; q < QT; ++q) {
-    r[q] = r_wave + 32 * q + col;
-    row_ok[q] = r[q] < a.R;
-    iq[q] = r[q] / a.G;
-    pos[q] = iq[q] + a.off;  // absolute key position of this row's query
-    hq[q] = kvh * a.G + r[q] % a.G;
-  }
+  const int r_wave = r_wg + wq * 32;
+  const int r = r_wave + col;
+  const bool row_ok = r < a.R;
+  const int iq = r / a.G;
+  const int pos = iq + a.off;  // absolute key position of this row's query
+  const int hq = kvh * a.G + r % a.G;
 
   const int r_last_wg = min(a.R, r_wg + S::BM) - 1;
   const int pmin_wg = r_wg / a.G + a.off;
   const int pmax_wg = r_last_wg / a.G + a.off;
-  const int r_last_wave = min(a.R - 1, r_wave + 32 * QT - 1);
+  const int r_last_wave = min(a.R - 1, r_wave + 31);
   const int pmin_w = min(r_wave, a.R - 1) / a.G + a.off;
   const int pmax_w = r_last_wave / a.G + a.off;
 
@@ -422,22 +415,21 @@ void attn_fwd_kernel(AttnArgs a) {
   }
 
   // ---- Q fragments (B operand of S^T = K Q^T), kept in registers ----
-  frag qf[QT][S::NQS];
-#pragma unroll
-  for (int q = 0; q < QT; ++q) {
+  frag qf[S::NQS];
+  {
     const char* qrow = (const char*)a.q +
-                       ((int64_t)b * a.qs[0] + (int64_t)hq[q] * a.qs[1] + (int64_t)iq[q] * a.qs[2]) * E::ES;
+                       ((int64_t)b * a.qs[0] + (int64_t)hq * a.qs[1] + (int64_t)iq * a.qs[2]) * E::ES;
 #pragma unroll
     for (int s = 0; s < S::NQS; ++s) {
       const int d = s * E::KQK + hl * E::EPL;
       if constexpr (E::ES == 2) {
         u32x4 v = {0u, 0u, 0u, 0u};
-        if (row_ok[q] && d < a.dqk) v = *(const u32x4*)(qrow + (int64_t)d * 2);
-        qf[q][s] = v;
+        if (row_ok && d < a.dqk) v = *(const u32x4*)(qrow + (int64_t)d * 2);
+        qf[s] = v;
       } else {
         float v = 0.f;
-        if (row_ok[q] && d < a.dqk) v = *(const float*)(qrow + (int64_t)d * 4);
-        qf[q][s] = v;
+        if (row_ok && d < a.dqk) v = *(const float*)(qrow + (int64_t)d * 4);
+        qf[s] = v;
       }
     }
   }
@@ -450,21 +442,17 @@ void attn_fwd_kernel(AttnArgs a) {
   if (c < 0.f) {
     c = -c;
 #pragma unroll
-    for (int q = 0; q < QT; ++q)
-#pragma unroll
-      for (int s = 0; s < S::NQS; ++s) {
-        if constexpr (E::ES == 2) qf[q][s] ^= 0x80008000u;
-        else qf[q][s] = -qf[q][s];
-      }
+    for (int s = 0; s < S::NQS; ++s) {
+      if constexpr (E::ES == 2) qf[s] ^= 0x80008000u;
+      else qf[s] = -qf[s];
+    }
   } else if (c == 0.f) {
     c = 1.f;
 #pragma unroll
-    for (int q = 0; q < QT; ++q)
-#pragma unroll
-      for (int s = 0; s < S::NQS; ++s) {
-        if constexpr (E::ES == 2) qf[q][s] = u32x4{0u, 0u, 0u, 0u};
-        else qf[q][s] = 0.f;
-      }
+    for (int s = 0; s < S::NQS; ++s) {
+      if constexpr (E::ES == 2) qf[s] = u32x4{0u, 0u, 0u, 0u};
+      else qf[s] = 0.f;
+    }
   }
 
   // Loop-invariant parts of the LDS operand addresses (16-bit types).  The
@@ -486,16 +474,11 @@ void attn_fwd_kernel(AttnArgs a) {
       voffl[tl] = (4 * (g >> 1) + (t16 >> 2)) * S::VROW + 16 * ((4 * tl + x) ^ y) + 8 * (t16 & 1);
   }
 
-  f32x16 oacc[QT][S::NDT];
-  float m_ref[QT];  // reference max of each row, log2 units (same in both lane halves)
-  float l_run[QT];  // this lane's share of each row sum (halves add up at the end)
+  f32x16 oacc[S::NDT];
 #pragma unroll
-  for (int q = 0; q < QT; ++q) {
-#pragma unroll
-    for (int t = 0; t < S::NDT; ++t) oacc[q][t] = f32x16{};
-    m_ref[q] = kNegInf;
-    l_run[q] = 0.f;
-  }
+  for (int t = 0; t < S::NDT; ++t) oacc[t] = f32x16{};
+  float m_ref = kNegInf;  // reference max of this row, log2 units (same in both lane halves)
+  float l_run = 0.f;      // this lane's share of the row sum (halves add up at the end)
 
   // Block 0 and the Q loads must have landed.  Waiting for everything here
   // also tells the compiler the Q loads are complete, so it puts no load
@@ -508,7 +491,7 @@ void attn_fwd_kernel(AttnArgs a) {
   }
 
   // ---- S^T = K Q^T of one block (this wave's BKW keys) ----
-  auto qk = [&](int j, f32x16 (&sacc)[QT][S::NKT]) __attribute__((always_inline)) {
+  auto qk = [&](int j, f32x16 (&sacc)[S::NKT]) __attribute__((always_inline)) {
     const SDPA_LDS char* kl = smem + (j & 1) * S::KBYTES;
     if constexpr (S::HOIST_K) {
       // Every K fragment of the block is read before the first product, so
@@ -524,16 +507,15 @@ void attn_fwd_kernel(AttnArgs a) {
       }
 #pragma unroll
       for (int kt = 0; kt < S::NKT; ++kt) {
-        sacc[0][kt] = f32x16{};
+        sacc[kt] = f32x16{};
 #pragma unroll
-        for (int s = 0; s < S::NQS; ++s) sacc[0][kt] = E::mma(kf[kt][s], qf[0][s], sacc[0][kt]);
+        for (int s = 0; s < S::NQS; ++s) sacc[kt] = E::mma(kf[kt][s], qf[s], sacc[kt]);
       }
       return;
     }
 #pragma unroll
     for (int kt = 0; kt < S::NKT; ++kt) {
-#pragma unroll
-      for (int q = 0; q < QT; ++q) sacc[q][kt] = f32x16{};
+      sacc[kt] = f32x16{};
       const SDPA_LDS char* ktile = kl + (wk * BKW + kt * 32) * S::KROW;
 #pragma unroll
       for (int s = 0; s < S::NQS; ++s) {
@@ -545,9 +527,7 @@ void attn_fwd_kernel(AttnArgs a) {
           const int d = 2 * s + hl;
           af = *(const SDPA_LDS float*)(ktile + col * S::KROW + (((d >> 2) ^ S::kx(col)) << 4) + (d & 3) * 4);
         }
-        // one K fragment feeds every row group of the wave
-#pragma unroll
-        for (int q = 0; q < QT; ++q) sacc[q][kt] = E::mma(af, qf[q][s], sacc[q][kt]);
+        sacc[kt] = E::mma(af, qf[s], sacc[kt]);
       }
     }
   };
@@ -580,64 +560,58 @@ void attn_fwd_kernel(AttnArgs a) {
   };
 
   // ---- mask edge blocks and fold the block max into the running max ----
-  auto mask_max = [&](int j, f32x16 (&sacc)[QT][S::NKT]) __attribute__((always_inline)) {
+  auto mask_max = [&](int j, f32x16 (&sacc)[S::NKT]) __attribute__((always_inline)) {
     const int kw = blk(j) * S::BK + wk * BKW;  // first key of this wave's slice
     // edge blocks: the diagonal, a window edge, the Lk tail
     const bool edge = (kw + BKW > a.Lk) || (a.mask != MASK_NONE && kw + BKW - 1 > pmin_w) ||
                       (a.mask == MASK_WINDOW && kw <= pmax_w - a.window);
+    if (edge) {
+      // Visible keys of this row form [lo, hi]; key of register e in tile kt
+      // is kw + 32 kt + 4 hl + off(e) with off(e) = 8 (e / 4) + e % 4.
+      int hi = a.Lk - 1, lo = 0;
+      if (a.mask != MASK_NONE) hi = min(hi, pos);
+      if (a.mask == MASK_WINDOW) lo = max(lo, pos - a.window + 1);
 #pragma unroll
-    for (int q = 0; q < QT; ++q) {
-      if (edge) {
-        // Visible keys of this row form [lo, hi]; key of register e in tile
-        // kt is kw + 32 kt + 4 hl + off(e) with off(e) = 8 (e / 4) + e % 4.
-        int hi = a.Lk - 1, lo = 0;
-        if (a.mask != MASK_NONE) hi = min(hi, pos[q]);
-        if (a.mask == MASK_WINDOW) lo = max(lo, pos[q] - a.window + 1);
+      for (int kt = 0; kt < S::NKT; ++kt) {
+        const int base = kw + kt * 32 + 4 * hl;
+        const unsigned span = (unsigned)(hi - lo);  // visible iff 0 <= key - lo <= span
+        const int first = lo - base;
 #pragma unroll
-        for (int kt = 0; kt < S::NKT; ++kt) {
-          const int base = kw + kt * 32 + 4 * hl;
-          const unsigned span = (unsigned)(hi - lo);  // visible iff 0 <= key - lo <= span
-          const int first = lo - base;
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int off = 8 * (e >> 2) + (e & 3);
-            if ((unsigned)(off - first) > span || hi < lo) sacc[q][kt][e] = kNegInf;
-          }
+        for (int e = 0; e < 16; ++e) {
+          const int off = 8 * (e >> 2) + (e & 3);
+          if ((unsigned)(off - first) > span || hi < lo) sacc[kt][e] = kNegInf;
         }
       }
-      // online softmax with lazy rescaling (scale c > 0)
-      float mx = kNegInf;
+    }
+    // online softmax with lazy rescaling (scale c > 0)
+    float mx = kNegInf;
 #pragma unroll
-      for (int kt = 0; kt < S::NKT; ++kt)
+    for (int kt = 0; kt < S::NKT; ++kt)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[q][kt][e]);
-      mx = wave_max32(mx);
-      const float mxs = mx * c;  // block max in log2 units (-inf if all masked)
-      const bool need = mxs > m_ref[q] + kRescale;
-      if (__builtin_expect(__builtin_amdgcn_ballot_w64(need) != 0, 0)) [[unlikely]] {
-        const float m_new = need ? mxs : m_ref[q];
-        const float alpha = need ? __builtin_amdgcn_exp2f(m_ref[q] - m_new) : 1.0f;
-        l_run[q] *= alpha;
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kt][e]);
+    mx = wave_max32(mx);
+    const float mxs = mx * c;  // block max in log2 units (-inf if all masked)
+    const bool need = mxs > m_ref + kRescale;
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(need) != 0, 0)) [[unlikely]] {
+      const float m_new = need ? mxs : m_ref;
+      const float alpha = need ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.0f;
+      l_run *= alpha;
 #pragma unroll
-        for (int t = 0; t < S::NDT; ++t) oacc[q][t] *= alpha;
-        m_ref[q] = m_new;
-      }
+      for (int t = 0; t < S::NDT; ++t) oacc[t] *= alpha;
+      m_ref = m_new;
     }
   };
 
   // ---- probabilities of a block against the reference max ----
-  auto expo = [&](f32x16 (&sacc)[QT][S::NKT]) __attribute__((always_inline)) {
+  auto expo = [&](f32x16 (&sacc)[S::NKT]) __attribute__((always_inline)) {
+    const float msub = (m_ref == kNegInf) ? 0.f : m_ref;
 #pragma unroll
-    for (int q = 0; q < QT; ++q) {
-      const float msub = (m_ref[q] == kNegInf) ? 0.f : m_ref[q];
+    for (int kt = 0; kt < S::NKT; ++kt) {
 #pragma unroll
-      for (int kt = 0; kt < S::NKT; ++kt) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[q][kt][e], c, -msub));
-          sacc[q][kt][e] = p;
-          l_run[q] += p;
-        }
+      for (int e = 0; e < 16; ++e) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][e], c, -msub));
+        sacc[kt][e] = p;
+        l_run += p;
       }
     }
   };
@@ -654,34 +628,24 @@ void attn_fwd_kernel(AttnArgs a) {
           for (int t = 0; t < S::NDT; ++t) vf[kt][s2][t] = vread(j, kt, s2, t);
     }
   };
-  auto pv = [&](int j, f32x16 (&sacc)[QT][S::NKT], vfrag_t& vf) __attribute__((always_inline)) {
+  auto pv = [&](int j, f32x16 (&sacc)[S::NKT], vfrag_t& vf) __attribute__((always_inline)) {
 #pragma unroll
     for (int kt = 0; kt < S::NKT; ++kt) {
 #pragma unroll
       for (int s2 = 0; s2 < 32 / E::KPV; ++s2) {
-        frag bf[QT];
+        frag bf;
+        if constexpr (E::ES == 2) {
+          u32x4 pk;
 #pragma unroll
-        for (int q = 0; q < QT; ++q) {
-          if constexpr (E::ES == 2) {
-            u32x4 pk;
-#pragma unroll
-            for (int w = 0; w < 4; ++w)
-              pk[w] = E::pack2(sacc[q][kt][8 * s2 + 2 * w], sacc[q][kt][8 * s2 + 2 * w + 1]);
-            bf[q] = pk;
-          } else {
-            bf[q] = sacc[q][kt][s2];
-          }
+          for (int w = 0; w < 4; ++w) pk[w] = E::pack2(sacc[kt][8 * s2 + 2 * w], sacc[kt][8 * s2 + 2 * w + 1]);
+          bf = pk;
+        } else {
+          bf = sacc[kt][s2];
         }
 #pragma unroll
         for (int t = 0; t < S::NDT; ++t) {
-          if constexpr (S::HOIST_V) {
-            oacc[0][t] = E::mma(vf[kt][s2][t], bf[0], oacc[0][t]);
-          } else {
-            // one V fragment feeds every row group of the wave
-            const frag af = vread(j, kt, s2, t);
-#pragma unroll
-            for (int q = 0; q < QT; ++q) oacc[q][t] = E::mma(af, bf[q], oacc[q][t]);
-          }
+          if constexpr (S::HOIST_V) oacc[t] = E::mma(vf[kt][s2][t], bf, oacc[t]);
+          else oacc[t] = E::mma(vread(j, kt, s2, t), bf, oacc[t]);
         }
       }
     }
@@ -697,7 +661,7 @@ void attn_fwd_kernel(AttnArgs a) {
     // overflow the 63-entry vector-memory counter, K waits for the end too
     // and part of block j + 1 lands first.)
     constexpr bool KEARLY = 2 * S::DMA_MAX <= 63;
-    f32x16 sacc[QT][S::NKT];
+    f32x16 sacc[S::NKT];
     for (int j = 0; j < nblk; ++j) {
       if (j + 1 < nblk) wait_vmcnt<S::DMA_MIN>();  // only block j + 1 may still be in flight
       else wait_vmcnt<0>();
@@ -729,7 +693,7 @@ void attn_fwd_kernel(AttnArgs a) {
     // ahead of V: K(j + 1) and V(j) are consumed in step j, after which
     // their buffers take K(j + 3) and V(j + 2).  Step j waits for K(j + 1)
     // and V(j); what may still be in flight is K(j + 2) and V(j + 1).
-    f32x16 sa[QT][S::NKT], sb[QT][S::NKT];
+    f32x16 sa[S::NKT], sb[S::NKT];
     if (nblk > 0) {
       __syncthreads();  // block 0 (waited for above) is visible to every wave
       qk(0, sa);
@@ -742,7 +706,7 @@ void attn_fwd_kernel(AttnArgs a) {
     // `more` (block j + 1 exists) is a literal at every call, so the
     // compute of a step is one branch-free stretch the scheduler can
     // interleave.
-    auto step = [&](int j, f32x16 (&cur)[QT][S::NKT], f32x16 (&nxt)[QT][S::NKT], const bool more)
+    auto step = [&](int j, f32x16 (&cur)[S::NKT], f32x16 (&nxt)[S::NKT], const bool more)
         __attribute__((always_inline)) {
       if (j + 2 < nblk) wait_vmcnt<S::DMA_MIN>();
       else if (more) wait_vmcnt<S::VDMA / S::NW>();
@@ -774,40 +738,38 @@ void attn_fwd_kernel(AttnArgs a) {
   }
 
   // ---- epilogue ----
-  float l_row[QT];
-#pragma unroll
-  for (int q = 0; q < QT; ++q) l_row[q] = wave_sum32(l_run[q]);  // both halves' keys
+  float l_row = wave_sum32(l_run);  // both halves' keys
 
   if constexpr (NWK > 1) {
     // Merge the NWK key slices of the same rows once every wave is done with
     // the tile buffers: waves wk > 0 leave their partial (m, l, O) in LDS,
-    // wave wk == 0 folds them into its own registers.  (One row group.)
+    // wave wk == 0 folds them into its own registers.
     SDPA_LDS float* mml = (SDPA_LDS float*)smem;            // [MSLOTS][32][2]
     SDPA_LDS float* mo = (SDPA_LDS float*)(smem + S::MLB);  // [MSLOTS][32][MROW]
     const int slot = wq * (NWK - 1) + (wk - 1);
     __syncthreads();
     if (wk > 0 && hl == 0) {
-      mml[(slot * 32 + col) * 2 + 0] = m_ref[0];
-      mml[(slot * 32 + col) * 2 + 1] = l_row[0];
+      mml[(slot * 32 + col) * 2 + 0] = m_ref;
+      mml[(slot * 32 + col) * 2 + 1] = l_row;
     }
     __syncthreads();
     float sc[NWK];  // weight of each slice's partial in the merged row
     if (wk == 0) {
-      float M = m_ref[0];
+      float M = m_ref;
 #pragma unroll
       for (int w = 1; w < NWK; ++w) M = fmaxf(M, mml[((wq * (NWK - 1) + w - 1) * 32 + col) * 2]);
       const float Mu = (M == kNegInf) ? 0.f : M;
-      sc[0] = __builtin_amdgcn_exp2f(m_ref[0] - Mu);
-      l_row[0] *= sc[0];
+      sc[0] = __builtin_amdgcn_exp2f(m_ref - Mu);
+      l_row *= sc[0];
 #pragma unroll
       for (int w = 1; w < NWK; ++w) {
         const int sl = (wq * (NWK - 1) + w - 1) * 32 + col;
         sc[w] = __builtin_amdgcn_exp2f(mml[sl * 2] - Mu);
-        l_row[0] += sc[w] * mml[sl * 2 + 1];
+        l_row += sc[w] * mml[sl * 2 + 1];
       }
 #pragma unroll
-      for (int t = 0; t < S::NDT; ++t) oacc[0][t] *= sc[0];
-      m_ref[0] = M;
+      for (int t = 0; t < S::NDT; ++t) oacc[t] *= sc[0];
+      m_ref = M;
     }
 #pragma unroll
     for (int t0 = 0; t0 < S::NDT; t0 += S::TPR) {
@@ -819,8 +781,8 @@ void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
           for (int i4 = 0; i4 < 4; ++i4) {
             const int d = t * 32 + 8 * i4 + 4 * hl;
-            *(SDPA_LDS f32x4*)(myo + d) = f32x4{oacc[0][t0 + t][4 * i4 + 0], oacc[0][t0 + t][4 * i4 + 1],
-                                                oacc[0][t0 + t][4 * i4 + 2], oacc[0][t0 + t][4 * i4 + 3]};
+            *(SDPA_LDS f32x4*)(myo + d) = f32x4{oacc[t0 + t][4 * i4 + 0], oacc[t0 + t][4 * i4 + 1],
+                                                oacc[t0 + t][4 * i4 + 2], oacc[t0 + t][4 * i4 + 3]};
           }
         }
       }
@@ -834,10 +796,10 @@ void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
             for (int i4 = 0; i4 < 4; ++i4) {
               const f32x4 v4 = *(const SDPA_LDS f32x4*)(po + t * 32 + 8 * i4 + 4 * hl);
-              oacc[0][t0 + t][4 * i4 + 0] += sc[w] * v4[0];
-              oacc[0][t0 + t][4 * i4 + 1] += sc[w] * v4[1];
-              oacc[0][t0 + t][4 * i4 + 2] += sc[w] * v4[2];
-              oacc[0][t0 + t][4 * i4 + 3] += sc[w] * v4[3];
+              oacc[t0 + t][4 * i4 + 0] += sc[w] * v4[0];
+              oacc[t0 + t][4 * i4 + 1] += sc[w] * v4[1];
+              oacc[t0 + t][4 * i4 + 2] += sc[w] * v4[2];
+              oacc[t0 + t][4 * i4 + 3] += sc[w] * v4[3];
             }
           }
         }
@@ -846,51 +808,46 @@ void attn_fwd_kernel(AttnArgs a) {
     if (wk > 0) return;
   }
 
+  if (!row_ok) return;
+  if (a.splits == 1) {
+    const float inv = 1.0f / l_row;
+    char* orow = (char*)a.o + ((int64_t)b * a.os[0] + (int64_t)hq * a.os[1] + (int64_t)iq * a.os[2]) * E::ES;
 #pragma unroll
-  for (int q = 0; q < QT; ++q) {
-    if (!row_ok[q]) continue;
-    if (a.splits == 1) {
-      const float inv = 1.0f / l_row[q];
-      char* orow =
-          (char*)a.o + ((int64_t)b * a.os[0] + (int64_t)hq[q] * a.os[1] + (int64_t)iq[q] * a.os[2]) * E::ES;
+    for (int t = 0; t < S::NDT; ++t) {
 #pragma unroll
-      for (int t = 0; t < S::NDT; ++t) {
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const int d = t * 32 + 8 * i4 + 4 * hl;
-          if (d < a.dv) {
-            const f32x16& o = oacc[q][t];
-            if constexpr (E::ES == 2) {
-              u32x2 w;
-              w[0] = E::pack2(o[4 * i4 + 0] * inv, o[4 * i4 + 1] * inv);
-              w[1] = E::pack2(o[4 * i4 + 2] * inv, o[4 * i4 + 3] * inv);
-              *(u32x2*)(orow + d * 2) = w;
-            } else {
-              *(float4*)(orow + d * 4) =
-                  make_float4(o[4 * i4 + 0] * inv, o[4 * i4 + 1] * inv, o[4 * i4 + 2] * inv, o[4 * i4 + 3] * inv);
-            }
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int d = t * 32 + 8 * i4 + 4 * hl;
+        if (d < a.dv) {
+          if constexpr (E::ES == 2) {
+            u32x2 w;
+            w[0] = E::pack2(oacc[t][4 * i4 + 0] * inv, oacc[t][4 * i4 + 1] * inv);
+            w[1] = E::pack2(oacc[t][4 * i4 + 2] * inv, oacc[t][4 * i4 + 3] * inv);
+            *(u32x2*)(orow + d * 2) = w;
+          } else {
+            *(float4*)(orow + d * 4) = make_float4(oacc[t][4 * i4 + 0] * inv, oacc[t][4 * i4 + 1] * inv,
+                                                   oacc[t][4 * i4 + 2] * inv, oacc[t][4 * i4 + 3] * inv);
           }
         }
       }
-      if (a.lse && hl == 0)
-        a.lse[((int64_t)b * a.Hq + hq[q]) * a.Lq + iq[q]] = (m_ref[q] + log2f(l_row[q])) * kLn2;
-    } else {
-      // split plan: this split's partial (O, m, l)
-      const int64_t ws_row = ((int64_t)z * a.R + r[q]) * a.splits + split;
-      float* wo = a.ws_o + ws_row * a.dv;
+    }
+    if (a.lse && hl == 0) a.lse[((int64_t)b * a.Hq + hq) * a.Lq + iq] = (m_ref + log2f(l_row)) * kLn2;
+    return;
+  }
+
+  // ---- split plan: this split's partial (O, m, l) ----
+  const int64_t ws_row = ((int64_t)z * a.R + r) * a.splits + split;
+  float* wo = a.ws_o + ws_row * a.dv;
 #pragma unroll
-      for (int t = 0; t < S::NDT; ++t) {
+  for (int t = 0; t < S::NDT; ++t) {
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const int d = t * 32 + 8 * i4 + 4 * hl;
-          if (d < a.dv)
-            *(float4*)(wo + d) = make_float4(oacc[q][t][4 * i4 + 0], oacc[q][t][4 * i4 + 1],
-                                             oacc[q][t][4 * i4 + 2], oacc[q][t][4 * i4 + 3]);
-        }
-      }
-      if (hl == 0) *(float2*)(a.ws_ml + ws_row * 2) = make_float2(m_ref[q], l_row[q]);
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int d = t * 32 + 8 * i4 + 4 * hl;
+      if (d < a.dv)
+        *(float4*)(wo + d) = make_float4(oacc[t][4 * i4 + 0], oacc[t][4 * i4 + 1], oacc[t][4 * i4 + 2],
+                                         oacc[t][4 * i4 + 3]);
     }
   }
+  if (hl == 0) *(float2*)(a.ws_ml + ws_row * 2) = make_float2(m_ref, l_row);
 }
 
 }  // namespace dev

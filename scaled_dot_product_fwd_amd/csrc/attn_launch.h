@@ -9,10 +9,10 @@
 
 namespace sdpa {
 
-template <class E, int DQK, int DV, int NWQ, int NWK, int BKW, int QT, int WPE>
+template <class E, int DQK, int DV, int NWQ, int NWK, int BKW, int WPE>
 int launch_one(const Plan& p, const AttnArgs& a, void* stream, std::string* err) {
-  using S = dev::Shape<E, DQK, DV, NWQ, NWK, BKW, QT>;
-  auto kern = dev::attn_fwd_kernel<E, DQK, DV, NWQ, NWK, BKW, QT, WPE>;
+  using S = dev::Shape<E, DQK, DV, NWQ, NWK, BKW>;
+  auto kern = dev::attn_fwd_kernel<E, DQK, DV, NWQ, NWK, BKW, WPE>;
   // Check the compiled kernel can run the workgroup size it is launched with,
   // once per instance: an oversized launch must fail loudly, never return
   // silently unwritten output (mlx PR #4185 "Add force_fused option to
@@ -50,11 +50,11 @@ int launch_one(const Plan& p, const AttnArgs& a, void* stream, std::string* err)
 #define SDPA_CASE(E, KIND, DQK, DV)                                                            \
   if (p.dqk_pad == DQK && p.dv_pad == DV) {                                                    \
     constexpr Family f_ = family_for(KIND, dev::E::ES, DQK, DV);                               \
-    if (p.fam.nwq != f_.nwq || p.fam.nwk != f_.nwk || p.fam.bkw != f_.bkw || p.fam.qt != f_.qt) { \
+    if (p.fam.nwq != f_.nwq || p.fam.nwk != f_.nwk || p.fam.bkw != f_.bkw) {                   \
       *err = "plan and kernel instance disagree on the wave arrangement";                      \
       return SDPA_E_PLAN;                                                                      \
     }                                                                                          \
-    return launch_one<dev::E, DQK, DV, f_.nwq, f_.nwk, f_.bkw, f_.qt,           \
+    return launch_one<dev::E, DQK, DV, f_.nwq, f_.nwk, f_.bkw,                  \
                       wpe_for(KIND, dev::E::ES, DQK, DV)>(p, a, stream, err);             \
   }
 

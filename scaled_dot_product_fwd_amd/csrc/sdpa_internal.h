@@ -47,10 +47,9 @@ struct CombineArgs {
 
 // Kernel family = how the waves of a workgroup divide the work.
 struct Family {
-  int nwq;     // waves stacked along query rows
-  int nwk;     // waves splitting each key block between them
-  int bkw;     // keys per wave per iteration (multiple of 32)
-  int qt = 1;  // groups of 32 query rows per wave
+  int nwq;   // waves stacked along query rows (32 rows each)
+  int nwk;   // waves splitting each key block between them
+  int bkw;   // keys per wave per iteration (multiple of 32)
 };
 
 enum : int { KIND_PREFILL = 0, KIND_SHORT = 1, KIND_DECODE = 2 };
