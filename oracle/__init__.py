@@ -17,6 +17,7 @@ is "parity unpinned".
 
 from .sdpa_ref import (  # noqa: F401
     MASK_KINDS,
+    mask_array,
     visible_mask,
     visible_pairs,
     sdpa_ref,

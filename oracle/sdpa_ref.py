@@ -22,6 +22,17 @@ What is computed
   and including its own, combined with causal masking, i.e. ``p - W < j <= p``
   (mlx PR #3552, Summary and the per-element rule "row_pos - col_pos >= W is
   masked" in Implementation).  ``window >= 1`` is required.
+* an optional explicit mask array broadcast over ``[B, Hq, Lq, Lk]`` (the
+  ``mask_arr`` argument beside the mask mode in mlx PR #3552, Public API; the
+  boolean and float mask specialisations listed in mlx PR #4185's validation
+  comment).  Boolean: True keeps the key, False removes it.  Float: the value
+  is added to the scaled score, ``scale * q.k + mask``, in natural-log units,
+  so ``-inf`` removes the key.  It combines with the mask mode: a key counts
+  only if the mode and the array both keep it.
+* a row that keeps no key at all (possible only through a mask array) has
+  output 0 and log-sum-exp ``-inf``: the limit of a row whose every score goes
+  to ``-inf``, and what the log-sum-exp merge of partial results gives for an
+  empty part.
 * the log-sum-exp of the visible scaled scores, natural log, per query row
   (the output that training needs; mlx PR #4185, API).
 
@@ -89,6 +100,51 @@ def visible_pairs(lq: int, lk: int, mask: str = "none", window: int = 0) -> int:
     return int(visible_mask(lq, lk, mask, window).sum())
 
 
+def mask_array(mask_arr, b: int, hq: int, lq: int, lk: int):
+    """The explicit mask broadcast to ``[b, hq, lq, lk]`` (numpy view), or None.
+
+    Boolean arrays stay boolean; anything else is upcast exactly to float64
+    and must hold no NaN and no ``+inf``.
+    """
+    if mask_arr is None:
+        return None
+    if hasattr(mask_arr, "detach"):
+        import torch
+
+        t = mask_arr.detach().to("cpu")
+        arr = t.numpy() if t.dtype == torch.bool else t.to(torch.float64).numpy()
+    else:
+        arr = np.asarray(mask_arr)
+    if arr.dtype != np.bool_:
+        arr = arr.astype(np.float64)
+        if np.isnan(arr).any() or np.isposinf(arr).any():
+            raise ValueError("an additive mask holds finite values or -inf")
+    if arr.ndim > 4:
+        raise ValueError("a mask array has at most 4 dims")
+    return np.broadcast_to(arr, (b, hq, lq, lk))
+
+
+def _apply(s: np.ndarray, vis: np.ndarray, arr) -> np.ndarray:
+    """Scores with removed keys at -inf: mode visibility, then the mask array."""
+    if arr is None:
+        return np.where(vis, s, -np.inf)
+    if arr.dtype == np.bool_:
+        return np.where(vis & arr, s, -np.inf)
+    return np.where(vis, s + arr, -np.inf)
+
+
+def _softmax_rows(s: np.ndarray):
+    """Softmax weights, denominators and maxima of score rows with -inf holes.
+
+    A row with no finite score gets weights 0, denominator 0 and max -inf.
+    """
+    m = s.max(axis=-1, keepdims=True)
+    empty = ~np.isfinite(m)
+    p = np.exp(s - np.where(empty, 0.0, m))  # exp(-inf) = 0 on removed keys
+    den = p.sum(axis=-1, keepdims=True)
+    return p, den, m, empty
+
+
 def _dims(q, k, v) -> Tuple[int, int, int, int, int, int, int]:
     if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
         raise ValueError("q, k, v must be [B, H, L, D]")
@@ -102,15 +158,19 @@ def _dims(q, k, v) -> Tuple[int, int, int, int, int, int, int]:
     return b, hq, hkv, lq, lk, dqk, dv
 
 
-def sdpa_ref(q, k, v, scale: float, mask: str = "none", window: int = 0, chunk: int = 512):
+def sdpa_ref(q, k, v, scale: float, mask: str = "none", window: int = 0, chunk: int = 512,
+             mask_arr=None):
     """Reference forward.  Returns ``(o, lse)`` in float64.
 
     ``o`` is ``[B, Hq, Lq, Dv]``, ``lse`` is ``[B, Hq, Lq]``.  ``scale`` is
     used as given (pass the same float32 value the GPU receives).
+    ``mask_arr`` is an optional boolean or additive array broadcastable to
+    ``[B, Hq, Lq, Lk]``.
     """
     q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
     b, hq, hkv, lq, lk, dqk, dv = _dims(q, k, v)
     vis = visible_mask(lq, lk, mask, window)
+    arr = mask_array(mask_arr, b, hq, lq, lk)
     group = hq // hkv
     scale = float(scale)
     o = np.zeros((b, hq, lq, dv), dtype=np.float64)
@@ -123,40 +183,42 @@ def sdpa_ref(q, k, v, scale: float, mask: str = "none", window: int = 0, chunk: 
             for r0 in range(0, lq, chunk):
                 r1 = min(lq, r0 + chunk)
                 s = scale * (q[bi, h, r0:r1] @ kt)  # [rows, Lk] scaled scores
-                s = np.where(vis[r0:r1], s, -np.inf)
-                m = s.max(axis=1, keepdims=True)  # every row has a visible key
-                p = np.exp(s - m)  # exp(-inf) = 0 on masked entries
-                den = p.sum(axis=1, keepdims=True)
-                o[bi, h, r0:r1] = (p @ vv) / den
-                lse[bi, h, r0:r1] = (m + np.log(den))[:, 0]
+                s = _apply(s, vis[r0:r1], None if arr is None else arr[bi, h, r0:r1])
+                p, den, m, empty = _softmax_rows(s)
+                with np.errstate(divide="ignore", invalid="ignore"):
+                    o[bi, h, r0:r1] = np.where(empty, 0.0, (p @ vv) / den)
+                    lse[bi, h, r0:r1] = np.where(empty, -np.inf, m + np.log(den))[:, 0]
     return o, lse
 
 
-def sdpa_probs(q, k, scale: float, mask: str = "none", window: int = 0) -> np.ndarray:
-    """Attention probabilities ``[B, Hq, Lq, Lk]`` (tiny shapes only)."""
+def sdpa_probs(q, k, scale: float, mask: str = "none", window: int = 0, mask_arr=None) -> np.ndarray:
+    """Attention probabilities ``[B, Hq, Lq, Lk]`` (tiny shapes only; an empty row is all 0)."""
     q, k = _as_f64(q), _as_f64(k)
     b, hq, lq, _ = q.shape
     hkv, lk = k.shape[1], k.shape[2]
     vis = visible_mask(lq, lk, mask, window)
+    arr = mask_array(mask_arr, b, hq, lq, lk)
     group = hq // hkv
     out = np.zeros((b, hq, lq, lk), dtype=np.float64)
     for bi in range(b):
         for h in range(hq):
             s = float(scale) * (q[bi, h] @ k[bi, h // group].T)
-            s = np.where(vis, s, -np.inf)
-            p = np.exp(s - s.max(axis=1, keepdims=True))
-            out[bi, h] = p / p.sum(axis=1, keepdims=True)
+            s = _apply(s, vis, None if arr is None else arr[bi, h])
+            p, den, _, empty = _softmax_rows(s)
+            with np.errstate(divide="ignore", invalid="ignore"):
+                out[bi, h] = np.where(empty, 0.0, p / den)
     return out
 
 
 def sdpa_ref_rows(q, k, v, scale: float, mask: str, window: int,
-                  picks: Iterable[Sequence[int]]):
+                  picks: Iterable[Sequence[int]], mask_arr=None):
     """Reference output for selected rows only, for full-size sampled checks.
 
     ``picks`` holds ``(b, h, i)`` triples.  Returns ``(o_rows [n, Dv],
     lse_rows [n])`` in float64, with the same definition as ``sdpa_ref``.
     ``q``, ``k`` and ``v`` may be torch CPU tensors; only the rows touched are
-    upcast.
+    upcast.  ``mask_arr`` (optional) broadcasts to ``[B, Hq, Lq, Lk]`` as in
+    ``sdpa_ref``; only the picked rows of it are read.
     """
     picks = [tuple(int(t) for t in p) for p in picks]
     b, hq, lq, _ = q.shape
@@ -164,6 +226,7 @@ def sdpa_ref_rows(q, k, v, scale: float, mask: str, window: int,
     dv = v.shape[3]
     _check_mask(lq, lk, mask, window)
     group = hq // hkv
+    arr = _mask_rows_view(mask_arr, b, hq, lq, lk)
     o = np.zeros((len(picks), dv), dtype=np.float64)
     lse = np.zeros(len(picks), dtype=np.float64)
     cache = {}
@@ -173,24 +236,47 @@ def sdpa_ref_rows(q, k, v, scale: float, mask: str, window: int,
             cache = {(bi, kvh): (_as_f64(k[bi, kvh]), _as_f64(v[bi, kvh]))}
         kk, vv = cache[(bi, kvh)]
         vis = _visible_row(i, lq, lk, mask, window)
-        s = float(scale) * (kk[vis] @ _as_f64(q[bi, h, i]))
+        s = float(scale) * (kk @ _as_f64(q[bi, h, i]))
+        s = _apply(s, vis, None if arr is None else arr(bi, h, i))
+        keep = np.isfinite(s)
+        if not keep.any():
+            o[n], lse[n] = 0.0, -math.inf
+            continue
+        s = s[keep]
         m = s.max()
         p = np.exp(s - m)
         den = p.sum()
-        o[n] = (p @ vv[vis]) / den
+        o[n] = (p @ vv[keep]) / den
         lse[n] = m + math.log(den)
     return o, lse
 
 
-def sdpa_loop(q, k, v, scale: float, mask: str = "none", window: int = 0):
+def _mask_rows_view(mask_arr, b, hq, lq, lk):
+    """Row accessor ``(b, h, i) -> mask row [lk]`` that upcasts one row at a time."""
+    if mask_arr is None:
+        return None
+    if hasattr(mask_arr, "detach"):
+        t = mask_arr.detach()
+        while t.dim() < 4:
+            t = t.unsqueeze(0)
+        t = t.expand(b, hq, lq, lk)
+        return lambda bi, h, i: mask_array(t[bi, h, i], 1, 1, 1, lk)[0, 0, 0]
+    arr = mask_array(mask_arr, b, hq, lq, lk)
+    return lambda bi, h, i: arr[bi, h, i]
+
+
+def sdpa_loop(q, k, v, scale: float, mask: str = "none", window: int = 0, mask_arr=None):
     """Second formulation in pure Python loops (tiny shapes only).
 
     Walks each query row over the explicit key index range it may see and
-    forms the softmax from ``exp(s - max)`` sums with ``math.fsum``.
+    forms the softmax from ``exp(s - max)`` sums with ``math.fsum``.  A mask
+    array entry is looked up per key: a boolean False or an additive -inf drops
+    the key, another additive value is added to its score.
     """
     q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
     b, hq, hkv, lq, lk, dqk, dv = _dims(q, k, v)
     _check_mask(lq, lk, mask, window)
+    arr = mask_array(mask_arr, b, hq, lq, lk)
     group = hq // hkv
     o = np.zeros((b, hq, lq, dv))
     lse = np.zeros((b, hq, lq))
@@ -205,9 +291,24 @@ def sdpa_loop(q, k, v, scale: float, mask: str = "none", window: int = 0):
                     lo, hi = 0, pos
                 else:
                     lo, hi = max(0, pos - window + 1), pos
-                keys = list(range(lo, hi + 1))
-                s = [float(scale) * math.fsum(q[bi, h, i, d] * k[bi, kvh, j, d] for d in range(dqk))
-                     for j in keys]
+                keys, s = [], []
+                for j in range(lo, hi + 1):
+                    sj = float(scale) * math.fsum(q[bi, h, i, d] * k[bi, kvh, j, d] for d in range(dqk))
+                    if arr is not None:
+                        a = arr[bi, h, i, j]
+                        if arr.dtype == np.bool_:
+                            if not a:
+                                continue
+                        elif a == -math.inf:
+                            continue
+                        else:
+                            sj += float(a)
+                    keys.append(j)
+                    s.append(sj)
+                if not keys:
+                    o[bi, h, i, :] = 0.0
+                    lse[bi, h, i] = -math.inf
+                    continue
                 mx = max(s)
                 w = [math.exp(x - mx) for x in s]
                 den = math.fsum(w)

@@ -288,3 +288,198 @@ def test_oracle_reads_torch_low_precision_exactly():
     q = t.reshape(1, 1, 1, 3)
     o, lse = sdpa_ref(q, q, q, 1.0, "none")
     np.testing.assert_array_equal(o[0, 0, 0], np.array([1.0 + 2 ** -7, 3.140625, -0.0078125]))
+
+
+# ---------------------------------------------------------------------------
+# Explicit mask arrays (boolean: True keeps a key; float: added to the scaled
+# score).  Pinned against the loop formulation, torch's CPU float64 attention
+# with the same array (a library special case), closed forms and invariants.
+# ---------------------------------------------------------------------------
+
+MASKED = [
+    # b, hq, hkv, lq, lk, dqk, dv, mode, window, mask shape (broadcast dims as 1)
+    (1, 2, 1, 3, 5, 4, 4, "none", 0, (3, 5)),
+    (2, 4, 2, 4, 6, 3, 5, "none", 0, (2, 4, 4, 6)),
+    (2, 4, 2, 4, 6, 3, 5, "none", 0, (2, 1, 1, 6)),
+    (1, 4, 1, 5, 7, 5, 3, "causal", 0, (1, 4, 5, 7)),
+    (2, 2, 2, 3, 8, 4, 2, "window", 3, (3, 8)),
+]
+
+
+def _bool_mask(shape, seed, keep=0.6):
+    return np.random.default_rng(seed).random(shape) < keep
+
+
+def _add_mask(shape, seed):
+    a = np.random.default_rng(seed).standard_normal(shape) * 2.0
+    a[np.random.default_rng(seed + 1).random(shape) < 0.25] = -np.inf
+    return a
+
+
+def _torch_sdpa(q, k, v, scale, attn_mask):
+    g = q.shape[1] // k.shape[1]
+    tk = torch.from_numpy(k).repeat_interleave(g, dim=1)
+    tv = torch.from_numpy(v).repeat_interleave(g, dim=1)
+    return torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), tk, tv, attn_mask=torch.from_numpy(np.ascontiguousarray(attn_mask)),
+        scale=scale).numpy()
+
+
+@pytest.mark.parametrize("case", MASKED)
+@pytest.mark.parametrize("kind", ["bool", "add"])
+def test_mask_array_matches_loop_brute_force(case, kind):
+    b, hq, hkv, lq, lk, dqk, dv, mode, w, shape = case
+    q, k, v = _case(b, hq, hkv, lq, lk, dqk, dv, seed=200 + lq + lk)
+    arr = _bool_mask(shape, 7) if kind == "bool" else _add_mask(shape, 7)
+    o, lse = sdpa_ref(q, k, v, 0.6, mode, w, mask_arr=arr)
+    o2, lse2 = sdpa_loop(q, k, v, 0.6, mode, w, mask_arr=arr)
+    np.testing.assert_allclose(o, o2, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, lse2, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("case", MASKED)
+@pytest.mark.parametrize("kind", ["bool", "add"])
+def test_mask_array_matches_torch_cpu_sdpa(case, kind):
+    """torch's float64 CPU attention takes the same array: boolean True keeps a
+    key, a float array is added to the scaled scores.  The mode's own rule is
+    written out here with index loops and folded into the array."""
+    b, hq, hkv, lq, lk, dqk, dv, mode, w, shape = case
+    q, k, v = _case(b, hq, hkv, lq, lk, dqk, dv, seed=300 + lq + lk)
+    rule = np.ones((lq, lk), dtype=bool)
+    for i in range(lq):
+        for j in range(lk):
+            p = i + lk - lq
+            if mode != "none" and j > p:
+                rule[i, j] = False
+            if mode == "window" and j <= p - w:
+                rule[i, j] = False
+    if kind == "bool":
+        arr = _bool_mask(shape, 9, keep=0.7)
+        full = np.broadcast_to(arr, (b, hq, lq, lk)) & rule
+        full = full | ~full.any(axis=-1, keepdims=True) & rule  # no empty row (torch gives NaN there)
+        arr = full
+        tmask = full
+    else:
+        arr = np.random.default_rng(9).standard_normal(shape) * 3.0
+        tmask = np.where(rule, np.broadcast_to(arr, (b, hq, lq, lk)), -np.inf)
+    o, lse = sdpa_ref(q, k, v, 0.45, mode, w, mask_arr=arr)
+    np.testing.assert_allclose(o, _torch_sdpa(q, k, v, 0.45, tmask), rtol=0, atol=1e-12)
+
+
+def test_additive_row_constant_shifts_lse_only():
+    """softmax is invariant to a per-row constant: O unchanged, lse moves by it."""
+    q, k, v = _case(1, 2, 1, 4, 6, 4, 3, seed=401)
+    base = _add_mask((2, 4, 6), 11)
+    shift = np.array([0.5, -3.0, 7.25, 0.0])[None, :, None]
+    o1, l1 = sdpa_ref(q, k, v, 0.8, "none", mask_arr=base)
+    o2, l2 = sdpa_ref(q, k, v, 0.8, "none", mask_arr=base + shift)
+    np.testing.assert_allclose(o2, o1, atol=1e-13)
+    np.testing.assert_allclose(l2 - l1, np.broadcast_to(shift[..., 0], l1.shape), atol=1e-13)
+
+
+def test_additive_log_weights_closed_form():
+    """Adding ln w_j to the scores weights key j by w_j: o = sum w e^s v / sum w e^s."""
+    q, k, v = _case(1, 1, 1, 2, 3, 4, 2, seed=411)
+    wts = np.array([0.25, 2.0, 5.0])
+    o, lse = sdpa_ref(q, k, v, 0.7, "none", mask_arr=np.log(wts))
+    for i in range(2):
+        e = [wts[j] * math.exp(0.7 * float(q[0, 0, i] @ k[0, 0, j])) for j in range(3)]
+        exp = sum(e[j] * v[0, 0, j] for j in range(3)) / sum(e)
+        np.testing.assert_allclose(o[0, 0, i], exp, atol=1e-14)
+        assert abs(lse[0, 0, i] - math.log(sum(e))) < 1e-13
+
+
+def test_boolean_and_additive_minus_inf_agree():
+    q, k, v = _case(2, 2, 1, 5, 7, 3, 3, seed=421)
+    keep = _bool_mask((5, 7), 13)
+    keep[:, 0] = True
+    o1, l1 = sdpa_ref(q, k, v, 0.5, "causal", mask_arr=keep)
+    o2, l2 = sdpa_ref(q, k, v, 0.5, "causal", mask_arr=np.where(keep, 0.0, -np.inf))
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+
+
+def test_all_true_and_zero_masks_equal_no_mask():
+    q, k, v = _case(1, 4, 2, 3, 6, 4, 4, seed=431)
+    o, lse = sdpa_ref(q, k, v, 0.5, "window", 2)
+    for arr in (np.ones((3, 6), dtype=bool), np.zeros((1, 1, 3, 6))):
+        o2, l2 = sdpa_ref(q, k, v, 0.5, "window", 2, mask_arr=arr)
+        np.testing.assert_array_equal(o, o2)
+        np.testing.assert_array_equal(lse, l2)
+
+
+def test_boolean_mask_of_the_mode_rule_equals_the_mode():
+    """An explicit [Lq, Lk] window array (how callers express a window without
+    the window mode) gives the window mode's result."""
+    q, k, v = _case(1, 2, 1, 6, 9, 4, 4, seed=441)
+    o, lse = sdpa_ref(q, k, v, 0.5, "window", 3)
+    o2, l2 = sdpa_ref(q, k, v, 0.5, "none", mask_arr=visible_mask(6, 9, "window", 3))
+    np.testing.assert_allclose(o, o2, atol=1e-15)
+    np.testing.assert_allclose(lse, l2, atol=1e-15)
+
+
+def test_single_kept_key_closed_form():
+    q, k, v = _case(1, 1, 1, 3, 5, 4, 3, seed=451)
+    arr = np.zeros((3, 5), dtype=bool)
+    arr[0, 4] = arr[1, 0] = arr[2, 2] = True
+    o, lse = sdpa_ref(q, k, v, 0.9, "none", mask_arr=arr)
+    for i, j in enumerate([4, 0, 2]):
+        np.testing.assert_array_equal(o[0, 0, i], v[0, 0, j])
+        assert abs(lse[0, 0, i] - 0.9 * float(q[0, 0, i] @ k[0, 0, j])) < 1e-14
+
+
+@pytest.mark.parametrize("kind", ["bool", "add"])
+def test_empty_rows_give_zero_output_and_minus_inf_lse(kind):
+    q, k, v = _case(1, 2, 1, 4, 5, 3, 3, seed=461)
+    keep = np.ones((2, 4, 5), dtype=bool)
+    keep[0, 1] = False
+    keep[1, 3] = False
+    arr = keep if kind == "bool" else np.where(keep, 0.5, -np.inf)
+    o, lse = sdpa_ref(q, k, v, 0.5, "none", mask_arr=arr)
+    for h, i in [(0, 1), (1, 3)]:
+        np.testing.assert_array_equal(o[0, h, i], 0.0)
+        assert lse[0, h, i] == -math.inf
+    o2, l2 = sdpa_loop(q, k, v, 0.5, "none", mask_arr=arr)
+    np.testing.assert_array_equal(o2[0, 0, 1], 0.0)
+    assert l2[0, 1, 3] == -math.inf
+    p = sdpa_probs(q, k, 0.5, "none", mask_arr=arr)
+    np.testing.assert_array_equal(p[0, 0, 1], 0.0)
+    np.testing.assert_allclose(p[0, 0, 0].sum(), 1.0, atol=1e-15)
+    orow, lrow = sdpa_ref_rows(q, k, v, 0.5, "none", 0, [(0, 0, 1), (0, 1, 2)], mask_arr=arr)
+    np.testing.assert_array_equal(orow[0], 0.0)
+    assert lrow[0] == -math.inf
+    np.testing.assert_allclose(orow[1], o[0, 1, 2], atol=1e-14)
+
+
+def test_per_head_masks_follow_query_heads_not_kv_heads():
+    """With GQA a [B, Hq, ...] mask is indexed by the query head: each head's
+    result equals a one-head run with that head's slice."""
+    q, k, v = _case(1, 4, 2, 3, 6, 4, 4, seed=471)
+    arr = _add_mask((1, 4, 3, 6), 17)
+    arr[..., 0] = 0.0
+    o, lse = sdpa_ref(q, k, v, 0.5, "none", mask_arr=arr)
+    for h in range(4):
+        o1, l1 = sdpa_ref(q[:, h:h + 1], k[:, h // 2:h // 2 + 1], v[:, h // 2:h // 2 + 1], 0.5, "none",
+                          mask_arr=arr[:, h:h + 1])
+        np.testing.assert_array_equal(o[:, h:h + 1], o1)
+        np.testing.assert_array_equal(lse[:, h:h + 1], l1)
+
+
+def test_mask_rows_accessor_reads_torch_broadcast_views():
+    q, k, v = _case(2, 2, 1, 3, 5, 4, 4, seed=481)
+    arr = torch.from_numpy(_add_mask((2, 1, 1, 5), 19)).to(torch.bfloat16)
+    o, lse = sdpa_ref(q, k, v, 0.5, "none", mask_arr=arr)
+    picks = list(itertools.product(range(2), range(2), range(3)))
+    orow, lrow = sdpa_ref_rows(q, k, v, 0.5, "none", 0, picks, mask_arr=arr)
+    for n, (bi, h, i) in enumerate(picks):
+        np.testing.assert_allclose(orow[n], o[bi, h, i], atol=1e-13)
+        assert abs(lrow[n] - lse[bi, h, i]) < 1e-13
+
+
+def test_bad_additive_values_raise():
+    q, k, v = _case(1, 1, 1, 2, 3, 2, 2, seed=491)
+    for bad in (np.inf, np.nan):
+        arr = np.zeros((2, 3))
+        arr[1, 1] = bad
+        with pytest.raises(ValueError):
+            sdpa_ref(q, k, v, 0.5, "none", mask_arr=arr)
