@@ -16,12 +16,25 @@
  *                     aligned to the last Lq keys) and sees keys j <= p;
  *   SDPA_MASK_WINDOW  causal and additionally p - window < j, i.e. the last
  *                     `window` key positions up to and including p.
- * The optional log-sum-exp output is lse[b,h,i] = ln sum_j exp(scale*q.k_j)
- * over the visible keys (natural log, float32).
+ * An explicit mask array (mlx PR #3552, Public API: the `mask_arr` argument
+ * beside the mask mode; its boolean and float kinds are the "bool mask" and
+ * "float mask" specialisations of mlx PR #4185's validation comment) may be
+ * given on top of the mask mode, through sdpa_forward_masked():
+ *   SDPA_MASK_ARRAY_BOOL  one byte per element, nonzero keeps the key;
+ *   SDPA_MASK_ARRAY_ADD   the q/k/v element type, added to the scaled score
+ *                         (natural-log units; -inf removes the key; +inf and
+ *                         NaN are not allowed).
+ * A key counts only if the mask mode keeps it and the array does too.  A row
+ * that keeps no key (possible only through an array) gets o = 0 and
+ * lse = -inf.
+ * The optional log-sum-exp output is lse[b,h,i] = ln sum_j exp(s_ij) over the
+ * kept keys, s_ij = scale*q_i.k_j (+ the additive mask), natural log, float32.
  *
  * Tensors (element strides; the head-dim stride is always 1):
  *   q [B, Hq,  Lq, Dqk]   k [B, Hkv, Lk, Dqk]   v [B, Hkv, Lk, Dv]
  *   o [B, Hq,  Lq, Dv]    lse [B, Hq, Lq] contiguous float32 (optional)
+ *   mask [B, Hq, Lq, Lk]  element strides mask_stride[] for (batch, query
+ *                         head, query); 0 broadcasts a dim; key stride 1
  * q, k, v and o share one element type (float32, float16 or bfloat16).
  * Accumulation is float32; o is rounded once, to nearest even.
  *
@@ -59,12 +72,18 @@ typedef enum {
 } sdpa_mask_t;
 
 typedef enum {
+  SDPA_MASK_ARRAY_NONE = 0,
+  SDPA_MASK_ARRAY_BOOL = 1,  /* uint8/bool elements, nonzero = keep */
+  SDPA_MASK_ARRAY_ADD = 2    /* q's element type, added to the scaled score */
+} sdpa_mask_array_t;
+
+typedef enum {
   SDPA_OK = 0,
   SDPA_E_NULL = -1,      /* a required pointer is NULL */
   SDPA_E_SHAPE = -2,     /* a size < 1, Hq not a multiple of Hkv, size overflow */
   SDPA_E_HEAD_DIM = -3,  /* head dim outside the instantiated set (e.g. 512) */
   SDPA_E_DTYPE = -4,     /* unknown element type */
-  SDPA_E_MASK = -5,      /* unknown mask, causal/window with Lq > Lk, bad window */
+  SDPA_E_MASK = -5,      /* unknown mask or mask array kind, causal/window with Lq > Lk, bad window */
   SDPA_E_STRIDE = -6,    /* stride or pointer alignment (16-byte rows) violated */
   SDPA_E_WORKSPACE = -7, /* workspace missing or smaller than required */
   SDPA_E_SCALE = -8,     /* scale is not finite */
@@ -90,6 +109,14 @@ typedef struct {
    * or 128). */
   int32_t num_splits;
   int32_t row_tile;
+  /* Explicit mask array (sdpa_forward_masked only).  mask_array is a
+   * sdpa_mask_array_t; mask_stride[] are element strides of its (batch, query
+   * head, query) dims, each >= 0 and a multiple of 16 bytes (0 broadcasts
+   * that dim).  The array is read in 16-byte pieces, so every row's storage
+   * must extend to Lk rounded up to a multiple of 16 bytes (pad the key
+   * dimension: the padding is never used). */
+  int32_t mask_array;
+  int64_t mask_stride[3];
 } sdpa_desc_t;
 
 /* Fills *desc with contiguous [B,H,L,D] strides for the given sizes, no mask,
@@ -110,6 +137,15 @@ int sdpa_workspace_bytes(const sdpa_desc_t* desc, size_t* bytes);
 int sdpa_forward(const sdpa_desc_t* desc, const void* q, const void* k, const void* v,
                  void* o, float* lse, void* workspace, size_t workspace_bytes,
                  sdpa_stream_t stream);
+
+/* Forward pass with an explicit mask array (see above): as sdpa_forward,
+ * plus `mask`, a 16-byte aligned device pointer to the array of kind
+ * desc->mask_array, laid out by desc->mask_stride.  mask must be NULL exactly
+ * when desc->mask_array is SDPA_MASK_ARRAY_NONE (then this is sdpa_forward).
+ * sdpa_forward itself rejects a desc that names a mask array. */
+int sdpa_forward_masked(const sdpa_desc_t* desc, const void* q, const void* k, const void* v,
+                        const void* mask, void* o, float* lse, void* workspace,
+                        size_t workspace_bytes, sdpa_stream_t stream);
 
 /* Writes a one-line, NUL-terminated description of the plan (kernel family,
  * tile, splits, grid, workspace) into buf.  Host only. */

@@ -16,14 +16,16 @@ from __future__ import annotations
 import math
 from typing import Optional, Tuple, Union
 
-from ._lib import (SDPA_BF16, SDPA_F16, SDPA_F32, SDPA_MASK_CAUSAL, SDPA_MASK_NONE,  # noqa: F401
+from ._lib import (SDPA_BF16, SDPA_F16, SDPA_F32, SDPA_MASK_ARRAY_ADD,  # noqa: F401
+                   SDPA_MASK_ARRAY_BOOL, SDPA_MASK_ARRAY_NONE, SDPA_MASK_CAUSAL, SDPA_MASK_NONE,
                    SDPA_MASK_WINDOW, SdpaError, SdpaRuntimeError, SdpaValueError, load,
                    sdpa_desc_init, sdpa_desc_t, sdpa_describe_plan, sdpa_forward,
-                   sdpa_last_error, sdpa_set_profile_events, sdpa_workspace_bytes)
+                   sdpa_forward_masked, sdpa_last_error, sdpa_set_profile_events,
+                   sdpa_workspace_bytes)
 
-__all__ = ["forward", "make_desc", "plan_for", "workspace_for", "sdpa_forward",
-           "sdpa_workspace_bytes", "sdpa_describe_plan", "sdpa_last_error", "sdpa_desc_init",
-           "sdpa_set_profile_events",
+__all__ = ["forward", "make_desc", "plan_for", "workspace_for", "pad_mask", "sdpa_forward",
+           "sdpa_forward_masked", "sdpa_workspace_bytes", "sdpa_describe_plan", "sdpa_last_error",
+           "sdpa_desc_init", "sdpa_set_profile_events",
            "SdpaError", "SdpaValueError", "SdpaRuntimeError"]
 
 _MASKS = {"none": SDPA_MASK_NONE, "causal": SDPA_MASK_CAUSAL, "window": SDPA_MASK_WINDOW}
@@ -40,7 +42,8 @@ def _dtype_code(dtype) -> int:
 
 def make_desc(q_shape, k_shape, v_shape, dtype: int, *, scale: Optional[float] = None,
               mask: str = "none", window_size: int = 0, q_stride=None, k_stride=None,
-              v_stride=None, o_stride=None, num_splits: int = 0, row_tile: int = 0) -> sdpa_desc_t:
+              v_stride=None, o_stride=None, num_splits: int = 0, row_tile: int = 0,
+              mask_array: int = SDPA_MASK_ARRAY_NONE, mask_stride=(0, 0, 0)) -> sdpa_desc_t:
     """Build a descriptor from shapes ``[B,H,L,D]`` (contiguous unless strides are given)."""
     if mask not in _MASKS:
         raise SdpaValueError(f"SDPA_E_MASK: mask must be one of {sorted(_MASKS)} (got {mask!r})")
@@ -66,7 +69,75 @@ def make_desc(q_shape, k_shape, v_shape, dtype: int, *, scale: Optional[float] =
     d.scale = float(1.0 / math.sqrt(dqk)) if scale is None else float(scale)
     d.num_splits = int(num_splits)
     d.row_tile = int(row_tile)
+    d.mask_array = int(mask_array)
+    for j, st in enumerate(mask_stride):
+        d.mask_stride[j] = int(st)
     return d
+
+
+def pad_mask(mask, dtype=None):
+    """Copy a mask array into storage whose rows are padded to 16 bytes.
+
+    Returns a view with the mask's shape (as ``bool`` or ``dtype``) whose key
+    rows live in a buffer rounded up to a multiple of 16 bytes, which is the
+    layout ``forward(attn_mask=...)`` reads.  Broadcast (size-1) dims stay
+    size 1.  This is a preparation step for callers, run once per mask, not
+    part of the attention call.
+    """
+    import torch
+
+    dt = torch.bool if mask.dtype == torch.bool else (dtype or mask.dtype)
+    esize = torch.empty((), dtype=dt).element_size()
+    lk = mask.shape[-1]
+    per = 16 // esize
+    lkp = (lk + per - 1) // per * per
+    buf = torch.zeros(tuple(mask.shape[:-1]) + (lkp,), dtype=dt, device=mask.device)
+    view = buf[..., :lk]
+    view.copy_(mask)
+    return view
+
+
+def _mask_layout(attn_mask, q, b, hq, lq, lk):
+    """(kind, element strides of (batch, head, query)) of a mask tensor, validated."""
+    import torch
+
+    if not isinstance(attn_mask, torch.Tensor):
+        raise SdpaValueError("SDPA_E_MASK: attn_mask must be a tensor")
+    if attn_mask.device != q.device:
+        raise SdpaValueError("SDPA_E_DEVICE: attn_mask must be on the device of q")
+    if attn_mask.dtype == torch.bool or attn_mask.dtype == torch.uint8:
+        kind = SDPA_MASK_ARRAY_BOOL
+    elif attn_mask.dtype == q.dtype:
+        kind = SDPA_MASK_ARRAY_ADD
+    else:
+        raise SdpaValueError("SDPA_E_DTYPE: attn_mask must be bool (True keeps a key) or q's dtype "
+                             "(added to the scaled scores)")
+    m = attn_mask
+    if m.dim() > 4:
+        raise SdpaValueError("SDPA_E_SHAPE: attn_mask has at most 4 dims")
+    while m.dim() < 4:
+        m = m.unsqueeze(0)
+    want = (b, hq, lq, lk)
+    for j in range(4):
+        if m.shape[j] not in (1, want[j]):
+            raise SdpaValueError(f"SDPA_E_SHAPE: attn_mask of shape {tuple(attn_mask.shape)} does not "
+                                 f"broadcast to [B, Hq, Lq, Lk] = {list(want)}")
+    if m.shape[3] != lk:
+        raise SdpaValueError("SDPA_E_SHAPE: attn_mask must span all Lk keys in its last dim")
+    if lk > 1 and m.stride(3) != 1:
+        raise SdpaValueError("SDPA_E_STRIDE: attn_mask must have unit stride in the key dim")
+    strides = [m.stride(j) if m.shape[j] > 1 else 0 for j in range(3)]
+    esize = m.element_size()
+    pad = 16 // esize
+    if m.data_ptr() % 16 or any((st * esize) % 16 for st in strides):
+        raise SdpaValueError("SDPA_E_STRIDE: attn_mask rows must start on 16-byte boundaries; "
+                             "prepare it with pad_mask()")
+    # every row is read up to Lk rounded up to 16 bytes
+    last = sum(st * (m.shape[j] - 1) for j, st in enumerate(strides)) + (lk + pad - 1) // pad * pad
+    if (m.storage_offset() + last) * esize > m.untyped_storage().nbytes():
+        raise SdpaValueError("SDPA_E_STRIDE: attn_mask rows must be readable up to Lk rounded up to "
+                             "16 bytes; prepare it with pad_mask()")
+    return kind, strides
 
 
 def plan_for(desc: sdpa_desc_t) -> str:
@@ -78,7 +149,7 @@ def workspace_for(desc: sdpa_desc_t) -> int:
 
 
 def forward(q, k, v, *, scale: Optional[float] = None, mask: str = "none", window_size: int = 0,
-            return_lse: bool = False, num_splits: int = 0, row_tile: int = 0,
+            attn_mask=None, return_lse: bool = False, num_splits: int = 0, row_tile: int = 0,
             out=None, lse_out=None, workspace=None, stream=None
             ) -> Union["torch.Tensor", Tuple["torch.Tensor", "torch.Tensor"]]:  # noqa: F821
     """Fused attention forward on the current HIP device.
@@ -87,8 +158,12 @@ def forward(q, k, v, *, scale: Optional[float] = None, mask: str = "none", windo
     dtype (float32/float16/bfloat16), unit stride in the head dim.  ``scale``
     defaults to ``1/sqrt(Dqk)``.  ``mask`` is ``"none"``, ``"causal"`` (query
     rows aligned to the last Lq keys) or ``"window"`` (causal plus the last
-    ``window_size`` keys).  Returns ``o`` (and the float32 log-sum-exp
-    ``[B,Hq,Lq]`` when ``return_lse``).  Validation errors raise
+    ``window_size`` keys).  ``attn_mask`` (optional) broadcasts to
+    ``[B,Hq,Lq,Lk]``: ``bool`` keeps the keys where True, q's dtype is added
+    to the scaled scores; it applies on top of ``mask``.  Its rows must start
+    on 16-byte boundaries and be readable up to Lk rounded up to 16 bytes
+    (``pad_mask`` prepares such a copy).  Returns ``o`` (and the float32
+    log-sum-exp ``[B,Hq,Lq]`` when ``return_lse``).  Validation errors raise
     ``SdpaValueError`` (a ``ValueError``) naming the constraint.
     """
     import torch
@@ -111,9 +186,13 @@ def forward(q, k, v, *, scale: Optional[float] = None, mask: str = "none", windo
         out = torch.empty((b, hq, lq, dv), dtype=q.dtype, device=q.device)
     elif out.shape != (b, hq, lq, dv) or out.dtype != q.dtype or out.stride(3) != 1:
         raise SdpaValueError("SDPA_E_SHAPE: out must be [B, Hq, Lq, Dv] in the input dtype")
+    kind, mstr = SDPA_MASK_ARRAY_NONE, (0, 0, 0)
+    if attn_mask is not None:
+        kind, mstr = _mask_layout(attn_mask, q, b, hq, lq, k.shape[2])
     desc = make_desc(q.shape, k.shape, v.shape, dt, scale=scale, mask=mask, window_size=window_size,
                      q_stride=q.stride()[:3], k_stride=k.stride()[:3], v_stride=v.stride()[:3],
-                     o_stride=out.stride()[:3], num_splits=num_splits, row_tile=row_tile)
+                     o_stride=out.stride()[:3], num_splits=num_splits, row_tile=row_tile,
+                     mask_array=kind, mask_stride=mstr)
     lse = None
     if return_lse:
         lse = lse_out if lse_out is not None else torch.empty((b, hq, lq), dtype=torch.float32,
@@ -133,6 +212,7 @@ def forward(q, k, v, *, scale: Optional[float] = None, mask: str = "none", windo
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     with torch.cuda.device(q.device):
-        sdpa_forward(desc, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                     lse.data_ptr() if lse is not None else 0, ws_ptr, ws_len, stream)
+        sdpa_forward_masked(desc, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                            attn_mask.data_ptr() if attn_mask is not None else 0, out.data_ptr(),
+                            lse.data_ptr() if lse is not None else 0, ws_ptr, ws_len, stream)
     return (out, lse) if return_lse else out

@@ -14,6 +14,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsdpa_fwd
 
 SDPA_F32, SDPA_F16, SDPA_BF16 = 0, 1, 2
 SDPA_MASK_NONE, SDPA_MASK_CAUSAL, SDPA_MASK_WINDOW = 0, 1, 2
+SDPA_MASK_ARRAY_NONE, SDPA_MASK_ARRAY_BOOL, SDPA_MASK_ARRAY_ADD = 0, 1, 2
 
 STATUS = {
     0: "SDPA_OK",
@@ -31,8 +32,8 @@ STATUS = {
 }
 STATUS_CODE = {v: k for k, v in STATUS.items()}
 
-EXPORTED = ("sdpa_desc_init", "sdpa_workspace_bytes", "sdpa_forward", "sdpa_describe_plan",
-            "sdpa_set_profile_events", "sdpa_last_error")
+EXPORTED = ("sdpa_desc_init", "sdpa_workspace_bytes", "sdpa_forward", "sdpa_forward_masked",
+            "sdpa_describe_plan", "sdpa_set_profile_events", "sdpa_last_error")
 
 
 class sdpa_desc_t(ctypes.Structure):
@@ -54,6 +55,8 @@ class sdpa_desc_t(ctypes.Structure):
         ("scale", ctypes.c_float),
         ("num_splits", ctypes.c_int32),
         ("row_tile", ctypes.c_int32),
+        ("mask_array", ctypes.c_int32),
+        ("mask_stride", ctypes.c_int64 * 3),
     ]
 
 
@@ -97,6 +100,10 @@ def load() -> ctypes.CDLL:
                                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                  ctypes.c_void_p]
     lib.sdpa_forward.restype = ctypes.c_int
+    lib.sdpa_forward_masked.argtypes = [P(sdpa_desc_t), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_size_t, ctypes.c_void_p]
+    lib.sdpa_forward_masked.restype = ctypes.c_int
     lib.sdpa_describe_plan.argtypes = [P(sdpa_desc_t), ctypes.c_char_p, ctypes.c_size_t]
     lib.sdpa_describe_plan.restype = ctypes.c_int
     lib.sdpa_set_profile_events.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
@@ -152,3 +159,11 @@ def sdpa_forward(desc: sdpa_desc_t, q: int, k: int, v: int, o: int, lse: int | N
     """Raw call with integer device addresses; raises on a non-zero status."""
     check(load().sdpa_forward(ctypes.byref(desc), q, k, v, o, lse or None, workspace or None,
                               workspace_bytes, stream or None))
+
+
+def sdpa_forward_masked(desc: sdpa_desc_t, q: int, k: int, v: int, mask: int | None, o: int,
+                        lse: int | None, workspace: int | None, workspace_bytes: int,
+                        stream: int | None) -> None:
+    """Raw call with an explicit mask array; raises on a non-zero status."""
+    check(load().sdpa_forward_masked(ctypes.byref(desc), q, k, v, mask or None, o, lse or None,
+                                     workspace or None, workspace_bytes, stream or None))

@@ -51,7 +51,8 @@ HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
 # the former and 1-3% for the latter (and no better for the small-dim prefill
 # and short-query units, which keep the default).
 _ILP = ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]
-UNIT_FLAGS = {f"inst_{t}_{k}.hip": _ILP for t in ("bf16", "f16", "f32") for k in ("prefill_large", "decode")}
+UNIT_FLAGS = {f"inst_{t}_{k}{m}.hip": _ILP for t in ("bf16", "f16", "f32")
+              for k in ("prefill_large", "decode") for m in ("", "_mask")}
 
 
 def _needs(obj: str, src: str) -> bool:

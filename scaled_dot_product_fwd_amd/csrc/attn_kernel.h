@@ -38,6 +38,14 @@
 // whose first key lies below the last row's window edge is masked, which is
 // exact for unaligned windows too.
 //
+// Explicit mask array (MA != MA_NONE): the block's [rows x keys] tile of
+// the array rides the same LDS DMA pipeline as K and V and is applied to the
+// scores of every block before the running max: a boolean array sends removed
+// keys to -inf, an additive one is added to the scaled scores (mlx PR #3552
+// "feat(fast): add sliding-window SDPA kernel path", Public API: the mask
+// array beside the mask mode).  A row that keeps no key ends with l = 0 and
+// writes 0.
+//
 // Split-K (mlx issue #3826, second and third comments: the block-parallel
 // reduction over S): the blocks of the range may be dealt out to `splits`
 // workgroups; each writes its unnormalised O with (m, l) and a combine kernel
@@ -69,6 +77,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kRescale = 8.0f;  // lazy-rescale threshold, log2 units
 
 // ---------------------------------------------------------------------------
@@ -98,6 +107,9 @@ struct BF16 {
   static __device__ __forceinline__ unsigned short to_store(float x) {
     return __builtin_bit_cast(unsigned short, (__bf16)x);
   }
+  static __device__ __forceinline__ float to_float(unsigned short h) {
+    return __builtin_bit_cast(float, (unsigned)h << 16);
+  }
 };
 
 struct F16 {
@@ -119,6 +131,9 @@ struct F16 {
   static __device__ __forceinline__ unsigned short to_store(float x) {
     return __builtin_bit_cast(unsigned short, (_Float16)x);
   }
+  static __device__ __forceinline__ float to_float(unsigned short h) {
+    return (float)__builtin_bit_cast(_Float16, h);
+  }
 };
 
 struct F32 {
@@ -137,7 +152,7 @@ constexpr int cmin(int a, int b) { return a < b ? a : b; }
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
 // Static shape of one kernel instance.
-template <class E, int DQK, int DV, int NWQ, int NWK, int BKW>
+template <class E, int DQK, int DV, int NWQ, int NWK, int BKW, int MA = MA_NONE>
 struct Shape {
   static constexpr int NW = NWQ * NWK;
   static constexpr int NT = NW * 64;
@@ -155,6 +170,16 @@ struct Shape {
   static constexpr int BUF = KBYTES + VBYTES;
   static constexpr int KDMA = KBYTES / 1024;   // 1 KB DMA instructions per tile
   static constexpr int VDMA = VBYTES / 1024;
+  // Mask array tile: BM rows of BK keys, MES bytes each, kept row-major in
+  // 16-byte slots (MNS per row).  Slot ^ msw(row) spreads the 32 rows a wave
+  // reads at one key offset over the 256-byte bank window.
+  static constexpr int MES = MA == MA_NONE ? 0 : (MA == MA_BOOL ? 1 : E::ES);
+  static constexpr int MROWB = BK * MES;
+  static constexpr int MNS = MROWB / 16;
+  static constexpr int MBYTES = BM * MROWB;
+  static constexpr int MDMA = MBYTES / 1024;
+  static constexpr int MRPW = MNS >= 16 ? 1 : 16 / cmax(MNS, 1);  // rows per 256-byte window
+  static __device__ __forceinline__ int msw(int row) { return MNS ? (row / MRPW) & (MNS - 1) : 0; }
   // Chunk swizzles (16-byte chunks; the LDS serves 256 bytes per cycle).
   // K: the QK operand read has 16 lanes of consecutive rows reading the same
   // logical chunk per cycle; chunk ^ kx(row) puts them in 16 distinct slots
@@ -169,12 +194,12 @@ struct Shape {
   static __device__ __forceinline__ int vy(int row) {
     return VG == 16 ? 4 * (row & 3) : (VG == 8 ? 2 * (row & 3) : 2 * (row & 1));
   }
-  // Two K buffers and two V buffers (see the kernel's block loop); the
-  // cross-wave merge below reuses them, and needs a little more than they
-  // hold for the smallest head dims.
+  // Two K buffers, two V buffers and two mask buffers (see the kernel's
+  // block loop); the cross-wave merge below reuses them, and needs a little
+  // more than they hold for the smallest head dims.
   static constexpr int MSLOTS = NWQ * (NWK - 1);
   static constexpr int MLB = (MSLOTS * 32 * 8 + 15) / 16 * 16;
-  static constexpr int LDS = cmax(2 * BUF, MLB + MSLOTS * 32 * (32 + 4) * 4);
+  static constexpr int LDS = cmax(2 * BUF + 2 * MBYTES, MLB + MSLOTS * 32 * (32 + 4) * 4);
   // Families that split the keys over waves (decode, short queries) have one
   // row tile per KV head in practice, so each K/V byte is read once per
   // launch: stream it past the caches.  Prefill row tiles re-read the same
@@ -189,8 +214,8 @@ struct Shape {
   // four-wave prefill tiles of the small head dims, 16-bit types.
   static constexpr bool PIPE = NWK == 1 && E::ES == 2 && NQS * 4 + NDT * 16 + 2 * NKT * 16 <= 144;
   // DMA instructions one block costs the wave that issues the fewest / most.
-  static constexpr int DMA_MIN = KDMA / NW + VDMA / NW;
-  static constexpr int DMA_MAX = (KDMA + NW - 1) / NW + (VDMA + NW - 1) / NW;
+  static constexpr int DMA_MIN = KDMA / NW + VDMA / NW + MDMA / NW;
+  static constexpr int DMA_MAX = (KDMA + NW - 1) / NW + (VDMA + NW - 1) / NW + (MDMA + NW - 1) / NW;
   // Cross-wave merge (NWK > 1), through the idle tile buffers: (m, l) of
   // the waves with wk > 0 first, as [slot][q][2]; then their O in rounds of
   // TPR dv tiles, as [slot][q][MROW] after the (m, l) bytes, TPR as large
@@ -206,7 +231,8 @@ struct Shape {
   static_assert(DMA_MAX <= 63, "vmcnt range");
   static_assert(BKW % 32 == 0, "BKW must be a multiple of 32");
   static_assert(DQK % E::KQK == 0 && DV % 32 == 0, "bad head-dim tile");
-  static_assert(KBYTES % 1024 == 0 && VBYTES % 1024 == 0, "tiles must be whole DMA instructions");
+  static_assert(KBYTES % 1024 == 0 && VBYTES % 1024 == 0 && MBYTES % 1024 == 0,
+                "tiles must be whole DMA instructions");
   static_assert(LDS <= 160 * 1024, "LDS budget of one workgroup exceeded");
 };
 
@@ -251,10 +277,10 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);  // expcnt, lgkmcnt: no wait
 }
 
-template <class E, int DQK, int DV, int NWQ, int NWK, int BKW, int WPE>
+template <class E, int DQK, int DV, int NWQ, int NWK, int BKW, int WPE, int MA>
 __global__ __launch_bounds__(NWQ * NWK * 64) __attribute__((amdgpu_waves_per_eu(WPE)))
 void attn_fwd_kernel(AttnArgs a) {
-  using S = Shape<E, DQK, DV, NWQ, NWK, BKW>;
+  using S = Shape<E, DQK, DV, NWQ, NWK, BKW, MA>;
   using frag = typename E::frag;
   __shared__ __attribute__((aligned(1024))) char smem_[S::LDS];
   // All LDS addressing goes through an LDS-typed pointer, so addresses stay
@@ -407,10 +433,49 @@ void attn_fwd_kernel(AttnArgs a) {
     }
   };
 
+  // Mask tile DMA: lane l of instruction i fills slot 64 i + l of the tile,
+  // i.e. row (64 i + l) / MNS, physical slot (64 i + l) % MNS, which holds
+  // logical slot physical ^ msw(row) of that row.  Rows past the packed rows
+  // re-read the last one; slots past Lk in the tail block re-read the slot
+  // holding key Lk - 1 (those keys are masked anyway).
+  constexpr int MPW = S::MDMA ? (S::MDMA + S::NW - 1) / S::NW : 1;
+  const char* mptr[MPW];
+  int mls[MPW];
+  if constexpr (MA != MA_NONE) {
+#pragma unroll
+    for (int ii = 0; ii < MPW; ++ii) {
+      const int sl = (ii * S::NW + wave_u) * 64 + lane;
+      const int row = sl / S::MNS;
+      mls[ii] = (sl % S::MNS) ^ S::msw(row);
+      const int pr = min(r_wg + row, a.R - 1);
+      const int hr = kvh * a.G + pr % a.G;
+      mptr[ii] = (const char*)a.mask_arr +
+                 ((int64_t)b * a.ms[0] + (int64_t)hr * a.ms[1] + (int64_t)(pr / a.G) * a.ms[2]) * S::MES +
+                 mls[ii] * 16;
+    }
+  }
+  auto dma_m = [&](int blk, int buf) __attribute__((always_inline)) {
+    if constexpr (MA != MA_NONE) {
+      const int k0 = blk * S::BK;
+      const unsigned ml = lds_base + 2 * S::KBYTES + 2 * S::VBYTES + buf * S::MBYTES;
+      const int64_t kb = (int64_t)k0 * S::MES;
+      const bool tail = k0 + S::BK > a.Lk;
+      const int lmax = tail ? ((a.Lk - 1 - k0) * S::MES) >> 4 : S::MNS;
+#pragma unroll
+      for (int ii = 0; ii < MPW; ++ii) {
+        if ((ii + 1) * S::NW > S::MDMA && ii * S::NW + wave_u >= S::MDMA) continue;
+        const char* src = mptr[ii] + kb;
+        if (tail) src += (int64_t)(min(mls[ii], lmax) - mls[ii]) * 16;
+        lds_dma16<false>(src, ml + (ii * S::NW + wave_u) * 1024);
+      }
+    }
+  };
+
   // Prologue: block 0 goes in flight ahead of the Q loads; block 1 follows
   // once both have landed (see below).
   if (nblk > 0) {
     dma_k(blk(0), 0);
+    dma_m(blk(0), 0);
     dma_v(blk(0), 0);
   }
 
@@ -454,6 +519,9 @@ void attn_fwd_kernel(AttnArgs a) {
       else qf[s] = 0.f;
     }
   }
+  // Factor from the scores in the accumulators to log2 units.  An additive
+  // mask is applied in log2 units (s c + m log2 e), after which it is 1.
+  const float cs = MA == MA_ADD ? 1.f : c;
 
   // Loop-invariant parts of the LDS operand addresses (16-bit types).  The
   // K swizzle only involves the lane's row inside a 32-key tile and the V
@@ -487,6 +555,7 @@ void attn_fwd_kernel(AttnArgs a) {
   wait_vmcnt<0>();
   if (nblk > 1) {
     dma_k(blk(1), 1);
+    dma_m(blk(1), 1);
     dma_v(blk(1), 1);
   }
 
@@ -562,6 +631,44 @@ void attn_fwd_kernel(AttnArgs a) {
   // ---- mask edge blocks and fold the block max into the running max ----
   auto mask_max = [&](int j, f32x16 (&sacc)[S::NKT]) __attribute__((always_inline)) {
     const int kw = blk(j) * S::BK + wk * BKW;  // first key of this wave's slice
+    if constexpr (MA != MA_NONE) {
+      // This lane's row of the block's mask tile: register e of tile kt is
+      // key wk BKW + 32 kt + 8 (e / 4) + 4 hl + e % 4 of the block, so each
+      // group of 4 registers reads 4 consecutive elements.
+      const int mrow = wq * 32 + col;
+      const SDPA_LDS char* mt = smem + 2 * S::KBYTES + 2 * S::VBYTES + (j & 1) * S::MBYTES + mrow * S::MROWB;
+      const int sw = S::msw(mrow);
+#pragma unroll
+      for (int kt = 0; kt < S::NKT; ++kt) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int byte = (wk * BKW + kt * 32 + 8 * g + 4 * hl) * S::MES;
+          const SDPA_LDS char* pa = mt + (((byte >> 4) ^ sw) << 4) + (byte & 15);
+          if constexpr (MA == MA_BOOL) {
+            const unsigned w = *(const SDPA_LDS unsigned*)pa;
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+              if (((w >> (8 * t)) & 0xffu) == 0u) sacc[kt][4 * g + t] = kNegInf;
+          } else {
+            float mv[4];
+            if constexpr (E::ES == 4) {
+              const f32x4 w = *(const SDPA_LDS f32x4*)pa;
+              mv[0] = w[0]; mv[1] = w[1]; mv[2] = w[2]; mv[3] = w[3];
+            } else {
+              const u32x2 w = *(const SDPA_LDS u32x2*)pa;
+#pragma unroll
+              for (int t = 0; t < 4; ++t) {
+                const unsigned short h = (unsigned short)(w[t >> 1] >> (16 * (t & 1)));
+                mv[t] = E::to_float(h);
+              }
+            }
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+              sacc[kt][4 * g + t] = __builtin_fmaf(sacc[kt][4 * g + t], c, mv[t] * kLog2e);
+          }
+        }
+      }
+    }
     // edge blocks: the diagonal, a window edge, the Lk tail
     const bool edge = (kw + BKW > a.Lk) || (a.mask != MASK_NONE && kw + BKW - 1 > pmin_w) ||
                       (a.mask == MASK_WINDOW && kw <= pmax_w - a.window);
@@ -590,7 +697,7 @@ void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kt][e]);
     mx = wave_max32(mx);
-    const float mxs = mx * c;  // block max in log2 units (-inf if all masked)
+    const float mxs = mx * cs;  // block max in log2 units (-inf if all masked)
     const bool need = mxs > m_ref + kRescale;
     if (__builtin_expect(__builtin_amdgcn_ballot_w64(need) != 0, 0)) [[unlikely]] {
       const float m_new = need ? mxs : m_ref;
@@ -609,7 +716,7 @@ void attn_fwd_kernel(AttnArgs a) {
     for (int kt = 0; kt < S::NKT; ++kt) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][e], c, -msub));
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][e], cs, -msub));
         sacc[kt][e] = p;
         l_run += p;
       }
@@ -680,8 +787,9 @@ void attn_fwd_kernel(AttnArgs a) {
       pv(j, sacc, vf);
       if (j + 2 < nblk) {
         if constexpr (!KEARLY) wait_vmcnt<63 - S::DMA_MAX>();
-        __syncthreads();  // every wave is done with V(j)
+        __syncthreads();  // every wave is done with V(j) and the mask tile of j
         if constexpr (!KEARLY) dma_k(blk(j + 2), j & 1);
+        dma_m(blk(j + 2), j & 1);
         dma_v(blk(j + 2), j & 1);
       }
     }
@@ -699,8 +807,9 @@ void attn_fwd_kernel(AttnArgs a) {
       qk(0, sa);
       mask_max(0, sa);
       if (nblk > 2) {
-        __syncthreads();  // every wave is done with K(0)
+        __syncthreads();  // every wave is done with K(0) and the mask tile of 0
         dma_k(blk(2), 0);
+        dma_m(blk(2), 0);
       }
     }
     // `more` (block j + 1 exists) is a literal at every call, so the
@@ -719,8 +828,11 @@ void attn_fwd_kernel(AttnArgs a) {
       pv(j, cur, vf);
       if (more) mask_max(j + 1, nxt);
       if (j + 2 < nblk) {
-        __syncthreads();  // every wave is done with K(j + 1) and V(j)
-        if (j + 3 < nblk) dma_k(blk(j + 3), (j + 1) & 1);
+        __syncthreads();  // every wave is done with K(j + 1), its mask tile and V(j)
+        if (j + 3 < nblk) {
+          dma_k(blk(j + 3), (j + 1) & 1);
+          dma_m(blk(j + 3), (j + 1) & 1);
+        }
         dma_v(blk(j + 2), j & 1);
       }
     };
@@ -810,7 +922,8 @@ void attn_fwd_kernel(AttnArgs a) {
 
   if (!row_ok) return;
   if (a.splits == 1) {
-    const float inv = 1.0f / l_row;
+    // l = 0 only for a row that a mask array left without keys: it writes 0
+    const float inv = (MA == MA_NONE || l_row > 0.f) ? 1.0f / l_row : 0.f;
     char* orow = (char*)a.o + ((int64_t)b * a.os[0] + (int64_t)hq * a.os[1] + (int64_t)iq * a.os[2]) * E::ES;
 #pragma unroll
     for (int t = 0; t < S::NDT; ++t) {

@@ -9,10 +9,10 @@
 
 namespace sdpa {
 
-template <class E, int DQK, int DV, int NWQ, int NWK, int BKW, int WPE>
+template <class E, int DQK, int DV, int NWQ, int NWK, int BKW, int WPE, int MA>
 int launch_one(const Plan& p, const AttnArgs& a, void* stream, std::string* err) {
-  using S = dev::Shape<E, DQK, DV, NWQ, NWK, BKW>;
-  auto kern = dev::attn_fwd_kernel<E, DQK, DV, NWQ, NWK, BKW, WPE>;
+  using S = dev::Shape<E, DQK, DV, NWQ, NWK, BKW, MA>;
+  auto kern = dev::attn_fwd_kernel<E, DQK, DV, NWQ, NWK, BKW, WPE, MA>;
   // Check the compiled kernel can run the workgroup size it is launched with,
   // once per instance: an oversized launch must fail loudly, never return
   // silently unwritten output (mlx PR #4185 "Add force_fused option to
@@ -45,40 +45,49 @@ int launch_one(const Plan& p, const AttnArgs& a, void* stream, std::string* err)
 
 }  // namespace sdpa
 
-// One dispatch case: the plan's padded dims select the instance; the wave
-// arrangement follows from the kind exactly as in the planner.
-#define SDPA_CASE(E, KIND, DQK, DV)                                                            \
+// One dispatch case: the plan's padded dims (and mask array kind MA) select
+// the instance; the wave arrangement follows from the kind exactly as in the
+// planner.
+#define SDPA_CASE(E, KIND, DQK, DV, MA)                                                        \
   if (p.dqk_pad == DQK && p.dv_pad == DV) {                                                    \
-    constexpr Family f_ = family_for(KIND, dev::E::ES, DQK, DV);                               \
-    if (p.fam.nwq != f_.nwq || p.fam.nwk != f_.nwk || p.fam.bkw != f_.bkw) {                   \
+    constexpr Family f_ = family_for(KIND, dev::E::ES, DQK, DV, mask_elem_bytes(MA, dev::E::ES)); \
+    if (p.fam.nwq != f_.nwq || p.fam.nwk != f_.nwk || p.fam.bkw != f_.bkw || p.mask_array != MA) { \
       *err = "plan and kernel instance disagree on the wave arrangement";                      \
       return SDPA_E_PLAN;                                                                      \
     }                                                                                          \
-    return launch_one<dev::E, DQK, DV, f_.nwq, f_.nwk, f_.bkw,                  \
-                      wpe_for(KIND, dev::E::ES, DQK, DV)>(p, a, stream, err);             \
+    return launch_one<dev::E, DQK, DV, f_.nwq, f_.nwk, f_.bkw,                                 \
+                      wpe_for(KIND, dev::E::ES, DQK, DV), MA>(p, a, stream, err);              \
   }
 
 // Head-dim pairs of the 16-bit types: equal padded dims plus (192, 128),
 // split at 192 so that the large ones can live in units of their own.
-#define SDPA_PAIRS16_SMALL(E, KIND) \
-  SDPA_CASE(E, KIND, 32, 32)         \
-  SDPA_CASE(E, KIND, 64, 64)         \
-  SDPA_CASE(E, KIND, 96, 96)         \
-  SDPA_CASE(E, KIND, 128, 128)       \
-  SDPA_CASE(E, KIND, 160, 160)
-#define SDPA_PAIRS16_LARGE(E, KIND) \
-  SDPA_CASE(E, KIND, 192, 192)       \
-  SDPA_CASE(E, KIND, 224, 224)       \
-  SDPA_CASE(E, KIND, 256, 256)       \
-  SDPA_CASE(E, KIND, 192, 128)
-#define SDPA_PAIRS16(E, KIND) SDPA_PAIRS16_SMALL(E, KIND) SDPA_PAIRS16_LARGE(E, KIND)
+#define SDPA_PAIRS16_SMALL(E, KIND, MA) \
+  SDPA_CASE(E, KIND, 32, 32, MA)         \
+  SDPA_CASE(E, KIND, 64, 64, MA)         \
+  SDPA_CASE(E, KIND, 96, 96, MA)         \
+  SDPA_CASE(E, KIND, 128, 128, MA)       \
+  SDPA_CASE(E, KIND, 160, 160, MA)
+#define SDPA_PAIRS16_LARGE(E, KIND, MA) \
+  SDPA_CASE(E, KIND, 192, 192, MA)       \
+  SDPA_CASE(E, KIND, 224, 224, MA)       \
+  SDPA_CASE(E, KIND, 256, 256, MA)       \
+  SDPA_CASE(E, KIND, 192, 128, MA)
+#define SDPA_PAIRS16(E, KIND, MA) SDPA_PAIRS16_SMALL(E, KIND, MA) SDPA_PAIRS16_LARGE(E, KIND, MA)
 
 // float32 stops at 128.
-#define SDPA_PAIRS32(E, KIND)  \
-  SDPA_CASE(E, KIND, 32, 32)   \
-  SDPA_CASE(E, KIND, 64, 64)   \
-  SDPA_CASE(E, KIND, 96, 96)   \
-  SDPA_CASE(E, KIND, 128, 128)
+#define SDPA_PAIRS32(E, KIND, MA)  \
+  SDPA_CASE(E, KIND, 32, 32, MA)   \
+  SDPA_CASE(E, KIND, 64, 64, MA)   \
+  SDPA_CASE(E, KIND, 96, 96, MA)   \
+  SDPA_CASE(E, KIND, 128, 128, MA)
+
+// Mask-array units: the plan's array kind picks the boolean or additive set.
+#define SDPA_BY_MASK_ARRAY(PAIRS, E, KIND) \
+  if (p.mask_array == MA_BOOL) {           \
+    PAIRS(E, KIND, MA_BOOL)                \
+  } else {                                 \
+    PAIRS(E, KIND, MA_ADD)                 \
+  }
 
 #define SDPA_NO_INSTANCE()                                                               \
   *err = "no kernel instance for dqk_pad=" + std::to_string(p.dqk_pad) +                 \

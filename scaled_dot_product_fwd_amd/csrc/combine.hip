@@ -5,7 +5,9 @@
 // For splits s with running max m_s (log2 units), sum l_s and unnormalised
 // output O_s:  M = max_s m_s,  w_s = 2^(m_s - M),  L = sum_s w_s l_s,
 // o = sum_s w_s O_s / L,  lse = ln2 * (M + log2 L).  A split that saw no
-// visible key has m_s = -inf and contributes w_s = 0.
+// visible key has m_s = -inf and contributes w_s = 0; a row with no visible
+// key in any split (possible only through a mask array) writes o = 0 and
+// lse = -inf.
 #include <hip/hip_runtime.h>
 
 #include <string>
@@ -89,7 +91,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a)
     float L = red_l[0];
 #pragma unroll
     for (int w = 1; w < kCombineThreads / 64; ++w) L += red_l[w];
-    const float inv = 1.0f / L;
+    const float inv = L > 0.f ? 1.0f / L : 0.f;  // L = 0: a mask array left the row no key
     char* orow = (char*)a.o + ((int64_t)b * a.os[0] + (int64_t)h * a.os[1] + (int64_t)i * a.os[2]) * E::ES;
     const int d = 4 * tid;
     if constexpr (E::ES == 2) {

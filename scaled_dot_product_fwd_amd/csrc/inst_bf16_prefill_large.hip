@@ -5,7 +5,7 @@
 
 namespace sdpa {
 int launch_attn_bf16_prefill_large(const Plan& p, const AttnArgs& a, void* stream, std::string* err) {
-  SDPA_PAIRS16_LARGE(BF16, KIND_PREFILL)
+  SDPA_PAIRS16_LARGE(BF16, KIND_PREFILL, MA_NONE)
   SDPA_NO_INSTANCE()
 }
 }  // namespace sdpa

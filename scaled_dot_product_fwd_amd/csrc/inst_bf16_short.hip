@@ -3,7 +3,7 @@
 
 namespace sdpa {
 int launch_attn_bf16_short(const Plan& p, const AttnArgs& a, void* stream, std::string* err) {
-  SDPA_PAIRS16(BF16, KIND_SHORT)
+  SDPA_PAIRS16(BF16, KIND_SHORT, MA_NONE)
   SDPA_NO_INSTANCE()
 }
 }  // namespace sdpa

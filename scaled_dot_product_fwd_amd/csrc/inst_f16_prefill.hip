@@ -5,7 +5,7 @@ namespace sdpa {
 int launch_attn_f16_prefill_large(const Plan& p, const AttnArgs& a, void* stream, std::string* err);
 
 int launch_attn_f16_prefill(const Plan& p, const AttnArgs& a, void* stream, std::string* err) {
-  SDPA_PAIRS16_SMALL(F16, KIND_PREFILL)
+  SDPA_PAIRS16_SMALL(F16, KIND_PREFILL, MA_NONE)
   return launch_attn_f16_prefill_large(p, a, stream, err);
 }
 }  // namespace sdpa

@@ -3,7 +3,7 @@
 
 namespace sdpa {
 int launch_attn_f32_short(const Plan& p, const AttnArgs& a, void* stream, std::string* err) {
-  SDPA_PAIRS32(F32, KIND_SHORT)
+  SDPA_PAIRS32(F32, KIND_SHORT, MA_NONE)
   SDPA_NO_INSTANCE()
 }
 }  // namespace sdpa

@@ -57,11 +57,12 @@ const char* mask_name(int m) {
 
 }  // namespace
 
-size_t attn_lds_bytes(int dtype, int dqk_pad, int dv_pad, const Family& f) {
-  // Mirrors Shape<> in attn_kernel.h: two K and two V tile buffers, which
-  // the cross-wave merge reuses (with a little more for the smallest dims).
+size_t attn_lds_bytes(int dtype, int dqk_pad, int dv_pad, const Family& f, int mes) {
+  // Mirrors Shape<> in attn_kernel.h: two K, two V and (with a mask array)
+  // two mask tile buffers, which the cross-wave merge reuses (with a little
+  // more for the smallest dims).
   const int es = dtype == SDPA_F32 ? 4 : 2;
-  const size_t tiles = (size_t)2 * f.nwk * f.bkw * (dqk_pad + dv_pad) * es;
+  const size_t tiles = (size_t)2 * f.nwk * f.bkw * ((dqk_pad + dv_pad) * es + 32 * f.nwq * mes);
   const size_t slots = (size_t)f.nwq * (f.nwk - 1);
   const size_t merge = (slots * 32 * 8 + 15) / 16 * 16 + slots * 32 * (32 + 4) * 4;
   return std::max(tiles, merge);
@@ -142,6 +143,23 @@ int make_plan(const sdpa_desc_t* d, Plan* p, std::string* err) {
       }
     }
   }
+  if (d->mask_array != SDPA_MASK_ARRAY_NONE && d->mask_array != SDPA_MASK_ARRAY_BOOL &&
+      d->mask_array != SDPA_MASK_ARRAY_ADD) {
+    return fail(err, SDPA_E_MASK, "mask_array must be SDPA_MASK_ARRAY_NONE, _BOOL or _ADD (got " +
+                                      std::to_string(d->mask_array) + ")");
+  }
+  const int ma = d->mask_array == SDPA_MASK_ARRAY_BOOL ? MA_BOOL : (d->mask_array == SDPA_MASK_ARRAY_ADD ? MA_ADD : MA_NONE);
+  const int mes = mask_elem_bytes(ma, es);
+  if (ma != MA_NONE) {
+    for (int j = 0; j < 3; ++j) {
+      if (d->mask_stride[j] < 0 || (d->mask_stride[j] * mes) % 16 != 0) {
+        std::ostringstream s;
+        s << "mask_stride[" << j << "] = " << d->mask_stride[j]
+          << " must be >= 0 and a multiple of 16 bytes (mask rows are read in 16-byte pieces; pad the key dim)";
+        return fail(err, SDPA_E_STRIDE, s.str());
+      }
+    }
+  }
   if (d->num_splits < 0 || d->num_splits > kMaxSplits) {
     return fail(err, SDPA_E_PLAN, "num_splits must be 0 (auto) or 1.." + std::to_string(kMaxSplits));
   }
@@ -166,7 +184,7 @@ int make_plan(const sdpa_desc_t* d, Plan* p, std::string* err) {
   const int64_t row_tiles = ceil_div(R, rows);
   const int64_t base = B * Hkv * row_tiles;
   const int kind = rows == 32 ? KIND_DECODE : (rows == 64 ? KIND_SHORT : KIND_PREFILL);
-  const Family fam = family_for(kind, d->dtype == SDPA_F32 ? 4 : 2, dqk_pad, dv_pad);
+  const Family fam = family_for(kind, es, dqk_pad, dv_pad, mes);
   const int64_t bk = (int64_t)fam.nwk * fam.bkw;
 
   // Key blocks a row tile visits (the longest tile; every tile for `none`).
@@ -184,7 +202,7 @@ int make_plan(const sdpa_desc_t* d, Plan* p, std::string* err) {
     // tiles exist: its partial outputs would cost HBM traffic comparable to
     // the K/V it reads, while an unsplit wave of large tiles already keeps
     // the MFMA units busy.
-    const size_t lds_need = attn_lds_bytes(d->dtype, dqk_pad, dv_pad, fam);
+    const size_t lds_need = attn_lds_bytes(d->dtype, dqk_pad, dv_pad, fam, mes);
     const int64_t by_waves = 4 * wpe_for(kind, d->dtype == SDPA_F32 ? 4 : 2, dqk_pad, dv_pad) /
                              (fam.nwq * fam.nwk);
     const int64_t resident = std::max<int64_t>(
@@ -212,6 +230,8 @@ int make_plan(const sdpa_desc_t* d, Plan* p, std::string* err) {
   p->splits = (int)splits;
   p->mask = mask;
   p->window = window;
+  p->mask_array = ma;
+  p->mes = mes;
   p->grid = base * splits;
   // Work items that read the same key blocks run in groups on one XCD, whose
   // L2 then serves the re-reads: the row tiles of one split, and neighbouring
@@ -230,7 +250,7 @@ int make_plan(const sdpa_desc_t* d, Plan* p, std::string* err) {
     const size_t o_bytes = (rows_total * (size_t)Dv * 4 + 255) / 256 * 256;
     p->workspace = o_bytes + rows_total * 8;
   }
-  p->lds_bytes = attn_lds_bytes(d->dtype, dqk_pad, dv_pad, fam);
+  p->lds_bytes = attn_lds_bytes(d->dtype, dqk_pad, dv_pad, fam, mes);
   return SDPA_OK;
 }
 
@@ -242,6 +262,7 @@ std::string describe(const sdpa_desc_t* d, const Plan& p) {
     << " waves=" << p.fam.nwq << "x" << p.fam.nwk << " block_keys=" << p.fam.nwk * p.fam.bkw
     << " row_tiles=" << p.row_tiles << " splits=" << p.splits << " mask=" << mask_name(p.mask);
   if (p.mask == MASK_WINDOW) s << "(" << p.window << ")";
+  if (p.mask_array != MA_NONE) s << " mask_array=" << (p.mask_array == MA_BOOL ? "bool" : "add");
   s << " grid=" << p.grid << " xcd_group=" << p.xcd_group << " combine_grid=" << p.combine_grid
     << " lds=" << p.lds_bytes
     << " workspace=" << p.workspace;

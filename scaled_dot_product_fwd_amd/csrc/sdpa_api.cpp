@@ -113,8 +113,8 @@ int sdpa_describe_plan(const sdpa_desc_t* d, char* buf, size_t len) {
   return ok();
 }
 
-int sdpa_forward(const sdpa_desc_t* d, const void* q, const void* k, const void* v, void* o, float* lse,
-                 void* workspace, size_t workspace_bytes, sdpa_stream_t stream) {
+int sdpa_forward_masked(const sdpa_desc_t* d, const void* q, const void* k, const void* v, const void* mask,
+                        void* o, float* lse, void* workspace, size_t workspace_bytes, sdpa_stream_t stream) {
   hipEvent_t ev_start = g_prof_start, ev_stop = g_prof_stop;  // consumed by this call
   g_prof_start = g_prof_stop = nullptr;
   if (!q || !k || !v || !o) return set_error(SDPA_E_NULL, "q, k, v and o must be non-NULL device pointers");
@@ -122,8 +122,12 @@ int sdpa_forward(const sdpa_desc_t* d, const void* q, const void* k, const void*
   std::string err;
   int rc = sdpa::make_plan(d, &p, &err);
   if (rc != SDPA_OK) return set_error(rc, err);
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
-    return set_error(SDPA_E_STRIDE, "q, k, v and o must be 16-byte aligned");
+  if ((p.mask_array != sdpa::MA_NONE) != (mask != nullptr))
+    return set_error(SDPA_E_NULL, p.mask_array != sdpa::MA_NONE
+                                      ? "desc names a mask array but mask is NULL"
+                                      : "mask is given but desc->mask_array is SDPA_MASK_ARRAY_NONE");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (mask && !aligned16(mask)))
+    return set_error(SDPA_E_STRIDE, "q, k, v, o and mask must be 16-byte aligned");
   if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u))
     return set_error(SDPA_E_STRIDE, "lse must be 4-byte aligned");
   if (p.workspace > 0) {
@@ -143,11 +147,13 @@ int sdpa_forward(const sdpa_desc_t* d, const void* q, const void* k, const void*
   a.v = v;
   a.o = o;
   a.lse = lse;
+  a.mask_arr = mask;
   for (int j = 0; j < 3; ++j) {
     a.qs[j] = d->q_stride[j];
     a.ks[j] = d->k_stride[j];
     a.vs[j] = d->v_stride[j];
     a.os[j] = d->o_stride[j];
+    a.ms[j] = mask ? d->mask_stride[j] : 0;
   }
   a.B = (int)d->batch;
   a.Hq = (int)d->heads_q;
@@ -174,13 +180,17 @@ int sdpa_forward(const sdpa_desc_t* d, const void* q, const void* k, const void*
   }
 
   using L = int (*)(const sdpa::Plan&, const sdpa::AttnArgs&, void*, std::string*);
-  // [dtype][kind]
-  static const L table[3][sdpa::kNumKinds] = {
-      {sdpa::launch_attn_f32_prefill, sdpa::launch_attn_f32_short, sdpa::launch_attn_f32_decode},
-      {sdpa::launch_attn_f16_prefill, sdpa::launch_attn_f16_short, sdpa::launch_attn_f16_decode},
-      {sdpa::launch_attn_bf16_prefill, sdpa::launch_attn_bf16_short, sdpa::launch_attn_bf16_decode},
+  // [with a mask array][dtype][kind]
+  static const L table[2][3][sdpa::kNumKinds] = {
+      {{sdpa::launch_attn_f32_prefill, sdpa::launch_attn_f32_short, sdpa::launch_attn_f32_decode},
+       {sdpa::launch_attn_f16_prefill, sdpa::launch_attn_f16_short, sdpa::launch_attn_f16_decode},
+       {sdpa::launch_attn_bf16_prefill, sdpa::launch_attn_bf16_short, sdpa::launch_attn_bf16_decode}},
+      {{sdpa::launch_attn_f32_prefill_mask, sdpa::launch_attn_f32_short_mask, sdpa::launch_attn_f32_decode_mask},
+       {sdpa::launch_attn_f16_prefill_mask, sdpa::launch_attn_f16_short_mask, sdpa::launch_attn_f16_decode_mask},
+       {sdpa::launch_attn_bf16_prefill_mask, sdpa::launch_attn_bf16_short_mask,
+        sdpa::launch_attn_bf16_decode_mask}},
   };
-  const L launch = table[p.dtype][p.kind];
+  const L launch = table[p.mask_array != sdpa::MA_NONE][p.dtype][p.kind];
   if (ev_start && hipEventRecord(ev_start, (hipStream_t)stream) != hipSuccess)
     return set_error(SDPA_E_HIP, "hipEventRecord(start) failed");
   rc = launch(p, a, stream, &err);
@@ -206,6 +216,15 @@ int sdpa_forward(const sdpa_desc_t* d, const void* q, const void* k, const void*
     if (rc != SDPA_OK) return set_error(rc, err);
   }
   return ok();
+}
+
+int sdpa_forward(const sdpa_desc_t* d, const void* q, const void* k, const void* v, void* o, float* lse,
+                 void* workspace, size_t workspace_bytes, sdpa_stream_t stream) {
+  if (d && d->mask_array != SDPA_MASK_ARRAY_NONE) {
+    g_prof_start = g_prof_stop = nullptr;
+    return set_error(SDPA_E_MASK, "desc names a mask array: call sdpa_forward_masked with the array");
+  }
+  return sdpa_forward_masked(d, q, k, v, nullptr, o, lse, workspace, workspace_bytes, stream);
 }
 
 int sdpa_set_profile_events(void* start, void* stop) {

@@ -22,7 +22,9 @@ struct AttnArgs {
   float* lse;          // nullable
   float* ws_o;         // split partial outputs [z][r][split][dv] (unnormalised)
   float* ws_ml;        // split partial (m, l) pairs [z][r][split][2], m in log2 units
+  const void* mask_arr; // explicit mask array (kernels instantiated for one)
   int64_t qs[3], ks[3], vs[3], os[3];  // element strides of (batch, head, position)
+  int64_t ms[3];       // mask array element strides of (batch, query head, query)
   int B, Hq, Hkv, Lq, Lk, dqk, dv, G;
   int R;               // packed rows per KV head = G * Lq; row r -> (g = r % G, i = r / G)
   int off;             // Lk - Lq: absolute key position of query row i is i + off
@@ -55,20 +57,30 @@ struct Family {
 enum : int { KIND_PREFILL = 0, KIND_SHORT = 1, KIND_DECODE = 2 };
 constexpr int kNumKinds = 3;
 
+// Explicit mask array kinds as the kernels see them (0: none).  Bytes per
+// mask element: 1 for a boolean array, the element size for an additive one.
+enum : int { MA_NONE = 0, MA_BOOL = 1, MA_ADD = 2 };
+constexpr int mask_elem_bytes(int ma, int elem_bytes) {
+  return ma == MA_NONE ? 0 : (ma == MA_BOOL ? 1 : elem_bytes);
+}
+
 // The wave arrangement of each kind, sized so that the two LDS buffers of K
-// and V tiles fit: prefill keeps two workgroups per CU (<= 80 KB), decode
+// and V tiles (and of the mask tile, mes bytes per element, when a mask
+// array is given) fit: prefill keeps two workgroups per CU (<= 80 KB), decode
 // takes the largest key block that fits one workgroup's 160 KB.  Shared by
 // the planner and the kernel instantiation units.
-constexpr Family family_for(int kind, int elem_bytes, int dqk_pad, int dv_pad) {
+constexpr Family family_for(int kind, int elem_bytes, int dqk_pad, int dv_pad, int mes = 0) {
   const int key_bytes = (dqk_pad + dv_pad) * elem_bytes;  // one key of K plus V
-  if (kind == KIND_DECODE) return key_bytes * 128 * 2 <= 160 * 1024 ? Family{1, 4, 32} : Family{1, 2, 32};
+  if (kind == KIND_DECODE)
+    return (key_bytes + 32 * mes) * 128 * 2 <= 160 * 1024 ? Family{1, 4, 32} : Family{1, 2, 32};
   if (kind == KIND_SHORT) return Family{2, 2, 32};
   // Prefill: 64-key blocks when two workgroups still fit per CU, or when the
   // head dims are so large that one workgroup per CU is all the registers
   // allow anyway (then the longer block halves the per-block overheads).
-  if (key_bytes * 64 * 2 <= 80 * 1024) return Family{4, 1, 64};
+  const int per_key = key_bytes + 128 * mes;  // K, V and a 128-row mask column
+  if (per_key * 64 * 2 <= 80 * 1024) return Family{4, 1, 64};
   const int dmax = dqk_pad > dv_pad ? dqk_pad : dv_pad;
-  return dmax >= 192 && key_bytes * 64 * 2 <= 160 * 1024 ? Family{4, 1, 64} : Family{4, 1, 32};
+  return dmax >= 192 && per_key * 64 * 2 <= 160 * 1024 ? Family{4, 1, 64} : Family{4, 1, 32};
 }
 
 // Waves per SIMD each kernel instance is compiled for: two (so one wave's
@@ -91,6 +103,8 @@ struct Plan {
   int row_tiles;
   int splits;
   int mask, window;      // canonical mask
+  int mask_array;        // MA_NONE / MA_BOOL / MA_ADD
+  int mes;               // bytes per mask array element (0 without one)
   int64_t grid;          // workgroups of the attention kernel
   int xcd_group;         // see AttnArgs::xcd_group
   int64_t combine_grid;  // workgroups of the combine kernel (0 when unsplit)
@@ -117,11 +131,21 @@ SDPA_DECLARE_LAUNCH(launch_attn_f16_decode)
 SDPA_DECLARE_LAUNCH(launch_attn_f32_prefill)
 SDPA_DECLARE_LAUNCH(launch_attn_f32_short)
 SDPA_DECLARE_LAUNCH(launch_attn_f32_decode)
+// the same with an explicit mask array (boolean or additive, from the plan)
+SDPA_DECLARE_LAUNCH(launch_attn_bf16_prefill_mask)
+SDPA_DECLARE_LAUNCH(launch_attn_bf16_short_mask)
+SDPA_DECLARE_LAUNCH(launch_attn_bf16_decode_mask)
+SDPA_DECLARE_LAUNCH(launch_attn_f16_prefill_mask)
+SDPA_DECLARE_LAUNCH(launch_attn_f16_short_mask)
+SDPA_DECLARE_LAUNCH(launch_attn_f16_decode_mask)
+SDPA_DECLARE_LAUNCH(launch_attn_f32_prefill_mask)
+SDPA_DECLARE_LAUNCH(launch_attn_f32_short_mask)
+SDPA_DECLARE_LAUNCH(launch_attn_f32_decode_mask)
 #undef SDPA_DECLARE_LAUNCH
 int launch_combine(const Plan& p, const CombineArgs& a, void* stream, std::string* err);
 
 // LDS bytes of an attention kernel instance (host mirror of the kernel's
 // static layout, used by the planner's capacity check).
-size_t attn_lds_bytes(int dtype, int dqk_pad, int dv_pad, const Family& f);
+size_t attn_lds_bytes(int dtype, int dqk_pad, int dv_pad, const Family& f, int mes = 0);
 
 }  // namespace sdpa

@@ -35,3 +35,30 @@ def make_qkv(b: int, hq: int, hkv: int, lq: int, lk: int, dqk: int, dv: int,
 def default_scale(dqk: int) -> float:
     """1/sqrt(Dqk) rounded to float32, the value handed to both sides."""
     return float(torch.tensor(dqk, dtype=torch.float64).rsqrt().to(torch.float32))
+
+
+def bool_mask(shape, seed: int, keep: float) -> torch.Tensor:
+    """CPU boolean mask array: each element True (key kept) with probability ``keep``."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    return torch.rand(tuple(shape), generator=g, dtype=torch.float32) < keep
+
+
+def additive_mask(shape, seed: int, dtype: torch.dtype, sigma: float = 2.0,
+                  minus_inf: float = 0.2) -> torch.Tensor:
+    """CPU additive mask array: N(0, sigma^2) values rounded to ``dtype``, and
+    -inf with probability ``minus_inf``."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    vals = torch.randn(tuple(shape), generator=g, dtype=torch.float32) * sigma
+    drop = torch.rand(tuple(shape), generator=g, dtype=torch.float32) < minus_inf
+    return vals.masked_fill(drop, float("-inf")).to(dtype)
+
+
+def padding_mask(b: int, lk: int, seed: int, min_len: int = 1) -> torch.Tensor:
+    """CPU key-padding mask ``[b, 1, 1, lk]``: batch row n keeps its first
+    len_n keys, len_n drawn uniformly from [min_len, lk]."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    lens = torch.randint(min_len, lk + 1, (b,), generator=g)
+    return (torch.arange(lk)[None, :] < lens[:, None]).reshape(b, 1, 1, lk)

@@ -198,3 +198,104 @@ def test_split_rows_beyond_one_grid_fall_back_to_unsplit():
     assert p["splits"] == "1"
     msg = _status(sdpa.sdpa_workspace_bytes, _desc(num_splits=2, **kw))
     assert "SDPA_E_PLAN" in msg and "2^31" in msg
+
+
+# ---------------------------------------------------------------------------
+# Explicit mask arrays
+# ---------------------------------------------------------------------------
+
+def test_desc_struct_layout_matches_the_header(tmp_path):
+    """ctypes mirror of sdpa_desc_t: every field offset and the size agree with
+    what the C compiler makes of include/sdpa.h."""
+    fields = [f for f, _ in _lib.sdpa_desc_t._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "sdpa.h"\nint main(void){\n' +
+                   "".join(f'printf("%zu\\n", offsetof(sdpa_desc_t, {f}));\n' for f in fields) +
+                   'printf("%zu\\n", sizeof(sdpa_desc_t));\nreturn 0;}\n')
+    exe = tmp_path / "layout"
+    import subprocess
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], check=True, capture_output=True,
+                                          text=True).stdout.split()]
+    want = [getattr(_lib.sdpa_desc_t, f).offset for f in fields] + [ctypes.sizeof(_lib.sdpa_desc_t)]
+    assert got == want
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(mask_array=3), "SDPA_E_MASK", "mask_array must be"),
+    (dict(mask_array=_lib.SDPA_MASK_ARRAY_BOOL, mask_stride=(0, 0, 8)), "SDPA_E_STRIDE", "mask_stride[2]"),
+    (dict(mask_array=_lib.SDPA_MASK_ARRAY_ADD, mask_stride=(0, 4, 16)), "SDPA_E_STRIDE", "mask_stride[1]"),
+    (dict(mask_array=_lib.SDPA_MASK_ARRAY_BOOL, mask_stride=(-16, 0, 16)), "SDPA_E_STRIDE", "mask_stride[0]"),
+])
+def test_mask_array_validation(kw, code, needle):
+    d = _desc(**kw)
+    msg = _status(sdpa.sdpa_workspace_bytes, d)
+    assert msg.startswith(code) and needle in msg, msg
+    msg = _status(sdpa.sdpa_forward_masked, d, 16, 16, 16, 16, 16, None, None, 0, None)
+    assert msg.startswith(code), msg
+
+
+def test_mask_array_pointer_must_match_the_desc():
+    d = _desc(mask_array=_lib.SDPA_MASK_ARRAY_BOOL, mask_stride=(0, 0, 16))
+    msg = _status(sdpa.sdpa_forward_masked, d, 16, 16, 16, None, 16, None, None, 0, None)
+    assert msg.startswith("SDPA_E_NULL") and "mask is NULL" in msg
+    msg = _status(sdpa.sdpa_forward_masked, _desc(), 16, 16, 16, 16, 16, None, None, 0, None)
+    assert msg.startswith("SDPA_E_NULL") and "SDPA_MASK_ARRAY_NONE" in msg
+    msg = _status(sdpa.sdpa_forward_masked, d, 16, 16, 16, 24, 16, None, None, 0, None)
+    assert msg.startswith("SDPA_E_STRIDE") and "16-byte aligned" in msg
+    # the plain entry point refuses a desc that names an array
+    msg = _status(sdpa.sdpa_forward, d, 16, 16, 16, 16, None, None, 0, None)
+    assert msg.startswith("SDPA_E_MASK") and "sdpa_forward_masked" in msg
+
+
+@pytest.mark.parametrize("dtype,d,kind,family,bk", [
+    # prefill: the mask tile joins K and V in LDS; 64-key blocks while two
+    # workgroups still fit a CU, else 32-key blocks (large dims keep 64)
+    (_lib.SDPA_BF16, 128, _lib.SDPA_MASK_ARRAY_NONE, "prefill", "64"),
+    (_lib.SDPA_BF16, 128, _lib.SDPA_MASK_ARRAY_BOOL, "prefill", "64"),
+    (_lib.SDPA_BF16, 128, _lib.SDPA_MASK_ARRAY_ADD, "prefill", "32"),
+    (_lib.SDPA_BF16, 256, _lib.SDPA_MASK_ARRAY_ADD, "prefill", "64"),
+    (_lib.SDPA_F32, 128, _lib.SDPA_MASK_ARRAY_ADD, "prefill", "32"),
+])
+def test_plan_masked_prefill_family(dtype, d, kind, family, bk):
+    p = _plan(b=1, hq=8, hkv=8, lq=2048, lk=2048, dqk=d, dv=d, dtype=dtype, mask_array=kind,
+              mask_stride=(0, 0, 2048))
+    assert p["family"] == family and p["block_keys"] == bk
+    if kind != _lib.SDPA_MASK_ARRAY_NONE:
+        assert p["mask_array"] == ("bool" if kind == _lib.SDPA_MASK_ARRAY_BOOL else "add")
+    assert int(p["lds"]) <= 160 * 1024
+
+
+def test_plan_masked_decode_keeps_lds_within_a_cu():
+    for d in (64, 128, 160, 256):
+        for kind in (_lib.SDPA_MASK_ARRAY_BOOL, _lib.SDPA_MASK_ARRAY_ADD):
+            p = _plan(b=1, hq=32, hkv=8, lq=1, lk=8192, dqk=d, dv=d, mask_array=kind,
+                      mask_stride=(0, 0, 0))
+            assert p["family"] == "decode" and int(p["lds"]) <= 160 * 1024
+    # D=160 decode: 4x32-key waves fit without a mask array, not with an additive one
+    assert _plan(hq=32, hkv=8, lq=1, lk=8192, dqk=160, dv=160)["block_keys"] == "128"
+    assert _plan(hq=32, hkv=8, lq=1, lk=8192, dqk=160, dv=160, mask_array=_lib.SDPA_MASK_ARRAY_ADD,
+                 mask_stride=(0, 0, 0))["block_keys"] == "64"
+
+
+def test_mask_layout_host_checks():
+    import torch
+
+    q = torch.zeros(2, 4, 5, 8, dtype=torch.bfloat16)
+    good = sdpa.pad_mask(torch.ones(5, 13, dtype=torch.bool))
+    assert good.shape == (5, 13) and good.stride() == (16, 1)
+    kind, st = sdpa._mask_layout(good, q, 2, 4, 5, 13)
+    assert kind == _lib.SDPA_MASK_ARRAY_BOOL and st == [0, 0, 16]
+    add = sdpa.pad_mask(torch.zeros(2, 1, 5, 13), dtype=torch.bfloat16)
+    kind, st = sdpa._mask_layout(add, q, 2, 4, 5, 13)
+    assert kind == _lib.SDPA_MASK_ARRAY_ADD and st == [5 * 16, 0, 16]
+    with pytest.raises(sdpa.SdpaValueError, match="16-byte"):
+        sdpa._mask_layout(torch.ones(5, 13, dtype=torch.bool), q, 2, 4, 5, 13)
+    with pytest.raises(sdpa.SdpaValueError, match="readable"):
+        # rows start on 16-byte boundaries, but the storage ends 3 bytes
+        # short of the last row's 16-byte rounding
+        sdpa._mask_layout(torch.ones(77, dtype=torch.bool).as_strided((5, 13), (16, 1)), q, 2, 4, 5, 13)
+    with pytest.raises(sdpa.SdpaValueError, match="broadcast"):
+        sdpa._mask_layout(good[:4], q, 2, 4, 5, 13)
+    with pytest.raises(sdpa.SdpaValueError, match="dtype"):
+        sdpa._mask_layout(torch.zeros(5, 16, dtype=torch.float32), q, 2, 4, 5, 16)
