@@ -20,8 +20,9 @@ kernel's algorithmic bytes per launch over its average duration, measured with
 HIP events recorded on the launch stream by the library's profiling hook) and
 ``cpu_baseline`` (the float64 oracle timed on the host cores).
 
-``--sweep`` additionally times every shape of the five workloads and writes a
-table (stderr) and JSON (``--sweep-out``).
+``--sweep`` additionally times every shape of the table below (the five
+workloads, then explicit mask arrays beside the same shapes without one) and
+writes a table (stderr) and JSON (``--sweep-out``).
 """
 
 from __future__ import annotations
@@ -54,13 +55,19 @@ PAGES_DECODE_US = {(4, 256): 218, (4, 1024): 217, (4, 4096): 255, (4, 8192): 305
                    (8, 16384): 444, (8, 32768): 728}
 
 
-def shape(name, b, hq, hkv, lq, lk, dqk, dv, dtype, mask, window, seed):
+def shape(name, b, hq, hkv, lq, lk, dqk, dv, dtype, mask, window, seed, arr=None, arr_window=0):
+    """One benchmark shape.  ``arr`` names an explicit mask array given on top
+    of the mode: "window_bool" (an [Lq, Lk] boolean band of the last
+    ``arr_window`` keys, what callers build without a window mode),
+    "bias_add" (an [Lq, Lk] additive N(0, 1) bias) or "pad_bool" (a
+    [B, 1, 1, Lk] key-padding mask)."""
     return dict(name=name, b=b, hq=hq, hkv=hkv, lq=lq, lk=lk, dqk=dqk, dv=dv, dtype=dtype,
-                mask=mask, window=window, seed=seed)
+                mask=mask, window=window, seed=seed, arr=arr, arr_window=arr_window)
 
 
 def all_shapes():
-    """Every shape of the five workloads; seeds are 1000 * workload + index."""
+    """Every shape of the five workloads (seeds 1000 * workload + index), then
+    the mask array shapes (seeds 6000 + index)."""
     out = [shape("tiny_f32", 1, 4, 4, 128, 128, 64, 64, "f32", "none", 0, 1000)]
     lks = [256, 1024, 4096, 8192, 16384, 32768]
     for j, hkv in enumerate((4, 8)):
@@ -78,6 +85,15 @@ def all_shapes():
     for i, L in enumerate((2048, 4096, 8192)):
         out.append(shape(f"window_l{L}_d256", 1, 16, 8, L, L, 256, 256, "bf16", "window", 1024, 5000 + i))
     out.append(shape("causal_l32768_d256", 1, 16, 2, 32768, 32768, 256, 256, "bf16", "causal", 0, 5003))
+    # explicit mask arrays, each beside the same shape without one
+    out.append(shape("maskarr_window_bool_l4096_d256", 1, 16, 8, 4096, 4096, 256, 256, "bf16", "none", 0,
+                     6000, arr="window_bool", arr_window=1024))
+    out.append(shape("causal_l4096_d128", 1, 16, 16, 4096, 4096, 128, 128, "bf16", "causal", 0, 6001))
+    out.append(shape("maskarr_bias_add_causal_l4096_d128", 1, 16, 16, 4096, 4096, 128, 128, "bf16", "causal", 0,
+                     6001, arr="bias_add"))
+    out.append(shape("decode_b4_hkv8_lk8192_d128", 4, 32, 8, 1, 8192, 128, 128, "bf16", "none", 0, 6002))
+    out.append(shape("maskarr_pad_decode_b4_hkv8_lk8192_d128", 4, 32, 8, 1, 8192, 128, 128, "bf16", "none", 0,
+                     6002, arr="pad_bool"))
     return out
 
 
@@ -111,13 +127,49 @@ def row_visible(i, s):
     return min(s["window"], pos + 1)
 
 
+def mask_array_bytes(s):
+    """Bytes of the distinct elements of the workload's mask array (0 without one)."""
+    arr = s.get("arr")
+    if arr is None:
+        return 0
+    if arr == "pad_bool":
+        return s["b"] * s["lk"]
+    return s["lq"] * s["lk"] * (1 if arr == "window_bool" else ES[s["dtype"]])
+
+
 def work(s):
-    """(algorithmic flops, algorithmic bytes) of one call."""
+    """(algorithmic flops, algorithmic bytes) of one call.
+
+    With a mask array every pair the mode keeps is evaluated: the array is
+    data, so which of its blocks are empty is not known ahead of the call.
+    Its distinct elements count once in the bytes.
+    """
     pairs = visible_pairs(s["lq"], s["lk"], s["mask"], s["window"])
     flops = 2 * s["b"] * s["hq"] * (s["dqk"] + s["dv"]) * pairs
     es = ES[s["dtype"]]
     nbytes = es * s["b"] * (s["hq"] * s["lq"] * (s["dqk"] + s["dv"]) + s["hkv"] * s["lk"] * (s["dqk"] + s["dv"]))
-    return flops, nbytes
+    return flops, nbytes + mask_array_bytes(s)
+
+
+def make_mask_array(s):
+    """CPU mask array of the workload (None without one)."""
+    import torch
+
+    from scaled_dot_product_fwd_amd.synth import additive_mask, padding_mask
+
+    arr = s.get("arr")
+    if arr is None:
+        return None
+    if arr == "pad_bool":
+        return padding_mask(s["b"], s["lk"], s["seed"] + 3, min_len=s["lk"] // 4)
+    if arr == "bias_add":
+        return additive_mask((s["lq"], s["lk"]), s["seed"] + 3, torch.bfloat16 if s["dtype"] == "bf16" else
+                             (torch.float16 if s["dtype"] == "f16" else torch.float32), sigma=1.0, minus_inf=0.0)
+    # band of the last arr_window key positions up to the query's own (rows
+    # aligned to the last Lq keys)
+    pos = torch.arange(s["lq"])[:, None] + (s["lk"] - s["lq"])
+    key = torch.arange(s["lk"])[None, :]
+    return (key <= pos) & (key > pos - s["arr_window"])
 
 
 def bound(s):
@@ -191,18 +243,25 @@ class Runner:
         self.nsets = nsets
         self.o = torch.empty((s["b"], s["hq"], s["lq"], s["dv"]), dtype=dt, device=dev)
         self.lse = torch.empty((s["b"], s["hq"], s["lq"]), dtype=torch.float32, device=dev)
+        self.mask_cpu = make_mask_array(s)
+        kind, mstr, self.mask = sdpa.SDPA_MASK_ARRAY_NONE, (0, 0, 0), None
+        if self.mask_cpu is not None:
+            self.mask = sdpa.pad_mask(self.mask_cpu.to(dev))
+            kind, mstr = sdpa._mask_layout(self.mask, self.q, s["b"], s["hq"], s["lq"], s["lk"])
         self.desc = sdpa.make_desc(self.q.shape, kd.shape, vd.shape, sdpa._dtype_code(dt), scale=self.scale,
-                                   mask=s["mask"], window_size=s["window"])
+                                   mask=s["mask"], window_size=s["window"], mask_array=kind, mask_stride=mstr)
         self.plan = sdpa.sdpa_describe_plan(self.desc)
         self.ws_bytes = sdpa.sdpa_workspace_bytes(self.desc)
         self.ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=dev)
         self.stream = torch.cuda.current_stream(dev).cuda_stream
         lib = sdpa.load()
-        self._fwd = lib.sdpa_forward
+        self._fwd = lib.sdpa_forward_masked
         self._prof = lib.sdpa_set_profile_events
         self._descref = ctypes.byref(self.desc)
-        self._args = [(self.q.data_ptr(), k_.data_ptr(), v_.data_ptr(), self.o.data_ptr(), self.lse.data_ptr(),
-                       self.ws.data_ptr() if self.ws_bytes else None, self.ws_bytes, self.stream)
+        mptr = self.mask.data_ptr() if self.mask is not None else None
+        self._args = [(self.q.data_ptr(), k_.data_ptr(), v_.data_ptr(), mptr, self.o.data_ptr(),
+                       self.lse.data_ptr(), self.ws.data_ptr() if self.ws_bytes else None, self.ws_bytes,
+                       self.stream)
                       for k_, v_ in self.kv]
 
     def step(self, i, events=None, j=None):
@@ -277,7 +336,8 @@ def cpu_baseline(s, runner, budget_s=12.0):
             kvh = (heads // g) % s["hkv"]
             hs = slice(kvh * g, (kvh + 1) * g)
             t0 = time.perf_counter()
-            sdpa_ref(q[:, hs], k[:, kvh:kvh + 1], v[:, kvh:kvh + 1], runner.scale, s["mask"], s["window"])
+            sdpa_ref(q[:, hs], k[:, kvh:kvh + 1], v[:, kvh:kvh + 1], runner.scale, s["mask"], s["window"],
+                     mask_arr=runner.mask_cpu)
             t_total += time.perf_counter() - t0
             heads += g
         frac = heads / s["hq"]
@@ -293,7 +353,7 @@ def cpu_baseline(s, runner, budget_s=12.0):
         for n0 in range(0, len(picks), 64):
             chunk = picks[n0:n0 + 64]
             t0 = time.perf_counter()
-            sdpa_ref_rows(q, k, v, runner.scale, s["mask"], s["window"], chunk)
+            sdpa_ref_rows(q, k, v, runner.scale, s["mask"], s["window"], chunk, mask_arr=runner.mask_cpu)
             t_total += time.perf_counter() - t0
             for (_, _, i) in chunk:
                 done_flops += 2 * (s["dqk"] + s["dv"]) * row_visible(i, s)
@@ -435,7 +495,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT, choices=sorted(SHAPES))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--sweep", action="store_true", help="also time every shape of the five workloads")
+    ap.add_argument("--sweep", action="store_true", help="also time every shape of the table")
     ap.add_argument("--sweep-out", default=os.path.join("gpurun_out", "sweep.json"))
     ap.add_argument("--sweep-only", default="", help="comma-separated name prefixes to sweep")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -486,6 +546,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": s["name"], "B": s["b"], "Hq": s["hq"], "Hkv": s["hkv"], "Lq": s["lq"],
                    "Lk": s["lk"], "Dqk": s["dqk"], "Dv": s["dv"], "mask": s["mask"], "window": s["window"],
+                   "mask_array": s["arr"],
                    "kv_sets": res["kv_sets"], "plan": res["plan"]},
         "roofline": {"bound": res["bound"], "achieved": round(res["achieved"], 3), "peak": res["peak"],
                      "unit": res["unit"], "frac": round(res["frac"], 4),

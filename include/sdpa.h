@@ -20,7 +20,8 @@
  * beside the mask mode; its boolean and float kinds are the "bool mask" and
  * "float mask" specialisations of mlx PR #4185's validation comment) may be
  * given on top of the mask mode, through sdpa_forward_masked():
- *   SDPA_MASK_ARRAY_BOOL  one byte per element, nonzero keeps the key;
+ *   SDPA_MASK_ARRAY_BOOL  one byte per element: 1 keeps the key, 0 removes
+ *                         it (a C/C++ bool; no other byte values);
  *   SDPA_MASK_ARRAY_ADD   the q/k/v element type, added to the scaled score
  *                         (natural-log units; -inf removes the key; +inf and
  *                         NaN are not allowed).
@@ -73,7 +74,7 @@ typedef enum {
 
 typedef enum {
   SDPA_MASK_ARRAY_NONE = 0,
-  SDPA_MASK_ARRAY_BOOL = 1,  /* uint8/bool elements, nonzero = keep */
+  SDPA_MASK_ARRAY_BOOL = 1,  /* bool bytes: 1 = keep, 0 = remove */
   SDPA_MASK_ARRAY_ADD = 2    /* q's element type, added to the scaled score */
 } sdpa_mask_array_t;
 

@@ -504,8 +504,10 @@ void attn_fwd_kernel(AttnArgs a) {
   // makes every visible key equally likely: Q = 0 with scale 1 gives exactly
   // that, and masked keys still reach -inf.
   float c = a.c;
+  float sn = a.scale;  // the same factor in natural-log units
   if (c < 0.f) {
     c = -c;
+    sn = -sn;
 #pragma unroll
     for (int s = 0; s < S::NQS; ++s) {
       if constexpr (E::ES == 2) qf[s] ^= 0x80008000u;
@@ -513,6 +515,7 @@ void attn_fwd_kernel(AttnArgs a) {
     }
   } else if (c == 0.f) {
     c = 1.f;
+    sn = 1.f;
 #pragma unroll
     for (int s = 0; s < S::NQS; ++s) {
       if constexpr (E::ES == 2) qf[s] = u32x4{0u, 0u, 0u, 0u};
@@ -520,8 +523,9 @@ void attn_fwd_kernel(AttnArgs a) {
     }
   }
   // Factor from the scores in the accumulators to log2 units.  An additive
-  // mask is applied in log2 units (s c + m log2 e), after which it is 1.
-  const float cs = MA == MA_ADD ? 1.f : c;
+  // mask is added in natural-log units (s scale + m, one fma), after which
+  // the factor is log2 e.
+  const float cs = MA == MA_ADD ? kLog2e : c;
 
   // Loop-invariant parts of the LDS operand addresses (16-bit types).  The
   // K swizzle only involves the lane's row inside a 32-key tile and the V
@@ -628,6 +632,32 @@ void attn_fwd_kernel(AttnArgs a) {
     }
   };
 
+  // ---- does a boolean mask array keep any key of block j for these rows? ----
+  // A block the array removes entirely adds nothing to the softmax: the wave
+  // skips its products and exponentials.  Reads the same elements as
+  // mask_max below; wave-uniform.  Always true otherwise: additive arrays are
+  // mostly dense biases, for which the check would only cost time.
+  auto mask_live = [&](int j) __attribute__((always_inline)) -> bool {
+    if constexpr (MA != MA_BOOL) {
+      return true;
+    } else {
+      const int mrow = wq * 32 + col;
+      const SDPA_LDS char* mt = smem + 2 * S::KBYTES + 2 * S::VBYTES + (j & 1) * S::MBYTES + mrow * S::MROWB;
+      const int sw = S::msw(mrow);
+      bool keep = false;
+#pragma unroll
+      for (int kt = 0; kt < S::NKT; ++kt) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int byte = (wk * BKW + kt * 32 + 8 * g + 4 * hl) * S::MES;
+          const SDPA_LDS char* pa = mt + (((byte >> 4) ^ sw) << 4) + (byte & 15);
+          keep |= *(const SDPA_LDS unsigned*)pa != 0u;
+        }
+      }
+      return __builtin_amdgcn_ballot_w64(keep) != 0;
+    }
+  };
+
   // ---- mask edge blocks and fold the block max into the running max ----
   auto mask_max = [&](int j, f32x16 (&sacc)[S::NKT]) __attribute__((always_inline)) {
     const int kw = blk(j) * S::BK + wk * BKW;  // first key of this wave's slice
@@ -645,10 +675,18 @@ void attn_fwd_kernel(AttnArgs a) {
           const int byte = (wk * BKW + kt * 32 + 8 * g + 4 * hl) * S::MES;
           const SDPA_LDS char* pa = mt + (((byte >> 4) ^ sw) << 4) + (byte & 15);
           if constexpr (MA == MA_BOOL) {
+            // bytes are 0 or 1: bit 0 of byte t, sign-extended, selects
+            // between the score and -inf bit by bit (bfe + bfi)
             const unsigned w = *(const SDPA_LDS unsigned*)pa;
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
-              if (((w >> (8 * t)) & 0xffu) == 0u) sacc[kt][4 * g + t] = kNegInf;
+            for (int t = 0; t < 4; ++t) {
+              const unsigned keep = (unsigned)((int)(w << (31 - 8 * t)) >> 31);
+              // copy out first: a bit cast of a vector element in place
+              // reads element 0 with this compiler
+              const float sv = sacc[kt][4 * g + t];
+              const unsigned sb = __builtin_bit_cast(unsigned, sv);
+              sacc[kt][4 * g + t] = __builtin_bit_cast(float, (sb & keep) | (0xFF800000u & ~keep));
+            }
           } else {
             float mv[4];
             if constexpr (E::ES == 4) {
@@ -663,8 +701,7 @@ void attn_fwd_kernel(AttnArgs a) {
               }
             }
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
-              sacc[kt][4 * g + t] = __builtin_fmaf(sacc[kt][4 * g + t], c, mv[t] * kLog2e);
+            for (int t = 0; t < 4; ++t) sacc[kt][4 * g + t] = __builtin_fmaf(sacc[kt][4 * g + t], sn, mv[t]);
           }
         }
       }
@@ -769,22 +806,31 @@ void attn_fwd_kernel(AttnArgs a) {
     // and part of block j + 1 lands first.)
     constexpr bool KEARLY = 2 * S::DMA_MAX <= 63;
     f32x16 sacc[S::NKT];
+    bool live_prev = true;
     for (int j = 0; j < nblk; ++j) {
       if (j + 1 < nblk) wait_vmcnt<S::DMA_MIN>();  // only block j + 1 may still be in flight
       else wait_vmcnt<0>();
       __syncthreads();  // every wave's share of block j has landed
-      qk(j, sacc);
+      // A boolean array's block is checked every 4th block while blocks are
+      // live and at every block after a removed one: dense masks pay for a
+      // quarter of the checks, a live run costs at most 3 unchecked blocks.
+      bool live = true;
+      if (MA == MA_BOOL && (!live_prev || (j & 3) == 0)) live = mask_live(j);
+      live_prev = live;
+      if (live) qk(j, sacc);
       if constexpr (KEARLY) {
         if (j + 2 < nblk) {
           __syncthreads();  // every wave is done with K(j)
           dma_k(blk(j + 2), j & 1);
         }
       }
-      vfrag_t vf;
-      vhoist(j, vf);  // in flight during the softmax
-      mask_max(j, sacc);
-      expo(sacc);
-      pv(j, sacc, vf);
+      if (live) {
+        vfrag_t vf;
+        vhoist(j, vf);  // in flight during the softmax
+        mask_max(j, sacc);
+        expo(sacc);
+        pv(j, sacc, vf);
+      }
       if (j + 2 < nblk) {
         if constexpr (!KEARLY) wait_vmcnt<63 - S::DMA_MAX>();
         __syncthreads();  // every wave is done with V(j) and the mask tile of j
@@ -802,8 +848,10 @@ void attn_fwd_kernel(AttnArgs a) {
     // their buffers take K(j + 3) and V(j + 2).  Step j waits for K(j + 1)
     // and V(j); what may still be in flight is K(j + 2) and V(j + 1).
     f32x16 sa[S::NKT], sb[S::NKT];
+    bool live_cur = true;  // the mask array keeps a key of the block in `cur`
     if (nblk > 0) {
       __syncthreads();  // block 0 (waited for above) is visible to every wave
+      live_cur = mask_live(0);
       qk(0, sa);
       mask_max(0, sa);
       if (nblk > 2) {
@@ -821,12 +869,27 @@ void attn_fwd_kernel(AttnArgs a) {
       else if (more) wait_vmcnt<S::VDMA / S::NW>();
       else wait_vmcnt<0>();
       __syncthreads();  // K(j + 1) and V(j) have landed for every wave
-      vfrag_t vf;
-      vhoist(j, vf);
-      expo(cur);
-      if (more) qk(j + 1, nxt);
-      pv(j, cur, vf);
-      if (more) mask_max(j + 1, nxt);
+      // The products of block j + 1 always run (they overlap this block's
+      // exponentials); whether the array keeps any of its keys is read here
+      // and decides, in the next step, whether its exponentials and PV
+      // products run.  Constant true without a boolean array.
+      // (checked as in the plain loop: every 4th block, or after a removed one)
+      bool ln = true;
+      if (MA == MA_BOOL && more && (!live_cur || ((j + 1) & 3) == 0)) ln = mask_live(j + 1);
+      if (MA != MA_BOOL || live_cur) {
+        vfrag_t vf;
+        vhoist(j, vf);
+        expo(cur);
+        if (more) qk(j + 1, nxt);
+        pv(j, cur, vf);
+        if (more) mask_max(j + 1, nxt);
+      } else {
+        if (more) {
+          qk(j + 1, nxt);
+          mask_max(j + 1, nxt);
+        }
+      }
+      live_cur = ln;
       if (j + 2 < nblk) {
         __syncthreads();  // every wave is done with K(j + 1), its mask tile and V(j)
         if (j + 3 < nblk) {

@@ -168,6 +168,7 @@ int sdpa_forward_masked(const sdpa_desc_t* d, const void* q, const void* k, cons
   a.mask = p.mask;
   a.window = p.window;
   a.c = (float)((double)d->scale * 1.4426950408889634074);  // log2(e)
+  a.scale = d->scale;
   a.splits = p.splits;
   a.row_tiles = p.row_tiles;
   a.heavy_first = p.mask != sdpa::MASK_NONE && p.row_tiles > 1;

@@ -31,6 +31,7 @@ struct AttnArgs {
   int mask;            // canonical mask kind
   int window;          // window size when mask == MASK_WINDOW
   float c;             // scale * log2(e): scores live in log2 units on the device
+  float scale;         // scale itself (an additive mask is added in natural-log units)
   int splits;          // key splits per row tile (1: normalise in place)
   int row_tiles;       // ceil(R / rows per workgroup)
   int heavy_first;     // causal/window prefill: visit the longest row tiles first

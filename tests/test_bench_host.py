@@ -21,7 +21,7 @@ def test_visible_pairs_closed_form_matches_oracle_count(lq, lk, mask, w):
 
 def test_workload_table_matches_the_five_workloads():
     names = [s["name"] for s in bench.all_shapes()]
-    assert len(names) == 1 + 12 + 20 + 3 + 4
+    assert len(names) == 1 + 12 + 20 + 3 + 4 + 5
     assert bench.DEFAULT in names
     s = bench.SHAPES[bench.DEFAULT]
     assert (s["hq"], s["hkv"], s["lq"], s["lk"], s["dqk"], s["dv"], s["dtype"]) == (64, 8, 1, 32768, 192, 128, "bf16")
@@ -58,3 +58,28 @@ def test_row_sampler_terminates_when_few_rows_exist():
     assert len(pick_rows(1, 64, 1, 64, 3)) == 64
     rows = pick_rows(1, 16, 8192, 64, 5, window=1024)
     assert len(rows) == 64 and all(0 <= i < 8192 for _, _, i in rows)
+
+
+def test_mask_array_workloads():
+    """The window band handed to the kernel is the oracle's window rule; the
+    masked workloads count every pair of their mode and the array's bytes."""
+    import numpy as np
+
+    s = bench.SHAPES["maskarr_window_bool_l4096_d256"]
+    band = bench.make_mask_array(dict(s, lq=300, lk=500, arr_window=64)).numpy()
+    assert (band == visible_mask(300, 500, "window", 64)).all()
+    flops, nbytes = bench.work(s)
+    assert flops == 2 * 16 * 512 * 4096 * 4096
+    assert nbytes == 2 * (16 * 4096 * 512 + 8 * 4096 * 512) + 4096 * 4096
+    assert bench.bound(s) == "mfma"
+    ref = bench.SHAPES["causal_l4096_d128"]
+    s = bench.SHAPES["maskarr_bias_add_causal_l4096_d128"]
+    assert bench.work(s)[0] == bench.work(ref)[0]
+    assert bench.work(s)[1] == bench.work(ref)[1] + 2 * 4096 * 4096
+    s = bench.SHAPES["maskarr_pad_decode_b4_hkv8_lk8192_d128"]
+    pad = bench.make_mask_array(s).numpy()
+    assert pad.shape == (4, 1, 1, 8192) and pad[..., 0].all()
+    lens = pad.sum(axis=-1).ravel()
+    assert (pad == (np.arange(8192)[None, None, None, :] < lens[:, None, None, None])).all()
+    assert bench.bound(s) == "hbm"
+    assert bench.work(s)[1] == bench.work(bench.SHAPES["decode_b4_hkv8_lk8192_d128"])[1] + 4 * 8192

@@ -165,3 +165,17 @@ def test_additive_bias_causal_prefill_sampled():
     L = 2048
     check_sampled(1, 8, 2, L, L, 128, 128, "bf16", "causal", 0, seed=93, nrows=24,
                   attn_mask=additive_mask((1, 8, L, L), 94, torch.bfloat16, sigma=1.0, minus_inf=0.0))
+
+
+@pytest.mark.parametrize("dt,d", [("bf16", 64), ("f16", 128), ("f32", 64), ("bf16", 256)])
+@pytest.mark.parametrize("kind", ["bool", "add"])
+def test_blocks_removed_by_the_array_are_skipped_exactly(dt, d, kind):
+    """A band mask leaves whole key blocks without a kept key (the kernel
+    skips their products): the result still matches the oracle, for the
+    pipelined small-dim loop and the plain loop, both array kinds."""
+    _say("dead blocks", dt, d, kind)
+    L, w = 400, 48
+    band = torch.from_numpy(visible_mask(L, L, "window", w))
+    arr = band if kind == "bool" else torch.where(band, torch.tensor(0.5), torch.tensor(float("-inf"))).to(
+        to_dtype(dt))
+    check_full(1, 2, 1, L, L, d, d, dt, "none", 0, seed=d, attn_mask=arr)
