@@ -21,6 +21,8 @@ from .sdpa_ref import (  # noqa: F401
     visible_mask,
     visible_pairs,
     sdpa_ref,
+    sdpa_ref_varlen,
+    visible_offset,
     sdpa_ref_rows,
     sdpa_probs,
     sdpa_loop,

@@ -35,6 +35,14 @@ What is computed
   empty part.
 * the log-sum-exp of the visible scaled scores, natural log, per query row
   (the output that training needs; mlx PR #4185, API).
+* optional per-batch lengths (``sdpa_ref_varlen``): batch entry b uses its
+  first ``q_lens[b]`` queries and first ``kv_lens[b]`` keys, and its query i
+  sits at key position ``i + kv_lens[b] - q_lens[b]``, the K-relative
+  coordinates of mlx PR #3552 (Implementation: ``qL_off = kL - qL``, which
+  the page notes also serves chunked prefill over a rotated cache) applied to
+  the valid part.  Rows past ``q_lens[b]`` are not part of the result.  A
+  row with no visible key (``kv_lens[b] = 0``, or a causal row placed before
+  the first key) has output 0 and log-sum-exp ``-inf``.
 
 Everything is evaluated in float64 after an exact upcast of the inputs, with
 the full score rows materialised, which is the unfused "matmul -> softmax ->
@@ -89,6 +97,23 @@ def _visible_row(i: int, lq: int, lk: int, mask: str, window: int) -> np.ndarray
     if mask == "none":
         return np.ones(lk, dtype=bool)
     pos = i + (lk - lq)
+    vis = key <= pos
+    if mask == "window":
+        vis &= key > pos - window
+    return vis
+
+
+def visible_offset(lq: int, lk: int, off: int, mask: str = "none", window: int = 0) -> np.ndarray:
+    """Boolean ``[lq, lk]`` visibility when query row i sits at key position
+    ``i + off`` (any integer offset; rows may see no key)."""
+    if mask not in MASK_KINDS:
+        raise ValueError(f"unknown mask kind {mask!r}")
+    if mask == "window" and window < 1:
+        raise ValueError("a sliding window needs window >= 1")
+    if mask == "none":
+        return np.ones((lq, lk), dtype=bool)
+    pos = np.arange(lq, dtype=np.int64)[:, None] + off
+    key = np.arange(lk, dtype=np.int64)[None, :]
     vis = key <= pos
     if mask == "window":
         vis &= key > pos - window
@@ -191,6 +216,50 @@ def sdpa_ref(q, k, v, scale: float, mask: str = "none", window: int = 0, chunk: 
     return o, lse
 
 
+def _lens(lens, n: int, cap: int, name: str) -> np.ndarray:
+    """Per-batch lengths as int64, all of them, or ``cap`` for each entry when absent."""
+    if lens is None:
+        return np.full(n, cap, dtype=np.int64)
+    if hasattr(lens, "detach"):
+        lens = lens.detach().to("cpu").numpy()
+    out = np.asarray(lens, dtype=np.int64).reshape(-1)
+    if out.shape[0] != n or (out < 0).any() or (out > cap).any():
+        raise ValueError(f"{name} must hold {n} lengths in [0, {cap}]")
+    return out
+
+
+def sdpa_ref_varlen(q, k, v, scale: float, mask: str = "none", window: int = 0, q_lens=None,
+                    kv_lens=None, mask_arr=None):
+    """Reference forward with per-batch lengths.  Returns ``(o, lse)`` in
+    float64 with the padded shapes; rows ``i >= q_lens[b]`` are NaN (they are
+    not part of the result).  ``mask_arr`` is indexed in the padded
+    coordinates ``(b, h, i, j)``."""
+    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    b, hq, hkv, lq, lk, dqk, dv = _dims(q, k, v)
+    ql = _lens(q_lens, b, lq, "q_lens")
+    kl = _lens(kv_lens, b, lk, "kv_lens")
+    arr = mask_array(mask_arr, b, hq, lq, lk)
+    group = hq // hkv
+    o = np.full((b, hq, lq, dv), np.nan)
+    lse = np.full((b, hq, lq), np.nan)
+    for bi in range(b):
+        nq, nk = int(ql[bi]), int(kl[bi])
+        vis = visible_offset(nq, nk, nk - nq, mask, window)
+        for h in range(hq):
+            kvh = h // group
+            s = float(scale) * (q[bi, h, :nq] @ k[bi, kvh, :nk].T)
+            s = _apply(s, vis, None if arr is None else arr[bi, h, :nq, :nk])
+            if nk == 0:
+                o[bi, h, :nq] = 0.0
+                lse[bi, h, :nq] = -np.inf
+                continue
+            p, den, m, empty = _softmax_rows(s)
+            with np.errstate(divide="ignore", invalid="ignore"):
+                o[bi, h, :nq] = np.where(empty, 0.0, (p @ v[bi, kvh, :nk]) / den)
+                lse[bi, h, :nq] = np.where(empty, -np.inf, m + np.log(den))[:, 0]
+    return o, lse
+
+
 def sdpa_probs(q, k, scale: float, mask: str = "none", window: int = 0, mask_arr=None) -> np.ndarray:
     """Attention probabilities ``[B, Hq, Lq, Lk]`` (tiny shapes only; an empty row is all 0)."""
     q, k = _as_f64(q), _as_f64(k)
@@ -211,20 +280,26 @@ def sdpa_probs(q, k, scale: float, mask: str = "none", window: int = 0, mask_arr
 
 
 def sdpa_ref_rows(q, k, v, scale: float, mask: str, window: int,
-                  picks: Iterable[Sequence[int]], mask_arr=None):
+                  picks: Iterable[Sequence[int]], mask_arr=None, q_lens=None, kv_lens=None):
     """Reference output for selected rows only, for full-size sampled checks.
 
     ``picks`` holds ``(b, h, i)`` triples.  Returns ``(o_rows [n, Dv],
     lse_rows [n])`` in float64, with the same definition as ``sdpa_ref``.
     ``q``, ``k`` and ``v`` may be torch CPU tensors; only the rows touched are
     upcast.  ``mask_arr`` (optional) broadcasts to ``[B, Hq, Lq, Lk]`` as in
-    ``sdpa_ref``; only the picked rows of it are read.
+    ``sdpa_ref``; only the picked rows of it are read.  ``q_lens`` /
+    ``kv_lens`` (optional) give per-batch lengths as in ``sdpa_ref_varlen``;
+    picked rows must lie below ``q_lens[b]``.
     """
     picks = [tuple(int(t) for t in p) for p in picks]
     b, hq, lq, _ = q.shape
     hkv, lk = k.shape[1], k.shape[2]
     dv = v.shape[3]
-    _check_mask(lq, lk, mask, window)
+    varlen = q_lens is not None or kv_lens is not None
+    if not varlen:
+        _check_mask(lq, lk, mask, window)
+    ql = _lens(q_lens, b, lq, "q_lens")
+    kl = _lens(kv_lens, b, lk, "kv_lens")
     group = hq // hkv
     arr = _mask_rows_view(mask_arr, b, hq, lq, lk)
     o = np.zeros((len(picks), dv), dtype=np.float64)
@@ -235,7 +310,14 @@ def sdpa_ref_rows(q, k, v, scale: float, mask: str, window: int,
         if (bi, kvh) not in cache:
             cache = {(bi, kvh): (_as_f64(k[bi, kvh]), _as_f64(v[bi, kvh]))}
         kk, vv = cache[(bi, kvh)]
-        vis = _visible_row(i, lq, lk, mask, window)
+        if varlen:
+            nq, nk = int(ql[bi]), int(kl[bi])
+            if i >= nq:
+                raise ValueError("a picked row lies past q_lens[b]")
+            vis = np.zeros(lk, dtype=bool)
+            vis[:nk] = visible_offset(1, nk, i + nk - nq, mask, window)[0]
+        else:
+            vis = _visible_row(i, lq, lk, mask, window)
         s = float(scale) * (kk @ _as_f64(q[bi, h, i]))
         s = _apply(s, vis, None if arr is None else arr(bi, h, i))
         keep = np.isfinite(s)
@@ -265,7 +347,8 @@ def _mask_rows_view(mask_arr, b, hq, lq, lk):
     return lambda bi, h, i: arr[bi, h, i]
 
 
-def sdpa_loop(q, k, v, scale: float, mask: str = "none", window: int = 0, mask_arr=None):
+def sdpa_loop(q, k, v, scale: float, mask: str = "none", window: int = 0, mask_arr=None,
+              q_lens=None, kv_lens=None):
     """Second formulation in pure Python loops (tiny shapes only).
 
     Walks each query row over the explicit key index range it may see and
@@ -275,22 +358,27 @@ def sdpa_loop(q, k, v, scale: float, mask: str = "none", window: int = 0, mask_a
     """
     q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
     b, hq, hkv, lq, lk, dqk, dv = _dims(q, k, v)
-    _check_mask(lq, lk, mask, window)
+    varlen = q_lens is not None or kv_lens is not None
+    if not varlen:
+        _check_mask(lq, lk, mask, window)
+    ql = _lens(q_lens, b, lq, "q_lens")
+    kl = _lens(kv_lens, b, lk, "kv_lens")
     arr = mask_array(mask_arr, b, hq, lq, lk)
     group = hq // hkv
-    o = np.zeros((b, hq, lq, dv))
-    lse = np.zeros((b, hq, lq))
+    o = np.full((b, hq, lq, dv), np.nan) if varlen else np.zeros((b, hq, lq, dv))
+    lse = np.full((b, hq, lq), np.nan) if varlen else np.zeros((b, hq, lq))
     for bi in range(b):
+        nq, nk = int(ql[bi]), int(kl[bi])
         for h in range(hq):
             kvh = h // group
-            for i in range(lq):
-                pos = i + lk - lq
+            for i in range(nq):
+                pos = i + nk - nq
                 if mask == "none":
-                    lo, hi = 0, lk - 1
+                    lo, hi = 0, nk - 1
                 elif mask == "causal":
-                    lo, hi = 0, pos
+                    lo, hi = 0, min(pos, nk - 1)
                 else:
-                    lo, hi = max(0, pos - window + 1), pos
+                    lo, hi = max(0, pos - window + 1), min(pos, nk - 1)
                 keys, s = [], []
                 for j in range(lo, hi + 1):
                     sj = float(scale) * math.fsum(q[bi, h, i, d] * k[bi, kvh, j, d] for d in range(dqk))

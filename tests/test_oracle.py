@@ -483,3 +483,109 @@ def test_bad_additive_values_raise():
         arr[1, 1] = bad
         with pytest.raises(ValueError):
             sdpa_ref(q, k, v, 0.5, "none", mask_arr=arr)
+
+
+# ---------------------------------------------------------------------------
+# Per-batch lengths (varlen): batch entry b uses its first q_lens[b] queries
+# and kv_lens[b] keys, query i at key position i + kv_lens[b] - q_lens[b].
+# ---------------------------------------------------------------------------
+
+from oracle import sdpa_ref_varlen, visible_offset  # noqa: E402
+
+VARLEN = [
+    # b, hq, hkv, lq, lk, dqk, dv, mode, window, q_lens, kv_lens
+    (3, 2, 1, 4, 7, 3, 4, "none", 0, [4, 2, 1], [7, 3, 0]),
+    (3, 4, 2, 5, 8, 4, 3, "causal", 0, [5, 3, 4], [8, 5, 2]),
+    (2, 2, 2, 6, 9, 3, 3, "window", 3, [6, 2], [9, 4]),
+    (2, 2, 1, 3, 6, 2, 2, "causal", 0, [3, 1], [6, 6]),
+]
+
+
+@pytest.mark.parametrize("case", VARLEN)
+def test_varlen_matches_loop_brute_force(case):
+    b, hq, hkv, lq, lk, dqk, dv, mode, w, ql, kl = case
+    q, k, v = _case(b, hq, hkv, lq, lk, dqk, dv, seed=600 + lq)
+    o, lse = sdpa_ref_varlen(q, k, v, 0.7, mode, w, ql, kl)
+    o2, l2 = sdpa_loop(q, k, v, 0.7, mode, w, q_lens=ql, kv_lens=kl)
+    np.testing.assert_allclose(o, o2, rtol=0, atol=1e-12)  # NaN rows (past q_lens) match too
+    np.testing.assert_allclose(lse, l2, rtol=0, atol=1e-12)
+    for bi in range(b):
+        assert np.isnan(o[bi, :, ql[bi]:]).all() and not np.isnan(o[bi, :, :ql[bi]]).any()
+
+
+@pytest.mark.parametrize("case", VARLEN)
+def test_varlen_entry_equals_the_unpadded_problem(case):
+    """Each entry with q_lens <= kv_lens equals the plain definition on its
+    valid slices (bottom-right aligned), and padding keys never matter."""
+    b, hq, hkv, lq, lk, dqk, dv, mode, w, ql, kl = case
+    q, k, v = _case(b, hq, hkv, lq, lk, dqk, dv, seed=610 + lq)
+    o, lse = sdpa_ref_varlen(q, k, v, 0.5, mode, w, ql, kl)
+    k2, v2 = k.copy(), v.copy()
+    for bi in range(b):
+        k2[bi, :, kl[bi]:] = 1e3
+        v2[bi, :, kl[bi]:] = -1e3
+        if 0 < ql[bi] <= kl[bi]:
+            so, sl = sdpa_ref(q[bi:bi + 1, :, :ql[bi]], k[bi:bi + 1, :, :kl[bi]], v[bi:bi + 1, :, :kl[bi]],
+                              0.5, mode, w)
+            np.testing.assert_allclose(o[bi:bi + 1, :, :ql[bi]], so, atol=1e-14)
+            np.testing.assert_allclose(lse[bi:bi + 1, :, :ql[bi]], sl, atol=1e-14)
+    o2, l2 = sdpa_ref_varlen(q, k2, v2, 0.5, mode, w, ql, kl)
+    np.testing.assert_array_equal(o2, o)
+    np.testing.assert_array_equal(l2, lse)
+
+
+def test_varlen_matches_torch_cpu_sdpa():
+    """torch's float64 attention per entry, with an explicit boolean mask over
+    the padded key range written out here from the length rule."""
+    b, hq, hkv, lq, lk, d = 3, 4, 2, 5, 9, 4
+    ql, kl = [5, 4, 2], [9, 6, 7]
+    q, k, v = _case(b, hq, hkv, lq, lk, d, d, seed=620)
+    o, _ = sdpa_ref_varlen(q, k, v, 0.45, "window", 3, ql, kl)
+    for bi in range(b):
+        m = np.zeros((lq, lk), dtype=bool)
+        for i in range(ql[bi]):
+            p = i + kl[bi] - ql[bi]
+            for j in range(kl[bi]):
+                m[i, j] = p - 3 < j <= p
+        got = _torch_sdpa(q[bi:bi + 1, :, :ql[bi]], k[bi:bi + 1], v[bi:bi + 1], 0.45, m[:ql[bi]])
+        np.testing.assert_allclose(o[bi:bi + 1, :, :ql[bi]], got, atol=1e-12)
+
+
+def test_varlen_empty_entries_and_rows_before_the_first_key():
+    q, k, v = _case(2, 2, 1, 4, 5, 3, 3, seed=630)
+    # entry 0: no keys at all; entry 1: causal, 4 queries on 2 keys -> the
+    # first two rows sit before key 0 and see nothing
+    o, lse = sdpa_ref_varlen(q, k, v, 0.5, "causal", 0, [3, 4], [0, 2])
+    np.testing.assert_array_equal(o[0, :, :3], 0.0)
+    assert np.isneginf(lse[0, :, :3]).all()
+    np.testing.assert_array_equal(o[1, :, :2], 0.0)
+    assert np.isneginf(lse[1, :, :2]).all()
+    np.testing.assert_allclose(o[1, 0, 2], v[1, 0, 0], atol=1e-15)  # row 2 sees key 0 only
+    assert abs(lse[1, 0, 2] - 0.5 * float(q[1, 0, 2] @ k[1, 0, 0])) < 1e-14
+
+
+def test_varlen_rows_accessor_agrees():
+    q, k, v = _case(2, 4, 2, 6, 9, 4, 4, seed=640)
+    ql, kl = [6, 3], [9, 5]
+    arr = _add_mask((2, 1, 6, 9), 23)
+    arr[..., 0] = 0.0
+    o, lse = sdpa_ref_varlen(q, k, v, 0.5, "causal", 0, ql, kl, mask_arr=arr)
+    picks = [(bi, h, i) for bi in range(2) for h in range(4) for i in range(ql[bi])]
+    orow, lrow = sdpa_ref_rows(q, k, v, 0.5, "causal", 0, picks, mask_arr=arr, q_lens=ql, kv_lens=kl)
+    for n, (bi, h, i) in enumerate(picks):
+        np.testing.assert_allclose(orow[n], o[bi, h, i], atol=1e-13)
+        assert (np.isneginf(lrow[n]) and np.isneginf(lse[bi, h, i])) or abs(lrow[n] - lse[bi, h, i]) < 1e-13
+
+
+def test_visible_offset_generalises_bottom_right():
+    for lq, lk, mode, w in [(4, 9, "causal", 0), (9, 9, "window", 3), (3, 3, "none", 0)]:
+        np.testing.assert_array_equal(visible_offset(lq, lk, lk - lq, mode, w), visible_mask(lq, lk, mode, w))
+    assert not visible_offset(3, 4, -3, "causal").any()  # every row before key 0
+    np.testing.assert_array_equal(visible_offset(2, 4, 1, "causal"), [[1, 1, 0, 0], [1, 1, 1, 0]])
+
+
+def test_bad_lengths_raise():
+    q, k, v = _case(2, 1, 1, 3, 4, 2, 2, seed=650)
+    for ql, kl in [([3, 4], [4, 4]), ([3, 3], [5, 4]), ([3, -1], [4, 4]), ([3], [4])]:
+        with pytest.raises(ValueError):
+            sdpa_ref_varlen(q, k, v, 0.5, "none", 0, ql, kl)
