@@ -148,6 +148,25 @@ int sdpa_forward_masked(const sdpa_desc_t* desc, const void* q, const void* k, c
                         const void* mask, void* o, float* lse, void* workspace,
                         size_t workspace_bytes, sdpa_stream_t stream);
 
+/* Forward pass with per-batch lengths: as sdpa_forward_masked (mask may be
+ * NULL, see there), plus two optional device arrays of desc->batch int32
+ * lengths (4-byte aligned, NULL = the full length for every entry):
+ *   q_lens[b]  in [0, Lq]  queries of entry b (rows i < q_lens[b]);
+ *   kv_lens[b] in [0, Lk]  keys of entry b (keys j < kv_lens[b]).
+ * Entry b's query i sits at key position i + kv_lens[b] - q_lens[b]: the
+ * K-relative coordinates of mlx PR #3552 "feat(fast): add sliding-window SDPA
+ * kernel path" (Implementation) applied to the valid part, which covers
+ * varlen decode and a chunk of queries appended to a cache that holds its own
+ * keys first (kv_lens = cached + chunk).  Keys j >= kv_lens[b] are never
+ * read.  Rows i >= q_lens[b] of o and lse are not written.  A row with no
+ * visible key (kv_lens[b] = 0, or a causal row placed before key 0 when
+ * q_lens[b] > kv_lens[b]) gets o = 0 and lse = -inf.  The arrays are read on
+ * the device only; values outside the stated ranges are clamped into them.
+ * The plan (splits, tiles, workspace) follows desc's padded Lq and Lk. */
+int sdpa_forward_varlen(const sdpa_desc_t* desc, const void* q, const void* k, const void* v,
+                        const void* mask, const int32_t* q_lens, const int32_t* kv_lens, void* o,
+                        float* lse, void* workspace, size_t workspace_bytes, sdpa_stream_t stream);
+
 /* Writes a one-line, NUL-terminated description of the plan (kernel family,
  * tile, splits, grid, workspace) into buf.  Host only. */
 int sdpa_describe_plan(const sdpa_desc_t* desc, char* buf, size_t len);

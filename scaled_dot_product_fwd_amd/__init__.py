@@ -20,11 +20,11 @@ from ._lib import (SDPA_BF16, SDPA_F16, SDPA_F32, SDPA_MASK_ARRAY_ADD,  # noqa: 
                    SDPA_MASK_ARRAY_BOOL, SDPA_MASK_ARRAY_NONE, SDPA_MASK_CAUSAL, SDPA_MASK_NONE,
                    SDPA_MASK_WINDOW, SdpaError, SdpaRuntimeError, SdpaValueError, load,
                    sdpa_desc_init, sdpa_desc_t, sdpa_describe_plan, sdpa_forward,
-                   sdpa_forward_masked, sdpa_last_error, sdpa_set_profile_events,
-                   sdpa_workspace_bytes)
+                   sdpa_forward_masked, sdpa_forward_varlen, sdpa_last_error,
+                   sdpa_set_profile_events, sdpa_workspace_bytes)
 
 __all__ = ["forward", "make_desc", "plan_for", "workspace_for", "pad_mask", "sdpa_forward",
-           "sdpa_forward_masked", "sdpa_workspace_bytes", "sdpa_describe_plan", "sdpa_last_error",
+           "sdpa_forward_masked", "sdpa_forward_varlen", "sdpa_workspace_bytes", "sdpa_describe_plan", "sdpa_last_error",
            "sdpa_desc_init", "sdpa_set_profile_events",
            "SdpaError", "SdpaValueError", "SdpaRuntimeError"]
 
@@ -149,7 +149,8 @@ def workspace_for(desc: sdpa_desc_t) -> int:
 
 
 def forward(q, k, v, *, scale: Optional[float] = None, mask: str = "none", window_size: int = 0,
-            attn_mask=None, return_lse: bool = False, num_splits: int = 0, row_tile: int = 0,
+            attn_mask=None, q_lens=None, kv_lens=None, return_lse: bool = False,
+            num_splits: int = 0, row_tile: int = 0,
             out=None, lse_out=None, workspace=None, stream=None
             ) -> Union["torch.Tensor", Tuple["torch.Tensor", "torch.Tensor"]]:  # noqa: F821
     """Fused attention forward on the current HIP device.
@@ -163,7 +164,11 @@ def forward(q, k, v, *, scale: Optional[float] = None, mask: str = "none", windo
     must hold only 0 and 1), q's dtype is added
     to the scaled scores; it applies on top of ``mask``.  Its rows must start
     on 16-byte boundaries and be readable up to Lk rounded up to 16 bytes
-    (``pad_mask`` prepares such a copy).  Returns ``o`` (and the float32
+    (``pad_mask`` prepares such a copy).  ``q_lens`` / ``kv_lens``
+    (optional int32 device tensors ``[B]``) give each batch entry's valid
+    queries and keys: entry b's query i sits at key position
+    ``i + kv_lens[b] - q_lens[b]``, keys past ``kv_lens[b]`` are never read,
+    and rows past ``q_lens[b]`` of the outputs are not written.  Returns ``o`` (and the float32
     log-sum-exp ``[B,Hq,Lq]`` when ``return_lse``).  Validation errors raise
     ``SdpaValueError`` (a ``ValueError``) naming the constraint.
     """
@@ -212,8 +217,17 @@ def forward(q, k, v, *, scale: Optional[float] = None, mask: str = "none", windo
     ws_len = workspace.numel() * workspace.element_size() if ws_ptr else 0
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
+    lens = []
+    for name, t in (("q_lens", q_lens), ("kv_lens", kv_lens)):
+        if t is None:
+            lens.append(0)
+            continue
+        if (not isinstance(t, torch.Tensor) or t.dtype != torch.int32 or t.dim() != 1 or t.shape[0] != b
+                or not t.is_contiguous() or t.device != q.device):
+            raise SdpaValueError(f"SDPA_E_SHAPE: {name} must be a contiguous int32 [B] tensor on q's device")
+        lens.append(t.data_ptr())
     with torch.cuda.device(q.device):
-        sdpa_forward_masked(desc, q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                            attn_mask.data_ptr() if attn_mask is not None else 0, out.data_ptr(),
-                            lse.data_ptr() if lse is not None else 0, ws_ptr, ws_len, stream)
+        sdpa_forward_varlen(desc, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                            attn_mask.data_ptr() if attn_mask is not None else 0, lens[0], lens[1],
+                            out.data_ptr(), lse.data_ptr() if lse is not None else 0, ws_ptr, ws_len, stream)
     return (out, lse) if return_lse else out

@@ -33,7 +33,7 @@ STATUS = {
 STATUS_CODE = {v: k for k, v in STATUS.items()}
 
 EXPORTED = ("sdpa_desc_init", "sdpa_workspace_bytes", "sdpa_forward", "sdpa_forward_masked",
-            "sdpa_describe_plan", "sdpa_set_profile_events", "sdpa_last_error")
+            "sdpa_forward_varlen", "sdpa_describe_plan", "sdpa_set_profile_events", "sdpa_last_error")
 
 
 class sdpa_desc_t(ctypes.Structure):
@@ -104,6 +104,9 @@ def load() -> ctypes.CDLL:
                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                         ctypes.c_size_t, ctypes.c_void_p]
     lib.sdpa_forward_masked.restype = ctypes.c_int
+    lib.sdpa_forward_varlen.argtypes = [P(sdpa_desc_t)] + [ctypes.c_void_p] * 9 + [ctypes.c_size_t,
+                                                                                    ctypes.c_void_p]
+    lib.sdpa_forward_varlen.restype = ctypes.c_int
     lib.sdpa_describe_plan.argtypes = [P(sdpa_desc_t), ctypes.c_char_p, ctypes.c_size_t]
     lib.sdpa_describe_plan.restype = ctypes.c_int
     lib.sdpa_set_profile_events.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
@@ -167,3 +170,12 @@ def sdpa_forward_masked(desc: sdpa_desc_t, q: int, k: int, v: int, mask: int | N
     """Raw call with an explicit mask array; raises on a non-zero status."""
     check(load().sdpa_forward_masked(ctypes.byref(desc), q, k, v, mask or None, o, lse or None,
                                      workspace or None, workspace_bytes, stream or None))
+
+
+def sdpa_forward_varlen(desc: sdpa_desc_t, q: int, k: int, v: int, mask: int | None,
+                        q_lens: int | None, kv_lens: int | None, o: int, lse: int | None,
+                        workspace: int | None, workspace_bytes: int, stream: int | None) -> None:
+    """Raw call with per-batch lengths (device int32 arrays); raises on a non-zero status."""
+    check(load().sdpa_forward_varlen(ctypes.byref(desc), q, k, v, mask or None, q_lens or None,
+                                     kv_lens or None, o, lse or None, workspace or None,
+                                     workspace_bytes, stream or None))

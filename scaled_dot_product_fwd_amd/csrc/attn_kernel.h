@@ -318,25 +318,39 @@ void attn_fwd_kernel(AttnArgs a) {
   const int b = z / a.Hkv;
   const int kvh = z % a.Hkv;
 
+  // ---- this batch entry's lengths ----
+  // With per-batch lengths, entry b uses its first Lq queries and Lk keys
+  // and query i sits at key position i + Lk - Lq: the K-relative coordinates
+  // of mlx PR #3552 "feat(fast): add sliding-window SDPA kernel path"
+  // (Implementation) applied to the valid part.  A tile wholly past the
+  // entry's queries has nothing to do (uniform: before any barrier or DMA).
+  int Lk = a.Lk, Lq = a.Lq;
+  if (a.kv_lens) Lk = min(max(a.kv_lens[b], 0), a.Lk);
+  if (a.q_lens) Lq = min(max(a.q_lens[b], 0), a.Lq);
+  const int R = a.G * Lq;  // packed rows of this entry
+  const int off = Lk - Lq;
+
   // ---- rows of this lane / wave / workgroup ----
   const int r_wg = rt * S::BM;
+  if (r_wg >= R) return;
   const int r_wave = r_wg + wq * 32;
   const int r = r_wave + col;
-  const bool row_ok = r < a.R;
+  const bool row_ok = r < R;
   const int iq = r / a.G;
-  const int pos = iq + a.off;  // absolute key position of this row's query
+  const int pos = iq + off;  // key position of this row's query
   const int hq = kvh * a.G + r % a.G;
 
-  const int r_last_wg = min(a.R, r_wg + S::BM) - 1;
-  const int pmin_wg = r_wg / a.G + a.off;
-  const int pmax_wg = r_last_wg / a.G + a.off;
-  const int r_last_wave = min(a.R - 1, r_wave + 31);
-  const int pmin_w = min(r_wave, a.R - 1) / a.G + a.off;
-  const int pmax_w = r_last_wave / a.G + a.off;
+  const int r_last_wg = min(R, r_wg + S::BM) - 1;
+  const int pmin_wg = r_wg / a.G + off;
+  const int pmax_wg = r_last_wg / a.G + off;
+  const int r_last_wave = min(R - 1, r_wave + 31);
+  const int pmin_w = min(r_wave, R - 1) / a.G + off;
+  const int pmax_w = r_last_wave / a.G + off;
 
   // ---- key block range of the tile, then of this split ----
-  int k_lo = 0, k_hi = a.Lk;
-  if (a.mask != MASK_NONE) k_hi = min(a.Lk, pmax_wg + 1);
+  // (a causal tile placed before the first key gets an empty range)
+  int k_lo = 0, k_hi = Lk;
+  if (a.mask != MASK_NONE) k_hi = min(Lk, pmax_wg + 1);
   if (a.mask == MASK_WINDOW) k_lo = max(0, pmin_wg - a.window + 1);
   const int kb_first = k_lo / S::BK;
   const int kb_end = (k_hi + S::BK - 1) / S::BK;
@@ -395,7 +409,7 @@ void attn_fwd_kernel(AttnArgs a) {
   auto dma_k = [&](int blk, int buf) __attribute__((always_inline)) {
     const int k0 = blk * S::BK;
     const unsigned kl = lds_base + buf * S::KBYTES;
-    if (k0 + S::BK <= a.Lk) {
+    if (k0 + S::BK <= Lk) {
       const char* kb = kbase + (int64_t)k0 * kstr;
 #pragma unroll
       for (int ii = 0; ii < KPW; ++ii)
@@ -407,7 +421,7 @@ void attn_fwd_kernel(AttnArgs a) {
         if ((ii + 1) * S::NW > S::KDMA && ii * S::NW + wave_u >= S::KDMA) continue;
         int row, colb;
         kslot((ii * S::NW + wave_u) * 64 + lane, row, colb);
-        const int grow = min(k0 + row, a.Lk - 1);
+        const int grow = min(k0 + row, Lk - 1);
         lds_dma16<S::STREAM>(kbase + (int64_t)grow * kstr + colb, kl + (ii * S::NW + wave_u) * 1024);
       }
     }
@@ -415,7 +429,7 @@ void attn_fwd_kernel(AttnArgs a) {
   auto dma_v = [&](int blk, int buf) __attribute__((always_inline)) {
     const int k0 = blk * S::BK;
     const unsigned vl = lds_base + 2 * S::KBYTES + buf * S::VBYTES;
-    if (k0 + S::BK <= a.Lk) {
+    if (k0 + S::BK <= Lk) {
       const char* vb = vbase + (int64_t)k0 * vstr;
 #pragma unroll
       for (int ii = 0; ii < VPW; ++ii)
@@ -427,7 +441,7 @@ void attn_fwd_kernel(AttnArgs a) {
         if ((ii + 1) * S::NW > S::VDMA && ii * S::NW + wave_u >= S::VDMA) continue;
         int row, colb;
         vslot((ii * S::NW + wave_u) * 64 + lane, row, colb);
-        const int grow = min(k0 + row, a.Lk - 1);
+        const int grow = min(k0 + row, Lk - 1);
         lds_dma16<S::STREAM>(vbase + (int64_t)grow * vstr + colb, vl + (ii * S::NW + wave_u) * 1024);
       }
     }
@@ -447,7 +461,7 @@ void attn_fwd_kernel(AttnArgs a) {
       const int sl = (ii * S::NW + wave_u) * 64 + lane;
       const int row = sl / S::MNS;
       mls[ii] = (sl % S::MNS) ^ S::msw(row);
-      const int pr = min(r_wg + row, a.R - 1);
+      const int pr = min(r_wg + row, R - 1);
       const int hr = kvh * a.G + pr % a.G;
       mptr[ii] = (const char*)a.mask_arr +
                  ((int64_t)b * a.ms[0] + (int64_t)hr * a.ms[1] + (int64_t)(pr / a.G) * a.ms[2]) * S::MES +
@@ -459,8 +473,8 @@ void attn_fwd_kernel(AttnArgs a) {
       const int k0 = blk * S::BK;
       const unsigned ml = lds_base + 2 * S::KBYTES + 2 * S::VBYTES + buf * S::MBYTES;
       const int64_t kb = (int64_t)k0 * S::MES;
-      const bool tail = k0 + S::BK > a.Lk;
-      const int lmax = tail ? ((a.Lk - 1 - k0) * S::MES) >> 4 : S::MNS;
+      const bool tail = k0 + S::BK > Lk;
+      const int lmax = tail ? ((Lk - 1 - k0) * S::MES) >> 4 : S::MNS;
 #pragma unroll
       for (int ii = 0; ii < MPW; ++ii) {
         if ((ii + 1) * S::NW > S::MDMA && ii * S::NW + wave_u >= S::MDMA) continue;
@@ -707,12 +721,12 @@ void attn_fwd_kernel(AttnArgs a) {
       }
     }
     // edge blocks: the diagonal, a window edge, the Lk tail
-    const bool edge = (kw + BKW > a.Lk) || (a.mask != MASK_NONE && kw + BKW - 1 > pmin_w) ||
+    const bool edge = (kw + BKW > Lk) || (a.mask != MASK_NONE && kw + BKW - 1 > pmin_w) ||
                       (a.mask == MASK_WINDOW && kw <= pmax_w - a.window);
     if (edge) {
       // Visible keys of this row form [lo, hi]; key of register e in tile kt
       // is kw + 32 kt + 4 hl + off(e) with off(e) = 8 (e / 4) + e % 4.
-      int hi = a.Lk - 1, lo = 0;
+      int hi = Lk - 1, lo = 0;
       if (a.mask != MASK_NONE) hi = min(hi, pos);
       if (a.mask == MASK_WINDOW) lo = max(lo, pos - a.window + 1);
 #pragma unroll
@@ -985,8 +999,9 @@ void attn_fwd_kernel(AttnArgs a) {
 
   if (!row_ok) return;
   if (a.splits == 1) {
-    // l = 0 only for a row that a mask array left without keys: it writes 0
-    const float inv = (MA == MA_NONE || l_row > 0.f) ? 1.0f / l_row : 0.f;
+    // l = 0 only for a row left without keys (by a mask array or its
+    // entry's lengths): it writes 0 and lse = -inf
+    const float inv = l_row > 0.f ? 1.0f / l_row : 0.f;
     char* orow = (char*)a.o + ((int64_t)b * a.os[0] + (int64_t)hq * a.os[1] + (int64_t)iq * a.os[2]) * E::ES;
 #pragma unroll
     for (int t = 0; t < S::NDT; ++t) {

@@ -36,6 +36,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a)
   const int z = row / a.R, r = row % a.R;
   const int b = z / a.Hkv, kvh = z % a.Hkv;
   const int g = r % a.G, i = r / a.G, h = kvh * a.G + g;
+  if (a.q_lens && i >= min(max(a.q_lens[b], 0), a.Lq)) return;  // past the entry's queries: not written
   const float* ml = a.ws_ml + (int64_t)row * a.splits * 2;
   const int tid = threadIdx.x;
   const int nc = a.dv / 4;              // 4-column groups: dv % 8 == 0, dv <= 4 * threads

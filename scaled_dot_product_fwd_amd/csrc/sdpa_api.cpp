@@ -113,8 +113,9 @@ int sdpa_describe_plan(const sdpa_desc_t* d, char* buf, size_t len) {
   return ok();
 }
 
-int sdpa_forward_masked(const sdpa_desc_t* d, const void* q, const void* k, const void* v, const void* mask,
-                        void* o, float* lse, void* workspace, size_t workspace_bytes, sdpa_stream_t stream) {
+int sdpa_forward_varlen(const sdpa_desc_t* d, const void* q, const void* k, const void* v, const void* mask,
+                        const int32_t* q_lens, const int32_t* kv_lens, void* o, float* lse, void* workspace,
+                        size_t workspace_bytes, sdpa_stream_t stream) {
   hipEvent_t ev_start = g_prof_start, ev_stop = g_prof_stop;  // consumed by this call
   g_prof_start = g_prof_stop = nullptr;
   if (!q || !k || !v || !o) return set_error(SDPA_E_NULL, "q, k, v and o must be non-NULL device pointers");
@@ -130,6 +131,9 @@ int sdpa_forward_masked(const sdpa_desc_t* d, const void* q, const void* k, cons
     return set_error(SDPA_E_STRIDE, "q, k, v, o and mask must be 16-byte aligned");
   if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u))
     return set_error(SDPA_E_STRIDE, "lse must be 4-byte aligned");
+  if ((q_lens && (reinterpret_cast<uintptr_t>(q_lens) & 3u)) ||
+      (kv_lens && (reinterpret_cast<uintptr_t>(kv_lens) & 3u)))
+    return set_error(SDPA_E_STRIDE, "q_lens and kv_lens must be 4-byte aligned");
   if (p.workspace > 0) {
     if (!workspace || workspace_bytes < p.workspace)
       return set_error(SDPA_E_WORKSPACE, "the plan needs a workspace of " + std::to_string(p.workspace) +
@@ -148,6 +152,8 @@ int sdpa_forward_masked(const sdpa_desc_t* d, const void* q, const void* k, cons
   a.o = o;
   a.lse = lse;
   a.mask_arr = mask;
+  a.q_lens = q_lens;
+  a.kv_lens = kv_lens;
   for (int j = 0; j < 3; ++j) {
     a.qs[j] = d->q_stride[j];
     a.ks[j] = d->k_stride[j];
@@ -164,7 +170,6 @@ int sdpa_forward_masked(const sdpa_desc_t* d, const void* q, const void* k, cons
   a.dv = (int)d->dim_v;
   a.G = (int)(d->heads_q / d->heads_kv);
   a.R = a.G * a.Lq;
-  a.off = a.Lk - a.Lq;
   a.mask = p.mask;
   a.window = p.window;
   a.c = (float)((double)d->scale * 1.4426950408889634074);  // log2(e)
@@ -204,6 +209,7 @@ int sdpa_forward_masked(const sdpa_desc_t* d, const void* q, const void* k, cons
     c.ws_ml = a.ws_ml;
     c.o = o;
     c.lse = lse;
+    c.q_lens = q_lens;
     for (int j = 0; j < 3; ++j) c.os[j] = d->o_stride[j];
     c.B = a.B;
     c.Hq = a.Hq;
@@ -219,13 +225,18 @@ int sdpa_forward_masked(const sdpa_desc_t* d, const void* q, const void* k, cons
   return ok();
 }
 
+int sdpa_forward_masked(const sdpa_desc_t* d, const void* q, const void* k, const void* v, const void* mask,
+                        void* o, float* lse, void* workspace, size_t workspace_bytes, sdpa_stream_t stream) {
+  return sdpa_forward_varlen(d, q, k, v, mask, nullptr, nullptr, o, lse, workspace, workspace_bytes, stream);
+}
+
 int sdpa_forward(const sdpa_desc_t* d, const void* q, const void* k, const void* v, void* o, float* lse,
                  void* workspace, size_t workspace_bytes, sdpa_stream_t stream) {
   if (d && d->mask_array != SDPA_MASK_ARRAY_NONE) {
     g_prof_start = g_prof_stop = nullptr;
     return set_error(SDPA_E_MASK, "desc names a mask array: call sdpa_forward_masked with the array");
   }
-  return sdpa_forward_masked(d, q, k, v, nullptr, o, lse, workspace, workspace_bytes, stream);
+  return sdpa_forward_varlen(d, q, k, v, nullptr, nullptr, nullptr, o, lse, workspace, workspace_bytes, stream);
 }
 
 int sdpa_set_profile_events(void* start, void* stop) {

@@ -23,11 +23,12 @@ struct AttnArgs {
   float* ws_o;         // split partial outputs [z][r][split][dv] (unnormalised)
   float* ws_ml;        // split partial (m, l) pairs [z][r][split][2], m in log2 units
   const void* mask_arr; // explicit mask array (kernels instantiated for one)
+  const int* q_lens;   // nullable [B]: valid queries per batch entry
+  const int* kv_lens;  // nullable [B]: valid keys per batch entry
   int64_t qs[3], ks[3], vs[3], os[3];  // element strides of (batch, head, position)
   int64_t ms[3];       // mask array element strides of (batch, query head, query)
   int B, Hq, Hkv, Lq, Lk, dqk, dv, G;
   int R;               // packed rows per KV head = G * Lq; row r -> (g = r % G, i = r / G)
-  int off;             // Lk - Lq: absolute key position of query row i is i + off
   int mask;            // canonical mask kind
   int window;          // window size when mask == MASK_WINDOW
   float c;             // scale * log2(e): scores live in log2 units on the device
@@ -44,6 +45,7 @@ struct CombineArgs {
   const float* ws_ml;
   void* o;
   float* lse;
+  const int* q_lens;  // nullable [B]: rows past an entry's queries are skipped
   int64_t os[3];
   int B, Hq, Hkv, Lq, dv, G, R, splits;
 };

@@ -299,3 +299,11 @@ def test_mask_layout_host_checks():
         sdpa._mask_layout(good[:4], q, 2, 4, 5, 13)
     with pytest.raises(sdpa.SdpaValueError, match="dtype"):
         sdpa._mask_layout(torch.zeros(5, 16, dtype=torch.float32), q, 2, 4, 5, 16)
+
+
+def test_varlen_length_arrays_must_be_aligned():
+    d = _desc()
+    msg = _status(sdpa.sdpa_forward_varlen, d, 16, 16, 16, None, 18, None, 16, None, None, 0, None)
+    assert msg.startswith("SDPA_E_STRIDE") and "q_lens" in msg
+    msg = _status(sdpa.sdpa_forward_varlen, d, 16, 16, 16, None, None, 22, 16, None, None, 0, None)
+    assert msg.startswith("SDPA_E_STRIDE") and "kv_lens" in msg
