@@ -55,14 +55,16 @@ PAGES_DECODE_US = {(4, 256): 218, (4, 1024): 217, (4, 4096): 255, (4, 8192): 305
                    (8, 16384): 444, (8, 32768): 728}
 
 
-def shape(name, b, hq, hkv, lq, lk, dqk, dv, dtype, mask, window, seed, arr=None, arr_window=0):
+def shape(name, b, hq, hkv, lq, lk, dqk, dv, dtype, mask, window, seed, arr=None, arr_window=0,
+          varlen=False):
     """One benchmark shape.  ``arr`` names an explicit mask array given on top
     of the mode: "window_bool" (an [Lq, Lk] boolean band of the last
     ``arr_window`` keys, what callers build without a window mode),
     "bias_add" (an [Lq, Lk] additive N(0, 1) bias) or "pad_bool" (a
-    [B, 1, 1, Lk] key-padding mask)."""
+    [B, 1, 1, Lk] key-padding mask).  ``varlen`` passes the same per-entry
+    key lengths as "pad_bool" uses as kv_lens instead."""
     return dict(name=name, b=b, hq=hq, hkv=hkv, lq=lq, lk=lk, dqk=dqk, dv=dv, dtype=dtype,
-                mask=mask, window=window, seed=seed, arr=arr, arr_window=arr_window)
+                mask=mask, window=window, seed=seed, arr=arr, arr_window=arr_window, varlen=varlen)
 
 
 def all_shapes():
@@ -94,6 +96,12 @@ def all_shapes():
     out.append(shape("decode_b4_hkv8_lk8192_d128", 4, 32, 8, 1, 8192, 128, 128, "bf16", "none", 0, 6002))
     out.append(shape("maskarr_pad_decode_b4_hkv8_lk8192_d128", 4, 32, 8, 1, 8192, 128, 128, "bf16", "none", 0,
                      6002, arr="pad_bool"))
+    # per-entry key lengths, beside the same lengths as a padding mask
+    out.append(shape("decode_b8_hkv8_lk8192_d128", 8, 32, 8, 1, 8192, 128, 128, "bf16", "none", 0, 7000))
+    out.append(shape("maskarr_pad_decode_b8_hkv8_lk8192_d128", 8, 32, 8, 1, 8192, 128, 128, "bf16", "none", 0,
+                     7000, arr="pad_bool"))
+    out.append(shape("varlen_decode_b8_hkv8_lk8192_d128", 8, 32, 8, 1, 8192, 128, 128, "bf16", "none", 0, 7000,
+                     varlen=True))
     return out
 
 
@@ -137,17 +145,34 @@ def mask_array_bytes(s):
     return s["lq"] * s["lk"] * (1 if arr == "window_bool" else ES[s["dtype"]])
 
 
+def kv_lengths(s):
+    """Per-entry key lengths of a shape with a padding mask or varlen (else None)."""
+    if s.get("arr") != "pad_bool" and not s.get("varlen"):
+        return None
+    from scaled_dot_product_fwd_amd.synth import lengths
+
+    return [int(x) for x in lengths(s["b"], s["lk"] // 4, s["lk"], s["seed"] + 3)]
+
+
 def work(s):
     """(algorithmic flops, algorithmic bytes) of one call.
 
     With a mask array every pair the mode keeps is evaluated: the array is
     data, so which of its blocks are empty is not known ahead of the call.
-    Its distinct elements count once in the bytes.
+    Its distinct elements count once in the bytes.  With per-entry lengths
+    only each entry's valid keys count.
     """
-    pairs = visible_pairs(s["lq"], s["lk"], s["mask"], s["window"])
-    flops = 2 * s["b"] * s["hq"] * (s["dqk"] + s["dv"]) * pairs
     es = ES[s["dtype"]]
-    nbytes = es * s["b"] * (s["hq"] * s["lq"] * (s["dqk"] + s["dv"]) + s["hkv"] * s["lk"] * (s["dqk"] + s["dv"]))
+    d = s["dqk"] + s["dv"]
+    if s.get("varlen"):
+        kl = kv_lengths(s)
+        pairs = sum(visible_pairs(s["lq"], n, s["mask"], s["window"]) for n in kl)
+        flops = 2 * s["hq"] * d * pairs
+        nbytes = es * (s["b"] * s["hq"] * s["lq"] * d + s["hkv"] * sum(kl) * d)
+        return flops, nbytes
+    pairs = visible_pairs(s["lq"], s["lk"], s["mask"], s["window"])
+    flops = 2 * s["b"] * s["hq"] * d * pairs
+    nbytes = es * s["b"] * (s["hq"] * s["lq"] * d + s["hkv"] * s["lk"] * d)
     return flops, nbytes + mask_array_bytes(s)
 
 
@@ -161,7 +186,7 @@ def make_mask_array(s):
     if arr is None:
         return None
     if arr == "pad_bool":
-        return padding_mask(s["b"], s["lk"], s["seed"] + 3, min_len=s["lk"] // 4)
+        return padding_mask(s["b"], s["lk"], s["seed"] + 3, min_len=s["lk"] // 4)  # lengths as kv_lengths(s)
     if arr == "bias_add":
         return additive_mask((s["lq"], s["lk"]), s["seed"] + 3, torch.bfloat16 if s["dtype"] == "bf16" else
                              (torch.float16 if s["dtype"] == "f16" else torch.float32), sigma=1.0, minus_inf=0.0)
@@ -254,12 +279,16 @@ class Runner:
         self.ws_bytes = sdpa.sdpa_workspace_bytes(self.desc)
         self.ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=dev)
         self.stream = torch.cuda.current_stream(dev).cuda_stream
+        self.kv_lens = None
+        if s.get("varlen"):
+            self.kv_lens = torch.tensor(kv_lengths(s), dtype=torch.int32, device=dev)
         lib = sdpa.load()
-        self._fwd = lib.sdpa_forward_masked
+        self._fwd = lib.sdpa_forward_varlen
         self._prof = lib.sdpa_set_profile_events
         self._descref = ctypes.byref(self.desc)
         mptr = self.mask.data_ptr() if self.mask is not None else None
-        self._args = [(self.q.data_ptr(), k_.data_ptr(), v_.data_ptr(), mptr, self.o.data_ptr(),
+        kvl = self.kv_lens.data_ptr() if self.kv_lens is not None else None
+        self._args = [(self.q.data_ptr(), k_.data_ptr(), v_.data_ptr(), mptr, None, kvl, self.o.data_ptr(),
                        self.lse.data_ptr(), self.ws.data_ptr() if self.ws_bytes else None, self.ws_bytes,
                        self.stream)
                       for k_, v_ in self.kv]
@@ -317,7 +346,7 @@ def cpu_baseline(s, runner, budget_s=12.0):
     budget, evenly spaced query rows are recomputed one by one instead.  The
     work done is scaled to the metric's unit.
     """
-    from oracle import sdpa_ref, sdpa_ref_rows
+    from oracle import sdpa_ref, sdpa_ref_rows, sdpa_ref_varlen
 
     try:
         from threadpoolctl import threadpool_info
@@ -336,8 +365,12 @@ def cpu_baseline(s, runner, budget_s=12.0):
             kvh = (heads // g) % s["hkv"]
             hs = slice(kvh * g, (kvh + 1) * g)
             t0 = time.perf_counter()
-            sdpa_ref(q[:, hs], k[:, kvh:kvh + 1], v[:, kvh:kvh + 1], runner.scale, s["mask"], s["window"],
-                     mask_arr=runner.mask_cpu)
+            if s.get("varlen"):
+                sdpa_ref_varlen(q[:, hs], k[:, kvh:kvh + 1], v[:, kvh:kvh + 1], runner.scale, s["mask"],
+                                s["window"], kv_lens=kv_lengths(s))
+            else:
+                sdpa_ref(q[:, hs], k[:, kvh:kvh + 1], v[:, kvh:kvh + 1], runner.scale, s["mask"], s["window"],
+                         mask_arr=runner.mask_cpu)
             t_total += time.perf_counter() - t0
             heads += g
         frac = heads / s["hq"]
@@ -353,7 +386,8 @@ def cpu_baseline(s, runner, budget_s=12.0):
         for n0 in range(0, len(picks), 64):
             chunk = picks[n0:n0 + 64]
             t0 = time.perf_counter()
-            sdpa_ref_rows(q, k, v, runner.scale, s["mask"], s["window"], chunk, mask_arr=runner.mask_cpu)
+            sdpa_ref_rows(q, k, v, runner.scale, s["mask"], s["window"], chunk, mask_arr=runner.mask_cpu,
+                          kv_lens=kv_lengths(s) if s.get("varlen") else None)
             t_total += time.perf_counter() - t0
             for (_, _, i) in chunk:
                 done_flops += 2 * (s["dqk"] + s["dv"]) * row_visible(i, s)
@@ -546,7 +580,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": s["name"], "B": s["b"], "Hq": s["hq"], "Hkv": s["hkv"], "Lq": s["lq"],
                    "Lk": s["lk"], "Dqk": s["dqk"], "Dv": s["dv"], "mask": s["mask"], "window": s["window"],
-                   "mask_array": s["arr"],
+                   "mask_array": s["arr"], "kv_lens": kv_lengths(s) if s.get("varlen") else None,
                    "kv_sets": res["kv_sets"], "plan": res["plan"]},
         "roofline": {"bound": res["bound"], "achieved": round(res["achieved"], 3), "peak": res["peak"],
                      "unit": res["unit"], "frac": round(res["frac"], 4),

@@ -55,10 +55,15 @@ def additive_mask(shape, seed: int, dtype: torch.dtype, sigma: float = 2.0,
     return vals.masked_fill(drop, float("-inf")).to(dtype)
 
 
-def padding_mask(b: int, lk: int, seed: int, min_len: int = 1) -> torch.Tensor:
-    """CPU key-padding mask ``[b, 1, 1, lk]``: batch row n keeps its first
-    len_n keys, len_n drawn uniformly from [min_len, lk]."""
+def lengths(n: int, lo: int, hi: int, seed: int) -> torch.Tensor:
+    """CPU int32 ``[n]``: lengths drawn uniformly from [lo, hi]."""
     g = torch.Generator(device="cpu")
     g.manual_seed(int(seed))
-    lens = torch.randint(min_len, lk + 1, (b,), generator=g)
+    return torch.randint(lo, hi + 1, (n,), generator=g).to(torch.int32)
+
+
+def padding_mask(b: int, lk: int, seed: int, min_len: int = 1) -> torch.Tensor:
+    """CPU key-padding mask ``[b, 1, 1, lk]``: batch row n keeps its first
+    len_n keys, the lengths being ``lengths(b, min_len, lk, seed)``."""
+    lens = lengths(b, min_len, lk, seed).to(torch.int64)
     return (torch.arange(lk)[None, :] < lens[:, None]).reshape(b, 1, 1, lk)

@@ -21,7 +21,7 @@ def test_visible_pairs_closed_form_matches_oracle_count(lq, lk, mask, w):
 
 def test_workload_table_matches_the_five_workloads():
     names = [s["name"] for s in bench.all_shapes()]
-    assert len(names) == 1 + 12 + 20 + 3 + 4 + 5
+    assert len(names) == 1 + 12 + 20 + 3 + 4 + 5 + 3
     assert bench.DEFAULT in names
     s = bench.SHAPES[bench.DEFAULT]
     assert (s["hq"], s["hkv"], s["lq"], s["lk"], s["dqk"], s["dv"], s["dtype"]) == (64, 8, 1, 32768, 192, 128, "bf16")
@@ -83,3 +83,14 @@ def test_mask_array_workloads():
     assert (pad == (np.arange(8192)[None, None, None, :] < lens[:, None, None, None])).all()
     assert bench.bound(s) == "hbm"
     assert bench.work(s)[1] == bench.work(bench.SHAPES["decode_b4_hkv8_lk8192_d128"])[1] + 4 * 8192
+
+
+def test_varlen_workload_counts_valid_keys_only():
+    s = bench.SHAPES["varlen_decode_b8_hkv8_lk8192_d128"]
+    kl = bench.kv_lengths(s)
+    assert len(kl) == 8 and all(2048 <= n <= 8192 for n in kl)
+    pad = bench.make_mask_array(bench.SHAPES["maskarr_pad_decode_b8_hkv8_lk8192_d128"]).numpy()
+    assert pad.sum(axis=-1).ravel().tolist() == kl  # the padding mask keeps the same keys
+    _, nbytes = bench.work(s)
+    assert nbytes == 2 * (8 * 32 * 256 + 8 * sum(kl) * 256)
+    assert bench.bound(s) == "hbm"
