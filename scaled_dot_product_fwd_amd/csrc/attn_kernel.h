@@ -152,14 +152,15 @@ constexpr int cmin(int a, int b) { return a < b ? a : b; }
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
 // Static shape of one kernel instance.
-template <class E, int DQK, int DV, int NWQ, int NWK, int BKW, int MA = MA_NONE>
+template <class E, int DQK, int DV, int NWQ, int NWK, int BKW, int MA = MA_NONE, int NWD = 1>
 struct Shape {
-  static constexpr int NW = NWQ * NWK;
+  static constexpr int NW = NWQ * NWK * NWD;
   static constexpr int NT = NW * 64;
   static constexpr int BM = NWQ * 32;          // rows per workgroup
   static constexpr int BK = NWK * BKW;         // keys per block
   static constexpr int NKT = BKW / 32;         // 32-key tiles per wave
   static constexpr int NDT = DV / 32;          // 32-wide dv tiles
+  static constexpr int NDTW = NDT / NWD;       // dv tiles one wave accumulates
   static constexpr int NQS = DQK / E::KQK;     // QK MFMAs per key tile
   static constexpr int KCH = DQK * E::ES / 16; // 16-byte chunks per K row
   static constexpr int VCH = DV * E::ES / 16;  // 16-byte chunks per V row
@@ -208,11 +209,12 @@ struct Shape {
   // Operand fragments read ahead of their products when the extra registers
   // (4 per fragment) stay within a budget (16-bit types only).
   static constexpr bool HOIST_K = E::ES == 2 && NKT * NQS * 4 <= 48;
-  static constexpr bool HOIST_V = E::ES == 2 && NKT * (32 / E::KPV) * NDT * 4 <= 48 && NQS * 4 + NDT * 16 <= 128;
+  static constexpr bool HOIST_V = NWD == 1 && E::ES == 2 && NKT * (32 / E::KPV) * NDT * 4 <= 48 &&
+                                  NQS * 4 + NDT * 16 <= 128;
   // Software-pipelined block loop (QK of the next block overlapping this
   // block's softmax) where two blocks of scores fit next to Q and O:
   // four-wave prefill tiles of the small head dims, 16-bit types.
-  static constexpr bool PIPE = NWK == 1 && E::ES == 2 && NQS * 4 + NDT * 16 + 2 * NKT * 16 <= 144;
+  static constexpr bool PIPE = NWK == 1 && NWD == 1 && E::ES == 2 && NQS * 4 + NDT * 16 + 2 * NKT * 16 <= 144;
   // DMA instructions one block costs the wave that issues the fewest / most.
   static constexpr int DMA_MIN = KDMA / NW + VDMA / NW + MDMA / NW;
   static constexpr int DMA_MAX = (KDMA + NW - 1) / NW + (VDMA + NW - 1) / NW + (MDMA + NW - 1) / NW;
@@ -228,6 +230,7 @@ struct Shape {
   static constexpr int TPR = merge_tiles();
   static constexpr int MROW = TPR * 32 + 4;  // +4 floats skew the rows across banks
   static_assert(NWK == 1 || TPR >= 1, "merge scratch must fit the tile buffers");
+  static_assert(NWD == 1 || (NWK == 1 && NDT % NWD == 0), "dv split: waves on rows only, whole dv tiles");
   static_assert(DMA_MAX <= 63, "vmcnt range");
   static_assert(BKW % 32 == 0, "BKW must be a multiple of 32");
   static_assert(DQK % E::KQK == 0 && DV % 32 == 0, "bad head-dim tile");
@@ -277,10 +280,10 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);  // expcnt, lgkmcnt: no wait
 }
 
-template <class E, int DQK, int DV, int NWQ, int NWK, int BKW, int WPE, int MA>
-__global__ __launch_bounds__(NWQ * NWK * 64) __attribute__((amdgpu_waves_per_eu(WPE)))
+template <class E, int DQK, int DV, int NWQ, int NWK, int BKW, int WPE, int MA, int NWD>
+__global__ __launch_bounds__(NWQ * NWK * NWD * 64) __attribute__((amdgpu_waves_per_eu(WPE)))
 void attn_fwd_kernel(AttnArgs a) {
-  using S = Shape<E, DQK, DV, NWQ, NWK, BKW, MA>;
+  using S = Shape<E, DQK, DV, NWQ, NWK, BKW, MA, NWD>;
   using frag = typename E::frag;
   __shared__ __attribute__((aligned(1024))) char smem_[S::LDS];
   // All LDS addressing goes through an LDS-typed pointer, so addresses stay
@@ -291,7 +294,12 @@ void attn_fwd_kernel(AttnArgs a) {
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wq = wave % NWQ;
-  const int wk = wave / NWQ;
+  const int wk = (wave / NWQ) % NWK;
+  // dv split (NWD > 1, the largest head dims): waves wd = 0..NWD-1 share the
+  // same rows, each computes their scores and softmax and accumulates the dv
+  // tiles [wd NDTW, (wd + 1) NDTW) of O, so no wave holds the whole O row
+  const int wd = wave / (NWQ * NWK);
+  const int tw0 = wd * S::NDTW;
   const int col = lane & 31;  // query column of this lane in S^T / O^T
   const int hl = lane >> 5;   // lane half
 
@@ -560,9 +568,9 @@ void attn_fwd_kernel(AttnArgs a) {
       voffl[tl] = (4 * (g >> 1) + (t16 >> 2)) * S::VROW + 16 * ((4 * tl + x) ^ y) + 8 * (t16 & 1);
   }
 
-  f32x16 oacc[S::NDT];
+  f32x16 oacc[S::NDTW];
 #pragma unroll
-  for (int t = 0; t < S::NDT; ++t) oacc[t] = f32x16{};
+  for (int t = 0; t < S::NDTW; ++t) oacc[t] = f32x16{};
   float m_ref = kNegInf;  // reference max of this row, log2 units (same in both lane halves)
   float l_run = 0.f;      // this lane's share of the row sum (halves add up at the end)
 
@@ -755,7 +763,7 @@ void attn_fwd_kernel(AttnArgs a) {
       const float alpha = need ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.0f;
       l_run *= alpha;
 #pragma unroll
-      for (int t = 0; t < S::NDT; ++t) oacc[t] *= alpha;
+      for (int t = 0; t < S::NDTW; ++t) oacc[t] *= alpha;
       m_ref = m_new;
     }
   };
@@ -783,7 +791,7 @@ void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
         for (int s2 = 0; s2 < 32 / E::KPV; ++s2)
 #pragma unroll
-          for (int t = 0; t < S::NDT; ++t) vf[kt][s2][t] = vread(j, kt, s2, t);
+          for (int t = 0; t < S::NDT; ++t) vf[kt][s2][t] = vread(j, kt, s2, t);  // NWD == 1 here
     }
   };
   auto pv = [&](int j, f32x16 (&sacc)[S::NKT], vfrag_t& vf) __attribute__((always_inline)) {
@@ -801,9 +809,9 @@ void attn_fwd_kernel(AttnArgs a) {
           bf = sacc[kt][s2];
         }
 #pragma unroll
-        for (int t = 0; t < S::NDT; ++t) {
+        for (int t = 0; t < S::NDTW; ++t) {
           if constexpr (S::HOIST_V) oacc[t] = E::mma(vf[kt][s2][t], bf, oacc[t]);
-          else oacc[t] = E::mma(vread(j, kt, s2, t), bf, oacc[t]);
+          else oacc[t] = E::mma(vread(j, kt, s2, tw0 + t), bf, oacc[t]);
         }
       }
     }
@@ -821,6 +829,9 @@ void attn_fwd_kernel(AttnArgs a) {
     constexpr bool KEARLY = 2 * S::DMA_MAX <= 63;
     f32x16 sacc[S::NKT];
     bool live_prev = true;
+    // A wave whose 32 rows all lie past the packed rows (a short query set
+    // in a multi-wave row tile) only helps with the loads.
+    const bool wave_rows = r_wave < R;
     for (int j = 0; j < nblk; ++j) {
       if (j + 1 < nblk) wait_vmcnt<S::DMA_MIN>();  // only block j + 1 may still be in flight
       else wait_vmcnt<0>();
@@ -828,8 +839,8 @@ void attn_fwd_kernel(AttnArgs a) {
       // A boolean array's block is checked every 4th block while blocks are
       // live and at every block after a removed one: dense masks pay for a
       // quarter of the checks, a live run costs at most 3 unchecked blocks.
-      bool live = true;
-      if (MA == MA_BOOL && (!live_prev || (j & 3) == 0)) live = mask_live(j);
+      bool live = wave_rows;
+      if (MA == MA_BOOL && wave_rows && (!live_prev || (j & 3) == 0)) live = mask_live(j);
       live_prev = live;
       if (live) qk(j, sacc);
       if constexpr (KEARLY) {
@@ -1004,10 +1015,10 @@ void attn_fwd_kernel(AttnArgs a) {
     const float inv = l_row > 0.f ? 1.0f / l_row : 0.f;
     char* orow = (char*)a.o + ((int64_t)b * a.os[0] + (int64_t)hq * a.os[1] + (int64_t)iq * a.os[2]) * E::ES;
 #pragma unroll
-    for (int t = 0; t < S::NDT; ++t) {
+    for (int t = 0; t < S::NDTW; ++t) {
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
-        const int d = t * 32 + 8 * i4 + 4 * hl;
+        const int d = (tw0 + t) * 32 + 8 * i4 + 4 * hl;
         if (d < a.dv) {
           if constexpr (E::ES == 2) {
             u32x2 w;
@@ -1021,7 +1032,7 @@ void attn_fwd_kernel(AttnArgs a) {
         }
       }
     }
-    if (a.lse && hl == 0) a.lse[((int64_t)b * a.Hq + hq) * a.Lq + iq] = (m_ref + log2f(l_row)) * kLn2;
+    if (a.lse && hl == 0 && wd == 0) a.lse[((int64_t)b * a.Hq + hq) * a.Lq + iq] = (m_ref + log2f(l_row)) * kLn2;
     return;
   }
 
@@ -1029,16 +1040,16 @@ void attn_fwd_kernel(AttnArgs a) {
   const int64_t ws_row = ((int64_t)z * a.R + r) * a.splits + split;
   float* wo = a.ws_o + ws_row * a.dv;
 #pragma unroll
-  for (int t = 0; t < S::NDT; ++t) {
+  for (int t = 0; t < S::NDTW; ++t) {
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
-      const int d = t * 32 + 8 * i4 + 4 * hl;
+      const int d = (tw0 + t) * 32 + 8 * i4 + 4 * hl;
       if (d < a.dv)
         *(float4*)(wo + d) = make_float4(oacc[t][4 * i4 + 0], oacc[t][4 * i4 + 1], oacc[t][4 * i4 + 2],
                                          oacc[t][4 * i4 + 3]);
     }
   }
-  if (hl == 0) *(float2*)(a.ws_ml + ws_row * 2) = make_float2(m_ref, l_row);
+  if (hl == 0 && wd == 0) *(float2*)(a.ws_ml + ws_row * 2) = make_float2(m_ref, l_row);
 }
 
 }  // namespace dev

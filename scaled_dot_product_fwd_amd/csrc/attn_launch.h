@@ -9,10 +9,10 @@
 
 namespace sdpa {
 
-template <class E, int DQK, int DV, int NWQ, int NWK, int BKW, int WPE, int MA>
+template <class E, int DQK, int DV, int NWQ, int NWK, int BKW, int WPE, int MA, int NWD>
 int launch_one(const Plan& p, const AttnArgs& a, void* stream, std::string* err) {
-  using S = dev::Shape<E, DQK, DV, NWQ, NWK, BKW, MA>;
-  auto kern = dev::attn_fwd_kernel<E, DQK, DV, NWQ, NWK, BKW, WPE, MA>;
+  using S = dev::Shape<E, DQK, DV, NWQ, NWK, BKW, MA, NWD>;
+  auto kern = dev::attn_fwd_kernel<E, DQK, DV, NWQ, NWK, BKW, WPE, MA, NWD>;
   // Check the compiled kernel can run the workgroup size it is launched with,
   // once per instance: an oversized launch must fail loudly, never return
   // silently unwritten output (mlx PR #4185 "Add force_fused option to
@@ -51,12 +51,13 @@ int launch_one(const Plan& p, const AttnArgs& a, void* stream, std::string* err)
 #define SDPA_CASE(E, KIND, DQK, DV, MA)                                                        \
   if (p.dqk_pad == DQK && p.dv_pad == DV) {                                                    \
     constexpr Family f_ = family_for(KIND, dev::E::ES, DQK, DV, mask_elem_bytes(MA, dev::E::ES)); \
-    if (p.fam.nwq != f_.nwq || p.fam.nwk != f_.nwk || p.fam.bkw != f_.bkw || p.mask_array != MA) { \
+    if (p.fam.nwq != f_.nwq || p.fam.nwk != f_.nwk || p.fam.bkw != f_.bkw || p.fam.nwd != f_.nwd || \
+        p.mask_array != MA) {                                                                  \
       *err = "plan and kernel instance disagree on the wave arrangement";                      \
       return SDPA_E_PLAN;                                                                      \
     }                                                                                          \
     return launch_one<dev::E, DQK, DV, f_.nwq, f_.nwk, f_.bkw,                                 \
-                      wpe_for(KIND, dev::E::ES, DQK, DV), MA>(p, a, stream, err);              \
+                      wpe_for(KIND, dev::E::ES, DQK, DV), MA, f_.nwd>(p, a, stream, err);      \
   }
 
 // Head-dim pairs of the 16-bit types: equal padded dims plus (192, 128),
@@ -73,6 +74,9 @@ int launch_one(const Plan& p, const AttnArgs& a, void* stream, std::string* err)
   SDPA_CASE(E, KIND, 256, 256, MA)       \
   SDPA_CASE(E, KIND, 192, 128, MA)
 #define SDPA_PAIRS16(E, KIND, MA) SDPA_PAIRS16_SMALL(E, KIND, MA) SDPA_PAIRS16_LARGE(E, KIND, MA)
+// head dim 512 (16-bit types, prefill family only: the planner sends every
+// query length there)
+#define SDPA_PAIRS16_XL(E, KIND, MA) SDPA_CASE(E, KIND, 512, 512, MA)
 
 // float32 stops at 128.
 #define SDPA_PAIRS32(E, KIND, MA)  \

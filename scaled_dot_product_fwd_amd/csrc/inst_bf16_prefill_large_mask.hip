@@ -3,8 +3,10 @@
 #include "attn_launch.h"
 
 namespace sdpa {
+int launch_attn_bf16_prefill_xl_mask(const Plan& p, const AttnArgs& a, void* stream, std::string* err);
+
 int launch_attn_bf16_prefill_large_mask(const Plan& p, const AttnArgs& a, void* stream, std::string* err) {
   SDPA_BY_MASK_ARRAY(SDPA_PAIRS16_LARGE, BF16, KIND_PREFILL)
-  SDPA_NO_INSTANCE()
+  return launch_attn_bf16_prefill_xl_mask(p, a, stream, err);
 }
 }  // namespace sdpa

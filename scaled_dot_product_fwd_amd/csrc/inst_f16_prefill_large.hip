@@ -4,8 +4,10 @@
 #include "attn_launch.h"
 
 namespace sdpa {
+int launch_attn_f16_prefill_xl(const Plan& p, const AttnArgs& a, void* stream, std::string* err);
+
 int launch_attn_f16_prefill_large(const Plan& p, const AttnArgs& a, void* stream, std::string* err) {
   SDPA_PAIRS16_LARGE(F16, KIND_PREFILL, MA_NONE)
-  SDPA_NO_INSTANCE()
+  return launch_attn_f16_prefill_xl(p, a, stream, err);
 }
 }  // namespace sdpa

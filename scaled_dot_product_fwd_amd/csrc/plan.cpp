@@ -28,7 +28,7 @@ constexpr int kTargetCUs = 256;        // gfx950 compute units (MI355X)
 constexpr int kWgsPerCU = 2;           // at most two resident workgroups per CU
 constexpr int64_t kMaxLen = 1 << 30;   // keeps every in-kernel index in int32
 constexpr int kMaxSplits = 1024;
-constexpr int kMaxDim = 256;
+constexpr int kMaxDim = 512;    // 16-bit types; float32 stops at 128
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -102,6 +102,8 @@ int make_plan(const sdpa_desc_t* d, Plan* p, std::string* err) {
   int dv_pad = (int)ceil_div(Dv, 32) * 32;
   if (dqk_pad == 192 && dv_pad <= 128) {
     dv_pad = 128;  // the asymmetric (192, 128) instance
+  } else if (dqk_pad > 256 || dv_pad > 256) {
+    dqk_pad = dv_pad = 512;  // the one instance above 256
   } else {
     const int m = dqk_pad > dv_pad ? dqk_pad : dv_pad;
     dqk_pad = dv_pad = m;  // zero padding in-kernel: no host copy
@@ -180,10 +182,17 @@ int make_plan(const sdpa_desc_t* d, Plan* p, std::string* err) {
   // tiles of a split share an L2: speculative verify Lq=16, G=4 measures
   // 4-12% faster than one 64-row tile); 64 rows (short family) for the rest
   // up to 64; 128 rows (prefill family) beyond.
-  int rows = d->row_tile ? d->row_tile : (R <= 32 || R == 64 ? 32 : (R <= 64 ? 64 : 128));
+  // Head dim 512 has one arrangement (two 32-row groups, each on two waves
+  // that split the dv tiles): 64 rows for every query length.
+  const bool xl = dqk_pad > 256;
+  if (xl && d->row_tile != 0 && d->row_tile != 64) {
+    return fail(err, SDPA_E_PLAN, "head dim 512 runs 64-row tiles only (row_tile must be 0 or 64, got " +
+                                      std::to_string(d->row_tile) + ")");
+  }
+  int rows = xl ? 64 : d->row_tile ? d->row_tile : (R <= 32 || R == 64 ? 32 : (R <= 64 ? 64 : 128));
   const int64_t row_tiles = ceil_div(R, rows);
   const int64_t base = B * Hkv * row_tiles;
-  const int kind = rows == 32 ? KIND_DECODE : (rows == 64 ? KIND_SHORT : KIND_PREFILL);
+  const int kind = xl ? KIND_PREFILL : rows == 32 ? KIND_DECODE : (rows == 64 ? KIND_SHORT : KIND_PREFILL);
   const Family fam = family_for(kind, es, dqk_pad, dv_pad, mes);
   const int64_t bk = (int64_t)fam.nwk * fam.bkw;
 
@@ -204,7 +213,7 @@ int make_plan(const sdpa_desc_t* d, Plan* p, std::string* err) {
     // the MFMA units busy.
     const size_t lds_need = attn_lds_bytes(d->dtype, dqk_pad, dv_pad, fam, mes);
     const int64_t by_waves = 4 * wpe_for(kind, d->dtype == SDPA_F32 ? 4 : 2, dqk_pad, dv_pad) /
-                             (fam.nwq * fam.nwk);
+                             (fam.nwq * fam.nwk * fam.nwd);
     const int64_t resident = std::max<int64_t>(
         1, std::min<int64_t>({(int64_t)kWgsPerCU, (160 * 1024) / (int64_t)lds_need, by_waves}));
     const int64_t target = (int64_t)kTargetCUs * resident;
@@ -259,7 +268,8 @@ std::string describe(const sdpa_desc_t* d, const Plan& p) {
   const char* fam = p.kind == KIND_DECODE ? "decode" : (p.kind == KIND_SHORT ? "short" : "prefill");
   s << "family=" << fam << " dtype=" << dtype_name(p.dtype) << " dqk=" << d->dim_qk << "->" << p.dqk_pad
     << " dv=" << d->dim_v << "->" << p.dv_pad << " rows_per_wg=" << p.rows_per_wg
-    << " waves=" << p.fam.nwq << "x" << p.fam.nwk << " block_keys=" << p.fam.nwk * p.fam.bkw
+    << " waves=" << p.fam.nwq << "x" << p.fam.nwk << (p.fam.nwd > 1 ? "x" + std::to_string(p.fam.nwd) : "")
+    << " block_keys=" << p.fam.nwk * p.fam.bkw
     << " row_tiles=" << p.row_tiles << " splits=" << p.splits << " mask=" << mask_name(p.mask);
   if (p.mask == MASK_WINDOW) s << "(" << p.window << ")";
   if (p.mask_array != MA_NONE) s << " mask_array=" << (p.mask_array == MA_BOOL ? "bool" : "add");

@@ -55,6 +55,7 @@ struct Family {
   int nwq;   // waves stacked along query rows (32 rows each)
   int nwk;   // waves splitting each key block between them
   int bkw;   // keys per wave per iteration (multiple of 32)
+  int nwd = 1;  // waves splitting the dv tiles of the same rows
 };
 
 enum : int { KIND_PREFILL = 0, KIND_SHORT = 1, KIND_DECODE = 2 };
@@ -74,6 +75,11 @@ constexpr int mask_elem_bytes(int ma, int elem_bytes) {
 // the planner and the kernel instantiation units.
 constexpr Family family_for(int kind, int elem_bytes, int dqk_pad, int dv_pad, int mes = 0) {
   const int key_bytes = (dqk_pad + dv_pad) * elem_bytes;  // one key of K plus V
+  // Head dims above 256 (512): a 32-row wave cannot hold Q and the whole O
+  // row in registers, so two waves share each 32 rows and split the dv
+  // tiles; 32-key blocks keep the two buffers at 128 KB.  Every query
+  // length uses this one arrangement.
+  if ((dqk_pad > dv_pad ? dqk_pad : dv_pad) > 256) return Family{2, 1, 32, 2};
   if (kind == KIND_DECODE)
     return (key_bytes + 32 * mes) * 128 * 2 <= 160 * 1024 ? Family{1, 4, 32} : Family{1, 2, 32};
   if (kind == KIND_SHORT) return Family{2, 2, 32};

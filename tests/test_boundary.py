@@ -57,7 +57,10 @@ def _status(fn, *args):
 @pytest.mark.parametrize("kw,code,needle", [
     (dict(lq=0), "SDPA_E_SHAPE", "every size must be >= 1"),
     (dict(hq=6, hkv=4), "SDPA_E_SHAPE", "multiple of heads_kv"),
-    (dict(dqk=512, dv=512), "SDPA_E_HEAD_DIM", "Dqk=512"),
+    (dict(dqk=1024, dv=1024), "SDPA_E_HEAD_DIM", "Dqk=1024"),
+    (dict(dqk=520, dv=512), "SDPA_E_HEAD_DIM", "from 8 to 512"),
+    (dict(dqk=512, dv=512, dtype=_lib.SDPA_F32), "SDPA_E_HEAD_DIM", "float32 supports head dims up to 128"),
+    (dict(dqk=512, dv=512, row_tile=128), "SDPA_E_PLAN", "64-row tiles"),
     (dict(dqk=72, dv=76), "SDPA_E_HEAD_DIM", "multiples of 8"),
     (dict(dqk=160, dv=160, dtype=_lib.SDPA_F32), "SDPA_E_HEAD_DIM", "float32 supports head dims up to 128"),
     (dict(dtype=7), "SDPA_E_DTYPE", "dtype"),
@@ -85,7 +88,7 @@ def test_validation_errors_name_the_constraint(kw, code, needle):
 
 def test_validation_errors_are_value_errors():
     with pytest.raises(ValueError):
-        sdpa.sdpa_workspace_bytes(_desc(dqk=512, dv=512))
+        sdpa.sdpa_workspace_bytes(_desc(dqk=1024, dv=1024))
 
 
 def test_forward_null_pointers():
@@ -109,7 +112,7 @@ def test_forward_missing_workspace():
 
 
 def test_last_error_is_cleared_by_success():
-    _status(sdpa.sdpa_workspace_bytes, _desc(dqk=512, dv=512))
+    _status(sdpa.sdpa_workspace_bytes, _desc(dqk=1024, dv=1024))
     assert sdpa.sdpa_last_error() != ""
     sdpa.sdpa_workspace_bytes(_desc())
     assert sdpa.sdpa_last_error() == ""
@@ -307,3 +310,16 @@ def test_varlen_length_arrays_must_be_aligned():
     assert msg.startswith("SDPA_E_STRIDE") and "q_lens" in msg
     msg = _status(sdpa.sdpa_forward_varlen, d, 16, 16, 16, None, None, 22, 16, None, None, 0, None)
     assert msg.startswith("SDPA_E_STRIDE") and "kv_lens" in msg
+
+
+@pytest.mark.parametrize("lq,dqk,dv", [(1, 512, 512), (8, 512, 512), (4096, 512, 512), (300, 320, 320),
+                                       (16, 512, 256)])
+def test_plan_head_dim_512(lq, dqk, dv):
+    """Head dims above 256 run the 512 instance: two 32-row groups whose waves
+    split the dv tiles, 32-key blocks (two buffers of 64 KB), any query length."""
+    p = _plan(b=1, hq=32, hkv=8, lq=lq, lk=8192, dqk=dqk, dv=dv, mask="causal")
+    assert p["family"] == "prefill" and p["rows_per_wg"] == "64" and p["waves"] == "2x1x2"
+    assert p["block_keys"] == "32" and p["dqk"].endswith("->512") and p["dv"].endswith("->512")
+    assert int(p["lds"]) == 2 * 32 * 2048
+    if lq == 1:
+        assert int(p["splits"]) > 1  # a decode call still spreads its keys over the chip

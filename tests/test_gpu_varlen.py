@@ -109,3 +109,9 @@ def test_varlen_decode_sampled_full_size():
     gl = np.array([lse[p] for p in picks])
     assert float(np.abs(go - ro).max()) <= TOL_O[torch.bfloat16]
     assert lse_err(gl, rl) <= TOL_LSE[torch.bfloat16]
+
+
+def test_varlen_head_dim_512():
+    case = (2, 8, 2, 4, 900, 512, 512, "bf16", "causal", 0, [4, 2], [900, 130])
+    _say("varlen d512")
+    _check(case)
