@@ -55,6 +55,13 @@ PAGES_DECODE_US = {(4, 256): 218, (4, 1024): 217, (4, 4096): 255, (4, 8192): 305
                    (8, 16384): 444, (8, 32768): 728}
 
 
+def pages_shape(s):
+    """True for the decode shapes the pages time (B=1, Hq=64, Lq=1, Dqk=192,
+    Dv=128, bf16, one of their Hkv / Lk), the only ones ``vs_baseline`` may use."""
+    return (s["b"], s["hq"], s["lq"], s["dqk"], s["dv"], s["dtype"]) == (1, 64, 1, 192, 128, "bf16") and \
+        (s["hkv"], s["lk"]) in PAGES_DECODE_US and s.get("arr") is None and not s.get("varlen")
+
+
 def shape(name, b, hq, hkv, lq, lk, dqk, dv, dtype, mask, window, seed, arr=None, arr_window=0,
           varlen=False):
     """One benchmark shape.  ``arr`` names an explicit mask array given on top
@@ -96,6 +103,9 @@ def all_shapes():
     out.append(shape("decode_b4_hkv8_lk8192_d128", 4, 32, 8, 1, 8192, 128, 128, "bf16", "none", 0, 6002))
     out.append(shape("maskarr_pad_decode_b4_hkv8_lk8192_d128", 4, 32, 8, 1, 8192, 128, 128, "bf16", "none", 0,
                      6002, arr="pad_bool"))
+    # head dim 512 (zero-padded MFMA dims above 256 land here too)
+    out.append(shape("causal_l8192_d512", 1, 16, 2, 8192, 8192, 512, 512, "bf16", "causal", 0, 8000))
+    out.append(shape("decode_d512_hkv8_lk16384", 1, 32, 8, 1, 16384, 512, 512, "bf16", "causal", 0, 8001))
     # per-entry key lengths, beside the same lengths as a padding mask
     out.append(shape("decode_b8_hkv8_lk8192_d128", 8, 32, 8, 1, 8192, 128, 128, "bf16", "none", 0, 7000))
     out.append(shape("maskarr_pad_decode_b8_hkv8_lk8192_d128", 8, 32, 8, 1, 8192, 128, 128, "bf16", "none", 0,
@@ -562,7 +572,7 @@ def main():
         calibration_copy(args.calibrate_copy_mib)
     cpu = None if args.no_cpu_baseline else cpu_baseline(s, runner)
     vs = None
-    if s["name"].startswith("decode_"):
+    if pages_shape(s):
         pages_us = PAGES_DECODE_US[(s["hkv"], s["lk"])]
         vs = res["step_value"] / (res["bytes"] / (pages_us * 1e-6) / 1e9)
     line = {

@@ -21,7 +21,7 @@ def test_visible_pairs_closed_form_matches_oracle_count(lq, lk, mask, w):
 
 def test_workload_table_matches_the_five_workloads():
     names = [s["name"] for s in bench.all_shapes()]
-    assert len(names) == 1 + 12 + 20 + 3 + 4 + 5 + 3
+    assert len(names) == 1 + 12 + 20 + 3 + 4 + 5 + 2 + 3
     assert bench.DEFAULT in names
     s = bench.SHAPES[bench.DEFAULT]
     assert (s["hq"], s["hkv"], s["lq"], s["lk"], s["dqk"], s["dv"], s["dtype"]) == (64, 8, 1, 32768, 192, 128, "bf16")
@@ -94,3 +94,9 @@ def test_varlen_workload_counts_valid_keys_only():
     _, nbytes = bench.work(s)
     assert nbytes == 2 * (8 * 32 * 256 + 8 * sum(kl) * 256)
     assert bench.bound(s) == "hbm"
+
+
+def test_vs_baseline_only_for_the_pages_decode_shapes():
+    pages = [n for n, s in bench.SHAPES.items() if bench.pages_shape(s)]
+    assert sorted(pages) == sorted(f"decode_hkv{h}_lk{lk}" for h in (4, 8)
+                                   for lk in (256, 1024, 4096, 8192, 16384, 32768))
