@@ -1,0 +1,108 @@
+"""Pins for the float64 backward oracle (no GPU): torch's float64 autograd
+through its CPU attention (library special case), central finite differences
+of the forward oracle, and exact invariants of the gradient formulas."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import sdpa_bwd_ref, sdpa_ref, visible_mask
+
+
+def _rand(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def _case(b, hq, hkv, lq, lk, dqk, dv, seed):
+    return (_rand((b, hq, lq, dqk), seed), _rand((b, hkv, lk, dqk), seed + 1),
+            _rand((b, hkv, lk, dv), seed + 2), _rand((b, hq, lq, dv), seed + 3))
+
+
+CASES = [
+    # b, hq, hkv, lq, lk, dqk, dv, mask, window
+    (1, 2, 2, 4, 6, 3, 5, "none", 0),
+    (2, 4, 2, 5, 5, 4, 4, "causal", 0),
+    (1, 4, 1, 3, 8, 5, 3, "causal", 0),
+    (1, 2, 1, 6, 9, 4, 2, "window", 3),
+]
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_bwd_matches_torch_autograd(case):
+    b, hq, hkv, lq, lk, dqk, dv, mask, w = case
+    q, k, v, do = _case(b, hq, hkv, lq, lk, dqk, dv, seed=700 + lq)
+    dq, dk, dvv = sdpa_bwd_ref(q, k, v, do, 0.6, mask, w)
+    g = hq // hkv
+    tq, tk, tv = (torch.from_numpy(x).requires_grad_(True) for x in (q, k, v))
+    m = torch.from_numpy(visible_mask(lq, lk, mask, w))
+    out = torch.nn.functional.scaled_dot_product_attention(
+        tq, tk.repeat_interleave(g, dim=1), tv.repeat_interleave(g, dim=1), attn_mask=m, scale=0.6)
+    out.backward(torch.from_numpy(do))
+    np.testing.assert_allclose(dq, tq.grad.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dk, tk.grad.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dvv, tv.grad.numpy(), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("case", CASES[1:3])
+def test_bwd_matches_finite_differences(case):
+    """dL/dx for L = sum(O * dO), central differences of the forward oracle."""
+    b, hq, hkv, lq, lk, dqk, dv, mask, w = case
+    q, k, v, do = _case(b, hq, hkv, lq, lk, dqk, dv, seed=710 + lq)
+    grads = sdpa_bwd_ref(q, k, v, do, 0.8, mask, w)
+    rng = np.random.default_rng(3)
+    h = 1e-6
+
+    def loss(qq, kk, vv):
+        return float((sdpa_ref(qq, kk, vv, 0.8, mask, w)[0] * do).sum())
+
+    for which, x in enumerate((q, k, v)):
+        for _ in range(6):
+            idx = tuple(int(rng.integers(n)) for n in x.shape)
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p = [q, k, v]
+            args_m = [q, k, v]
+            args_p[which], args_m[which] = xp, xm
+            fd = (loss(*args_p) - loss(*args_m)) / (2 * h)
+            assert abs(fd - grads[which][idx]) < 1e-7 * max(1.0, abs(fd)), (which, idx, fd, grads[which][idx])
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_bwd_invariants(case):
+    """Rows of dS sum to 0, so the keys' dK sum to 0; rows of P sum to 1, so
+    the keys' dV sum to the group's summed dO."""
+    b, hq, hkv, lq, lk, dqk, dv, mask, w = case
+    q, k, v, do = _case(b, hq, hkv, lq, lk, dqk, dv, seed=720 + lq)
+    _, dk, dvv = sdpa_bwd_ref(q, k, v, do, 0.7, mask, w)
+    g = hq // hkv
+    np.testing.assert_allclose(dk.sum(axis=2), 0.0, atol=1e-12)
+    for kvh in range(hkv):
+        np.testing.assert_allclose(dvv[:, kvh].sum(axis=1), do[:, kvh * g:(kvh + 1) * g].sum(axis=(1, 2)),
+                                   atol=1e-12)
+
+
+def test_bwd_unseen_keys_get_no_gradient():
+    q, k, v, do = _case(1, 2, 1, 3, 10, 4, 4, seed=730)
+    _, dk, dvv = sdpa_bwd_ref(q, k, v, do, 0.5, "window", 2)  # rows see keys 6..9 only
+    np.testing.assert_array_equal(dk[:, :, :6], 0.0)
+    np.testing.assert_array_equal(dvv[:, :, :6], 0.0)
+    assert np.abs(dk[:, :, 6:]).sum() > 0 and np.abs(dvv[:, :, 7:]).sum() > 0
+
+
+def test_bwd_scale_zero():
+    q, k, v, do = _case(1, 2, 2, 3, 5, 4, 3, seed=740)
+    dq, dk, dvv = sdpa_bwd_ref(q, k, v, do, 0.0, "none")
+    np.testing.assert_array_equal(dq, 0.0)
+    np.testing.assert_array_equal(dk, 0.0)
+    # uniform P = 1/Lk: every key's dV is the rows' summed dO over Lk
+    np.testing.assert_allclose(dvv, np.broadcast_to(do.sum(axis=2, keepdims=True) / 5, (1, 2, 5, 3)), atol=1e-15)
+
+
+def test_bwd_single_key_closed_form():
+    """One key: P = 1, dV = sum of dO over the rows, dS = 0 so dQ = dK = 0."""
+    q, k, v, do = _case(1, 2, 1, 3, 1, 4, 3, seed=750)
+    dq, dk, dvv = sdpa_bwd_ref(q, k, v, do, 0.9, "none")
+    np.testing.assert_allclose(dq, 0.0, atol=1e-15)
+    np.testing.assert_allclose(dk, 0.0, atol=1e-15)
+    np.testing.assert_allclose(dvv[0, 0, 0], do[0].sum(axis=(0, 1)), atol=1e-14)
