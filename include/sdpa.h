@@ -167,6 +167,23 @@ int sdpa_forward_varlen(const sdpa_desc_t* desc, const void* q, const void* k, c
                         const void* mask, const int32_t* q_lens, const int32_t* kv_lens, void* o,
                         float* lse, void* workspace, size_t workspace_bytes, sdpa_stream_t stream);
 
+/* Backward pass (mlx PR #4185, Background and API: training needs the
+ * log-sum-exp; mlx PR #3552, Outstanding: the VJP).  Given the forward's
+ * inputs, its output o and log-sum-exp lse (contiguous float32 [B,Hq,Lq], as
+ * sdpa_forward writes it) and the upstream gradient dout, writes
+ *   dq = scale dS K,  dk = scale dS^T Q,  dv = P^T dout,
+ *   P = softmax(scale Q K^T + mask),  dS = P (dout V^T - rowsum(dout o)),
+ * with grouped-query sums over each KV head's query heads.  dout uses
+ * desc's o strides, dq the q strides, dk / dv the k / v strides; all in the
+ * input type (float16 or bfloat16), head dims up to 128, the causal and
+ * window modes (no mask array).  Deterministic (no atomics).  Needs a
+ * workspace of sdpa_backward_workspace_bytes() bytes (256-byte aligned).
+ * Enqueues three kernels on `stream`. */
+int sdpa_backward_workspace_bytes(const sdpa_desc_t* desc, size_t* bytes);
+int sdpa_backward(const sdpa_desc_t* desc, const void* q, const void* k, const void* v, const void* o,
+                  const void* dout, const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                  size_t workspace_bytes, sdpa_stream_t stream);
+
 /* Writes a one-line, NUL-terminated description of the plan (kernel family,
  * tile, splits, grid, workspace) into buf.  Host only. */
 int sdpa_describe_plan(const sdpa_desc_t* desc, char* buf, size_t len);

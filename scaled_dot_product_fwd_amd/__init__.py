@@ -20,10 +20,11 @@ from ._lib import (SDPA_BF16, SDPA_F16, SDPA_F32, SDPA_MASK_ARRAY_ADD,  # noqa: 
                    SDPA_MASK_ARRAY_BOOL, SDPA_MASK_ARRAY_NONE, SDPA_MASK_CAUSAL, SDPA_MASK_NONE,
                    SDPA_MASK_WINDOW, SdpaError, SdpaRuntimeError, SdpaValueError, load,
                    sdpa_desc_init, sdpa_desc_t, sdpa_describe_plan, sdpa_forward,
-                   sdpa_forward_masked, sdpa_forward_varlen, sdpa_last_error,
-                   sdpa_set_profile_events, sdpa_workspace_bytes)
+                   sdpa_backward, sdpa_backward_workspace_bytes, sdpa_forward_masked,
+                   sdpa_forward_varlen, sdpa_last_error, sdpa_set_profile_events,
+                   sdpa_workspace_bytes)
 
-__all__ = ["forward", "make_desc", "plan_for", "workspace_for", "pad_mask", "sdpa_forward",
+__all__ = ["forward", "backward", "sdpa_backward", "sdpa_backward_workspace_bytes", "make_desc", "plan_for", "workspace_for", "pad_mask", "sdpa_forward",
            "sdpa_forward_masked", "sdpa_forward_varlen", "sdpa_workspace_bytes", "sdpa_describe_plan", "sdpa_last_error",
            "sdpa_desc_init", "sdpa_set_profile_events",
            "SdpaError", "SdpaValueError", "SdpaRuntimeError"]
@@ -231,3 +232,52 @@ def forward(q, k, v, *, scale: Optional[float] = None, mask: str = "none", windo
                             attn_mask.data_ptr() if attn_mask is not None else 0, lens[0], lens[1],
                             out.data_ptr(), lse.data_ptr() if lse is not None else 0, ws_ptr, ws_len, stream)
     return (out, lse) if return_lse else out
+
+
+def backward(q, k, v, o, dout, lse, *, scale: Optional[float] = None, mask: str = "none",
+             window_size: int = 0, dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Gradients ``(dq, dk, dv)`` of the fused forward on the current HIP device.
+
+    ``q, k, v`` and ``scale``, ``mask``, ``window_size`` as given to
+    ``forward``; ``o`` and ``lse`` its output and float32 log-sum-exp
+    (``return_lse=True``); ``dout`` the upstream gradient, shaped and strided
+    like ``o``.  float16 / bfloat16, head dims up to 128, no mask array.
+    Deterministic.
+    """
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        if not isinstance(t, torch.Tensor) or t.dim() != 4 or not t.is_cuda or t.stride(3) != 1:
+            raise SdpaValueError(f"SDPA_E_SHAPE: {name} must be a 4-D GPU tensor with unit head-dim stride")
+        if t.dtype != q.dtype:
+            raise SdpaValueError("SDPA_E_DTYPE: q, k, v, o and dout must share one dtype")
+    if dout.shape != o.shape or dout.stride() != o.stride():
+        raise SdpaValueError("SDPA_E_STRIDE: dout must have o's shape and strides")
+    b, hq, lq, _ = q.shape
+    if (lse.shape != (b, hq, lq) or lse.dtype != torch.float32 or not lse.is_contiguous()
+            or lse.device != q.device):
+        raise SdpaValueError("SDPA_E_SHAPE: lse must be the forward's contiguous float32 [B, Hq, Lq]")
+    dt = _dtype_code(q.dtype)
+    desc = make_desc(q.shape, k.shape, v.shape, dt, scale=scale, mask=mask, window_size=window_size,
+                     q_stride=q.stride()[:3], k_stride=k.stride()[:3], v_stride=v.stride()[:3],
+                     o_stride=o.stride()[:3])
+    outs = []
+    for name, given, like in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if given is None:
+            given = torch.empty_strided(like.shape, like.stride(), dtype=like.dtype, device=like.device)
+        elif given.shape != like.shape or given.stride() != like.stride() or given.dtype != like.dtype:
+            raise SdpaValueError(f"SDPA_E_STRIDE: {name} must have the shape, strides and dtype of its input")
+        outs.append(given)
+    nbytes = sdpa_backward_workspace_bytes(desc)
+    if workspace is None or workspace.numel() * workspace.element_size() < nbytes:
+        if stream is not None:
+            raise SdpaValueError(f"SDPA_E_WORKSPACE: the backward pass on an explicit stream needs a caller "
+                                 f"workspace of {nbytes} bytes")
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    with torch.cuda.device(q.device):
+        sdpa_backward(desc, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                      lse.data_ptr(), outs[0].data_ptr(), outs[1].data_ptr(), outs[2].data_ptr(),
+                      workspace.data_ptr(), workspace.numel() * workspace.element_size(), stream)
+    return tuple(outs)

@@ -1,0 +1,485 @@
+// Backward pass of fused attention for gfx950: dQ, dK, dV of
+// O = softmax(scale Q K^T + mask) V, given dO and the forward's log-sum-exp.
+//
+// With P recomputed from the saved log-sum-exp (no running max: P = 2^(s c -
+// lse2) is final), the gradients are dV = P^T dO, dS = P (dO V^T - D) with
+// D_i = dO_i . O_i, dQ = scale dS K and dK = scale dS^T Q (mlx PR #4185
+// "Add force_fused option to scaled_dot_product_attention", API: the
+// log-sum-exp is the output training needs; mlx PR #3552 "feat(fast): add
+// sliding-window SDPA kernel path", Outstanding: the VJP was not extended).
+//
+// Three kernels, none with atomics, so every result is deterministic:
+//   bwd_prep   per packed row: D, the log-sum-exp in log2 units, the query
+//              index; laid out in packed-row order so tiles of rows are
+//              contiguous.
+//   bwd_dq     a row tile (128 packed rows, one 32-row group per wave) walks
+//              the key blocks: S^T = K Q^T and dP^T = V dO^T (Q, dO in
+//              registers), dS^T, then dQ^T += K^T dS^T through the
+//              transposing LDS read of the K tile -- the forward's layout
+//              with dS^T in place of P^T and K in place of V.
+//   bwd_dkdv   a key tile (128 keys, 32 per wave; K and V rows stay in LDS)
+//              walks the query blocks (32 packed rows, shared by the waves):
+//              S = Q K^T and dP = dO V^T with the keys on the lanes, then
+//              dV^T += dO^T P and dK^T += Q^T dS through transposing reads of
+//              the Q and dO tiles.  Packed rows cover all G query heads of
+//              the KV head, so grouped-query sums come out of the loop.
+// Tiles move by the same 16-byte LDS DMA as the forward (counted waits).
+#include <hip/hip_runtime.h>
+
+#include <string>
+
+#include "attn_kernel.h"
+
+namespace sdpa {
+namespace dev {
+
+// LDS tile whose rows hold D 16-bit elements: logical 16-byte chunk c of
+// row r sits at chunk c ^ sw(r), a permutation inside aligned groups of KG
+// chunks, so 16 consecutive rows reading one logical chunk spread over the
+// 256-byte bank window.
+template <int D>
+struct Tile {
+  static constexpr int ROWB = D * 2;
+  static constexpr int CH = ROWB / 16;
+  static constexpr int KG = (CH % 16 == 0) ? 16 : (CH % 8 == 0) ? 8 : 4;
+  static constexpr int KSH = KG == 16 ? 0 : (KG == 8 ? 1 : 2);
+  static __device__ __forceinline__ int sw(int row) { return (row >> KSH) & (KG - 1); }
+  static __device__ __forceinline__ int off(int row, int chunk) { return row * ROWB + 16 * (chunk ^ sw(row)); }
+};
+
+// MFMA operand of 8 consecutive elements of tile row `row` (k-step s, lane
+// half hl): the A operand with rows on the lanes, or the B operand with
+// columns on the lanes.
+template <int D>
+__device__ __forceinline__ u32x4 row_frag(const SDPA_LDS char* t, int row, int s, int hl) {
+  return *(const SDPA_LDS u32x4*)(t + Tile<D>::off(row, 2 * s + hl));
+}
+
+// A operand of tile^T: output rows are the tile columns 32 tt .. 32 tt + 31,
+// the k dimension is 16 tile rows from row0, in the order pack_frag uses
+// for the B operand (the forward's V^T read).
+template <int D>
+__device__ __forceinline__ u32x4 tr_frag(const SDPA_LDS char* t, int row0, int tt, int lane) {
+  const int g = lane >> 4, t16 = lane & 15;
+  const int r = row0 + 4 * (g >> 1) + (t16 >> 2);
+  const int chunk = 4 * tt + 2 * (g & 1) + ((t16 & 3) >> 1);
+  const int b8 = 8 * (t16 & 1);
+  const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SDPA_LDS i16x4*)(t + Tile<D>::off(r, chunk) + b8));
+  const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SDPA_LDS i16x4*)(t + Tile<D>::off(r + 8, chunk) + b8));
+  const u32x2 h0 = __builtin_bit_cast(u32x2, v0), h1 = __builtin_bit_cast(u32x2, v1);
+  u32x4 f;
+  f[0] = h0[0];
+  f[1] = h0[1];
+  f[2] = h1[0];
+  f[3] = h1[1];
+  return f;
+}
+
+// B operand from an accumulator (rows = the k dimension of the next
+// product): registers 8 s2 .. 8 s2 + 7, rounded to the input type.
+template <class E>
+__device__ __forceinline__ u32x4 pack_frag(const f32x16& x, int s2) {
+  u32x4 pk;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) pk[w] = E::pack2(x[8 * s2 + 2 * w], x[8 * s2 + 2 * w + 1]);
+  return pk;
+}
+
+// LDS DMA of NR rows into `lds`: the 1 KB instructions are dealt out to the
+// NW waves; rowptr(row) is the row's global base; chunks past the real width
+// (vch chunks) re-read the last real one (their products are discarded or
+// meet zero operands).
+template <int D, int NR, int NW, class RowPtr>
+__device__ __forceinline__ void dma_rows(unsigned lds, int wave_u, int lane, int vch, RowPtr rowptr) {
+  using T = Tile<D>;
+  constexpr int NI = NR * T::ROWB / 1024;
+  static_assert(NR * T::ROWB % 1024 == 0, "tiles must be whole DMA instructions");
+  constexpr int PW = (NI + NW - 1) / NW;
+#pragma unroll
+  for (int ii = 0; ii < PW; ++ii) {
+    const int ins = ii * NW + wave_u;
+    if ((ii + 1) * NW > NI && ins >= NI) continue;
+    const int sl = ins * 64 + lane;
+    const int row = sl / T::CH;
+    const int lch = (sl % T::CH) ^ T::sw(row);
+    lds_dma16<false>(rowptr(row) + min(lch, vch - 1) * 16, lds + ins * 1024);
+  }
+}
+
+template <class E>
+__device__ __forceinline__ float lo16(unsigned w) {
+  return E::to_float((unsigned short)(w & 0xffffu));
+}
+template <class E>
+__device__ __forceinline__ float hi16(unsigned w) {
+  return E::to_float((unsigned short)(w >> 16));
+}
+
+// ---- per packed row: D = dO . O, lse in log2 units, query index ----
+// 16 lanes per row, 8 elements each (dv <= 128).
+template <class E>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
+  const int tid = threadIdx.x;
+  const int l16 = tid & 15;
+  const int64_t grow = (int64_t)blockIdx.x * 16 + (tid >> 4);  // z * Rp + r
+  const int64_t Z = (int64_t)a.B * a.Hkv;
+  if (grow >= Z * a.Rp) return;  // no barriers below
+  const int z = (int)(grow / a.Rp), r = (int)(grow % a.Rp);
+  const int b = z / a.Hkv, kvh = z % a.Hkv;
+  const bool ok = r < a.R;
+  float dsum = 0.f, lse2 = __builtin_inff();
+  if (ok) {
+    const int i = r / a.G, h = kvh * a.G + r % a.G;
+    const int d0 = 8 * l16;
+    if (d0 < a.dv) {
+      const char* orow = (const char*)a.o + ((int64_t)b * a.os[0] + (int64_t)h * a.os[1] + (int64_t)i * a.os[2]) * 2;
+      const char* drow =
+          (const char*)a.dout + ((int64_t)b * a.os[0] + (int64_t)h * a.os[1] + (int64_t)i * a.os[2]) * 2;
+      const u32x4 ov = *(const u32x4*)(orow + d0 * 2);
+      const u32x4 dw = *(const u32x4*)(drow + d0 * 2);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) dsum += lo16<E>(ov[w]) * lo16<E>(dw[w]) + hi16<E>(ov[w]) * hi16<E>(dw[w]);
+    }
+    const float l = a.lse[((int64_t)b * a.Hq + h) * a.Lq + i];
+    lse2 = l == kNegInf ? __builtin_inff() : l * kLog2e;  // a row without keys gets P = 0
+  }
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) dsum += __shfl_xor(dsum, o, 16);
+  if (l16 == 0) {
+    a.ws_lse2[grow] = lse2;
+    a.ws_d[grow] = dsum;
+  }
+  if (z == 0 && l16 == 1) a.ws_qi[r] = min(r, a.R - 1) / a.G;
+}
+
+// ---- dQ: rows on the lanes, walking the key blocks ----
+template <class E, int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void bwd_dq_kernel(BwdArgs a) {
+  using T = Tile<D>;
+  constexpr int BK = D <= 64 ? 64 : 32;  // keys per block
+  constexpr int NKT = BK / 32;
+  constexpr int NQS = D / 16;
+  constexpr int NDT = D / 32;
+  constexpr int TB = BK * T::ROWB;  // one K or V tile
+  constexpr int NI = TB / 1024;
+  constexpr int DMA_MIN = 2 * (NI / 4);
+  constexpr int DMA_MAX = 2 * ((NI + 3) / 4);
+  static_assert(2 * DMA_MAX <= 63, "vmcnt range");
+  __shared__ __attribute__((aligned(1024))) char smem_[4 * TB];  // K0 K1 V0 V1
+  SDPA_LDS char* const smem = (SDPA_LDS char*)smem_;
+  const unsigned lds_base = (unsigned)(uintptr_t)smem;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int col = lane & 31, hl = lane >> 5;
+  const int row_tiles = (a.R + 127) / 128;
+  const int rt = blockIdx.x % row_tiles;
+  const int z = blockIdx.x / row_tiles;
+  const int b = z / a.Hkv, kvh = z % a.Hkv;
+  const int r_wg = rt * 128;
+  const int r = r_wg + wave * 32 + col;
+  const bool row_ok = r < a.R;
+  const int rc = min(r, a.R - 1);
+  const int iq = rc / a.G;
+  const int hq = kvh * a.G + rc % a.G;
+  const int pos = iq + a.off;
+  const int pmax_wg = (min(a.R, r_wg + 128) - 1) / a.G + a.off;
+  const int pmin_wg = r_wg / a.G + a.off;
+
+  int k_lo = 0, k_hi = a.Lk;
+  if (a.mask != MASK_NONE) k_hi = min(a.Lk, pmax_wg + 1);
+  if (a.mask == MASK_WINDOW) k_lo = max(0, pmin_wg - a.window + 1);
+  const int kb_first = k_lo / BK;
+  const int nblk = max(0, (k_hi + BK - 1) / BK - kb_first);
+
+  const char* kbase = (const char*)a.k + ((int64_t)b * a.ks[0] + (int64_t)kvh * a.ks[1]) * 2;
+  const char* vbase = (const char*)a.v + ((int64_t)b * a.vs[0] + (int64_t)kvh * a.vs[1]) * 2;
+  const int64_t kstr = a.ks[2] * 2, vstr = a.vs[2] * 2;
+  auto dma = [&](int blk, int buf) __attribute__((always_inline)) {
+    const int k0 = blk * BK;
+    dma_rows<D, BK, 4>(lds_base + buf * TB, wave_u, lane, a.dqk / 8,
+                       [&](int row) { return kbase + (int64_t)min(k0 + row, a.Lk - 1) * kstr; });
+    dma_rows<D, BK, 4>(lds_base + (2 + buf) * TB, wave_u, lane, a.dv / 8,
+                       [&](int row) { return vbase + (int64_t)min(k0 + row, a.Lk - 1) * vstr; });
+  };
+  if (nblk > 0) dma(kb_first, 0);
+
+  // Q and dO fragments (B operands), zero past the real dims and rows
+  u32x4 qf[NQS], of[NQS];
+  {
+    const char* qrow = (const char*)a.q + ((int64_t)b * a.qs[0] + (int64_t)hq * a.qs[1] + (int64_t)iq * a.qs[2]) * 2;
+    const char* drow =
+        (const char*)a.dout + ((int64_t)b * a.os[0] + (int64_t)hq * a.os[1] + (int64_t)iq * a.os[2]) * 2;
+#pragma unroll
+    for (int s = 0; s < NQS; ++s) {
+      const int d = 16 * s + 8 * hl;
+      qf[s] = (row_ok && d < a.dqk) ? *(const u32x4*)(qrow + d * 2) : u32x4{0u, 0u, 0u, 0u};
+      of[s] = (row_ok && d < a.dv) ? *(const u32x4*)(drow + d * 2) : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  const int64_t wrow = (int64_t)z * a.Rp + rc;
+  const float lse2 = row_ok ? a.ws_lse2[wrow] : __builtin_inff();
+  const float drow_d = row_ok ? a.ws_d[wrow] : 0.f;
+  f32x16 acc[NDT];
+#pragma unroll
+  for (int t = 0; t < NDT; ++t) acc[t] = f32x16{};
+  wait_vmcnt<0>();  // block 0 and the register loads have landed
+  if (nblk > 1) dma(kb_first + 1, 1);
+
+  for (int j = 0; j < nblk; ++j) {
+    if (j + 1 < nblk) wait_vmcnt<DMA_MIN>();
+    else wait_vmcnt<0>();
+    __syncthreads();
+    const SDPA_LDS char* kt_ = smem + (j & 1) * TB;
+    const SDPA_LDS char* vt_ = smem + (2 + (j & 1)) * TB;
+    const int k0 = (kb_first + j) * BK;
+    f32x16 sacc[NKT], pacc[NKT];
+#pragma unroll
+    for (int kt = 0; kt < NKT; ++kt) {
+      sacc[kt] = f32x16{};
+      pacc[kt] = f32x16{};
+#pragma unroll
+      for (int s = 0; s < NQS; ++s) {
+        sacc[kt] = E::mma(row_frag<D>(kt_, kt * 32 + col, s, hl), qf[s], sacc[kt]);
+        pacc[kt] = E::mma(row_frag<D>(vt_, kt * 32 + col, s, hl), of[s], pacc[kt]);
+      }
+      // register e: key k0 + 32 kt + 8 (e / 4) + 4 hl + e % 4 of this row
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int key = k0 + kt * 32 + 8 * (e >> 2) + 4 * hl + (e & 3);
+        bool vis = key < a.Lk;
+        if (a.mask != MASK_NONE) vis = vis && key <= pos;
+        if (a.mask == MASK_WINDOW) vis = vis && key > pos - a.window;
+        const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][e], a.c, -lse2)) : 0.f;
+        sacc[kt][e] = p * (pacc[kt][e] - drow_d);  // dS^T (without the scale)
+      }
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const u32x4 bf = pack_frag<E>(sacc[kt], s2);
+#pragma unroll
+        for (int t = 0; t < NDT; ++t) acc[t] = E::mma(tr_frag<D>(kt_, kt * 32 + 16 * s2, t, lane), bf, acc[t]);
+      }
+    }
+    if (j + 2 < nblk) {
+      __syncthreads();  // every wave is done with block j's buffers
+      dma(kb_first + j + 2, j & 1);
+    }
+  }
+
+  if (!row_ok) return;
+  char* orow = (char*)a.grad_q + ((int64_t)b * a.qs[0] + (int64_t)hq * a.qs[1] + (int64_t)iq * a.qs[2]) * 2;
+#pragma unroll
+  for (int t = 0; t < NDT; ++t) {
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int d = t * 32 + 8 * i4 + 4 * hl;
+      if (d < a.dqk) {
+        u32x2 w;
+        w[0] = E::pack2(acc[t][4 * i4 + 0] * a.scale, acc[t][4 * i4 + 1] * a.scale);
+        w[1] = E::pack2(acc[t][4 * i4 + 2] * a.scale, acc[t][4 * i4 + 3] * a.scale);
+        *(u32x2*)(orow + d * 2) = w;
+      }
+    }
+  }
+}
+
+// ---- dK, dV: keys on the lanes, walking the query blocks ----
+template <class E, int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void bwd_dkdv_kernel(BwdArgs a) {
+  using T = Tile<D>;
+  constexpr int BQ = 32;  // packed rows per block
+  constexpr int NQS = D / 16;
+  constexpr int NDT = D / 32;
+  constexpr int REG = 128 * T::ROWB;  // K (or V) rows of the tile's 128 keys
+  constexpr int TQ = BQ * T::ROWB;    // one Q or dO tile
+  constexpr int NIQ = TQ / 1024;
+  constexpr int BUF = 2 * TQ + 512;   // Q, dO, then lse2 / D / query index (3 x 128 bytes)
+  constexpr int DMA_MIN = 2 * (NIQ / 4);
+  constexpr int DMA_MAX = 2 * ((NIQ + 3) / 4) + 1;
+  static_assert(2 * DMA_MAX <= 63, "vmcnt range");
+  __shared__ __attribute__((aligned(1024))) char smem_[2 * REG + 2 * BUF];
+  SDPA_LDS char* const smem = (SDPA_LDS char*)smem_;
+  const unsigned lds_base = (unsigned)(uintptr_t)smem;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int col = lane & 31, hl = lane >> 5;
+  const int key_tiles = (a.Lk + 127) / 128;
+  const int kti = blockIdx.x % key_tiles;
+  const int z = blockIdx.x / key_tiles;
+  const int b = z / a.Hkv, kvh = z % a.Hkv;
+  const int k_wg = kti * 128;
+  const int key = k_wg + wave * 32 + col;  // this lane's key
+
+  // packed rows that may see a key of the tile: causal needs pos >= k_wg,
+  // a window pos - W < k_wg + 127
+  int64_t r_lo = 0, r_hi = a.R;
+  if (a.mask != MASK_NONE) r_lo = (int64_t)max(0, k_wg - a.off) * a.G;
+  if (a.mask == MASK_WINDOW) {
+    const int64_t i_hi = (int64_t)min(a.Lk - 1, k_wg + 127) + a.window - 1 - a.off;  // last query that sees it
+    r_hi = min<int64_t>(a.R, i_hi < 0 ? 0 : (i_hi + 1) * a.G);
+  }
+  const int jb0 = (int)(min<int64_t>(r_lo, a.R) / BQ);
+  const int nblk = r_hi > r_lo ? (int)((r_hi + BQ - 1) / BQ) - jb0 : 0;
+
+  const char* kbase = (const char*)a.k + ((int64_t)b * a.ks[0] + (int64_t)kvh * a.ks[1]) * 2;
+  const char* vbase = (const char*)a.v + ((int64_t)b * a.vs[0] + (int64_t)kvh * a.vs[1]) * 2;
+  const int64_t kstr = a.ks[2] * 2, vstr = a.vs[2] * 2;
+  const SDPA_LDS char* kreg = smem;
+  const SDPA_LDS char* vreg = smem + REG;
+  dma_rows<D, 128, 4>(lds_base, wave_u, lane, a.dqk / 8,
+                      [&](int row) { return kbase + (int64_t)min(k_wg + row, a.Lk - 1) * kstr; });
+  dma_rows<D, 128, 4>(lds_base + REG, wave_u, lane, a.dv / 8,
+                      [&](int row) { return vbase + (int64_t)min(k_wg + row, a.Lk - 1) * vstr; });
+
+  auto dma_blk = [&](int jb, int buf) __attribute__((always_inline)) {
+    const unsigned qb = lds_base + 2 * REG + buf * BUF;
+    const int r0 = jb * BQ;
+    auto qrow = [&](int row) {
+      const int rr = min(r0 + row, a.R - 1);
+      const int i = rr / a.G, h = kvh * a.G + rr % a.G;
+      return (const char*)a.q + ((int64_t)b * a.qs[0] + (int64_t)h * a.qs[1] + (int64_t)i * a.qs[2]) * 2;
+    };
+    auto drow = [&](int row) {
+      const int rr = min(r0 + row, a.R - 1);
+      const int i = rr / a.G, h = kvh * a.G + rr % a.G;
+      return (const char*)a.dout + ((int64_t)b * a.os[0] + (int64_t)h * a.os[1] + (int64_t)i * a.os[2]) * 2;
+    };
+    dma_rows<D, BQ, 4>(qb, wave_u, lane, a.dqk / 8, qrow);
+    dma_rows<D, BQ, 4>(qb + TQ, wave_u, lane, a.dv / 8, drow);
+    if (wave_u == 0) {
+      // 32 rows of lse2, D and the query index: 8 lanes (16 bytes) each
+      if (lane < 24) {
+        const int part = lane >> 3, q4 = 4 * (lane & 7);
+        const char* src = part == 0 ? (const char*)(a.ws_lse2 + (int64_t)z * a.Rp + r0 + q4)
+                          : part == 1 ? (const char*)(a.ws_d + (int64_t)z * a.Rp + r0 + q4)
+                                      : (const char*)(a.ws_qi + r0 + q4);
+        lds_dma16<false>(src, qb + 2 * TQ);
+      }
+    }
+  };
+  if (nblk > 0) dma_blk(jb0, 0);
+  f32x16 dk[NDT], dv[NDT];
+#pragma unroll
+  for (int t = 0; t < NDT; ++t) {
+    dk[t] = f32x16{};
+    dv[t] = f32x16{};
+  }
+  wait_vmcnt<0>();  // K, V rows and block 0 have landed
+  if (nblk > 1) dma_blk(jb0 + 1, 1);
+
+  for (int j = 0; j < nblk; ++j) {
+    if (j + 1 < nblk) wait_vmcnt<DMA_MIN>();
+    else wait_vmcnt<0>();
+    __syncthreads();
+    const SDPA_LDS char* qt = smem + 2 * REG + (j & 1) * BUF;
+    const SDPA_LDS char* dt = qt + TQ;
+    const SDPA_LDS char* sm = qt + 2 * TQ;
+    f32x16 sacc = f32x16{}, pacc = f32x16{};
+#pragma unroll
+    for (int s = 0; s < NQS; ++s) {
+      const bool dq_ok = 16 * s + 8 * hl < a.dqk, dv_ok = 16 * s + 8 * hl < a.dv;
+      u32x4 qa = row_frag<D>(qt, col, s, hl), da = row_frag<D>(dt, col, s, hl);
+      if (!dq_ok) qa = u32x4{0u, 0u, 0u, 0u};  // padded head dims add nothing
+      if (!dv_ok) da = u32x4{0u, 0u, 0u, 0u};
+      sacc = E::mma(qa, row_frag<D>(kreg, wave * 32 + col, s, hl), sacc);
+      pacc = E::mma(da, row_frag<D>(vreg, wave * 32 + col, s, hl), pacc);
+    }
+    // register e: packed row r0 + 8 (e / 4) + 4 hl + e % 4 of this lane's key
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int rb = 8 * g + 4 * hl;
+      const f32x4 l4 = *(const SDPA_LDS f32x4*)(sm + rb * 4);
+      const f32x4 d4 = *(const SDPA_LDS f32x4*)(sm + 128 + rb * 4);
+      const u32x4 i4 = *(const SDPA_LDS u32x4*)(sm + 256 + rb * 4);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int e = 4 * g + t;
+        const int pos = (int)i4[t] + a.off;
+        bool vis = true;
+        if (a.mask != MASK_NONE) vis = key <= pos;
+        if (a.mask == MASK_WINDOW) vis = vis && key > pos - a.window;
+        const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[e], a.c, -l4[t])) : 0.f;
+        sacc[e] = p;                     // P
+        pacc[e] = p * (pacc[e] - d4[t]);  // dS (without the scale)
+      }
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const u32x4 bp = pack_frag<E>(sacc, s2);
+      const u32x4 bs = pack_frag<E>(pacc, s2);
+#pragma unroll
+      for (int t = 0; t < NDT; ++t) {
+        dv[t] = E::mma(tr_frag<D>(dt, 16 * s2, t, lane), bp, dv[t]);
+        dk[t] = E::mma(tr_frag<D>(qt, 16 * s2, t, lane), bs, dk[t]);
+      }
+    }
+    if (j + 2 < nblk) {
+      __syncthreads();  // every wave is done with block j's buffers
+      dma_blk(jb0 + j + 2, j & 1);
+    }
+  }
+
+  if (key >= a.Lk) return;
+  char* krow = (char*)a.grad_k + ((int64_t)b * a.ks[0] + (int64_t)kvh * a.ks[1] + (int64_t)key * a.ks[2]) * 2;
+  char* vrow = (char*)a.grad_v + ((int64_t)b * a.vs[0] + (int64_t)kvh * a.vs[1] + (int64_t)key * a.vs[2]) * 2;
+#pragma unroll
+  for (int t = 0; t < NDT; ++t) {
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int d = t * 32 + 8 * i4 + 4 * hl;
+      if (d < a.dqk) {
+        u32x2 w;
+        w[0] = E::pack2(dk[t][4 * i4 + 0] * a.scale, dk[t][4 * i4 + 1] * a.scale);
+        w[1] = E::pack2(dk[t][4 * i4 + 2] * a.scale, dk[t][4 * i4 + 3] * a.scale);
+        *(u32x2*)(krow + d * 2) = w;
+      }
+      if (d < a.dv) {
+        u32x2 w;
+        w[0] = E::pack2(dv[t][4 * i4 + 0], dv[t][4 * i4 + 1]);
+        w[1] = E::pack2(dv[t][4 * i4 + 2], dv[t][4 * i4 + 3]);
+        *(u32x2*)(vrow + d * 2) = w;
+      }
+    }
+  }
+}
+
+template <class E, int D>
+int launch_bwd_dims(const BwdPlan& p, const BwdArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(bwd_prep_kernel<E>, dim3((unsigned)p.prep_grid), dim3(256), 0, s, a);
+  if (p.dq_grid > 0) hipLaunchKernelGGL((bwd_dq_kernel<E, D>), dim3((unsigned)p.dq_grid), dim3(256), 0, s, a);
+  if (p.dkdv_grid > 0)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<E, D>), dim3((unsigned)p.dkdv_grid), dim3(256), 0, s, a);
+  return SDPA_OK;
+}
+
+template <class E>
+int launch_bwd_type(const BwdPlan& p, const BwdArgs& a, hipStream_t s) {
+  switch (p.d_pad) {
+    case 32: return launch_bwd_dims<E, 32>(p, a, s);
+    case 64: return launch_bwd_dims<E, 64>(p, a, s);
+    case 96: return launch_bwd_dims<E, 96>(p, a, s);
+    case 128: return launch_bwd_dims<E, 128>(p, a, s);
+    default: return SDPA_E_HEAD_DIM;
+  }
+}
+
+}  // namespace dev
+
+int launch_backward(const BwdPlan& p, const BwdArgs& a, void* stream, std::string* err) {
+  const hipStream_t s = (hipStream_t)stream;
+  const int rc = p.dtype == SDPA_BF16 ? dev::launch_bwd_type<dev::BF16>(p, a, s)
+                                      : dev::launch_bwd_type<dev::F16>(p, a, s);
+  if (rc != SDPA_OK) {
+    *err = "no backward kernel for padded head dim " + std::to_string(p.d_pad);
+    return rc;
+  }
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    *err = std::string("backward kernel launch failed: ") + hipGetErrorString(e);
+    return SDPA_E_HIP;
+  }
+  return SDPA_OK;
+}
+
+}  // namespace sdpa

@@ -263,6 +263,41 @@ int make_plan(const sdpa_desc_t* d, Plan* p, std::string* err) {
   return SDPA_OK;
 }
 
+int make_bwd_plan(const sdpa_desc_t* d, BwdPlan* p, std::string* err) {
+  // Everything the forward checks (shapes, strides, masks, scale) holds here
+  // too; the backward adds its own limits.
+  Plan fp;
+  const int rc = make_plan(d, &fp, err);
+  if (rc != SDPA_OK) return rc;
+  if (d->dtype == SDPA_F32)
+    return fail(err, SDPA_E_DTYPE, "the backward pass runs float16 and bfloat16 only");
+  if (d->dim_qk > 128 || d->dim_v > 128) {
+    std::ostringstream s;
+    s << "no backward kernel for head dims (Dqk=" << d->dim_qk << ", Dv=" << d->dim_v
+      << "): the backward pass supports head dims up to 128";
+    return fail(err, SDPA_E_HEAD_DIM, s.str());
+  }
+  if (d->mask_array != SDPA_MASK_ARRAY_NONE)
+    return fail(err, SDPA_E_MASK, "the backward pass takes the causal / window modes, not a mask array");
+  const int64_t m = std::max(d->dim_qk, d->dim_v);
+  const int64_t G = d->heads_q / d->heads_kv;
+  const int64_t R = G * d->len_q;
+  const int64_t Z = d->batch * d->heads_kv;
+  p->dtype = d->dtype;
+  p->d_pad = (int)ceil_div(m, 32) * 32;
+  p->mask = fp.mask;
+  p->window = fp.window;
+  p->Rp = (int)ceil_div(R, 32) * 32;
+  p->prep_grid = ceil_div(Z * p->Rp, 16);  // 16 rows per 256-thread workgroup
+  p->dq_grid = Z * ceil_div(R, 128);       // 128 packed rows per workgroup
+  p->dkdv_grid = Z * ceil_div(d->len_k, 128);  // 128 keys per workgroup
+  if (p->prep_grid > 0x7fffffffLL || p->dq_grid > 0x7fffffffLL || p->dkdv_grid > 0x7fffffffLL)
+    return fail(err, SDPA_E_SHAPE, "grid too large");
+  // [lse2][D] per (batch, KV head, packed row), then the query index per row
+  p->workspace = ((size_t)(2 * Z * p->Rp + p->Rp) * 4 + 255) / 256 * 256;
+  return SDPA_OK;
+}
+
 std::string describe(const sdpa_desc_t* d, const Plan& p) {
   std::ostringstream s;
   const char* fam = p.kind == KIND_DECODE ? "decode" : (p.kind == KIND_SHORT ? "short" : "prefill");

@@ -239,6 +239,78 @@ int sdpa_forward(const sdpa_desc_t* d, const void* q, const void* k, const void*
   return sdpa_forward_varlen(d, q, k, v, nullptr, nullptr, nullptr, o, lse, workspace, workspace_bytes, stream);
 }
 
+int sdpa_backward_workspace_bytes(const sdpa_desc_t* d, size_t* bytes) {
+  if (!bytes) return set_error(SDPA_E_NULL, "bytes is NULL");
+  sdpa::BwdPlan p;
+  std::string err;
+  const int rc = sdpa::make_bwd_plan(d, &p, &err);
+  if (rc != SDPA_OK) return set_error(rc, err);
+  *bytes = p.workspace;
+  return ok();
+}
+
+int sdpa_backward(const sdpa_desc_t* d, const void* q, const void* k, const void* v, const void* o,
+                  const void* dout, const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                  size_t workspace_bytes, sdpa_stream_t stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv)
+    return set_error(SDPA_E_NULL, "q, k, v, o, dout, lse, dq, dk and dv must be non-NULL device pointers");
+  sdpa::BwdPlan p;
+  std::string err;
+  int rc = sdpa::make_bwd_plan(d, &p, &err);
+  if (rc != SDPA_OK) return set_error(rc, err);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(dq) ||
+      !aligned16(dk) || !aligned16(dv))
+    return set_error(SDPA_E_STRIDE, "q, k, v, o, dout, dq, dk and dv must be 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(lse) & 3u) return set_error(SDPA_E_STRIDE, "lse must be 4-byte aligned");
+  if (!workspace || workspace_bytes < p.workspace)
+    return set_error(SDPA_E_WORKSPACE, "the backward pass needs a workspace of " + std::to_string(p.workspace) +
+                                           " bytes (got " + std::to_string(workspace_bytes) + ")");
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+    return set_error(SDPA_E_WORKSPACE, "workspace must be 256-byte aligned");
+  rc = check_device(&err);
+  if (rc != SDPA_OK) return set_error(rc, err);
+
+  sdpa::BwdArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dout = dout;
+  a.lse = lse;
+  a.grad_q = dq;
+  a.grad_k = dk;
+  a.grad_v = dv;
+  for (int j = 0; j < 3; ++j) {
+    a.qs[j] = d->q_stride[j];
+    a.ks[j] = d->k_stride[j];
+    a.vs[j] = d->v_stride[j];
+    a.os[j] = d->o_stride[j];
+  }
+  a.B = (int)d->batch;
+  a.Hq = (int)d->heads_q;
+  a.Hkv = (int)d->heads_kv;
+  a.Lq = (int)d->len_q;
+  a.Lk = (int)d->len_k;
+  a.dqk = (int)d->dim_qk;
+  a.dv = (int)d->dim_v;
+  a.G = (int)(d->heads_q / d->heads_kv);
+  a.R = a.G * a.Lq;
+  a.Rp = p.Rp;
+  a.off = a.Lk - a.Lq;
+  a.mask = p.mask;
+  a.window = p.window;
+  a.c = (float)((double)d->scale * 1.4426950408889634074);
+  a.scale = d->scale;
+  const size_t zrp = (size_t)d->batch * d->heads_kv * p.Rp;
+  a.ws_lse2 = static_cast<float*>(workspace);
+  a.ws_d = a.ws_lse2 + zrp;
+  a.ws_qi = reinterpret_cast<int*>(a.ws_d + zrp);
+  rc = sdpa::launch_backward(p, a, stream, &err);
+  if (rc != SDPA_OK) return set_error(rc, err);
+  return ok();
+}
+
 int sdpa_set_profile_events(void* start, void* stop) {
   if ((start == nullptr) != (stop == nullptr))
     return set_error(SDPA_E_NULL, "start and stop must both be set or both be NULL");

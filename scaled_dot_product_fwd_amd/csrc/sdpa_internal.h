@@ -153,6 +153,42 @@ SDPA_DECLARE_LAUNCH(launch_attn_f32_decode_mask)
 #undef SDPA_DECLARE_LAUNCH
 int launch_combine(const Plan& p, const CombineArgs& a, void* stream, std::string* err);
 
+// ---------------------------------------------------------------------------
+// Backward pass (dQ, dK, dV).
+// ---------------------------------------------------------------------------
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;   // strides of o
+  const float* lse;   // forward log-sum-exp [B, Hq, Lq], natural log
+  void* grad_q;       // dQ, strides of q
+  void* grad_k;       // dK, strides of k
+  void* grad_v;       // dV, strides of v
+  float* ws_lse2;     // [B*Hkv][Rp] lse in log2 units per packed row (+inf: row has no gradient)
+  float* ws_d;        // [B*Hkv][Rp] D = dO . O per packed row
+  int* ws_qi;         // [Rp] query index of packed row r (r / G)
+  int64_t qs[3], ks[3], vs[3], os[3];
+  int B, Hq, Hkv, Lq, Lk, dqk, dv, G, R, Rp;
+  int off;            // Lk - Lq
+  int mask, window;
+  float c;            // scale * log2(e), any sign
+  float scale;
+};
+
+struct BwdPlan {
+  int dtype;
+  int d_pad;          // both head dims padded to this (32, 64, 96 or 128)
+  int mask, window;   // canonical
+  int Rp;             // packed rows rounded up to 32
+  int64_t prep_grid, dq_grid, dkdv_grid;
+  size_t workspace;
+};
+
+int make_bwd_plan(const sdpa_desc_t* d, BwdPlan* p, std::string* err);
+int launch_backward(const BwdPlan& p, const BwdArgs& a, void* stream, std::string* err);
+
 // LDS bytes of an attention kernel instance (host mirror of the kernel's
 // static layout, used by the planner's capacity check).
 size_t attn_lds_bytes(int dtype, int dqk_pad, int dv_pad, const Family& f, int mes = 0);

@@ -1,0 +1,98 @@
+"""GPU parity of the backward pass (dQ, dK, dV) against the float64 oracle.
+
+The forward runs on the GPU first (its o and lse feed the backward, as in
+training); the oracle's gradients come from the definition alone.  Bound:
+max |g - ref| <= TOL_REL * max |ref| per gradient, with TOL_REL = 2e-2 for
+bfloat16 and 4e-3 for float16 -- about five units of the type's rounding
+(2^-8, 2^-11): P and dS are rounded to the input type before their matrix
+products and each output once more, while the float32 accumulation adds
+far less.
+"""
+
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import scaled_dot_product_fwd_amd as sdpa
+from oracle import sdpa_bwd_ref
+from scaled_dot_product_fwd_amd.synth import default_scale, make_qkv, randn
+
+pytestmark = pytest.mark.gpu
+
+TOL_REL = {torch.bfloat16: 2e-2, torch.float16: 4e-3}
+
+
+def _say(*a):
+    print("CASE", *a, flush=True)
+
+
+def run_bwd(b, hq, hkv, lq, lk, dqk, dv, dt, mask, w, seed, scale=None):
+    q, k, v = make_qkv(b, hq, hkv, lq, lk, dqk, dv, dt, seed)
+    do = randn((b, hq, lq, dv), seed + 3, dt)
+    scale = default_scale(dqk) if scale is None else scale
+    dev = torch.device("cuda", 0)
+    qd, kd, vd, dod = q.to(dev), k.to(dev), v.to(dev), do.to(dev)
+    o, lse = sdpa.forward(qd, kd, vd, scale=scale, mask=mask, window_size=w, return_lse=True)
+    grads = [torch.full_like(x, float("nan")) for x in (qd, kd, vd)]
+    gq, gk, gv = sdpa.backward(qd, kd, vd, o, dod, lse, scale=scale, mask=mask, window_size=w,
+                               dq=grads[0], dk=grads[1], dv=grads[2])
+    torch.cuda.synchronize()
+    ref = sdpa_bwd_ref(q, k, v, do, scale, mask, w)
+    return [g.cpu().double().numpy() for g in (gq, gk, gv)], ref
+
+
+def check_bwd(case, scale=None):
+    b, hq, hkv, lq, lk, dqk, dv, dt, mask, w = case
+    dt = {"bf16": torch.bfloat16, "f16": torch.float16}[dt]
+    got, ref = run_bwd(b, hq, hkv, lq, lk, dqk, dv, dt, mask, w, zlib.crc32(repr(case).encode()) % 10000, scale)
+    errs = []
+    for name, g, r in zip(("dq", "dk", "dv"), got, ref):
+        assert not np.isnan(g).any(), f"unwritten {name} elements"
+        scale_ref = max(float(np.abs(r).max()), 1e-30)
+        e = float(np.abs(g - r).max()) / scale_ref
+        errs.append(e)
+        assert e <= TOL_REL[dt], f"{name}: max|g - ref| / max|ref| = {e:.3e} > {TOL_REL[dt]:.0e}"
+    print("  rel errors dq dk dv", " ".join(f"{e:.2e}" for e in errs), flush=True)
+
+
+CASES = [
+    # b, hq, hkv, lq, lk, dqk, dv, dtype, mask, window
+    (1, 4, 4, 128, 128, 64, 64, "bf16", "none", 0),
+    (1, 4, 2, 200, 200, 64, 64, "bf16", "causal", 0),
+    (2, 4, 1, 77, 300, 128, 128, "f16", "causal", 0),
+    (1, 2, 2, 150, 333, 96, 96, "bf16", "window", 37),
+    (1, 8, 2, 130, 130, 128, 128, "bf16", "none", 0),
+    (1, 2, 2, 100, 100, 32, 32, "f16", "causal", 0),
+    (1, 4, 2, 1, 500, 128, 128, "bf16", "causal", 0),
+    (1, 2, 1, 70, 70, 72, 72, "bf16", "none", 0),
+    (1, 3, 1, 40, 90, 48, 40, "f16", "causal", 0),
+    (1, 2, 2, 257, 257, 128, 128, "bf16", "window", 100),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "-".join(str(x) for x in c))
+def test_bwd_cases(case):
+    _say(case)
+    check_bwd(case)
+
+
+@pytest.mark.parametrize("scale", [-0.2, 0.0])
+def test_bwd_negative_and_zero_scale(scale):
+    _say("bwd scale", scale)
+    check_bwd((1, 2, 1, 60, 90, 64, 64, "bf16", "causal", 0), scale=scale)
+
+
+def test_bwd_is_deterministic():
+    _say("bwd determinism")
+    a, _ = run_bwd(1, 4, 2, 150, 150, 64, 64, torch.bfloat16, "causal", 0, 5)
+    b, _ = run_bwd(1, 4, 2, 150, 150, 64, 64, torch.bfloat16, "causal", 0, 5)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+
+
+def test_bwd_causal_l1024_d128():
+    """Training-size layer: B=1, Hq=8, Hkv=2, L=1024, D=128, causal."""
+    _say("bwd causal L=1024 D=128")
+    check_bwd((1, 8, 2, 1024, 1024, 128, 128, "bf16", "causal", 0))
