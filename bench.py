@@ -63,15 +63,16 @@ def pages_shape(s):
 
 
 def shape(name, b, hq, hkv, lq, lk, dqk, dv, dtype, mask, window, seed, arr=None, arr_window=0,
-          varlen=False):
+          varlen=False, bwd=False):
     """One benchmark shape.  ``arr`` names an explicit mask array given on top
     of the mode: "window_bool" (an [Lq, Lk] boolean band of the last
     ``arr_window`` keys, what callers build without a window mode),
     "bias_add" (an [Lq, Lk] additive N(0, 1) bias) or "pad_bool" (a
     [B, 1, 1, Lk] key-padding mask).  ``varlen`` passes the same per-entry
-    key lengths as "pad_bool" uses as kv_lens instead."""
+    key lengths as "pad_bool" uses as kv_lens instead.  ``bwd`` times the
+    backward pass (dQ, dK, dV) of the shape instead of the forward."""
     return dict(name=name, b=b, hq=hq, hkv=hkv, lq=lq, lk=lk, dqk=dqk, dv=dv, dtype=dtype,
-                mask=mask, window=window, seed=seed, arr=arr, arr_window=arr_window, varlen=varlen)
+                mask=mask, window=window, seed=seed, arr=arr, arr_window=arr_window, varlen=varlen, bwd=bwd)
 
 
 def all_shapes():
@@ -106,6 +107,8 @@ def all_shapes():
     # head dim 512 (zero-padded MFMA dims above 256 land here too)
     out.append(shape("causal_l8192_d512", 1, 16, 2, 8192, 8192, 512, 512, "bf16", "causal", 0, 8000))
     out.append(shape("decode_d512_hkv8_lk16384", 1, 32, 8, 1, 16384, 512, 512, "bf16", "causal", 0, 8001))
+    # backward pass, beside the forward of the same shape (causal_l4096_d128)
+    out.append(shape("bwd_causal_l4096_d128", 1, 16, 16, 4096, 4096, 128, 128, "bf16", "causal", 0, 6001, bwd=True))
     # per-entry key lengths, beside the same lengths as a padding mask
     out.append(shape("decode_b8_hkv8_lk8192_d128", 8, 32, 8, 1, 8192, 128, 128, "bf16", "none", 0, 7000))
     out.append(shape("maskarr_pad_decode_b8_hkv8_lk8192_d128", 8, 32, 8, 1, 8192, 128, 128, "bf16", "none", 0,
@@ -174,6 +177,13 @@ def work(s):
     """
     es = ES[s["dtype"]]
     d = s["dqk"] + s["dv"]
+    if s.get("bwd"):
+        # recompute S once, then dP, dV, dQ, dK: 2 (3 Dqk + 2 Dv) per visible pair;
+        # read q, k, v, o, dO (+ lse), write dq, dk, dv
+        pairs = visible_pairs(s["lq"], s["lk"], s["mask"], s["window"])
+        flops = 2 * s["b"] * s["hq"] * (3 * s["dqk"] + 2 * s["dv"]) * pairs
+        nbytes = es * s["b"] * (s["hq"] * s["lq"] * 2 * d + s["hkv"] * s["lk"] * 2 * d) + 4 * s["b"] * s["hq"] * s["lq"]
+        return flops, nbytes
     if s.get("varlen"):
         kl = kv_lengths(s)
         pairs = sum(visible_pairs(s["lq"], n, s["mask"], s["window"]) for n in kl)
@@ -241,6 +251,10 @@ class HipEvents:
             self.start.append(a.value)
             self.stop.append(b.value)
 
+    def record(self, ev, stream):
+        if self.hip.hipEventRecord(ctypes.c_void_p(ev), ctypes.c_void_p(stream)):
+            raise RuntimeError("hipEventRecord failed")
+
     def elapsed_ms(self, i):
         ms = ctypes.c_float()
         if self.hip.hipEventElapsedTime(ctypes.byref(ms), self.start[i], self.stop[i]):
@@ -250,6 +264,53 @@ class HipEvents:
     def close(self):
         for e in self.start + self.stop:
             self.hip.hipEventDestroy(e)
+
+
+class BwdRunner:
+    """Pre-built inputs (q, k, v, the forward's o and lse, dO), outputs and
+    workspace for repeated raw backward calls.  The HIP events bracket the
+    whole call (its three kernels) on the launch stream."""
+
+    def __init__(self, s):
+        import torch
+
+        import scaled_dot_product_fwd_amd as sdpa
+        from scaled_dot_product_fwd_amd.synth import DTYPES, default_scale, make_qkv, randn
+
+        self.s = s
+        self.sdpa = sdpa
+        dt = DTYPES[s["dtype"]]
+        dev = torch.device("cuda", 0)
+        q, k, v = make_qkv(s["b"], s["hq"], s["hkv"], s["lq"], s["lk"], s["dqk"], s["dv"], dt, s["seed"])
+        do = randn((s["b"], s["hq"], s["lq"], s["dv"]), s["seed"] + 3, dt)
+        self.cpu = (q, k, v, do)
+        self.scale = default_scale(s["dqk"])
+        self.q, self.k, self.v, self.do = q.to(dev), k.to(dev), v.to(dev), do.to(dev)
+        self.o, self.lse = sdpa.forward(self.q, self.k, self.v, scale=self.scale, mask=s["mask"],
+                                        window_size=s["window"], return_lse=True)
+        self.g = [torch.empty_like(x) for x in (self.q, self.k, self.v)]
+        self.desc = sdpa.make_desc(self.q.shape, self.k.shape, self.v.shape, sdpa._dtype_code(dt),
+                                   scale=self.scale, mask=s["mask"], window_size=s["window"])
+        self.plan = "backward: prep + dq (128-row tiles) + dk/dv (128-key tiles)"
+        self.ws_bytes = sdpa.sdpa_backward_workspace_bytes(self.desc)
+        self.ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=dev)
+        self.stream = torch.cuda.current_stream(dev).cuda_stream
+        self.nsets = 1
+        lib = sdpa.load()
+        self._bwd = lib.sdpa_backward
+        self._descref = ctypes.byref(self.desc)
+        self._args = (self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(), self.o.data_ptr(),
+                      self.do.data_ptr(), self.lse.data_ptr(), self.g[0].data_ptr(), self.g[1].data_ptr(),
+                      self.g[2].data_ptr(), self.ws.data_ptr(), self.ws_bytes, self.stream)
+
+    def step(self, i, events=None, j=None):
+        if events is not None:
+            events.record(events.start[j], self.stream)
+        rc = self._bwd(self._descref, *self._args)
+        if events is not None:
+            events.record(events.stop[j], self.stream)
+        if rc:
+            self.sdpa._lib.check(rc)
 
 
 class Runner:
@@ -356,19 +417,33 @@ def cpu_baseline(s, runner, budget_s=12.0):
     budget, evenly spaced query rows are recomputed one by one instead.  The
     work done is scaled to the metric's unit.
     """
-    from oracle import sdpa_ref, sdpa_ref_rows, sdpa_ref_varlen
+    from oracle import sdpa_bwd_ref, sdpa_ref, sdpa_ref_rows, sdpa_ref_varlen
 
     try:
         from threadpoolctl import threadpool_info
         cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
         cores = os.cpu_count() or 1
-    q, k, v = runner.cpu
+    q, k, v = runner.cpu[:3]
     g = s["hq"] // s["hkv"]
     flops, nbytes = work(s)
     group_flops = flops / s["hkv"]
     t_total, frac, sample = 0.0, 0.0, ""
-    if group_flops < 20e9 * budget_s:  # one group fits the budget at a modest 20 GFLOP/s
+    if s.get("bwd"):
+        # whole query heads (with their KV head) until the budget is spent
+        do = runner.cpu[3]
+        heads = 0
+        t_start = time.perf_counter()
+        while time.perf_counter() - t_start < budget_s and heads < s["b"] * s["hq"]:
+            bi, h = divmod(heads, s["hq"])
+            t0 = time.perf_counter()
+            sdpa_bwd_ref(q[bi:bi + 1, h:h + 1], k[bi:bi + 1, h // g:h // g + 1], v[bi:bi + 1, h // g:h // g + 1],
+                         do[bi:bi + 1, h:h + 1], runner.scale, s["mask"], s["window"])
+            t_total += time.perf_counter() - t0
+            heads += 1
+        frac = heads / (s["b"] * s["hq"])
+        sample = f"{heads} query heads' gradients ({frac:.3f} of one step)"
+    elif group_flops < 20e9 * budget_s:  # one group fits the budget at a modest 20 GFLOP/s
         heads = 0
         t_start = time.perf_counter()
         while time.perf_counter() - t_start < budget_s and heads < 50 * s["hq"]:
@@ -508,7 +583,7 @@ def measure(s, steps, warmup):
     import torch
 
     floor = 3 * INFINITY_CACHE if bound(s) == "hbm" else 0
-    r = Runner(s, floor)
+    r = BwdRunner(s) if s.get("bwd") else Runner(s, floor)
     ms, kms = time_steps(r, steps, warmup)
     flops, nbytes = work(s)
     kmean = sum(kms) / len(kms)
@@ -591,6 +666,7 @@ def main():
         "config": {"workload": s["name"], "B": s["b"], "Hq": s["hq"], "Hkv": s["hkv"], "Lq": s["lq"],
                    "Lk": s["lk"], "Dqk": s["dqk"], "Dv": s["dv"], "mask": s["mask"], "window": s["window"],
                    "mask_array": s["arr"], "kv_lens": kv_lengths(s) if s.get("varlen") else None,
+                   "pass": "backward" if s.get("bwd") else "forward",
                    "kv_sets": res["kv_sets"], "plan": res["plan"]},
         "roofline": {"bound": res["bound"], "achieved": round(res["achieved"], 3), "peak": res["peak"],
                      "unit": res["unit"], "frac": round(res["frac"], 4),

@@ -21,7 +21,7 @@ def test_visible_pairs_closed_form_matches_oracle_count(lq, lk, mask, w):
 
 def test_workload_table_matches_the_five_workloads():
     names = [s["name"] for s in bench.all_shapes()]
-    assert len(names) == 1 + 12 + 20 + 3 + 4 + 5 + 2 + 3
+    assert len(names) == 1 + 12 + 20 + 3 + 4 + 5 + 2 + 1 + 3
     assert bench.DEFAULT in names
     s = bench.SHAPES[bench.DEFAULT]
     assert (s["hq"], s["hkv"], s["lq"], s["lk"], s["dqk"], s["dv"], s["dtype"]) == (64, 8, 1, 32768, 192, 128, "bf16")
@@ -100,3 +100,11 @@ def test_vs_baseline_only_for_the_pages_decode_shapes():
     pages = [n for n, s in bench.SHAPES.items() if bench.pages_shape(s)]
     assert sorted(pages) == sorted(f"decode_hkv{h}_lk{lk}" for h in (4, 8)
                                    for lk in (256, 1024, 4096, 8192, 16384, 32768))
+
+
+def test_backward_workload_counts_five_products():
+    s = bench.SHAPES["bwd_causal_l4096_d128"]
+    f_fwd, _ = bench.work(bench.SHAPES["causal_l4096_d128"])
+    f_bwd, _ = bench.work(s)
+    assert f_bwd * 4 == f_fwd * 10  # 2 (3 Dqk + 2 Dv) vs 2 (Dqk + Dv) per pair at Dqk = Dv
+    assert bench.bound(s) == "mfma"
