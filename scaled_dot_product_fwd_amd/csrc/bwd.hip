@@ -35,15 +35,26 @@ namespace dev {
 
 // LDS tile whose rows hold D 16-bit elements: logical 16-byte chunk c of
 // row r sits at chunk c ^ sw(r), a permutation inside aligned groups of KG
-// chunks, so 16 consecutive rows reading one logical chunk spread over the
-// 256-byte bank window.
+// chunks.  The backward reads the same tile both ways -- 16 consecutive rows
+// at one logical chunk (row operands) and 4 consecutive rows at 4
+// consecutive chunks (transposing reads) -- so sw must spread both over the
+// 256-byte bank window: with u = r >> KSH (rows sharing a window differ in
+// the low KSH bits), sw is a bijection of u's low bits whose two top bits
+// change with u's lowest bits.  (The forward's K swizzle alone is 4x
+// conflicted on the transposing reads at D = 128, its V swizzle 4x on row
+// reads.)
 template <int D>
 struct Tile {
   static constexpr int ROWB = D * 2;
   static constexpr int CH = ROWB / 16;
   static constexpr int KG = (CH % 16 == 0) ? 16 : (CH % 8 == 0) ? 8 : 4;
   static constexpr int KSH = KG == 16 ? 0 : (KG == 8 ? 1 : 2);
-  static __device__ __forceinline__ int sw(int row) { return (row >> KSH) & (KG - 1); }
+  static __device__ __forceinline__ int sw(int row) {
+    const int u = row >> KSH;
+    if constexpr (KG == 16) return ((u & 3) << 2) | ((u >> 2) & 3);
+    else if constexpr (KG == 8) return ((u & 1) << 2) | ((u >> 1) & 3);
+    else return u & 3;
+  }
   static __device__ __forceinline__ int off(int row, int chunk) { return row * ROWB + 16 * (chunk ^ sw(row)); }
 };
 
@@ -185,6 +196,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
   const int pos = iq + a.off;
   const int pmax_wg = (min(a.R, r_wg + 128) - 1) / a.G + a.off;
   const int pmin_wg = r_wg / a.G + a.off;
+  const int pmin_w = min(r_wg + wave * 32, a.R - 1) / a.G + a.off;
+  const int pmax_w = min(r_wg + wave * 32 + 31, a.R - 1) / a.G + a.off;
 
   int k_lo = 0, k_hi = a.Lk;
   if (a.mask != MASK_NONE) k_hi = min(a.Lk, pmax_wg + 1);
@@ -243,15 +256,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
         sacc[kt] = E::mma(row_frag<D>(kt_, kt * 32 + col, s, hl), qf[s], sacc[kt]);
         pacc[kt] = E::mma(row_frag<D>(vt_, kt * 32 + col, s, hl), of[s], pacc[kt]);
       }
-      // register e: key k0 + 32 kt + 8 (e / 4) + 4 hl + e % 4 of this row
+      // register e: key k0 + 32 kt + 8 (e / 4) + 4 hl + e % 4 of this row;
+      // only tiles on a mask edge or past Lk test each key
+      const int kw = k0 + kt * 32;
+      const bool edge = (kw + 32 > a.Lk) || (a.mask != MASK_NONE && kw + 31 > pmin_w) ||
+                        (a.mask == MASK_WINDOW && kw <= pmax_w - a.window);
+      if (edge) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int key = k0 + kt * 32 + 8 * (e >> 2) + 4 * hl + (e & 3);
-        bool vis = key < a.Lk;
-        if (a.mask != MASK_NONE) vis = vis && key <= pos;
-        if (a.mask == MASK_WINDOW) vis = vis && key > pos - a.window;
-        const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][e], a.c, -lse2)) : 0.f;
-        sacc[kt][e] = p * (pacc[kt][e] - drow_d);  // dS^T (without the scale)
+        for (int e = 0; e < 16; ++e) {
+          const int key = kw + 8 * (e >> 2) + 4 * hl + (e & 3);
+          bool vis = key < a.Lk;
+          if (a.mask != MASK_NONE) vis = vis && key <= pos;
+          if (a.mask == MASK_WINDOW) vis = vis && key > pos - a.window;
+          const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][e], a.c, -lse2)) : 0.f;
+          sacc[kt][e] = p * (pacc[kt][e] - drow_d);  // dS^T (without the scale)
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][e], a.c, -lse2));
+          sacc[kt][e] = p * (pacc[kt][e] - drow_d);
+        }
       }
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
@@ -385,23 +410,41 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
       sacc = E::mma(qa, row_frag<D>(kreg, wave * 32 + col, s, hl), sacc);
       pacc = E::mma(da, row_frag<D>(vreg, wave * 32 + col, s, hl), pacc);
     }
-    // register e: packed row r0 + 8 (e / 4) + 4 hl + e % 4 of this lane's key
+    // register e: packed row r0 + 8 (e / 4) + 4 hl + e % 4 of this lane's
+    // key.  Only blocks on a mask edge for this wave's 32 keys test each
+    // pair (rows past R carry lse2 = +inf, so their P is 0 either way).
+    const int r0 = (jb0 + j) * BQ;
+    const int pmin_b = r0 / a.G + a.off;
+    const int pmax_b = min(r0 + BQ - 1, a.R - 1) / a.G + a.off;
+    const int kw = k_wg + wave * 32;
+    const bool edge = (a.mask != MASK_NONE && kw + 31 > pmin_b) ||
+                      (a.mask == MASK_WINDOW && kw <= pmax_b - a.window);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int rb = 8 * g + 4 * hl;
       const f32x4 l4 = *(const SDPA_LDS f32x4*)(sm + rb * 4);
       const f32x4 d4 = *(const SDPA_LDS f32x4*)(sm + 128 + rb * 4);
-      const u32x4 i4 = *(const SDPA_LDS u32x4*)(sm + 256 + rb * 4);
+      if (edge) {
+        const u32x4 i4 = *(const SDPA_LDS u32x4*)(sm + 256 + rb * 4);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int e = 4 * g + t;
-        const int pos = (int)i4[t] + a.off;
-        bool vis = true;
-        if (a.mask != MASK_NONE) vis = key <= pos;
-        if (a.mask == MASK_WINDOW) vis = vis && key > pos - a.window;
-        const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[e], a.c, -l4[t])) : 0.f;
-        sacc[e] = p;                     // P
-        pacc[e] = p * (pacc[e] - d4[t]);  // dS (without the scale)
+        for (int t = 0; t < 4; ++t) {
+          const int e = 4 * g + t;
+          const int pos = (int)i4[t] + a.off;
+          bool vis = true;
+          if (a.mask != MASK_NONE) vis = key <= pos;
+          if (a.mask == MASK_WINDOW) vis = vis && key > pos - a.window;
+          const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[e], a.c, -l4[t])) : 0.f;
+          sacc[e] = p;                     // P
+          pacc[e] = p * (pacc[e] - d4[t]);  // dS (without the scale)
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int e = 4 * g + t;
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[e], a.c, -l4[t]));
+          sacc[e] = p;
+          pacc[e] = p * (pacc[e] - d4[t]);
+        }
       }
     }
 #pragma unroll
