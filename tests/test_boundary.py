@@ -323,3 +323,23 @@ def test_plan_head_dim_512(lq, dqk, dv):
     assert int(p["lds"]) == 2 * 32 * 2048
     if lq == 1:
         assert int(p["splits"]) > 1  # a decode call still spreads its keys over the chip
+
+
+@pytest.mark.parametrize("b,hq,hkv,lq", [(1, 4, 2, 200), (1, 4, 2, 1), (2, 8, 2, 130), (1, 2, 1, 257)])
+def test_backward_workspace_covers_whole_row_blocks(b, hq, hkv, lq):
+    """Per (batch, KV head) the workspace holds lse2 and D for Rp packed rows,
+    Rp = G * Lq rounded up to the dK/dV kernel's 32-row block, then Rp query
+    indices: a block's tile of them never leaves its entry."""
+    d = _desc(b=b, hq=hq, hkv=hkv, lq=lq, lk=300, dqk=64, dv=64, mask="causal")
+    rp = -(-(hq // hkv) * lq // 32) * 32
+    want = -(-(2 * b * hkv * rp + rp) * 4 // 256) * 256
+    assert sdpa.sdpa_backward_workspace_bytes(d) == want
+
+
+def test_backward_validation():
+    for kw, code, needle in [(dict(dtype=_lib.SDPA_F32), "SDPA_E_DTYPE", "float16 and bfloat16"),
+                             (dict(dqk=256, dv=256), "SDPA_E_HEAD_DIM", "up to 128"),
+                             (dict(mask_array=_lib.SDPA_MASK_ARRAY_BOOL, mask_stride=(0, 0, 16)), "SDPA_E_MASK",
+                              "mask array")]:
+        msg = _status(sdpa.sdpa_backward_workspace_bytes, _desc(**kw))
+        assert msg.startswith(code) and needle in msg, msg
