@@ -78,6 +78,18 @@ int launch_one(const Plan& p, const AttnArgs& a, void* stream, std::string* err)
 // query length there)
 #define SDPA_PAIRS16_XL(E, KIND, MA) SDPA_CASE(E, KIND, 512, 512, MA)
 
+// head dims up to 128 (the wide family), 16-bit types
+#define SDPA_PAIRS16_UPTO128(E, KIND, MA) \
+  SDPA_CASE(E, KIND, 32, 32, MA)         \
+  SDPA_CASE(E, KIND, 64, 64, MA)         \
+  SDPA_CASE(E, KIND, 96, 96, MA)         \
+  SDPA_CASE(E, KIND, 128, 128, MA)
+// float32 wide: head dims up to 96 (two waves per SIMD)
+#define SDPA_PAIRS32_UPTO96(E, KIND, MA) \
+  SDPA_CASE(E, KIND, 32, 32, MA)         \
+  SDPA_CASE(E, KIND, 64, 64, MA)         \
+  SDPA_CASE(E, KIND, 96, 96, MA)
+
 // float32 stops at 128.
 #define SDPA_PAIRS32(E, KIND, MA)  \
   SDPA_CASE(E, KIND, 32, 32, MA)   \

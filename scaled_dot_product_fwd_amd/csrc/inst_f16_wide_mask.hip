@@ -1,0 +1,9 @@
+// f16 attention kernels with an explicit mask array, wide family.
+#include "attn_launch.h"
+
+namespace sdpa {
+int launch_attn_f16_wide_mask(const Plan& p, const AttnArgs& a, void* stream, std::string* err) {
+  SDPA_BY_MASK_ARRAY(SDPA_PAIRS16_UPTO128, F16, KIND_WIDE)
+  SDPA_NO_INSTANCE()
+}
+}  // namespace sdpa

@@ -165,8 +165,8 @@ int make_plan(const sdpa_desc_t* d, Plan* p, std::string* err) {
   if (d->num_splits < 0 || d->num_splits > kMaxSplits) {
     return fail(err, SDPA_E_PLAN, "num_splits must be 0 (auto) or 1.." + std::to_string(kMaxSplits));
   }
-  if (d->row_tile != 0 && d->row_tile != 32 && d->row_tile != 64 && d->row_tile != 128) {
-    return fail(err, SDPA_E_PLAN, "row_tile must be 0 (auto), 32, 64 or 128 (got " +
+  if (d->row_tile != 0 && d->row_tile != 32 && d->row_tile != 64 && d->row_tile != 128 && d->row_tile != 256) {
+    return fail(err, SDPA_E_PLAN, "row_tile must be 0 (auto), 32, 64, 128 or 256 (got " +
                                       std::to_string(d->row_tile) + ")");
   }
 
@@ -189,10 +189,21 @@ int make_plan(const sdpa_desc_t* d, Plan* p, std::string* err) {
     return fail(err, SDPA_E_PLAN, "head dim 512 runs 64-row tiles only (row_tile must be 0 or 64, got " +
                                       std::to_string(d->row_tile) + ")");
   }
-  int rows = xl ? 64 : d->row_tile ? d->row_tile : (R <= 32 || R == 64 ? 32 : (R <= 64 ? 64 : 128));
+  // 256 rows (wide family: eight 32-row waves, K/V read once per 256 rows)
+  // for 128 < R <= 256 where its two waves per SIMD fit (head dims up to
+  // 128, float32 up to 96): two 128-row tiles would read K/V twice
+  // (speculative verify Lq=48, G=4, Lk=32768: 48 -> measured below).
+  const bool wide_ok = !xl && std::max(dqk_pad, dv_pad) <= (d->dtype == SDPA_F32 ? 96 : 128);
+  if (d->row_tile == 256 && !wide_ok) {
+    return fail(err, SDPA_E_PLAN, "row_tile 256 needs head dims up to 128 (float32: 96)");
+  }
+  int rows = xl ? 64
+             : d->row_tile ? d->row_tile
+                           : (R <= 32 || R == 64 ? 32 : (R <= 64 ? 64 : (R <= 128 || !wide_ok || R > 256 ? 128 : 256)));
   const int64_t row_tiles = ceil_div(R, rows);
   const int64_t base = B * Hkv * row_tiles;
-  const int kind = xl ? KIND_PREFILL : rows == 32 ? KIND_DECODE : (rows == 64 ? KIND_SHORT : KIND_PREFILL);
+  const int kind = xl ? KIND_PREFILL
+                      : rows == 32 ? KIND_DECODE : (rows == 64 ? KIND_SHORT : (rows == 256 ? KIND_WIDE : KIND_PREFILL));
   const Family fam = family_for(kind, es, dqk_pad, dv_pad, mes);
   const int64_t bk = (int64_t)fam.nwk * fam.bkw;
 
@@ -300,7 +311,10 @@ int make_bwd_plan(const sdpa_desc_t* d, BwdPlan* p, std::string* err) {
 
 std::string describe(const sdpa_desc_t* d, const Plan& p) {
   std::ostringstream s;
-  const char* fam = p.kind == KIND_DECODE ? "decode" : (p.kind == KIND_SHORT ? "short" : "prefill");
+  const char* fam = p.kind == KIND_DECODE  ? "decode"
+                    : p.kind == KIND_SHORT ? "short"
+                    : p.kind == KIND_WIDE  ? "wide"
+                                           : "prefill";
   s << "family=" << fam << " dtype=" << dtype_name(p.dtype) << " dqk=" << d->dim_qk << "->" << p.dqk_pad
     << " dv=" << d->dim_v << "->" << p.dv_pad << " rows_per_wg=" << p.rows_per_wg
     << " waves=" << p.fam.nwq << "x" << p.fam.nwk << (p.fam.nwd > 1 ? "x" + std::to_string(p.fam.nwd) : "")

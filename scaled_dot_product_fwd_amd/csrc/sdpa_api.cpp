@@ -188,13 +188,18 @@ int sdpa_forward_varlen(const sdpa_desc_t* d, const void* q, const void* k, cons
   using L = int (*)(const sdpa::Plan&, const sdpa::AttnArgs&, void*, std::string*);
   // [with a mask array][dtype][kind]
   static const L table[2][3][sdpa::kNumKinds] = {
-      {{sdpa::launch_attn_f32_prefill, sdpa::launch_attn_f32_short, sdpa::launch_attn_f32_decode},
-       {sdpa::launch_attn_f16_prefill, sdpa::launch_attn_f16_short, sdpa::launch_attn_f16_decode},
-       {sdpa::launch_attn_bf16_prefill, sdpa::launch_attn_bf16_short, sdpa::launch_attn_bf16_decode}},
-      {{sdpa::launch_attn_f32_prefill_mask, sdpa::launch_attn_f32_short_mask, sdpa::launch_attn_f32_decode_mask},
-       {sdpa::launch_attn_f16_prefill_mask, sdpa::launch_attn_f16_short_mask, sdpa::launch_attn_f16_decode_mask},
+      {{sdpa::launch_attn_f32_prefill, sdpa::launch_attn_f32_short, sdpa::launch_attn_f32_decode,
+        sdpa::launch_attn_f32_wide},
+       {sdpa::launch_attn_f16_prefill, sdpa::launch_attn_f16_short, sdpa::launch_attn_f16_decode,
+        sdpa::launch_attn_f16_wide},
+       {sdpa::launch_attn_bf16_prefill, sdpa::launch_attn_bf16_short, sdpa::launch_attn_bf16_decode,
+        sdpa::launch_attn_bf16_wide}},
+      {{sdpa::launch_attn_f32_prefill_mask, sdpa::launch_attn_f32_short_mask, sdpa::launch_attn_f32_decode_mask,
+        sdpa::launch_attn_f32_wide_mask},
+       {sdpa::launch_attn_f16_prefill_mask, sdpa::launch_attn_f16_short_mask, sdpa::launch_attn_f16_decode_mask,
+        sdpa::launch_attn_f16_wide_mask},
        {sdpa::launch_attn_bf16_prefill_mask, sdpa::launch_attn_bf16_short_mask,
-        sdpa::launch_attn_bf16_decode_mask}},
+        sdpa::launch_attn_bf16_decode_mask, sdpa::launch_attn_bf16_wide_mask}},
   };
   const L launch = table[p.mask_array != sdpa::MA_NONE][p.dtype][p.kind];
   if (ev_start && hipEventRecord(ev_start, (hipStream_t)stream) != hipSuccess)

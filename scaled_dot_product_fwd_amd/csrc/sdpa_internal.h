@@ -58,8 +58,8 @@ struct Family {
   int nwd = 1;  // waves splitting the dv tiles of the same rows
 };
 
-enum : int { KIND_PREFILL = 0, KIND_SHORT = 1, KIND_DECODE = 2 };
-constexpr int kNumKinds = 3;
+enum : int { KIND_PREFILL = 0, KIND_SHORT = 1, KIND_DECODE = 2, KIND_WIDE = 3 };
+constexpr int kNumKinds = 4;
 
 // Explicit mask array kinds as the kernels see them (0: none).  Bytes per
 // mask element: 1 for a boolean array, the element size for an additive one.
@@ -83,6 +83,10 @@ constexpr Family family_for(int kind, int elem_bytes, int dqk_pad, int dv_pad, i
   if (kind == KIND_DECODE)
     return (key_bytes + 32 * mes) * 128 * 2 <= 160 * 1024 ? Family{1, 4, 32} : Family{1, 2, 32};
   if (kind == KIND_SHORT) return Family{2, 2, 32};
+  // Wide: eight 32-row waves share each 64-key block, so up to 256 packed
+  // rows read K/V once (head dims up to 128, two waves per SIMD).
+  if (kind == KIND_WIDE)
+    return (key_bytes + 256 * mes) * 64 * 2 <= 160 * 1024 ? Family{8, 1, 64} : Family{8, 1, 32};
   // Prefill: 64-key blocks when two workgroups still fit per CU, or when the
   // head dims are so large that one workgroup per CU is all the registers
   // allow anyway (then the longer block halves the per-block overheads).
@@ -98,6 +102,7 @@ constexpr Family family_for(int kind, int elem_bytes, int dqk_pad, int dv_pad, i
 constexpr int wpe_for(int kind, int elem_bytes, int dqk_pad, int dv_pad) {
   const int dmax = dqk_pad > dv_pad ? dqk_pad : dv_pad;
   if (kind == KIND_DECODE) return 1;
+  if (kind == KIND_WIDE) return 2;
   if (elem_bytes == 4) return dmax <= 96 ? 2 : 1;
   if (dqk_pad == 192 && dv_pad == 128) return 2;
   return dmax <= (kind == KIND_PREFILL ? 160 : 128) ? 2 : 1;
@@ -105,7 +110,7 @@ constexpr int wpe_for(int kind, int elem_bytes, int dqk_pad, int dv_pad) {
 
 struct Plan {
   int dtype;
-  int kind;              // KIND_PREFILL / KIND_SHORT / KIND_DECODE
+  int kind;              // KIND_PREFILL / KIND_SHORT / KIND_DECODE / KIND_WIDE
   int dqk_pad, dv_pad;   // head dims rounded up to the instantiated tile dims
   Family fam;
   int rows_per_wg;       // 32 * nwq
@@ -150,6 +155,13 @@ SDPA_DECLARE_LAUNCH(launch_attn_f16_decode_mask)
 SDPA_DECLARE_LAUNCH(launch_attn_f32_prefill_mask)
 SDPA_DECLARE_LAUNCH(launch_attn_f32_short_mask)
 SDPA_DECLARE_LAUNCH(launch_attn_f32_decode_mask)
+// 256-row tiles (head dims up to 128), without and with a mask array
+SDPA_DECLARE_LAUNCH(launch_attn_bf16_wide)
+SDPA_DECLARE_LAUNCH(launch_attn_f16_wide)
+SDPA_DECLARE_LAUNCH(launch_attn_f32_wide)
+SDPA_DECLARE_LAUNCH(launch_attn_bf16_wide_mask)
+SDPA_DECLARE_LAUNCH(launch_attn_f16_wide_mask)
+SDPA_DECLARE_LAUNCH(launch_attn_f32_wide_mask)
 #undef SDPA_DECLARE_LAUNCH
 int launch_combine(const Plan& p, const CombineArgs& a, void* stream, std::string* err);
 

@@ -138,7 +138,8 @@ def test_plan_decode_config_splits_keys():
 
 
 @pytest.mark.parametrize("lq,fam,tiles", [(1, "decode", 1), (8, "decode", 1), (12, "short", 1),
-                                          (16, "decode", 2), (24, "prefill", 1), (64, "prefill", 2)])
+                                          (16, "decode", 2), (24, "prefill", 1), (48, "wide", 1),
+                                          (64, "wide", 1), (65, "prefill", 3)])
 def test_plan_verify_window_family(lq, fam, tiles):
     p = _plan(hq=32, hkv=8, lq=lq, lk=16384, dqk=128, dv=128, dtype=_lib.SDPA_F16)
     assert p["family"] == fam and int(p["row_tiles"]) == tiles
@@ -182,8 +183,8 @@ def test_split_workspace_layout():
 
 
 def test_plan_xcd_grouping():
-    p = _plan(hq=32, hkv=8, lq=64, lk=32768, dqk=128, dv=128, dtype=_lib.SDPA_F16)
-    assert int(p["row_tiles"]) == 2 and int(p["splits"]) > 1 and p["xcd_group"] == "8"
+    p = _plan(hq=32, hkv=8, lq=96, lk=32768, dqk=128, dv=128, dtype=_lib.SDPA_F16)
+    assert int(p["row_tiles"]) == 3 and int(p["splits"]) > 1 and p["xcd_group"] == "8"
     p = _plan(hq=64, hkv=8, lq=1, lk=32768, dqk=192, dv=128)
     assert p["xcd_group"] == "0"
     p = _plan(hq=16, hkv=8, lq=4096, lk=4096, dqk=256, dv=256, mask="window", window_size=1024)
@@ -343,3 +344,19 @@ def test_backward_validation():
                               "mask array")]:
         msg = _status(sdpa.sdpa_backward_workspace_bytes, _desc(**kw))
         assert msg.startswith(code) and needle in msg, msg
+
+
+def test_plan_wide_family_limits():
+    # 128 < R <= 256 with head dims up to 128: one 256-row tile
+    p = _plan(hq=8, hkv=1, lq=30, lk=4096, dqk=128, dv=128)
+    assert p["family"] == "wide" and p["rows_per_wg"] == "256" and p["waves"] == "8x1"
+    # larger dims keep 128-row tiles; forcing 256 there is refused
+    assert _plan(hq=8, hkv=1, lq=30, lk=4096, dqk=256, dv=256)["family"] == "prefill"
+    msg = _status(sdpa.sdpa_workspace_bytes, _desc(hq=8, hkv=1, lq=30, lk=4096, dqk=256, dv=256, row_tile=256))
+    assert msg.startswith("SDPA_E_PLAN") and "row_tile 256" in msg
+    assert _plan(hq=8, hkv=1, lq=30, lk=4096, dqk=128, dv=128, dtype=_lib.SDPA_F32)["family"] == "prefill"
+    assert _plan(hq=8, hkv=1, lq=30, lk=4096, dqk=96, dv=96, dtype=_lib.SDPA_F32)["family"] == "wide"
+    # an additive mask array keeps the LDS within one workgroup's 160 KB
+    p = _plan(hq=8, hkv=1, lq=30, lk=4096, dqk=96, dv=96, dtype=_lib.SDPA_F32,
+              mask_array=_lib.SDPA_MASK_ARRAY_ADD, mask_stride=(0, 0, 4096))
+    assert p["family"] == "wide" and int(p["lds"]) <= 160 * 1024

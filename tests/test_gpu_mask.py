@@ -179,3 +179,10 @@ def test_blocks_removed_by_the_array_are_skipped_exactly(dt, d, kind):
     arr = band if kind == "bool" else torch.where(band, torch.tensor(0.5), torch.tensor(float("-inf"))).to(
         to_dtype(dt))
     check_full(1, 2, 1, L, L, d, d, dt, "none", 0, seed=d, attn_mask=arr)
+
+
+@pytest.mark.parametrize("kind", ["bool", "add"])
+def test_mask_array_wide_family(kind):
+    _say("wide + mask array", kind)
+    check_full(1, 32, 8, 48, 700, 128, 128, "bf16", "causal", 0, seed=61,
+               attn_mask=_mask(kind, (1, 32, 48, 700), 62, "bf16"))

@@ -231,7 +231,7 @@ def test_more_splits_than_key_blocks(splits):
     check_full(1, 4, 1, 2, 150, 64, 64, "f16", "none", 0, seed=55, num_splits=splits)
 
 
-@pytest.mark.parametrize("lq", [48, 64])
+@pytest.mark.parametrize("lq", [96, 130])
 def test_split_plan_with_several_row_tiles(lq):
     """Split plans with more than one row tile per KV head deal their work
     items to XCDs in groups; every row must still come out exactly once."""
@@ -240,3 +240,25 @@ def test_split_plan_with_several_row_tiles(lq):
     plan = dict(t.split("=", 1) for t in sdpa.sdpa_describe_plan(d).split())
     assert int(plan["row_tiles"]) > 1 and int(plan["splits"]) > 1 and plan["xcd_group"] == "8"
     check_full(1, 32, 8, lq, 3000, 128, 128, "f16", "none", 0, seed=61)
+
+
+WIDE = [
+    # 128 < packed rows <= 256: the wide family (256-row tiles, eight waves)
+    (1, 32, 8, 48, 2000, 128, 128, "f16", "none", 0),
+    (1, 32, 8, 64, 1500, 128, 128, "bf16", "causal", 0),
+    (2, 2, 1, 200, 333, 64, 64, "bf16", "causal", 0),
+    (1, 4, 2, 90, 300, 96, 96, "f32", "window", 40),
+    (1, 2, 2, 129, 129, 72, 72, "bf16", "none", 0),
+]
+
+
+@pytest.mark.parametrize("case", WIDE, ids=lambda c: "-".join(str(x) for x in c))
+def test_wide_family(case):
+    b, hq, hkv, lq, lk, dqk, dv, dt, mask, w = case
+    _say("wide", case)
+    check_full(b, hq, hkv, lq, lk, dqk, dv, dt, mask, w, seed=zlib.crc32(repr(case).encode()) % 10000)
+
+
+def test_forced_256_row_tiles_on_a_long_prefill():
+    _say("row_tile 256 prefill")
+    check_full(1, 4, 2, 300, 300, 128, 128, "bf16", "causal", 0, seed=3, row_tile=256)

@@ -115,3 +115,9 @@ def test_varlen_head_dim_512():
     case = (2, 8, 2, 4, 900, 512, 512, "bf16", "causal", 0, [4, 2], [900, 130])
     _say("varlen d512")
     _check(case)
+
+
+def test_varlen_wide_family():
+    case = (2, 32, 8, 48, 1200, 128, 128, "bf16", "causal", 0, [48, 20], [1200, 300])
+    _say("varlen wide")
+    _check(case)
