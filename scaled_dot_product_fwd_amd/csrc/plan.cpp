@@ -25,7 +25,6 @@ namespace sdpa {
 namespace {
 
 constexpr int kTargetCUs = 256;        // gfx950 compute units (MI355X)
-constexpr int kWgsPerCU = 2;           // at most two resident workgroups per CU
 constexpr int64_t kMaxLen = 1 << 30;   // keeps every in-kernel index in int32
 constexpr int kMaxSplits = 1024;
 constexpr int kMaxDim = 512;    // 16-bit types; float32 stops at 128
@@ -217,17 +216,15 @@ int make_plan(const sdpa_desc_t* d, Plan* p, std::string* err) {
     splits = d->num_splits;
   } else {
     // Split the key range when the row tiles alone leave the chip idle: aim
-    // for one full round of resident workgroups (LDS and the waves each
-    // instance is compiled for decide how many fit a CU).  A full-size prefill tile (128 rows) is only split when very few
-    // tiles exist: its partial outputs would cost HBM traffic comparable to
-    // the K/V it reads, while an unsplit wave of large tiles already keeps
-    // the MFMA units busy.
-    const size_t lds_need = attn_lds_bytes(d->dtype, dqk_pad, dv_pad, fam, mes);
-    const int64_t by_waves = 4 * wpe_for(kind, d->dtype == SDPA_F32 ? 4 : 2, dqk_pad, dv_pad) /
-                             (fam.nwq * fam.nwk * fam.nwd);
-    const int64_t resident = std::max<int64_t>(
-        1, std::min<int64_t>({(int64_t)kWgsPerCU, (160 * 1024) / (int64_t)lds_need, by_waves}));
-    const int64_t target = (int64_t)kTargetCUs * resident;
+    // for one workgroup per CU.  A second resident workgroup does not raise a
+    // CU's throughput for these kernels (MFMA and the softmax's VALU work
+    // share each SIMD's issue), while every extra split adds partial-result
+    // traffic and combine work: speculative verify at Lk = 16384, Lq = 32 runs
+    // 39.2 us with 64 splits and 29.3 us with 32.  A full-size prefill tile
+    // (128 rows) is only split when very few tiles exist: its partial outputs
+    // would cost HBM traffic comparable to the K/V it reads, while an unsplit
+    // wave of large tiles already keeps the MFMA units busy.
+    const int64_t target = kTargetCUs;
     const bool starved = rows < 128 ? base < target : base < kTargetCUs / 4;
     if (starved) splits = std::min<int64_t>(ceil_div(target, base), nblocks);
     splits = std::max<int64_t>(1, std::min<int64_t>(splits, kMaxSplits));

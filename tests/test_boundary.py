@@ -177,9 +177,13 @@ def test_forward_without_gpu_tensors_raises():
 
 
 def test_split_workspace_layout():
-    d = _desc(b=2, hq=16, hkv=4, lq=1, lk=5000, dqk=64, dv=64, num_splits=16)
+    # per packed row and split: the unnormalised partial output in float32,
+    # then an (m, l) float32 pair
     rows = 2 * 16 * 1
-    assert sdpa.sdpa_workspace_bytes(d) >= rows * 16 * (64 * 4 + 8)
+    for dtype in (_lib.SDPA_BF16, _lib.SDPA_F16, _lib.SDPA_F32):
+        d = _desc(b=2, hq=16, hkv=4, lq=1, lk=5000, dqk=64, dv=64, num_splits=16, dtype=dtype)
+        o_bytes = (rows * 16 * 64 * 4 + 255) // 256 * 256
+        assert sdpa.sdpa_workspace_bytes(d) == o_bytes + rows * 16 * 8
 
 
 def test_plan_xcd_grouping():
