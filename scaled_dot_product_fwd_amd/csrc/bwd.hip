@@ -117,6 +117,19 @@ __device__ __forceinline__ void dma_rows(unsigned lds, int wave_u, int lane, int
   }
 }
 
+// s_waitcnt takes its count as an immediate: wait until at most n (a
+// wave-uniform count, 0 <= n <= N) vector memory operations are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_upto(int n) {
+  if constexpr (N > 0) {
+    if (n < N) {
+      wait_vmcnt_upto<N - 1>(n);
+      return;
+    }
+  }
+  wait_vmcnt<N>();
+}
+
 template <class E>
 __device__ __forceinline__ float lo16(unsigned w) {
   return E::to_float((unsigned short)(w & 0xffffu));
@@ -173,7 +186,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
   constexpr int NDT = D / 32;
   constexpr int TB = BK * T::ROWB;  // one K or V tile
   constexpr int NI = TB / 1024;
-  constexpr int DMA_MIN = 2 * (NI / 4);
   constexpr int DMA_MAX = 2 * ((NI + 3) / 4);
   static_assert(2 * DMA_MAX <= 63, "vmcnt range");
   __shared__ __attribute__((aligned(1024))) char smem_[4 * TB];  // K0 K1 V0 V1
@@ -208,12 +220,37 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
   const char* kbase = (const char*)a.k + ((int64_t)b * a.ks[0] + (int64_t)kvh * a.ks[1]) * 2;
   const char* vbase = (const char*)a.v + ((int64_t)b * a.vs[0] + (int64_t)kvh * a.vs[1]) * 2;
   const int64_t kstr = a.ks[2] * 2, vstr = a.vs[2] * 2;
+  // Per-lane part of each DMA source (row and swizzled chunk of the tile),
+  // fixed for the whole loop; a block adds its first key's row offset.  The
+  // tail block (keys past Lk) clamps each row to the last key instead.
+  constexpr int PW = (NI + 3) / 4;
+  int krow[PW], kcb[PW], vcb[PW];
+  int64_t kofs[PW], vofs[PW];
+#pragma unroll
+  for (int ii = 0; ii < PW; ++ii) {
+    const int sl = (ii * 4 + wave_u) * 64 + lane;
+    const int row = sl / T::CH;
+    const int lch = (sl % T::CH) ^ T::sw(row);
+    krow[ii] = row;
+    kcb[ii] = min(lch, a.dqk / 8 - 1) * 16;
+    vcb[ii] = min(lch, a.dv / 8 - 1) * 16;
+    kofs[ii] = (int64_t)row * kstr + kcb[ii];
+    vofs[ii] = (int64_t)row * vstr + vcb[ii];
+  }
   auto dma = [&](int blk, int buf) __attribute__((always_inline)) {
     const int k0 = blk * BK;
-    dma_rows<D, BK, 4>(lds_base + buf * TB, wave_u, lane, a.dqk / 8,
-                       [&](int row) { return kbase + (int64_t)min(k0 + row, a.Lk - 1) * kstr; });
-    dma_rows<D, BK, 4>(lds_base + (2 + buf) * TB, wave_u, lane, a.dv / 8,
-                       [&](int row) { return vbase + (int64_t)min(k0 + row, a.Lk - 1) * vstr; });
+    const bool full = k0 + BK <= a.Lk;
+    const char* kb = kbase + (int64_t)k0 * kstr;
+    const char* vb = vbase + (int64_t)k0 * vstr;
+#pragma unroll
+    for (int ii = 0; ii < PW; ++ii) {
+      const int ins = ii * 4 + wave_u;
+      if ((ii + 1) * 4 > NI && ins >= NI) continue;
+      const char* ks = full ? kb + kofs[ii] : kbase + (int64_t)min(k0 + krow[ii], a.Lk - 1) * kstr + kcb[ii];
+      const char* vs = full ? vb + vofs[ii] : vbase + (int64_t)min(k0 + krow[ii], a.Lk - 1) * vstr + vcb[ii];
+      lds_dma16<false>(ks, lds_base + buf * TB + ins * 1024);
+      lds_dma16<false>(vs, lds_base + (2 + buf) * TB + ins * 1024);
+    }
   };
   if (nblk > 0) dma(kb_first, 0);
 
@@ -238,9 +275,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
   for (int t = 0; t < NDT; ++t) acc[t] = f32x16{};
   wait_vmcnt<0>();  // block 0 and the register loads have landed
   if (nblk > 1) dma(kb_first + 1, 1);
+  // DMA instructions this wave issues per block (K and V each): while block
+  // j + 1 is in flight, block j has landed once no more than these remain
+  const int dma_w = 2 * max(0, (NI - wave_u + 3) / 4);
 
   for (int j = 0; j < nblk; ++j) {
-    if (j + 1 < nblk) wait_vmcnt<DMA_MIN>();
+    if (j + 1 < nblk) wait_vmcnt_upto<DMA_MAX>(dma_w);
     else wait_vmcnt<0>();
     __syncthreads();
     const SDPA_LDS char* kt_ = smem + (j & 1) * TB;
@@ -319,7 +359,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
   constexpr int TQ = BQ * T::ROWB;    // one Q or dO tile
   constexpr int NIQ = TQ / 1024;
   constexpr int BUF = 2 * TQ + 512;   // Q, dO, then lse2 / D / query index (3 x 128 bytes)
-  constexpr int DMA_MIN = 2 * (NIQ / 4);
   constexpr int DMA_MAX = 2 * ((NIQ + 3) / 4) + 1;
   static_assert(2 * DMA_MAX <= 63, "vmcnt range");
   __shared__ __attribute__((aligned(1024))) char smem_[2 * REG + 2 * BUF];
@@ -357,21 +396,56 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
   dma_rows<D, 128, 4>(lds_base + REG, wave_u, lane, a.dv / 8,
                       [&](int row) { return vbase + (int64_t)min(k_wg + row, a.Lk - 1) * vstr; });
 
+  // Q / dO rows of this lane's DMA instructions: packed row r0 + rq[ii] of
+  // each block, i.e. query (r0 + rq) / G of head kvh G + (r0 + rq) % G.  The
+  // blocks are fetched in order, one BQ rows after the other, so the
+  // (head, query) pair and the element offsets advance by fixed steps
+  // instead of a division per row; rows past R read row R - 1.
+  constexpr int PWQ = (NIQ + 3) / 4;
+  int rq[PWQ], gq[PWQ], cq[PWQ], co[PWQ];
+  int64_t qo[PWQ], oo[PWQ];
+  const int gq_step = BQ % a.G, iq_step = BQ / a.G;
+  const int64_t q_step = (int64_t)iq_step * a.qs[2] + (int64_t)gq_step * a.qs[1];
+  const int64_t o_step = (int64_t)iq_step * a.os[2] + (int64_t)gq_step * a.os[1];
+  const int64_t q_wrap = a.qs[2] - (int64_t)a.G * a.qs[1], o_wrap = a.os[2] - (int64_t)a.G * a.os[1];
+  const int64_t q_head = (int64_t)b * a.qs[0] + (int64_t)kvh * a.G * a.qs[1];
+  const int64_t o_head = (int64_t)b * a.os[0] + (int64_t)kvh * a.G * a.os[1];
+  const int64_t q_last = q_head + (int64_t)((a.R - 1) % a.G) * a.qs[1] + (int64_t)((a.R - 1) / a.G) * a.qs[2];
+  const int64_t o_last = o_head + (int64_t)((a.R - 1) % a.G) * a.os[1] + (int64_t)((a.R - 1) / a.G) * a.os[2];
+#pragma unroll
+  for (int ii = 0; ii < PWQ; ++ii) {
+    const int sl = (ii * 4 + wave_u) * 64 + lane;
+    const int row = sl / T::CH;
+    const int lch = (sl % T::CH) ^ T::sw(row);
+    rq[ii] = row;
+    cq[ii] = min(lch, a.dqk / 8 - 1) * 16;
+    co[ii] = min(lch, a.dv / 8 - 1) * 16;
+    const int rr = jb0 * BQ + row;
+    gq[ii] = rr % a.G;
+    qo[ii] = q_head + (int64_t)gq[ii] * a.qs[1] + (int64_t)(rr / a.G) * a.qs[2];
+    oo[ii] = o_head + (int64_t)gq[ii] * a.os[1] + (int64_t)(rr / a.G) * a.os[2];
+  }
+
+  // Block jb into buffer buf; calls come in the order jb0, jb0 + 1, ...
   auto dma_blk = [&](int jb, int buf) __attribute__((always_inline)) {
     const unsigned qb = lds_base + 2 * REG + buf * BUF;
     const int r0 = jb * BQ;
-    auto qrow = [&](int row) {
-      const int rr = min(r0 + row, a.R - 1);
-      const int i = rr / a.G, h = kvh * a.G + rr % a.G;
-      return (const char*)a.q + ((int64_t)b * a.qs[0] + (int64_t)h * a.qs[1] + (int64_t)i * a.qs[2]) * 2;
-    };
-    auto drow = [&](int row) {
-      const int rr = min(r0 + row, a.R - 1);
-      const int i = rr / a.G, h = kvh * a.G + rr % a.G;
-      return (const char*)a.dout + ((int64_t)b * a.os[0] + (int64_t)h * a.os[1] + (int64_t)i * a.os[2]) * 2;
-    };
-    dma_rows<D, BQ, 4>(qb, wave_u, lane, a.dqk / 8, qrow);
-    dma_rows<D, BQ, 4>(qb + TQ, wave_u, lane, a.dv / 8, drow);
+#pragma unroll
+    for (int ii = 0; ii < PWQ; ++ii) {
+      const int ins = ii * 4 + wave_u;
+      if ((ii + 1) * 4 > NIQ && ins >= NIQ) continue;
+      const bool in = r0 + rq[ii] < a.R;
+      lds_dma16<false>((const char*)a.q + (in ? qo[ii] : q_last) * 2 + cq[ii], qb + ins * 1024);
+      lds_dma16<false>((const char*)a.dout + (in ? oo[ii] : o_last) * 2 + co[ii], qb + TQ + ins * 1024);
+      gq[ii] += gq_step;
+      qo[ii] += q_step;
+      oo[ii] += o_step;
+      if (gq[ii] >= a.G) {
+        gq[ii] -= a.G;
+        qo[ii] += q_wrap;
+        oo[ii] += o_wrap;
+      }
+    }
     if (wave_u == 0) {
       // 32 rows of lse2, D and the query index: 8 lanes (16 bytes) each
       if (lane < 24) {
@@ -391,10 +465,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
     dv[t] = f32x16{};
   }
   wait_vmcnt<0>();  // K, V rows and block 0 have landed
+  if (a.dqk < D || a.dv < D) {
+    // Padded head dims: zero the K and V columns past the real ones, so the
+    // Q and dO columns there (re-read copies of the last real chunk) add
+    // nothing to S and dP.  Every wave's K/V DMA must have landed first.
+    __syncthreads();
+    SDPA_LDS char* kw_ = smem;
+    for (int idx = tid; idx < 128 * T::CH; idx += 256) {
+      const int row = idx / T::CH, c = idx % T::CH;
+      if (8 * c >= a.dqk) *(SDPA_LDS u32x4*)(kw_ + T::off(row, c)) = u32x4{0u, 0u, 0u, 0u};
+      if (8 * c >= a.dv) *(SDPA_LDS u32x4*)(kw_ + REG + T::off(row, c)) = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
   if (nblk > 1) dma_blk(jb0 + 1, 1);
+  // DMA instructions this wave issues per block (Q and dO each, plus the
+  // lse2 / D / query-index tile on wave 0): while block j + 1 is in flight,
+  // block j has landed once no more than these remain
+  const int dma_w = 2 * max(0, (NIQ - wave_u + 3) / 4) + (wave_u == 0 ? 1 : 0);
+  // First and last packed row of the current block as (query, head in the
+  // group) pairs, stepped by BQ rows per block like the DMA rows.
+  const int g_step = BQ % a.G, i_step = BQ / a.G;
+  int i_first = (jb0 * BQ) / a.G, g_first = (jb0 * BQ) % a.G;
+  int i_last = (jb0 * BQ + BQ - 1) / a.G, g_last = (jb0 * BQ + BQ - 1) % a.G;
+  const int i_rmax = (a.R - 1) / a.G;
+  const int kw = k_wg + wave_u * 32;  // this wave's first key
 
   for (int j = 0; j < nblk; ++j) {
-    if (j + 1 < nblk) wait_vmcnt<DMA_MIN>();
+    if (j + 1 < nblk) wait_vmcnt_upto<DMA_MAX>(dma_w);
     else wait_vmcnt<0>();
     __syncthreads();
     const SDPA_LDS char* qt = smem + 2 * REG + (j & 1) * BUF;
@@ -403,20 +500,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
     f32x16 sacc = f32x16{}, pacc = f32x16{};
 #pragma unroll
     for (int s = 0; s < NQS; ++s) {
-      const bool dq_ok = 16 * s + 8 * hl < a.dqk, dv_ok = 16 * s + 8 * hl < a.dv;
-      u32x4 qa = row_frag<D>(qt, col, s, hl), da = row_frag<D>(dt, col, s, hl);
-      if (!dq_ok) qa = u32x4{0u, 0u, 0u, 0u};  // padded head dims add nothing
-      if (!dv_ok) da = u32x4{0u, 0u, 0u, 0u};
-      sacc = E::mma(qa, row_frag<D>(kreg, wave * 32 + col, s, hl), sacc);
-      pacc = E::mma(da, row_frag<D>(vreg, wave * 32 + col, s, hl), pacc);
+      sacc = E::mma(row_frag<D>(qt, col, s, hl), row_frag<D>(kreg, wave * 32 + col, s, hl), sacc);
+      pacc = E::mma(row_frag<D>(dt, col, s, hl), row_frag<D>(vreg, wave * 32 + col, s, hl), pacc);
     }
     // register e: packed row r0 + 8 (e / 4) + 4 hl + e % 4 of this lane's
     // key.  Only blocks on a mask edge for this wave's 32 keys test each
     // pair (rows past R carry lse2 = +inf, so their P is 0 either way).
     const int r0 = (jb0 + j) * BQ;
-    const int pmin_b = r0 / a.G + a.off;
-    const int pmax_b = min(r0 + BQ - 1, a.R - 1) / a.G + a.off;
-    const int kw = k_wg + wave * 32;
+    const int pmin_b = i_first + a.off;
+    const int pmax_b = (r0 + BQ - 1 < a.R ? i_last : i_rmax) + a.off;
+    i_first += i_step;
+    g_first += g_step;
+    if (g_first >= a.G) {
+      g_first -= a.G;
+      ++i_first;
+    }
+    i_last += i_step;
+    g_last += g_step;
+    if (g_last >= a.G) {
+      g_last -= a.G;
+      ++i_last;
+    }
     const bool edge = (a.mask != MASK_NONE && kw + 31 > pmin_b) ||
                       (a.mask == MASK_WINDOW && kw <= pmax_b - a.window);
 #pragma unroll
