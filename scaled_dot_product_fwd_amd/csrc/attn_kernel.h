@@ -320,9 +320,33 @@ void attn_fwd_kernel(AttnArgs a) {
   }
   int rt = id % a.row_tiles;
   id /= a.row_tiles;
-  const int split = id % a.splits;
-  const int z = id / a.splits;
+  int split = id % a.splits;
+  int z = id / a.splits;
   if (a.heavy_first) rt = a.row_tiles - 1 - rt;
+  // Splits of this row tile's key range, and (balanced lengths) the first
+  // partial row of its batch entry's workspace segment, in units of R rows.
+  int nsp = a.splits;
+  int64_t seg = 0;
+  if (a.kv_balance > 0) {
+    // The B * splits workgroups of KV head z % Hkv go to the batch entries
+    // in proportion to their key blocks, so a long entry is not left to the
+    // same few workgroups as a short one.  Uniform: before any barrier.
+    const int kvh_ = z % a.Hkv;
+    const int W = a.B * a.splits;
+    const int w = (z / a.Hkv) * a.splits + split;
+    const int T = kv_balance_total(a.kv_lens, a.B, a.Lk, a.kv_balance);
+    int P = 0, e = 0, s_e = 0;
+    for (; e < a.B; ++e) {
+      s_e = kv_balance_count(kv_balance_blocks(a.kv_lens, e, a.Lk, a.kv_balance), W, a.B, T);
+      if (w < P + s_e) break;
+      P += s_e;
+    }
+    if (e == a.B) return;  // a workgroup the rounding left without work
+    split = w - P;
+    nsp = s_e;
+    z = e * a.Hkv + kvh_;
+    seg = (int64_t)kvh_ * W + P;
+  }
   const int b = z / a.Hkv;
   const int kvh = z % a.Hkv;
 
@@ -368,8 +392,8 @@ void attn_fwd_kernel(AttnArgs a) {
   // blocks, so the whole grid streams one region of memory together rather
   // than `splits` regions far apart (which maps unevenly onto the HBM
   // channels).  Block j of this workgroup is blk(j).
-  const int nblk = split < nb ? (nb - 1 - split) / a.splits + 1 : 0;
-  auto blk = [&](int j) { return kb_first + split + j * a.splits; };
+  const int nblk = split < nb ? (nb - 1 - split) / nsp + 1 : 0;
+  auto blk = [&](int j) { return kb_first + split + j * nsp; };
 
   // ---- LDS DMA of one key block into buffer `buf` ----
   // Each wave issues KPW + VPW DMA instructions per block; lane l of
@@ -1037,7 +1061,10 @@ void attn_fwd_kernel(AttnArgs a) {
   }
 
   // ---- split plan: this split's partial (O, m, l) ----
-  const int64_t ws_row = ((int64_t)z * a.R + r) * a.splits + split;
+  // partial row: [z][r][split], or with balanced lengths the entry's segment
+  // [seg R, (seg + nsp) R) of its KV head, laid out [r][split]
+  const int64_t ws_row = a.kv_balance > 0 ? seg * a.R + (int64_t)r * nsp + split
+                                          : ((int64_t)z * a.R + r) * a.splits + split;
   float* wo = a.ws_o + ws_row * a.dv;
 #pragma unroll
   for (int t = 0; t < S::NDTW; ++t) {

@@ -18,7 +18,7 @@ namespace sdpa {
 namespace dev {
 
 constexpr int kCombineThreads = 256;
-constexpr int kCombineMaxSplits = 1024;
+constexpr int kCombineMaxSplits = kMaxSplitsPerRow;
 constexpr int kCombineRegs = 8;  // partial outputs a thread holds in registers
 
 // One workgroup per packed row.  Thread (g, c) owns 4 head-dim columns c of
@@ -37,21 +37,34 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a)
   const int b = z / a.Hkv, kvh = z % a.Hkv;
   const int g = r % a.G, i = r / a.G, h = kvh * a.G + g;
   if (a.q_lens && i >= min(max(a.q_lens[b], 0), a.Lq)) return;  // past the entry's queries: not written
-  const float* ml = a.ws_ml + (int64_t)row * a.splits * 2;
+  // this row's partials: [row][split], or with balanced lengths [r][split]
+  // inside its entry's segment of the KV head (see kv_balance_count)
+  int ns = a.splits;
+  int64_t prow = (int64_t)row * a.splits;  // first partial of the row
+  if (a.kv_balance > 0) {
+    const int W = a.B * a.splits;
+    const int T = kv_balance_total(a.kv_lens, a.B, a.Lk, a.kv_balance);
+    int P = 0;
+    for (int e = 0; e < b; ++e)
+      P += kv_balance_count(kv_balance_blocks(a.kv_lens, e, a.Lk, a.kv_balance), W, a.B, T);
+    ns = kv_balance_count(kv_balance_blocks(a.kv_lens, b, a.Lk, a.kv_balance), W, a.B, T);
+    prow = ((int64_t)kvh * W + P) * a.R + (int64_t)r * ns;
+  }
+  const float* ml = a.ws_ml + prow * 2;
   const int tid = threadIdx.x;
   const int nc = a.dv / 4;              // 4-column groups: dv % 8 == 0, dv <= 4 * threads
   const int ng = kCombineThreads / nc;  // split groups
   const int gi = tid / nc, c = tid % nc;
-  const float* wo = a.ws_o + (int64_t)row * a.splits * a.dv + 4 * c;
+  const float* wo = a.ws_o + prow * a.dv + 4 * c;
 
   f32x4 v[kCombineRegs];
 #pragma unroll
   for (int u = 0; u < kCombineRegs; ++u) {
     const int sp = gi + u * ng;
-    v[u] = (gi < ng && sp < a.splits) ? *(const f32x4*)(wo + (int64_t)sp * a.dv) : f32x4{0.f, 0.f, 0.f, 0.f};
+    v[u] = (gi < ng && sp < ns) ? *(const f32x4*)(wo + (int64_t)sp * a.dv) : f32x4{0.f, 0.f, 0.f, 0.f};
   }
   float mx = kNegInf, lp_m = kNegInf, lp_l = 0.f;
-  for (int sp = tid; sp < a.splits; sp += kCombineThreads) {
+  for (int sp = tid; sp < ns; sp += kCombineThreads) {
     const float2 q = *(const float2*)(ml + 2 * sp);
     msh[sp] = q.x;
     if (sp == tid) { lp_m = q.x; lp_l = q.y; }  // first pair of this thread, kept for the sum
@@ -67,8 +80,8 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a)
   const float Mu = (M == kNegInf) ? 0.f : M;
 
   // L = sum_s 2^(m_s - M) l_s
-  float lp = tid < a.splits ? __builtin_amdgcn_exp2f(lp_m - Mu) * lp_l : 0.f;
-  for (int sp = tid + kCombineThreads; sp < a.splits; sp += kCombineThreads)
+  float lp = tid < ns ? __builtin_amdgcn_exp2f(lp_m - Mu) * lp_l : 0.f;
+  for (int sp = tid + kCombineThreads; sp < ns; sp += kCombineThreads)
     lp += __builtin_amdgcn_exp2f(msh[sp] - Mu) * ml[2 * sp + 1];
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) lp += __shfl_xor(lp, o);
@@ -79,9 +92,9 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a)
 #pragma unroll
     for (int u = 0; u < kCombineRegs; ++u) {
       const int sp = gi + u * ng;
-      if (sp < a.splits) acc += __builtin_amdgcn_exp2f(msh[sp] - Mu) * v[u];
+      if (sp < ns) acc += __builtin_amdgcn_exp2f(msh[sp] - Mu) * v[u];
     }
-    for (int sp = gi + kCombineRegs * ng; sp < a.splits; sp += ng)
+    for (int sp = gi + kCombineRegs * ng; sp < ns; sp += ng)
       acc += __builtin_amdgcn_exp2f(msh[sp] - Mu) * *(const f32x4*)(wo + (int64_t)sp * a.dv);
   }
   part[tid] = acc;

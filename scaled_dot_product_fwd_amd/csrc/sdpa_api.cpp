@@ -178,6 +178,10 @@ int sdpa_forward_varlen(const sdpa_desc_t* d, const void* q, const void* k, cons
   a.row_tiles = p.row_tiles;
   a.heavy_first = p.mask != sdpa::MASK_NONE && p.row_tiles > 1;
   a.xcd_group = p.xcd_group;
+  // Per-batch key lengths on a split plan: deal the workgroups by the
+  // entries' key blocks (a window's tiles see about W keys whatever the
+  // length, so it keeps the even deal).
+  a.kv_balance = (kv_lens && p.splits > 1 && p.mask != sdpa::MASK_WINDOW) ? p.fam.nwk * p.fam.bkw : 0;
   if (p.splits > 1) {
     const size_t rows_total = (size_t)d->batch * d->heads_kv * a.R * p.splits;
     const size_t o_bytes = (rows_total * (size_t)d->dim_v * 4 + 255) / 256 * 256;
@@ -215,6 +219,9 @@ int sdpa_forward_varlen(const sdpa_desc_t* d, const void* q, const void* k, cons
     c.o = o;
     c.lse = lse;
     c.q_lens = q_lens;
+    c.kv_lens = kv_lens;
+    c.kv_balance = a.kv_balance;
+    c.Lk = a.Lk;
     for (int j = 0; j < 3; ++j) c.os[j] = d->o_stride[j];
     c.B = a.B;
     c.Hq = a.Hq;

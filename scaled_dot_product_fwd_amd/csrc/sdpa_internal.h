@@ -37,7 +37,45 @@ struct AttnArgs {
   int row_tiles;       // ceil(R / rows per workgroup)
   int heavy_first;     // causal/window prefill: visit the longest row tiles first
   int xcd_group;       // > 0: consecutive work items run in groups of this many on one XCD
+  int kv_balance;      // > 0 (split plans with kv_lens): deal each KV head's B * splits
+                       // workgroups to the batch entries by their blocks of this many keys
 };
+
+// Largest number of split partials one packed row may have (the combine
+// holds their maxima in LDS).
+constexpr int kMaxSplitsPerRow = 1024;
+
+// Balanced per-batch key lengths: the W = B * splits workgroups of a KV head
+// are dealt to the batch entries in proportion to their key blocks (blocks
+// of `bk` keys): entry e with nb_e > 0 blocks gets
+//   s_e = min(nb_e, 1 + nb_e (W - B) / T, kMaxSplitsPerRow)
+// workgroups, the consecutive ones from P_e = s_0 + ... + s_(e-1); an empty
+// entry gets none.  T is all entries' blocks, so the s_e add up to at most W
+// (the rest of the workgroups have nothing to do).  The attention kernel and
+// the combine both use these, so they agree on where each entry's partials
+// sit.
+#if defined(__HIPCC__)
+#define SDPA_HD __host__ __device__
+#else
+#define SDPA_HD
+#endif
+SDPA_HD inline int kv_balance_blocks(const int* kv_lens, int e, int Lk, int bk) {
+  const int len = kv_lens[e] < 0 ? 0 : (kv_lens[e] > Lk ? Lk : kv_lens[e]);
+  return (len + bk - 1) / bk;
+}
+SDPA_HD inline int kv_balance_total(const int* kv_lens, int B, int Lk, int bk) {
+  int T = 0;
+  for (int e = 0; e < B; ++e) T += kv_balance_blocks(kv_lens, e, Lk, bk);
+  return T;
+}
+SDPA_HD inline int kv_balance_count(int nb, int W, int B, int T) {
+  if (nb <= 0) return 0;
+  int s = 1 + (int)((int64_t)nb * (W - B) / T);
+  if (s > nb) s = nb;
+  if (s > kMaxSplitsPerRow) s = kMaxSplitsPerRow;
+  return s;
+}
+#undef SDPA_HD
 
 // Arguments of the split combine kernel.
 struct CombineArgs {
@@ -46,8 +84,10 @@ struct CombineArgs {
   void* o;
   float* lse;
   const int* q_lens;  // nullable [B]: rows past an entry's queries are skipped
+  const int* kv_lens; // nullable [B]: with kv_balance, where each entry's partials sit
   int64_t os[3];
-  int B, Hq, Hkv, Lq, dv, G, R, splits;
+  int B, Hq, Hkv, Lq, Lk, dv, G, R, splits;
+  int kv_balance;     // see AttnArgs::kv_balance
 };
 
 // Kernel family = how the waves of a workgroup divide the work.

@@ -121,3 +121,19 @@ def test_varlen_wide_family():
     case = (2, 32, 8, 48, 1200, 128, 128, "bf16", "causal", 0, [48, 20], [1200, 300])
     _say("varlen wide")
     _check(case)
+
+
+@pytest.mark.parametrize("splits", [0, 4, 16, 1024])
+def test_varlen_balanced_deal(splits):
+    """Split plans with kv_lens deal each KV head's workgroups to the entries
+    by their key blocks: skewed lengths, an empty entry, entries shorter than
+    one block and more splits than blocks must all merge back exactly."""
+    case = (6, 8, 2, 1, 5000, 128, 128, "bf16", "none", 0, None, [5000, 3, 0, 4999, 64, 2500])
+    _say("varlen balanced deal", splits)
+    _check(case, num_splits=splits)
+
+
+def test_varlen_balanced_deal_causal_rows():
+    case = (4, 8, 2, 6, 3000, 64, 64, "f16", "causal", 0, [6, 2, 6, 1], [3000, 40, 6, 1777])
+    _say("varlen balanced deal causal")
+    _check(case, num_splits=24)
