@@ -490,12 +490,26 @@ def cpu_baseline(s, runner, budget_s=12.0):
             "sample": f"{sample} of the same workload, float64 numpy, {t_total:.1f} s"}
 
 
-def kernel_source_hash():
+def kernel_source_hash(name):
+    """Fingerprint of what a counter run of workload ``name`` measured: every
+    device-side source (kernels, launchers, argument set-up; the host planner
+    is left out) plus the plan the planner makes for the workload, so a
+    planner change that alters this workload's launch also invalidates it."""
+    import scaled_dot_product_fwd_amd as sdpa
+    from scaled_dot_product_fwd_amd.synth import DTYPES
+
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "scaled_dot_product_fwd_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
+        if f == "plan.cpp":
+            continue
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
+    s = SHAPES[name]
+    desc = sdpa.make_desc((s["b"], s["hq"], s["lq"], s["dqk"]), (s["b"], s["hkv"], s["lk"], s["dqk"]),
+                          (s["b"], s["hkv"], s["lk"], s["dv"]), sdpa._dtype_code(DTYPES[s["dtype"]]),
+                          mask=s["mask"], window_size=s["window"])
+    h.update(sdpa.sdpa_describe_plan(desc).encode())
     return h.hexdigest()[:16]
 
 
@@ -506,7 +520,7 @@ def traffic_from_profiles(name):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_source_hash") != kernel_source_hash():
+    if t.get("kernel_source_hash") != kernel_source_hash(name):
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -553,7 +567,7 @@ def summarize_pmc(fetch_dir, write_dir, name, copy_mib, commands):
         return k, v
 
     copy_bytes = 2 * copy_mib * (1 << 20)  # read once, written once
-    out = {"workload": name, "kernel_source_hash": kernel_source_hash(), "commands": commands,
+    out = {"workload": name, "kernel_source_hash": kernel_source_hash(name), "commands": commands,
            "copy": {"kernel": "float32 dst = src * 1", "bytes_read": copy_bytes // 2,
                     "bytes_written": copy_bytes // 2}}
     total = 0.0

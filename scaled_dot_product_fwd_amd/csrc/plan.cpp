@@ -224,9 +224,12 @@ int make_plan(const sdpa_desc_t* d, Plan* p, std::string* err) {
     // (128 rows) is only split when very few tiles exist: its partial outputs
     // would cost HBM traffic comparable to the K/V it reads, while an unsplit
     // wave of large tiles already keeps the MFMA units busy.
+    // A range of three key blocks or fewer stays whole: its extra blocks cost
+    // less than the combine launch that splitting adds (decode at Lk = 256,
+    // two 128-key blocks: 12.6 us split, 10.3 us whole).
     const int64_t target = kTargetCUs;
     const bool starved = rows < 128 ? base < target : base < kTargetCUs / 4;
-    if (starved) splits = std::min<int64_t>(ceil_div(target, base), nblocks);
+    if (starved && nblocks > 3) splits = std::min<int64_t>(ceil_div(target, base), nblocks);
     splits = std::max<int64_t>(1, std::min<int64_t>(splits, kMaxSplits));
   }
   if (base * splits > 0x7fffffffLL) return fail(err, SDPA_E_SHAPE, "grid too large");
