@@ -629,7 +629,7 @@ def main():
     ap.add_argument("--workload", default=DEFAULT, choices=sorted(SHAPES))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true", help="also time every shape of the table")
-    ap.add_argument("--sweep-out", default=os.path.join("gpurun_out", "sweep.json"))
+    ap.add_argument("--sweep-out", default="", help="with --sweep: also write the rows to this JSON file")
     ap.add_argument("--sweep-only", default="", help="comma-separated name prefixes to sweep")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="after timing, run a plain copy of this many MiB (counter calibration)")
@@ -706,9 +706,10 @@ def main():
             print(f"  {sh['name']:28s} kernel {r['kernel_ms_mean'] * 1e3:9.2f} us  step {r['ms_per_step'] * 1e3:9.2f} us"
                   f"  {r['achieved']:9.2f} {r['unit']:8s} {100 * r['frac']:6.2f}% of {r['bound']}",
                   file=sys.stderr, flush=True)
-        os.makedirs(os.path.dirname(args.sweep_out) or ".", exist_ok=True)
-        with open(args.sweep_out, "w") as f:
-            json.dump(rows, f, indent=1)
+        if args.sweep_out:
+            os.makedirs(os.path.dirname(args.sweep_out) or ".", exist_ok=True)
+            with open(args.sweep_out, "w") as f:
+                json.dump(rows, f, indent=1)
     print(json.dumps(line), flush=True)
 
 
