@@ -644,7 +644,7 @@ def main():
                       args.calibrate_copy_mib, args.pmc_command)
         return
     if args.gpus != 1:
-        print(f"bench.py runs on exactly one GPU (got --gpus {args.gpus}); this build has no multi-GPU path",
+        print(f"bench.py runs on exactly one GPU (got --gpus {args.gpus}): multi-GPU runs are not supported",
               file=sys.stderr)
         sys.exit(2)
     import torch
