@@ -137,3 +137,14 @@ def test_varlen_balanced_deal_causal_rows():
     case = (4, 8, 2, 6, 3000, 64, 64, "f16", "causal", 0, [6, 2, 6, 1], [3000, 40, 6, 1777])
     _say("varlen balanced deal causal")
     _check(case, num_splits=24)
+
+
+def test_varlen_balanced_deal_many_entries():
+    """Forty entries, most of them with a share of one or two workgroups:
+    lengths from 0 to the full cache."""
+    rng = np.random.default_rng(2024)
+    kl = [int(x) for x in rng.integers(0, 2049, size=40)]
+    kl[3], kl[17], kl[39] = 0, 2048, 1
+    case = (40, 8, 2, 1, 2048, 64, 64, "f16", "none", 0, None, kl)
+    _say("varlen balanced deal, 40 entries")
+    _check(case)
