@@ -161,9 +161,9 @@ def forward(q, k, v, *, scale: Optional[float] = None, mask: str = "none", windo
     defaults to ``1/sqrt(Dqk)``.  ``mask`` is ``"none"``, ``"causal"`` (query
     rows aligned to the last Lq keys) or ``"window"`` (causal plus the last
     ``window_size`` keys).  ``attn_mask`` (optional) broadcasts to
-    ``[B,Hq,Lq,Lk]``: ``bool`` keeps the keys where True (a ``uint8`` array
-    must hold only 0 and 1), q's dtype is added
-    to the scaled scores; it applies on top of ``mask``.  Its rows must start
+    ``[B,Hq,Lq,Lk]``: a ``bool`` array (or a ``uint8`` one holding only 0
+    and 1) keeps the keys where it is true; an array in q's dtype is added
+    to the scaled scores.  It applies on top of ``mask``.  Its rows must start
     on 16-byte boundaries and be readable up to Lk rounded up to 16 bytes
     (``pad_mask`` prepares such a copy).  ``q_lens`` / ``kv_lens``
     (optional int32 device tensors ``[B]``) give each batch entry's valid
