@@ -49,7 +49,9 @@
 // Split-K (mlx issue #3826, second and third comments: the block-parallel
 // reduction over S): the blocks of the range may be dealt out to `splits`
 // workgroups; each writes its unnormalised O with (m, l) and a combine kernel
-// merges them by log-sum-exp.
+// merges them by log-sum-exp.  With per-batch key lengths the workgroups of a
+// KV head are dealt to the batch entries by their key blocks instead of
+// evenly (kv_balance_count).
 //
 // Lazy rescaling: the reference max m of a row only moves when a block's max
 // exceeds it by more than kRescale (log2 units); otherwise the block is
