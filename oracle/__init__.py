@@ -27,4 +27,4 @@ from .sdpa_ref import (  # noqa: F401
     sdpa_probs,
     sdpa_loop,
 )
-from .sdpa_bwd_ref import sdpa_bwd_ref  # noqa: F401
+from .sdpa_bwd_ref import sdpa_bwd_ref, sdpa_bwd_ref_varlen  # noqa: F401

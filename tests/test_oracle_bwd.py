@@ -6,7 +6,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import sdpa_bwd_ref, sdpa_ref, visible_mask
+from oracle import sdpa_bwd_ref, sdpa_bwd_ref_varlen, sdpa_ref, sdpa_ref_varlen, visible_mask
 
 
 def _rand(shape, seed):
@@ -106,3 +106,57 @@ def test_bwd_single_key_closed_form():
     np.testing.assert_allclose(dq, 0.0, atol=1e-15)
     np.testing.assert_allclose(dk, 0.0, atol=1e-15)
     np.testing.assert_allclose(dvv[0, 0, 0], do[0].sum(axis=(0, 1)), atol=1e-14)
+
+
+# ---- per-batch lengths ----
+
+VARLEN = [
+    # b, hq, hkv, lq, lk, dqk, dv, mask, window, q_lens, kv_lens
+    (3, 4, 2, 5, 7, 3, 4, "causal", 0, [5, 2, 3], [7, 3, 0]),
+    (2, 2, 1, 4, 6, 4, 3, "none", 0, [4, 1], [2, 6]),
+    (2, 2, 2, 6, 8, 3, 3, "window", 3, [6, 4], [8, 5]),
+    (2, 4, 2, 4, 5, 2, 2, "causal", 0, [4, 3], [2, 5]),  # entry 0: more queries than keys
+]
+
+
+def test_bwd_varlen_full_lengths_is_the_dense_gradient():
+    q, k, v, do = _case(2, 4, 2, 5, 7, 3, 4, seed=730)
+    a = sdpa_bwd_ref(q, k, v, do, 0.7, "causal", 0)
+    c = sdpa_bwd_ref_varlen(q, k, v, do, 0.7, "causal", 0, [5, 5], [7, 7])
+    for x, y in zip(a, c):
+        np.testing.assert_array_equal(x, y)
+
+
+@pytest.mark.parametrize("case", VARLEN)
+def test_bwd_varlen_matches_finite_differences(case):
+    """dL/dx for L = sum over the valid output rows of O * dO, by central
+    differences of the forward's per-length oracle; every position past the
+    lengths has gradient 0."""
+    b, hq, hkv, lq, lk, dqk, dv, mask, w, ql, kl = case
+    q, k, v, do = _case(b, hq, hkv, lq, lk, dqk, dv, seed=740 + lq)
+    grads = sdpa_bwd_ref_varlen(q, k, v, do, 0.9, mask, w, ql, kl)
+    h = 1e-6
+
+    def loss(qq, kk, vv):
+        o, _ = sdpa_ref_varlen(qq, kk, vv, 0.9, mask, w, ql, kl)
+        return float(np.nansum(o * do))
+
+    for which, x in enumerate((q, k, v)):
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p = [q, k, v]
+            args_m = [q, k, v]
+            args_p[which], args_m[which] = xp, xm
+            fd = (loss(*args_p) - loss(*args_m)) / (2 * h)
+            assert abs(fd - grads[which][idx]) < 1e-7 * max(1.0, abs(fd)), (which, idx, fd, grads[which][idx])
+
+
+def test_bwd_varlen_rows_without_keys():
+    """A causal entry with more queries than keys: its first rows see no key,
+    output the constant 0 and take no gradient; keys past kv_lens get none."""
+    q, k, v, do = _case(1, 2, 1, 4, 6, 3, 3, seed=760)
+    dq, dk, dv = sdpa_bwd_ref_varlen(q, k, v, do, 0.5, "causal", 0, [4], [2])
+    assert (dq[0, :, :2] == 0).all() and np.abs(dq[0, :, 2:]).max() > 0
+    assert (dk[0, :, 2:] == 0).all() and (dv[0, :, 2:] == 0).all()
