@@ -184,6 +184,19 @@ int sdpa_backward(const sdpa_desc_t* desc, const void* q, const void* k, const v
                   const void* dout, const float* lse, void* dq, void* dk, void* dv, void* workspace,
                   size_t workspace_bytes, sdpa_stream_t stream);
 
+/* Backward with per-batch lengths (the counterpart of sdpa_forward_varlen,
+ * same q_lens / kv_lens semantics: nullable int32 device arrays [B], entry b
+ * uses its first q_lens[b] queries and kv_lens[b] keys, query i at key
+ * position i + kv_lens[b] - q_lens[b]).  Every gradient position past an
+ * entry's lengths is written as 0, as is dq of a row that sees no key:
+ * those outputs depend on no input.  The padded rows and keys are never
+ * read (a row or key past the lengths reads the entry's last valid one), so
+ * they may hold anything. */
+int sdpa_backward_varlen(const sdpa_desc_t* desc, const void* q, const void* k, const void* v, const void* o,
+                         const void* dout, const float* lse, const int32_t* q_lens, const int32_t* kv_lens,
+                         void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                         sdpa_stream_t stream);
+
 /* Writes a one-line, NUL-terminated description of the plan (kernel family,
  * tile, splits, grid, workspace) into buf.  Host only. */
 int sdpa_describe_plan(const sdpa_desc_t* desc, char* buf, size_t len);

@@ -20,11 +20,11 @@ from ._lib import (SDPA_BF16, SDPA_F16, SDPA_F32, SDPA_MASK_ARRAY_ADD,  # noqa: 
                    SDPA_MASK_ARRAY_BOOL, SDPA_MASK_ARRAY_NONE, SDPA_MASK_CAUSAL, SDPA_MASK_NONE,
                    SDPA_MASK_WINDOW, SdpaError, SdpaRuntimeError, SdpaValueError, load,
                    sdpa_desc_init, sdpa_desc_t, sdpa_describe_plan, sdpa_forward,
-                   sdpa_backward, sdpa_backward_workspace_bytes, sdpa_forward_masked,
+                   sdpa_backward, sdpa_backward_varlen, sdpa_backward_workspace_bytes, sdpa_forward_masked,
                    sdpa_forward_varlen, sdpa_last_error, sdpa_set_profile_events,
                    sdpa_workspace_bytes)
 
-__all__ = ["forward", "backward", "sdpa_backward", "sdpa_backward_workspace_bytes", "make_desc", "plan_for", "workspace_for", "pad_mask", "sdpa_forward",
+__all__ = ["forward", "backward", "sdpa_backward", "sdpa_backward_varlen", "sdpa_backward_workspace_bytes", "make_desc", "plan_for", "workspace_for", "pad_mask", "sdpa_forward",
            "sdpa_forward_masked", "sdpa_forward_varlen", "sdpa_workspace_bytes", "sdpa_describe_plan", "sdpa_last_error",
            "sdpa_desc_init", "sdpa_set_profile_events",
            "SdpaError", "SdpaValueError", "SdpaRuntimeError"]
@@ -235,14 +235,16 @@ def forward(q, k, v, *, scale: Optional[float] = None, mask: str = "none", windo
 
 
 def backward(q, k, v, o, dout, lse, *, scale: Optional[float] = None, mask: str = "none",
-             window_size: int = 0, dq=None, dk=None, dv=None, workspace=None, stream=None):
+             window_size: int = 0, q_lens=None, kv_lens=None, dq=None, dk=None, dv=None, workspace=None,
+             stream=None):
     """Gradients ``(dq, dk, dv)`` of the fused forward on the current HIP device.
 
-    ``q, k, v`` and ``scale``, ``mask``, ``window_size`` as given to
-    ``forward``; ``o`` and ``lse`` its output and float32 log-sum-exp
-    (``return_lse=True``); ``dout`` the upstream gradient, shaped and strided
-    like ``o``.  float16 / bfloat16, head dims up to 128, no mask array.
-    Deterministic.
+    ``q, k, v`` and ``scale``, ``mask``, ``window_size``, ``q_lens``,
+    ``kv_lens`` as given to ``forward``; ``o`` and ``lse`` its output and
+    float32 log-sum-exp (``return_lse=True``); ``dout`` the upstream
+    gradient, shaped and strided like ``o``.  With per-batch lengths every
+    gradient position past them is 0.  float16 / bfloat16, head dims up to
+    128, no mask array.  Deterministic.
     """
     import torch
 
@@ -276,8 +278,18 @@ def backward(q, k, v, o, dout, lse, *, scale: Optional[float] = None, mask: str 
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
+    lens = []
+    for name, t in (("q_lens", q_lens), ("kv_lens", kv_lens)):
+        if t is None:
+            lens.append(0)
+            continue
+        if (not isinstance(t, torch.Tensor) or t.dtype != torch.int32 or t.dim() != 1 or t.shape[0] != b
+                or not t.is_contiguous() or t.device != q.device):
+            raise SdpaValueError(f"SDPA_E_SHAPE: {name} must be a contiguous int32 [B] tensor on q's device")
+        lens.append(t.data_ptr())
     with torch.cuda.device(q.device):
-        sdpa_backward(desc, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
-                      lse.data_ptr(), outs[0].data_ptr(), outs[1].data_ptr(), outs[2].data_ptr(),
-                      workspace.data_ptr(), workspace.numel() * workspace.element_size(), stream)
+        sdpa_backward_varlen(desc, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                             lse.data_ptr(), lens[0], lens[1], outs[0].data_ptr(), outs[1].data_ptr(),
+                             outs[2].data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                             stream)
     return tuple(outs)

@@ -33,7 +33,8 @@ STATUS = {
 STATUS_CODE = {v: k for k, v in STATUS.items()}
 
 EXPORTED = ("sdpa_desc_init", "sdpa_workspace_bytes", "sdpa_forward", "sdpa_forward_masked",
-            "sdpa_forward_varlen", "sdpa_backward_workspace_bytes", "sdpa_backward", "sdpa_describe_plan",
+            "sdpa_forward_varlen", "sdpa_backward_workspace_bytes", "sdpa_backward", "sdpa_backward_varlen",
+            "sdpa_describe_plan",
             "sdpa_set_profile_events", "sdpa_last_error")
 
 
@@ -112,6 +113,9 @@ def load() -> ctypes.CDLL:
     lib.sdpa_backward_workspace_bytes.restype = ctypes.c_int
     lib.sdpa_backward.argtypes = [P(sdpa_desc_t)] + [ctypes.c_void_p] * 10 + [ctypes.c_size_t, ctypes.c_void_p]
     lib.sdpa_backward.restype = ctypes.c_int
+    lib.sdpa_backward_varlen.argtypes = [P(sdpa_desc_t)] + [ctypes.c_void_p] * 12 + [ctypes.c_size_t,
+                                                                                     ctypes.c_void_p]
+    lib.sdpa_backward_varlen.restype = ctypes.c_int
     lib.sdpa_describe_plan.argtypes = [P(sdpa_desc_t), ctypes.c_char_p, ctypes.c_size_t]
     lib.sdpa_describe_plan.restype = ctypes.c_int
     lib.sdpa_set_profile_events.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
@@ -197,3 +201,11 @@ def sdpa_backward(desc: sdpa_desc_t, q: int, k: int, v: int, o: int, dout: int, 
     """Raw backward call with integer device addresses; raises on a non-zero status."""
     check(load().sdpa_backward(ctypes.byref(desc), q, k, v, o, dout, lse, dq, dk, dv, workspace or None,
                                workspace_bytes, stream or None))
+
+
+def sdpa_backward_varlen(desc: sdpa_desc_t, q: int, k: int, v: int, o: int, dout: int, lse: int, q_lens: int,
+                         kv_lens: int, dq: int, dk: int, dv: int, workspace: int | None, workspace_bytes: int,
+                         stream: int | None) -> None:
+    """Raw backward call with per-batch lengths (0 for an absent array); raises on a non-zero status."""
+    check(load().sdpa_backward_varlen(ctypes.byref(desc), q, k, v, o, dout, lse, q_lens or None, kv_lens or None,
+                                      dq, dk, dv, workspace or None, workspace_bytes, stream or None))

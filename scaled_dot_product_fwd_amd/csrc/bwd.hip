@@ -139,6 +139,21 @@ __device__ __forceinline__ float hi16(unsigned w) {
   return E::to_float((unsigned short)(w >> 16));
 }
 
+// Batch entry b's valid queries and keys (per-batch lengths, clamped to the
+// padded shape; the whole padded shape without them).  Its query i sits at
+// key position i + Lk_b - Lq_b.
+struct EntryLens {
+  int Lq, Lk, R, off;
+};
+__device__ __forceinline__ EntryLens entry_lens(const BwdArgs& a, int b) {
+  EntryLens e;
+  e.Lq = a.q_lens ? min(max(a.q_lens[b], 0), a.Lq) : a.Lq;
+  e.Lk = a.kv_lens ? min(max(a.kv_lens[b], 0), a.Lk) : a.Lk;
+  e.R = a.G * e.Lq;
+  e.off = e.Lk - e.Lq;
+  return e;
+}
+
 // ---- per packed row: D = dO . O, lse in log2 units, query index ----
 // 16 lanes per row, 8 elements each (dv <= 128).
 template <class E>
@@ -150,7 +165,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
   if (grow >= Z * a.Rp) return;  // no barriers below
   const int z = (int)(grow / a.Rp), r = (int)(grow % a.Rp);
   const int b = z / a.Hkv, kvh = z % a.Hkv;
-  const bool ok = r < a.R;
+  const bool ok = r < entry_lens(a, b).R;  // rows past the entry's queries: P = 0, D = 0
   float dsum = 0.f, lse2 = __builtin_inff();
   if (ok) {
     const int i = r / a.G, h = kvh * a.G + r % a.G;
@@ -199,20 +214,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
   const int rt = blockIdx.x % row_tiles;
   const int z = blockIdx.x / row_tiles;
   const int b = z / a.Hkv, kvh = z % a.Hkv;
+  const EntryLens en = entry_lens(a, b);
   const int r_wg = rt * 128;
   const int r = r_wg + wave * 32 + col;
-  const bool row_ok = r < a.R;
-  const int rc = min(r, a.R - 1);
+  if (r_wg >= en.R) {
+    // Every row of the tile lies past the entry's queries (uniform, before
+    // any barrier): their gradient is 0.
+    if (r < a.R) {
+      const int iz = r / a.G, hz = kvh * a.G + r % a.G;
+      char* zrow = (char*)a.grad_q + ((int64_t)b * a.qs[0] + (int64_t)hz * a.qs[1] + (int64_t)iz * a.qs[2]) * 2;
+      for (int d = 8 * hl; d < a.dqk; d += 16)
+        *(u32x4*)(zrow + d * 2) = u32x4{0u, 0u, 0u, 0u};
+    }
+    return;
+  }
+  const bool row_ok = r < en.R;
+  const int rc = min(r, en.R - 1);  // rows past the entry read its last row (their P is 0)
   const int iq = rc / a.G;
   const int hq = kvh * a.G + rc % a.G;
-  const int pos = iq + a.off;
-  const int pmax_wg = (min(a.R, r_wg + 128) - 1) / a.G + a.off;
-  const int pmin_wg = r_wg / a.G + a.off;
-  const int pmin_w = min(r_wg + wave * 32, a.R - 1) / a.G + a.off;
-  const int pmax_w = min(r_wg + wave * 32 + 31, a.R - 1) / a.G + a.off;
+  const int pos = iq + en.off;
+  const int pmax_wg = (min(en.R, r_wg + 128) - 1) / a.G + en.off;
+  const int pmin_wg = r_wg / a.G + en.off;
+  const int pmin_w = min(r_wg + wave * 32, en.R - 1) / a.G + en.off;
+  const int pmax_w = min(r_wg + wave * 32 + 31, en.R - 1) / a.G + en.off;
 
-  int k_lo = 0, k_hi = a.Lk;
-  if (a.mask != MASK_NONE) k_hi = min(a.Lk, pmax_wg + 1);
+  int k_lo = 0, k_hi = en.Lk;
+  if (a.mask != MASK_NONE) k_hi = min(en.Lk, pmax_wg + 1);
   if (a.mask == MASK_WINDOW) k_lo = max(0, pmin_wg - a.window + 1);
   const int kb_first = k_lo / BK;
   const int nblk = max(0, (k_hi + BK - 1) / BK - kb_first);
@@ -239,15 +266,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
   }
   auto dma = [&](int blk, int buf) __attribute__((always_inline)) {
     const int k0 = blk * BK;
-    const bool full = k0 + BK <= a.Lk;
+    const bool full = k0 + BK <= en.Lk;
     const char* kb = kbase + (int64_t)k0 * kstr;
     const char* vb = vbase + (int64_t)k0 * vstr;
 #pragma unroll
     for (int ii = 0; ii < PW; ++ii) {
       const int ins = ii * 4 + wave_u;
       if ((ii + 1) * 4 > NI && ins >= NI) continue;
-      const char* ks = full ? kb + kofs[ii] : kbase + (int64_t)min(k0 + krow[ii], a.Lk - 1) * kstr + kcb[ii];
-      const char* vs = full ? vb + vofs[ii] : vbase + (int64_t)min(k0 + krow[ii], a.Lk - 1) * vstr + vcb[ii];
+      const char* ks = full ? kb + kofs[ii] : kbase + (int64_t)min(k0 + krow[ii], en.Lk - 1) * kstr + kcb[ii];
+      const char* vs = full ? vb + vofs[ii] : vbase + (int64_t)min(k0 + krow[ii], en.Lk - 1) * vstr + vcb[ii];
       lds_dma16<false>(ks, lds_base + buf * TB + ins * 1024);
       lds_dma16<false>(vs, lds_base + (2 + buf) * TB + ins * 1024);
     }
@@ -299,13 +326,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
       // register e: key k0 + 32 kt + 8 (e / 4) + 4 hl + e % 4 of this row;
       // only tiles on a mask edge or past Lk test each key
       const int kw = k0 + kt * 32;
-      const bool edge = (kw + 32 > a.Lk) || (a.mask != MASK_NONE && kw + 31 > pmin_w) ||
+      const bool edge = (kw + 32 > en.Lk) || (a.mask != MASK_NONE && kw + 31 > pmin_w) ||
                         (a.mask == MASK_WINDOW && kw <= pmax_w - a.window);
       if (edge) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int key = kw + 8 * (e >> 2) + 4 * hl + (e & 3);
-          bool vis = key < a.Lk;
+          bool vis = key < en.Lk;
           if (a.mask != MASK_NONE) vis = vis && key <= pos;
           if (a.mask == MASK_WINDOW) vis = vis && key > pos - a.window;
           const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][e], a.c, -lse2)) : 0.f;
@@ -331,8 +358,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
     }
   }
 
-  if (!row_ok) return;
-  char* orow = (char*)a.grad_q + ((int64_t)b * a.qs[0] + (int64_t)hq * a.qs[1] + (int64_t)iq * a.qs[2]) * 2;
+  if (r >= a.R) return;
+  // rows past the entry's queries write their gradient, 0 (their P was 0)
+  const int iw = row_ok ? iq : r / a.G, hw = row_ok ? hq : kvh * a.G + r % a.G;
+  char* orow = (char*)a.grad_q + ((int64_t)b * a.qs[0] + (int64_t)hw * a.qs[1] + (int64_t)iw * a.qs[2]) * 2;
 #pragma unroll
   for (int t = 0; t < NDT; ++t) {
 #pragma unroll
@@ -372,29 +401,42 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
   const int kti = blockIdx.x % key_tiles;
   const int z = blockIdx.x / key_tiles;
   const int b = z / a.Hkv, kvh = z % a.Hkv;
+  const EntryLens en = entry_lens(a, b);
   const int k_wg = kti * 128;
   const int key = k_wg + wave * 32 + col;  // this lane's key
+  if (k_wg >= en.Lk || en.R == 0) {
+    // No key of the tile is valid, or the entry has no queries (uniform,
+    // before any barrier): every gradient of the tile's keys is 0.
+    if (key < a.Lk) {
+      char* zk = (char*)a.grad_k + ((int64_t)b * a.ks[0] + (int64_t)kvh * a.ks[1] + (int64_t)key * a.ks[2]) * 2;
+      char* zv = (char*)a.grad_v + ((int64_t)b * a.vs[0] + (int64_t)kvh * a.vs[1] + (int64_t)key * a.vs[2]) * 2;
+      for (int d = 8 * hl; d < a.dqk; d += 16) *(u32x4*)(zk + d * 2) = u32x4{0u, 0u, 0u, 0u};
+      for (int d = 8 * hl; d < a.dv; d += 16) *(u32x4*)(zv + d * 2) = u32x4{0u, 0u, 0u, 0u};
+    }
+    return;
+  }
 
   // packed rows that may see a key of the tile: causal needs pos >= k_wg,
   // a window pos - W < k_wg + 127
-  int64_t r_lo = 0, r_hi = a.R;
-  if (a.mask != MASK_NONE) r_lo = (int64_t)max(0, k_wg - a.off) * a.G;
+  int64_t r_lo = 0, r_hi = en.R;
+  if (a.mask != MASK_NONE) r_lo = (int64_t)max(0, k_wg - en.off) * a.G;
   if (a.mask == MASK_WINDOW) {
-    const int64_t i_hi = (int64_t)min(a.Lk - 1, k_wg + 127) + a.window - 1 - a.off;  // last query that sees it
-    r_hi = min<int64_t>(a.R, i_hi < 0 ? 0 : (i_hi + 1) * a.G);
+    const int64_t i_hi = (int64_t)min(en.Lk - 1, k_wg + 127) + a.window - 1 - en.off;  // last query that sees it
+    r_hi = min<int64_t>(en.R, i_hi < 0 ? 0 : (i_hi + 1) * a.G);
   }
-  const int jb0 = (int)(min<int64_t>(r_lo, a.R) / BQ);
+  const int jb0 = (int)(min<int64_t>(r_lo, en.R) / BQ);
   const int nblk = r_hi > r_lo ? (int)((r_hi + BQ - 1) / BQ) - jb0 : 0;
 
+  // K / V rows past the entry's keys re-read its last key (their P is 0)
   const char* kbase = (const char*)a.k + ((int64_t)b * a.ks[0] + (int64_t)kvh * a.ks[1]) * 2;
   const char* vbase = (const char*)a.v + ((int64_t)b * a.vs[0] + (int64_t)kvh * a.vs[1]) * 2;
   const int64_t kstr = a.ks[2] * 2, vstr = a.vs[2] * 2;
   const SDPA_LDS char* kreg = smem;
   const SDPA_LDS char* vreg = smem + REG;
   dma_rows<D, 128, 4>(lds_base, wave_u, lane, a.dqk / 8,
-                      [&](int row) { return kbase + (int64_t)min(k_wg + row, a.Lk - 1) * kstr; });
+                      [&](int row) { return kbase + (int64_t)min(k_wg + row, en.Lk - 1) * kstr; });
   dma_rows<D, 128, 4>(lds_base + REG, wave_u, lane, a.dv / 8,
-                      [&](int row) { return vbase + (int64_t)min(k_wg + row, a.Lk - 1) * vstr; });
+                      [&](int row) { return vbase + (int64_t)min(k_wg + row, en.Lk - 1) * vstr; });
 
   // Q / dO rows of this lane's DMA instructions: packed row r0 + rq[ii] of
   // each block, i.e. query (r0 + rq) / G of head kvh G + (r0 + rq) % G.  The
@@ -410,8 +452,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
   const int64_t q_wrap = a.qs[2] - (int64_t)a.G * a.qs[1], o_wrap = a.os[2] - (int64_t)a.G * a.os[1];
   const int64_t q_head = (int64_t)b * a.qs[0] + (int64_t)kvh * a.G * a.qs[1];
   const int64_t o_head = (int64_t)b * a.os[0] + (int64_t)kvh * a.G * a.os[1];
-  const int64_t q_last = q_head + (int64_t)((a.R - 1) % a.G) * a.qs[1] + (int64_t)((a.R - 1) / a.G) * a.qs[2];
-  const int64_t o_last = o_head + (int64_t)((a.R - 1) % a.G) * a.os[1] + (int64_t)((a.R - 1) / a.G) * a.os[2];
+  const int64_t q_last = q_head + (int64_t)((en.R - 1) % a.G) * a.qs[1] + (int64_t)((en.R - 1) / a.G) * a.qs[2];
+  const int64_t o_last = o_head + (int64_t)((en.R - 1) % a.G) * a.os[1] + (int64_t)((en.R - 1) / a.G) * a.os[2];
 #pragma unroll
   for (int ii = 0; ii < PWQ; ++ii) {
     const int sl = (ii * 4 + wave_u) * 64 + lane;
@@ -434,7 +476,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
     for (int ii = 0; ii < PWQ; ++ii) {
       const int ins = ii * 4 + wave_u;
       if ((ii + 1) * 4 > NIQ && ins >= NIQ) continue;
-      const bool in = r0 + rq[ii] < a.R;
+      const bool in = r0 + rq[ii] < en.R;
       lds_dma16<false>((const char*)a.q + (in ? qo[ii] : q_last) * 2 + cq[ii], qb + ins * 1024);
       lds_dma16<false>((const char*)a.dout + (in ? oo[ii] : o_last) * 2 + co[ii], qb + TQ + ins * 1024);
       gq[ii] += gq_step;
@@ -487,7 +529,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
   const int g_step = BQ % a.G, i_step = BQ / a.G;
   int i_first = (jb0 * BQ) / a.G, g_first = (jb0 * BQ) % a.G;
   int i_last = (jb0 * BQ + BQ - 1) / a.G, g_last = (jb0 * BQ + BQ - 1) % a.G;
-  const int i_rmax = (a.R - 1) / a.G;
+  const int i_rmax = (en.R - 1) / a.G;
   const int kw = k_wg + wave_u * 32;  // this wave's first key
 
   for (int j = 0; j < nblk; ++j) {
@@ -504,11 +546,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
       pacc = E::mma(row_frag<D>(dt, col, s, hl), row_frag<D>(vreg, wave * 32 + col, s, hl), pacc);
     }
     // register e: packed row r0 + 8 (e / 4) + 4 hl + e % 4 of this lane's
-    // key.  Only blocks on a mask edge for this wave's 32 keys test each
-    // pair (rows past R carry lse2 = +inf, so their P is 0 either way).
+    // key.  Only blocks on a mask edge for this wave's 32 keys, or with keys
+    // past the entry's length, test each pair (rows past the entry's
+    // queries carry lse2 = +inf, so their P is 0 either way).
     const int r0 = (jb0 + j) * BQ;
-    const int pmin_b = i_first + a.off;
-    const int pmax_b = (r0 + BQ - 1 < a.R ? i_last : i_rmax) + a.off;
+    const int pmin_b = i_first + en.off;
+    const int pmax_b = (r0 + BQ - 1 < en.R ? i_last : i_rmax) + en.off;
     i_first += i_step;
     g_first += g_step;
     if (g_first >= a.G) {
@@ -521,7 +564,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
       g_last -= a.G;
       ++i_last;
     }
-    const bool edge = (a.mask != MASK_NONE && kw + 31 > pmin_b) ||
+    const bool edge = (kw + 32 > en.Lk) || (a.mask != MASK_NONE && kw + 31 > pmin_b) ||
                       (a.mask == MASK_WINDOW && kw <= pmax_b - a.window);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -533,9 +576,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           const int e = 4 * g + t;
-          const int pos = (int)i4[t] + a.off;
-          bool vis = true;
-          if (a.mask != MASK_NONE) vis = key <= pos;
+          const int pos = (int)i4[t] + en.off;
+          bool vis = key < en.Lk;
+          if (a.mask != MASK_NONE) vis = vis && key <= pos;
           if (a.mask == MASK_WINDOW) vis = vis && key > pos - a.window;
           const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[e], a.c, -l4[t])) : 0.f;
           sacc[e] = p;                     // P

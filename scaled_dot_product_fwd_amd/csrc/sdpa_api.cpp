@@ -261,9 +261,10 @@ int sdpa_backward_workspace_bytes(const sdpa_desc_t* d, size_t* bytes) {
   return ok();
 }
 
-int sdpa_backward(const sdpa_desc_t* d, const void* q, const void* k, const void* v, const void* o,
-                  const void* dout, const float* lse, void* dq, void* dk, void* dv, void* workspace,
-                  size_t workspace_bytes, sdpa_stream_t stream) {
+int sdpa_backward_varlen(const sdpa_desc_t* d, const void* q, const void* k, const void* v, const void* o,
+                         const void* dout, const float* lse, const int32_t* q_lens, const int32_t* kv_lens,
+                         void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                         sdpa_stream_t stream) {
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv)
     return set_error(SDPA_E_NULL, "q, k, v, o, dout, lse, dq, dk and dv must be non-NULL device pointers");
   sdpa::BwdPlan p;
@@ -293,6 +294,8 @@ int sdpa_backward(const sdpa_desc_t* d, const void* q, const void* k, const void
   a.grad_q = dq;
   a.grad_k = dk;
   a.grad_v = dv;
+  a.q_lens = q_lens;
+  a.kv_lens = kv_lens;
   for (int j = 0; j < 3; ++j) {
     a.qs[j] = d->q_stride[j];
     a.ks[j] = d->k_stride[j];
@@ -321,6 +324,13 @@ int sdpa_backward(const sdpa_desc_t* d, const void* q, const void* k, const void
   rc = sdpa::launch_backward(p, a, stream, &err);
   if (rc != SDPA_OK) return set_error(rc, err);
   return ok();
+}
+
+int sdpa_backward(const sdpa_desc_t* d, const void* q, const void* k, const void* v, const void* o,
+                  const void* dout, const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                  size_t workspace_bytes, sdpa_stream_t stream) {
+  return sdpa_backward_varlen(d, q, k, v, o, dout, lse, nullptr, nullptr, dq, dk, dv, workspace, workspace_bytes,
+                              stream);
 }
 
 int sdpa_set_profile_events(void* start, void* stop) {

@@ -221,9 +221,11 @@ struct BwdArgs {
   float* ws_lse2;     // [B*Hkv][Rp] lse in log2 units per packed row (+inf: row has no gradient)
   float* ws_d;        // [B*Hkv][Rp] D = dO . O per packed row
   int* ws_qi;         // [Rp] query index of packed row r (r / G)
+  const int* q_lens;  // nullable [B]: valid queries per batch entry
+  const int* kv_lens; // nullable [B]: valid keys per batch entry
   int64_t qs[3], ks[3], vs[3], os[3];
   int B, Hq, Hkv, Lq, Lk, dqk, dv, G, R, Rp;
-  int off;            // Lk - Lq
+  int off;            // Lk - Lq (an entry with lengths uses its own)
   int mask, window;
   float c;            // scale * log2(e), any sign
   float scale;

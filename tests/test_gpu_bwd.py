@@ -96,3 +96,67 @@ def test_bwd_causal_l1024_d128():
     """Training-size layer: B=1, Hq=8, Hkv=2, L=1024, D=128, causal."""
     _say("bwd causal L=1024 D=128")
     check_bwd((1, 8, 2, 1024, 1024, 128, 128, "bf16", "causal", 0))
+
+
+# ---- per-batch lengths ----
+# Positions past the lengths hold NaN in q, k, v and dout (and the forward
+# leaves o / lse there unwritten, NaN): the backward must never read them,
+# and every gradient position past the lengths must come back exactly 0.
+
+VARLEN = [
+    # b, hq, hkv, lq, lk, dqk, dv, dtype, mask, window, q_lens, kv_lens
+    (3, 4, 2, 70, 300, 64, 64, "bf16", "causal", 0, [70, 5, 33], [300, 40, 0]),
+    (2, 8, 2, 1, 700, 128, 128, "bf16", "none", 0, None, [700, 129]),
+    (2, 4, 4, 150, 150, 96, 96, "f16", "causal", 0, [150, 77], [150, 100]),
+    (2, 2, 1, 90, 260, 128, 128, "bf16", "window", 50, [90, 60], [260, 61]),
+    (2, 4, 2, 40, 50, 32, 32, "f16", "causal", 0, [40, 30], [20, 50]),  # entry 0: more queries than keys
+]
+
+
+def _poison(x, lens, dim_len):
+    """NaN at positions i >= lens[b] along dim 2 of a [B, H, L, D] tensor."""
+    if lens is None:
+        return x
+    x = x.clone()
+    for bi, n in enumerate(lens):
+        x[bi, :, n:] = float("nan")
+    return x
+
+
+@pytest.mark.parametrize("case", VARLEN, ids=lambda c: "-".join(str(x) for x in c[:10]))
+def test_bwd_varlen(case):
+    from oracle import sdpa_bwd_ref_varlen
+
+    b, hq, hkv, lq, lk, dqk, dv, dt, mask, w, ql, kl = case
+    _say("bwd varlen", case)
+    dt = {"bf16": torch.bfloat16, "f16": torch.float16}[dt]
+    seed = zlib.crc32(repr(case).encode()) % 10000
+    q, k, v = make_qkv(b, hq, hkv, lq, lk, dqk, dv, dt, seed)
+    do = randn((b, hq, lq, dv), seed + 3, dt)
+    scale = default_scale(dqk)
+    ref = sdpa_bwd_ref_varlen(q, k, v, do, scale, mask, w, ql, kl)
+    dev = torch.device("cuda", 0)
+    qd, dod = _poison(q, ql, lq).to(dev), _poison(do, ql, lq).to(dev)
+    kd, vd = _poison(k, kl, lk).to(dev), _poison(v, kl, lk).to(dev)
+    qt = None if ql is None else torch.tensor(ql, dtype=torch.int32, device=dev)
+    kt = None if kl is None else torch.tensor(kl, dtype=torch.int32, device=dev)
+    o = torch.full((b, hq, lq, dv), float("nan"), dtype=dt, device=dev)
+    lse = torch.full((b, hq, lq), float("nan"), dtype=torch.float32, device=dev)
+    sdpa.forward(qd, kd, vd, scale=scale, mask=mask, window_size=w, q_lens=qt, kv_lens=kt, return_lse=True,
+                 out=o, lse_out=lse)
+    grads = [torch.full_like(x, float("nan")) for x in (qd, kd, vd)]
+    gq, gk, gv = sdpa.backward(qd, kd, vd, o, dod, lse, scale=scale, mask=mask, window_size=w, q_lens=qt,
+                               kv_lens=kt, dq=grads[0], dk=grads[1], dv=grads[2])
+    torch.cuda.synchronize()
+    errs = []
+    for name, g, r, lens in zip(("dq", "dk", "dv"), (gq, gk, gv), ref, (ql, kl, kl)):
+        g = g.cpu().double().numpy()
+        assert not np.isnan(g).any(), f"{name}: NaN (unwritten, or a padded position was read)"
+        if lens is not None:
+            for bi, n in enumerate(lens):
+                assert (g[bi, :, n:] == 0).all(), f"{name}: non-zero gradient past the lengths of entry {bi}"
+        scale_ref = max(float(np.abs(r).max()), 1e-30)
+        e = float(np.abs(g - r).max()) / scale_ref
+        errs.append(e)
+        assert e <= TOL_REL[dt], f"{name}: max|g - ref| / max|ref| = {e:.3e} > {TOL_REL[dt]:.0e}"
+    print("  rel errors dq dk dv", " ".join(f"{e:.2e}" for e in errs), flush=True)
