@@ -364,3 +364,22 @@ def test_plan_wide_family_limits():
     p = _plan(hq=8, hkv=1, lq=30, lk=4096, dqk=96, dv=96, dtype=_lib.SDPA_F32,
               mask_array=_lib.SDPA_MASK_ARRAY_ADD, mask_stride=(0, 0, 4096))
     assert p["family"] == "wide" and int(p["lds"]) <= 160 * 1024
+
+
+def test_backward_varlen_validates_before_any_launch():
+    """The per-length backward shares the backward's checks, in order, and
+    returns before touching the device: missing pointers, then the plan,
+    then alignment, then the workspace."""
+    d = _desc(b=2, hq=4, hkv=2, lq=8, lk=16, dqk=64, dv=64, mask="causal")
+    ptr = 1 << 20  # aligned, never dereferenced on the host
+    lens = ptr
+    bwd = sdpa.sdpa_backward_varlen
+    msg = _status(bwd, d, 0, ptr, ptr, ptr, ptr, ptr, lens, lens, ptr, ptr, ptr, ptr, 1 << 20, 0)
+    assert msg.startswith("SDPA_E_NULL"), msg
+    msg = _status(bwd, _desc(dtype=_lib.SDPA_F32), ptr, ptr, ptr, ptr, ptr, ptr, lens, lens, ptr, ptr, ptr,
+                  ptr, 1 << 20, 0)
+    assert msg.startswith("SDPA_E_DTYPE"), msg
+    msg = _status(bwd, d, ptr + 8, ptr, ptr, ptr, ptr, ptr, lens, lens, ptr, ptr, ptr, ptr, 1 << 20, 0)
+    assert msg.startswith("SDPA_E_STRIDE"), msg
+    msg = _status(bwd, d, ptr, ptr, ptr, ptr, ptr, ptr, lens, lens, ptr, ptr, ptr, ptr, 16, 0)
+    assert msg.startswith("SDPA_E_WORKSPACE"), msg
