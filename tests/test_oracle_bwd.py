@@ -160,3 +160,57 @@ def test_bwd_varlen_rows_without_keys():
     dq, dk, dv = sdpa_bwd_ref_varlen(q, k, v, do, 0.5, "causal", 0, [4], [2])
     assert (dq[0, :, :2] == 0).all() and np.abs(dq[0, :, 2:]).max() > 0
     assert (dk[0, :, 2:] == 0).all() and (dv[0, :, 2:] == 0).all()
+
+
+# ---- explicit mask arrays ----
+
+def test_bwd_mask_arrays_match_torch_autograd():
+    """Boolean and additive mask arrays (broadcast over heads), through
+    torch's float64 autograd with the combined mask written out."""
+    b, hq, hkv, lq, lk, d = 2, 4, 2, 5, 7, 3
+    q, k, v, do = _case(b, hq, hkv, lq, lk, d, d, seed=780)
+    rng = np.random.default_rng(781)
+    keep = rng.random((b, 1, lq, lk)) < 0.7
+    keep[..., 0] = True  # key 0 is visible to every row under causal (Lk > Lq): no row is left empty
+    vis = visible_mask(lq, lk, "causal", 0)
+    add = rng.standard_normal((1, hq, lq, lk))
+    g = hq // hkv
+    for arr, tmask in ((keep, torch.from_numpy(np.broadcast_to(keep, (b, hq, lq, lk)) & vis)),
+                       (add, torch.from_numpy(np.where(vis, np.broadcast_to(add, (b, hq, lq, lk)), -np.inf)))):
+        dq, dk, dvv = sdpa_bwd_ref(q, k, v, do, 0.6, "causal", 0, mask_arr=arr)
+        tq, tk, tv = (torch.from_numpy(x).requires_grad_(True) for x in (q, k, v))
+        out = torch.nn.functional.scaled_dot_product_attention(
+            tq, tk.repeat_interleave(g, dim=1), tv.repeat_interleave(g, dim=1), attn_mask=tmask, scale=0.6)
+        out.backward(torch.from_numpy(do))
+        np.testing.assert_allclose(dq, tq.grad.numpy(), rtol=0, atol=1e-12)
+        np.testing.assert_allclose(dk, tk.grad.numpy(), rtol=0, atol=1e-12)
+        np.testing.assert_allclose(dvv, tv.grad.numpy(), rtol=0, atol=1e-12)
+
+
+def test_bwd_varlen_mask_array_matches_finite_differences():
+    """Per-batch lengths with a boolean array that removes every key of one
+    row (that row's output is the constant 0): central differences of the
+    per-length forward oracle, every element."""
+    b, hq, hkv, lq, lk, d = 2, 2, 1, 4, 5, 2
+    q, k, v, do = _case(b, hq, hkv, lq, lk, d, d, seed=790)
+    keep = np.random.default_rng(791).random((b, hq, lq, lk)) < 0.6
+    keep[0, 1, 2, :] = False
+    ql, kl = [4, 3], [5, 4]
+    grads = sdpa_bwd_ref_varlen(q, k, v, do, 0.7, "none", 0, ql, kl, mask_arr=keep)
+    h = 1e-6
+
+    def loss(qq, kk, vv):
+        o, _ = sdpa_ref_varlen(qq, kk, vv, 0.7, "none", 0, ql, kl, mask_arr=keep)
+        return float(np.nansum(o * do))
+
+    for which, x in enumerate((q, k, v)):
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p = [q, k, v]
+            args_m = [q, k, v]
+            args_p[which], args_m[which] = xp, xm
+            fd = (loss(*args_p) - loss(*args_m)) / (2 * h)
+            assert abs(fd - grads[which][idx]) < 1e-7 * max(1.0, abs(fd)), (which, idx, fd, grads[which][idx])
+    assert (grads[0][0, 1, 2] == 0).all()
