@@ -176,7 +176,8 @@ int sdpa_forward_varlen(const sdpa_desc_t* desc, const void* q, const void* k, c
  * with grouped-query sums over each KV head's query heads.  dout uses
  * desc's o strides, dq the q strides, dk / dv the k / v strides; all in the
  * input type (float16 or bfloat16), head dims up to 128, the causal and
- * window modes (no mask array).  Deterministic (no atomics).  Needs a
+ * window modes (a mask array goes through sdpa_backward_varlen).
+ * Deterministic (no atomics).  Needs a
  * workspace of sdpa_backward_workspace_bytes() bytes (256-byte aligned).
  * Enqueues three kernels on `stream`. */
 int sdpa_backward_workspace_bytes(const sdpa_desc_t* desc, size_t* bytes);
@@ -184,17 +185,20 @@ int sdpa_backward(const sdpa_desc_t* desc, const void* q, const void* k, const v
                   const void* dout, const float* lse, void* dq, void* dk, void* dv, void* workspace,
                   size_t workspace_bytes, sdpa_stream_t stream);
 
-/* Backward with per-batch lengths (the counterpart of sdpa_forward_varlen,
- * same q_lens / kv_lens semantics: nullable int32 device arrays [B], entry b
- * uses its first q_lens[b] queries and kv_lens[b] keys, query i at key
- * position i + kv_lens[b] - q_lens[b]).  Every gradient position past an
- * entry's lengths is written as 0, as is dq of a row that sees no key:
- * those outputs depend on no input.  The padded rows and keys are never
- * read (a row or key past the lengths reads the entry's last valid one), so
- * they may hold anything. */
-int sdpa_backward_varlen(const sdpa_desc_t* desc, const void* q, const void* k, const void* v, const void* o,
-                         const void* dout, const float* lse, const int32_t* q_lens, const int32_t* kv_lens,
-                         void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+/* Backward with an explicit mask array and / or per-batch lengths (the
+ * counterpart of sdpa_forward_varlen, same arguments and meaning: `mask` as
+ * in sdpa_forward_masked, required iff desc->mask_array is not NONE;
+ * q_lens / kv_lens nullable int32 device arrays [B], entry b using its first
+ * q_lens[b] queries and kv_lens[b] keys, query i at key position
+ * i + kv_lens[b] - q_lens[b]).  The mask array is a constant of the forward:
+ * no gradient is produced for it.  Every gradient position past an entry's
+ * lengths is written as 0, as is dq of a row left without keys: those
+ * outputs depend on no input.  The padded rows and keys are never read (a
+ * row or key past the lengths reads the entry's last valid one), so they
+ * may hold anything. */
+int sdpa_backward_varlen(const sdpa_desc_t* desc, const void* q, const void* k, const void* v, const void* mask,
+                         const int32_t* q_lens, const int32_t* kv_lens, const void* o, const void* dout,
+                         const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
                          sdpa_stream_t stream);
 
 /* Writes a one-line, NUL-terminated description of the plan (kernel family,

@@ -235,16 +235,17 @@ def forward(q, k, v, *, scale: Optional[float] = None, mask: str = "none", windo
 
 
 def backward(q, k, v, o, dout, lse, *, scale: Optional[float] = None, mask: str = "none",
-             window_size: int = 0, q_lens=None, kv_lens=None, dq=None, dk=None, dv=None, workspace=None,
-             stream=None):
+             window_size: int = 0, attn_mask=None, q_lens=None, kv_lens=None, dq=None, dk=None, dv=None,
+             workspace=None, stream=None):
     """Gradients ``(dq, dk, dv)`` of the fused forward on the current HIP device.
 
-    ``q, k, v`` and ``scale``, ``mask``, ``window_size``, ``q_lens``,
-    ``kv_lens`` as given to ``forward``; ``o`` and ``lse`` its output and
-    float32 log-sum-exp (``return_lse=True``); ``dout`` the upstream
-    gradient, shaped and strided like ``o``.  With per-batch lengths every
-    gradient position past them is 0.  float16 / bfloat16, head dims up to
-    128, no mask array.  Deterministic.
+    ``q, k, v`` and ``scale``, ``mask``, ``window_size``, ``attn_mask``,
+    ``q_lens``, ``kv_lens`` as given to ``forward``; ``o`` and ``lse`` its
+    output and float32 log-sum-exp (``return_lse=True``); ``dout`` the
+    upstream gradient, shaped and strided like ``o``.  The mask array is a
+    constant (no gradient for it).  With per-batch lengths every gradient
+    position past them is 0.  float16 / bfloat16, head dims up to 128.
+    Deterministic.
     """
     import torch
 
@@ -260,9 +261,12 @@ def backward(q, k, v, o, dout, lse, *, scale: Optional[float] = None, mask: str 
             or lse.device != q.device):
         raise SdpaValueError("SDPA_E_SHAPE: lse must be the forward's contiguous float32 [B, Hq, Lq]")
     dt = _dtype_code(q.dtype)
+    kind, mstr = SDPA_MASK_ARRAY_NONE, (0, 0, 0)
+    if attn_mask is not None:
+        kind, mstr = _mask_layout(attn_mask, q, b, hq, lq, k.shape[2])
     desc = make_desc(q.shape, k.shape, v.shape, dt, scale=scale, mask=mask, window_size=window_size,
                      q_stride=q.stride()[:3], k_stride=k.stride()[:3], v_stride=v.stride()[:3],
-                     o_stride=o.stride()[:3])
+                     o_stride=o.stride()[:3], mask_array=kind, mask_stride=mstr)
     outs = []
     for name, given, like in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
         if given is None:
@@ -288,8 +292,9 @@ def backward(q, k, v, o, dout, lse, *, scale: Optional[float] = None, mask: str 
             raise SdpaValueError(f"SDPA_E_SHAPE: {name} must be a contiguous int32 [B] tensor on q's device")
         lens.append(t.data_ptr())
     with torch.cuda.device(q.device):
-        sdpa_backward_varlen(desc, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
-                             lse.data_ptr(), lens[0], lens[1], outs[0].data_ptr(), outs[1].data_ptr(),
+        sdpa_backward_varlen(desc, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                             attn_mask.data_ptr() if attn_mask is not None else 0, lens[0], lens[1],
+                             o.data_ptr(), dout.data_ptr(), lse.data_ptr(), outs[0].data_ptr(), outs[1].data_ptr(),
                              outs[2].data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                              stream)
     return tuple(outs)

@@ -113,7 +113,7 @@ def load() -> ctypes.CDLL:
     lib.sdpa_backward_workspace_bytes.restype = ctypes.c_int
     lib.sdpa_backward.argtypes = [P(sdpa_desc_t)] + [ctypes.c_void_p] * 10 + [ctypes.c_size_t, ctypes.c_void_p]
     lib.sdpa_backward.restype = ctypes.c_int
-    lib.sdpa_backward_varlen.argtypes = [P(sdpa_desc_t)] + [ctypes.c_void_p] * 12 + [ctypes.c_size_t,
+    lib.sdpa_backward_varlen.argtypes = [P(sdpa_desc_t)] + [ctypes.c_void_p] * 13 + [ctypes.c_size_t,
                                                                                      ctypes.c_void_p]
     lib.sdpa_backward_varlen.restype = ctypes.c_int
     lib.sdpa_describe_plan.argtypes = [P(sdpa_desc_t), ctypes.c_char_p, ctypes.c_size_t]
@@ -203,9 +203,11 @@ def sdpa_backward(desc: sdpa_desc_t, q: int, k: int, v: int, o: int, dout: int, 
                                workspace_bytes, stream or None))
 
 
-def sdpa_backward_varlen(desc: sdpa_desc_t, q: int, k: int, v: int, o: int, dout: int, lse: int, q_lens: int,
-                         kv_lens: int, dq: int, dk: int, dv: int, workspace: int | None, workspace_bytes: int,
-                         stream: int | None) -> None:
-    """Raw backward call with per-batch lengths (0 for an absent array); raises on a non-zero status."""
-    check(load().sdpa_backward_varlen(ctypes.byref(desc), q, k, v, o, dout, lse, q_lens or None, kv_lens or None,
-                                      dq, dk, dv, workspace or None, workspace_bytes, stream or None))
+def sdpa_backward_varlen(desc: sdpa_desc_t, q: int, k: int, v: int, mask: int, q_lens: int, kv_lens: int, o: int,
+                         dout: int, lse: int, dq: int, dk: int, dv: int, workspace: int | None,
+                         workspace_bytes: int, stream: int | None) -> None:
+    """Raw backward call with a mask array and / or per-batch lengths (0 for an
+    absent one); raises on a non-zero status."""
+    check(load().sdpa_backward_varlen(ctypes.byref(desc), q, k, v, mask or None, q_lens or None, kv_lens or None,
+                                      o, dout, lse, dq, dk, dv, workspace or None, workspace_bytes,
+                                      stream or None))

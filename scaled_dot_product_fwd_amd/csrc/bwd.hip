@@ -192,7 +192,9 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
 }
 
 // ---- dQ: rows on the lanes, walking the key blocks ----
-template <class E, int D>
+// MASKED: instantiated for an explicit mask array (a.ma != MA_NONE); the
+// plain instance carries none of its code or registers.
+template <class E, int D, bool MASKED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void bwd_dq_kernel(BwdArgs a) {
   using T = Tile<D>;
   constexpr int BK = D <= 64 ? 64 : 32;  // keys per block
@@ -297,6 +299,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
   const int64_t wrow = (int64_t)z * a.Rp + rc;
   const float lse2 = row_ok ? a.ws_lse2[wrow] : __builtin_inff();
   const float drow_d = row_ok ? a.ws_d[wrow] : 0.f;
+  // this row of the mask array (rows past the entry read its last row)
+  const char* mrow = MASKED ? (const char*)a.mask_arr + ((int64_t)b * a.ms[0] + (int64_t)hq * a.ms[1] +
+                                                                 (int64_t)iq * a.ms[2]) * a.mes
+                                     : nullptr;
   f32x16 acc[NDT];
 #pragma unroll
   for (int t = 0; t < NDT; ++t) acc[t] = f32x16{};
@@ -328,7 +334,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
       const int kw = k0 + kt * 32;
       const bool edge = (kw + 32 > en.Lk) || (a.mask != MASK_NONE && kw + 31 > pmin_w) ||
                         (a.mask == MASK_WINDOW && kw <= pmax_w - a.window);
-      if (edge) {
+      if constexpr (MASKED) {
+        // Mask array: each group of 4 registers covers 4 consecutive keys,
+        // read as one 4-byte (boolean) or 8-byte (additive) load; keys past
+        // Lk read the row's first group and are masked anyway.  An additive
+        // value joins the exponent in log2 units, as in the forward.
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int kk = kw + 8 * g + 4 * hl;
+          const char* pm = mrow + (kk < a.Lk ? kk : 0) * a.mes;
+          unsigned mb = 0xffffffffu;
+          u32x2 mw = {0u, 0u};
+          if (a.ma == MA_BOOL) mb = *(const unsigned*)pm;
+          else mw = *(const u32x2*)pm;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const int e = 4 * g + t;
+            const int key = kk + t;
+            bool vis = key < en.Lk;
+            if (a.mask != MASK_NONE) vis = vis && key <= pos;
+            if (a.mask == MASK_WINDOW) vis = vis && key > pos - a.window;
+            float madd = 0.f;
+            if (a.ma == MA_BOOL) vis = vis && ((mb >> (8 * t)) & 0xffu) != 0u;
+            else madd = E::to_float((unsigned short)(mw[t >> 1] >> (16 * (t & 1)))) * kLog2e;
+            const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][e], a.c, madd - lse2)) : 0.f;
+            sacc[kt][e] = vis ? p * (pacc[kt][e] - drow_d) : 0.f;  // dS^T (without the scale)
+          }
+        }
+      } else if (edge) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int key = kw + 8 * (e >> 2) + 4 * hl + (e & 3);
@@ -378,7 +411,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
 }
 
 // ---- dK, dV: keys on the lanes, walking the query blocks ----
-template <class E, int D>
+template <class E, int D, bool MASKED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void bwd_dkdv_kernel(BwdArgs a) {
   using T = Tile<D>;
   constexpr int BQ = 32;  // packed rows per block
@@ -531,6 +564,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
   int i_last = (jb0 * BQ + BQ - 1) / a.G, g_last = (jb0 * BQ + BQ - 1) % a.G;
   const int i_rmax = (en.R - 1) / a.G;
   const int kw = k_wg + wave_u * 32;  // this wave's first key
+  // this lane's key column of the mask array, batch entry b
+  const char* mkey = MASKED ? (const char*)a.mask_arr + ((int64_t)b * a.ms[0] + (key < a.Lk ? key : 0)) * a.mes
+                                     : nullptr;
 
   for (int j = 0; j < nblk; ++j) {
     if (j + 1 < nblk) wait_vmcnt_upto<DMA_MAX>(dma_w);
@@ -571,7 +607,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
       const int rb = 8 * g + 4 * hl;
       const f32x4 l4 = *(const SDPA_LDS f32x4*)(sm + rb * 4);
       const f32x4 d4 = *(const SDPA_LDS f32x4*)(sm + 128 + rb * 4);
-      if (edge) {
+      if constexpr (MASKED) {
+        // Mask array: element (packed row, this lane's key) read one by one;
+        // the row's (query head, query) come from its query index, rows past
+        // R from row R - 1, keys past Lk from key 0 (masked anyway).
+        const u32x4 i4 = *(const SDPA_LDS u32x4*)(sm + 256 + rb * 4);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int e = 4 * g + t;
+          const int iq = (int)i4[t];
+          const int rr = min(r0 + rb + t, a.R - 1);
+          const int hq = kvh * a.G + (rr - iq * a.G);
+          const char* pm = mkey + ((int64_t)hq * a.ms[1] + (int64_t)iq * a.ms[2]) * a.mes;
+          const int pos = iq + en.off;
+          bool vis = key < en.Lk;
+          if (a.mask != MASK_NONE) vis = vis && key <= pos;
+          if (a.mask == MASK_WINDOW) vis = vis && key > pos - a.window;
+          float madd = 0.f;
+          if (a.ma == MA_BOOL) vis = vis && *(const unsigned char*)pm != 0;
+          else madd = E::to_float(*(const unsigned short*)pm) * kLog2e;
+          const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[e], a.c, madd - l4[t])) : 0.f;
+          sacc[e] = p;                                  // P
+          pacc[e] = vis ? p * (pacc[e] - d4[t]) : 0.f;  // dS (without the scale)
+        }
+      } else if (edge) {
         const u32x4 i4 = *(const SDPA_LDS u32x4*)(sm + 256 + rb * 4);
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
@@ -637,9 +696,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
 template <class E, int D>
 int launch_bwd_dims(const BwdPlan& p, const BwdArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(bwd_prep_kernel<E>, dim3((unsigned)p.prep_grid), dim3(256), 0, s, a);
-  if (p.dq_grid > 0) hipLaunchKernelGGL((bwd_dq_kernel<E, D>), dim3((unsigned)p.dq_grid), dim3(256), 0, s, a);
-  if (p.dkdv_grid > 0)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<E, D>), dim3((unsigned)p.dkdv_grid), dim3(256), 0, s, a);
+  const bool masked = a.ma != MA_NONE;
+  if (p.dq_grid > 0) {
+    if (masked) hipLaunchKernelGGL((bwd_dq_kernel<E, D, true>), dim3((unsigned)p.dq_grid), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((bwd_dq_kernel<E, D, false>), dim3((unsigned)p.dq_grid), dim3(256), 0, s, a);
+  }
+  if (p.dkdv_grid > 0) {
+    if (masked) hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, true>), dim3((unsigned)p.dkdv_grid), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, false>), dim3((unsigned)p.dkdv_grid), dim3(256), 0, s, a);
+  }
   return SDPA_OK;
 }
 

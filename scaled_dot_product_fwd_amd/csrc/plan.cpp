@@ -288,8 +288,6 @@ int make_bwd_plan(const sdpa_desc_t* d, BwdPlan* p, std::string* err) {
       << "): the backward pass supports head dims up to 128";
     return fail(err, SDPA_E_HEAD_DIM, s.str());
   }
-  if (d->mask_array != SDPA_MASK_ARRAY_NONE)
-    return fail(err, SDPA_E_MASK, "the backward pass takes the causal / window modes, not a mask array");
   const int64_t m = std::max(d->dim_qk, d->dim_v);
   const int64_t G = d->heads_q / d->heads_kv;
   const int64_t R = G * d->len_q;

@@ -261,9 +261,9 @@ int sdpa_backward_workspace_bytes(const sdpa_desc_t* d, size_t* bytes) {
   return ok();
 }
 
-int sdpa_backward_varlen(const sdpa_desc_t* d, const void* q, const void* k, const void* v, const void* o,
-                         const void* dout, const float* lse, const int32_t* q_lens, const int32_t* kv_lens,
-                         void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+int sdpa_backward_varlen(const sdpa_desc_t* d, const void* q, const void* k, const void* v, const void* mask,
+                         const int32_t* q_lens, const int32_t* kv_lens, const void* o, const void* dout,
+                         const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
                          sdpa_stream_t stream) {
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv)
     return set_error(SDPA_E_NULL, "q, k, v, o, dout, lse, dq, dk and dv must be non-NULL device pointers");
@@ -271,9 +271,13 @@ int sdpa_backward_varlen(const sdpa_desc_t* d, const void* q, const void* k, con
   std::string err;
   int rc = sdpa::make_bwd_plan(d, &p, &err);
   if (rc != SDPA_OK) return set_error(rc, err);
+  const bool has_arr = d->mask_array != SDPA_MASK_ARRAY_NONE;
+  if (has_arr != (mask != nullptr))
+    return set_error(SDPA_E_NULL, has_arr ? "desc names a mask array but mask is NULL"
+                                          : "mask is given but desc->mask_array is SDPA_MASK_ARRAY_NONE");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(dq) ||
-      !aligned16(dk) || !aligned16(dv))
-    return set_error(SDPA_E_STRIDE, "q, k, v, o, dout, dq, dk and dv must be 16-byte aligned");
+      !aligned16(dk) || !aligned16(dv) || (mask && !aligned16(mask)))
+    return set_error(SDPA_E_STRIDE, "q, k, v, o, dout, dq, dk, dv and mask must be 16-byte aligned");
   if (reinterpret_cast<uintptr_t>(lse) & 3u) return set_error(SDPA_E_STRIDE, "lse must be 4-byte aligned");
   if (!workspace || workspace_bytes < p.workspace)
     return set_error(SDPA_E_WORKSPACE, "the backward pass needs a workspace of " + std::to_string(p.workspace) +
@@ -296,7 +300,12 @@ int sdpa_backward_varlen(const sdpa_desc_t* d, const void* q, const void* k, con
   a.grad_v = dv;
   a.q_lens = q_lens;
   a.kv_lens = kv_lens;
+  a.mask_arr = mask;
+  a.ma = d->mask_array == SDPA_MASK_ARRAY_BOOL ? sdpa::MA_BOOL
+                                                : (d->mask_array == SDPA_MASK_ARRAY_ADD ? sdpa::MA_ADD : sdpa::MA_NONE);
+  a.mes = sdpa::mask_elem_bytes(a.ma, 2);
   for (int j = 0; j < 3; ++j) {
+    a.ms[j] = mask ? d->mask_stride[j] : 0;
     a.qs[j] = d->q_stride[j];
     a.ks[j] = d->k_stride[j];
     a.vs[j] = d->v_stride[j];
@@ -329,8 +338,10 @@ int sdpa_backward_varlen(const sdpa_desc_t* d, const void* q, const void* k, con
 int sdpa_backward(const sdpa_desc_t* d, const void* q, const void* k, const void* v, const void* o,
                   const void* dout, const float* lse, void* dq, void* dk, void* dv, void* workspace,
                   size_t workspace_bytes, sdpa_stream_t stream) {
-  return sdpa_backward_varlen(d, q, k, v, o, dout, lse, nullptr, nullptr, dq, dk, dv, workspace, workspace_bytes,
-                              stream);
+  if (d && d->mask_array != SDPA_MASK_ARRAY_NONE)
+    return set_error(SDPA_E_MASK, "desc names a mask array: call sdpa_backward_varlen with the array");
+  return sdpa_backward_varlen(d, q, k, v, nullptr, nullptr, nullptr, o, dout, lse, dq, dk, dv, workspace,
+                              workspace_bytes, stream);
 }
 
 int sdpa_set_profile_events(void* start, void* stop) {

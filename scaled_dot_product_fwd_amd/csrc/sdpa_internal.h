@@ -223,6 +223,9 @@ struct BwdArgs {
   int* ws_qi;         // [Rp] query index of packed row r (r / G)
   const int* q_lens;  // nullable [B]: valid queries per batch entry
   const int* kv_lens; // nullable [B]: valid keys per batch entry
+  const void* mask_arr;  // explicit mask array of the forward (ma != MA_NONE)
+  int64_t ms[3];         // its element strides of (batch, query head, query)
+  int ma, mes;           // MA_NONE / MA_BOOL / MA_ADD, bytes per element
   int64_t qs[3], ks[3], vs[3], os[3];
   int B, Hq, Hkv, Lq, Lk, dqk, dv, G, R, Rp;
   int off;            // Lk - Lq (an entry with lengths uses its own)

@@ -343,11 +343,12 @@ def test_backward_workspace_covers_whole_row_blocks(b, hq, hkv, lq):
 
 def test_backward_validation():
     for kw, code, needle in [(dict(dtype=_lib.SDPA_F32), "SDPA_E_DTYPE", "float16 and bfloat16"),
-                             (dict(dqk=256, dv=256), "SDPA_E_HEAD_DIM", "up to 128"),
-                             (dict(mask_array=_lib.SDPA_MASK_ARRAY_BOOL, mask_stride=(0, 0, 16)), "SDPA_E_MASK",
-                              "mask array")]:
+                             (dict(dqk=256, dv=256), "SDPA_E_HEAD_DIM", "up to 128")]:
         msg = _status(sdpa.sdpa_backward_workspace_bytes, _desc(**kw))
         assert msg.startswith(code) and needle in msg, msg
+    # a mask array is planned like the forward's (its strides are checked there)
+    d = _desc(mask_array=_lib.SDPA_MASK_ARRAY_BOOL, mask_stride=(0, 0, 16))
+    assert sdpa.sdpa_backward_workspace_bytes(d) > 0
 
 
 def test_plan_wide_family_limits():
@@ -367,19 +368,24 @@ def test_plan_wide_family_limits():
 
 
 def test_backward_varlen_validates_before_any_launch():
-    """The per-length backward shares the backward's checks, in order, and
-    returns before touching the device: missing pointers, then the plan,
-    then alignment, then the workspace."""
+    """The per-length / masked backward shares the backward's checks, in
+    order, and returns before touching the device: missing pointers, the
+    plan, the mask pointer against the descriptor, alignment, workspace."""
     d = _desc(b=2, hq=4, hkv=2, lq=8, lk=16, dqk=64, dv=64, mask="causal")
     ptr = 1 << 20  # aligned, never dereferenced on the host
-    lens = ptr
     bwd = sdpa.sdpa_backward_varlen
-    msg = _status(bwd, d, 0, ptr, ptr, ptr, ptr, ptr, lens, lens, ptr, ptr, ptr, ptr, 1 << 20, 0)
-    assert msg.startswith("SDPA_E_NULL"), msg
-    msg = _status(bwd, _desc(dtype=_lib.SDPA_F32), ptr, ptr, ptr, ptr, ptr, ptr, lens, lens, ptr, ptr, ptr,
-                  ptr, 1 << 20, 0)
-    assert msg.startswith("SDPA_E_DTYPE"), msg
-    msg = _status(bwd, d, ptr + 8, ptr, ptr, ptr, ptr, ptr, lens, lens, ptr, ptr, ptr, ptr, 1 << 20, 0)
-    assert msg.startswith("SDPA_E_STRIDE"), msg
-    msg = _status(bwd, d, ptr, ptr, ptr, ptr, ptr, ptr, lens, lens, ptr, ptr, ptr, ptr, 16, 0)
-    assert msg.startswith("SDPA_E_WORKSPACE"), msg
+
+    def call(desc, q=ptr, mask=0, ws_bytes=1 << 20):
+        return _status(bwd, desc, q, ptr, ptr, mask, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ws_bytes, 0)
+
+    assert call(d, q=0).startswith("SDPA_E_NULL")
+    assert call(_desc(dtype=_lib.SDPA_F32)).startswith("SDPA_E_DTYPE")
+    assert call(d, mask=ptr).startswith("SDPA_E_NULL")  # a mask the descriptor does not name
+    dm = _desc(b=2, hq=4, hkv=2, lq=8, lk=16, dqk=64, dv=64, mask_array=_lib.SDPA_MASK_ARRAY_BOOL,
+               mask_stride=(0, 0, 16))
+    assert call(dm).startswith("SDPA_E_NULL")  # the descriptor names a mask that is missing
+    assert call(d, q=ptr + 8).startswith("SDPA_E_STRIDE")
+    assert call(d, ws_bytes=16).startswith("SDPA_E_WORKSPACE")
+    # the plain backward refuses a descriptor with a mask array
+    msg = _status(sdpa.sdpa_backward, dm, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, 1 << 20, 0)
+    assert msg.startswith("SDPA_E_MASK"), msg

@@ -160,3 +160,51 @@ def test_bwd_varlen(case):
         errs.append(e)
         assert e <= TOL_REL[dt], f"{name}: max|g - ref| / max|ref| = {e:.3e} > {TOL_REL[dt]:.0e}"
     print("  rel errors dq dk dv", " ".join(f"{e:.2e}" for e in errs), flush=True)
+
+
+# ---- explicit mask arrays ----
+
+MASKED = [
+    # b, hq, hkv, lq, lk, d, dtype, mode, window, mask shape, kind, q_lens, kv_lens
+    (2, 4, 2, 96, 200, 64, "bf16", "causal", 0, (2, 1, 96, 200), "bool", None, None),
+    (1, 4, 4, 130, 130, 128, "f16", "none", 0, (1, 4, 130, 130), "add", None, None),
+    (2, 2, 1, 70, 260, 96, "bf16", "window", 60, (1, 1, 70, 260), "add", None, None),
+    (2, 8, 2, 1, 513, 128, "bf16", "none", 0, (2, 1, 1, 513), "bool", None, None),
+    (3, 4, 2, 40, 150, 64, "f16", "causal", 0, (3, 1, 40, 150), "bool", [40, 17, 40], [150, 90, 33]),
+]
+
+
+@pytest.mark.parametrize("case", MASKED, ids=lambda c: "-".join(str(x) for x in c[:11]))
+def test_bwd_mask_array(case):
+    from oracle import sdpa_bwd_ref_varlen
+    from scaled_dot_product_fwd_amd.synth import additive_mask, bool_mask
+
+    b, hq, hkv, lq, lk, d, dt, mode, w, mshape, kind, ql, kl = case
+    _say("bwd mask array", case)
+    dt = {"bf16": torch.bfloat16, "f16": torch.float16}[dt]
+    seed = zlib.crc32(repr(case).encode()) % 10000
+    q, k, v = make_qkv(b, hq, hkv, lq, lk, d, d, dt, seed)
+    do = randn((b, hq, lq, d), seed + 3, dt)
+    arr = bool_mask(mshape, seed + 5, keep=0.7) if kind == "bool" else additive_mask(mshape, seed + 5, dt)
+    scale = default_scale(d)
+    ref = sdpa_bwd_ref_varlen(q, k, v, do, scale, mode, w, ql, kl, mask_arr=arr)
+    dev = torch.device("cuda", 0)
+    qd, kd, vd, dod = q.to(dev), k.to(dev), v.to(dev), do.to(dev)
+    md = sdpa.pad_mask(arr.to(dev))
+    qt = None if ql is None else torch.tensor(ql, dtype=torch.int32, device=dev)
+    kt = None if kl is None else torch.tensor(kl, dtype=torch.int32, device=dev)
+    o, lse = sdpa.forward(qd, kd, vd, scale=scale, mask=mode, window_size=w, attn_mask=md, q_lens=qt,
+                          kv_lens=kt, return_lse=True)
+    grads = [torch.full_like(x, float("nan")) for x in (qd, kd, vd)]
+    gq, gk, gv = sdpa.backward(qd, kd, vd, o, dod, lse, scale=scale, mask=mode, window_size=w, attn_mask=md,
+                               q_lens=qt, kv_lens=kt, dq=grads[0], dk=grads[1], dv=grads[2])
+    torch.cuda.synchronize()
+    errs = []
+    for name, g, r in zip(("dq", "dk", "dv"), (gq, gk, gv), ref):
+        g = g.cpu().double().numpy()
+        assert not np.isnan(g).any(), f"{name}: NaN"
+        scale_ref = max(float(np.abs(r).max()), 1e-30)
+        e = float(np.abs(g - r).max()) / scale_ref
+        errs.append(e)
+        assert e <= TOL_REL[dt], f"{name}: max|g - ref| / max|ref| = {e:.3e} > {TOL_REL[dt]:.0e}"
+    print("  rel errors dq dk dv", " ".join(f"{e:.2e}" for e in errs), flush=True)
