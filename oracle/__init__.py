@@ -8,7 +8,7 @@ from ``scaled_dot_product_fwd_amd``.
 
 The oracle is the plain definition of attention written out in float64 with the
 score matrix materialised (row chunks bound the memory), i.e. the unfused
-unfused matmul-softmax-matmul sequence that the fused kernels replace.
+matmul-softmax-matmul sequence that the fused kernels replace.
 
 Every function is pinned in ``tests/test_oracle.py`` against brute force on tiny
 inputs, closed forms, invariants and a library special case.  No function here
