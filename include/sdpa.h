@@ -17,8 +17,8 @@
  *   SDPA_MASK_WINDOW  causal and additionally p - window < j, i.e. the last
  *                     `window` key positions up to and including p.
  * An explicit mask array (mlx PR #3552, Public API: the `mask_arr` argument
- * beside the mask mode; its boolean and float kinds are the "bool mask" and
- * "float mask" specialisations of mlx PR #4185's validation comment) may be
+ * beside the mask mode; its boolean and floating-point kinds are the two
+ * mask specialisations that mlx PR #4185's validation tells apart) may be
  * given on top of the mask mode, through sdpa_forward_masked():
  *   SDPA_MASK_ARRAY_BOOL  one byte per element: 1 keeps the key, 0 removes
  *                         it (a C/C++ bool; no other byte values);

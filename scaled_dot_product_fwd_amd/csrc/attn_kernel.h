@@ -4,8 +4,8 @@
 // contiguous range of key blocks, and walks that range block by block with an
 // online softmax (running row max m and row sum l, rescaled accumulator), so
 // the Lq x Lk score matrix never exists (mlx PR #4185 "Add force_fused option
-// to scaled_dot_product_attention", Background: tiled K/V keep the transient
-// bounded regardless of kL).
+// to scaled_dot_product_attention", Background: with K/V taken in tiles the
+// temporary memory does not grow with the key length).
 //
 // Data flow per key block (BK = NWK * BKW keys):
 //   HBM/L2 --LDS DMA (global_load_lds, 16 B per lane)--> LDS K tile [key][d]

@@ -1,6 +1,7 @@
 // Split combine: merges the per-split partial results of one packed row by
 // log-sum-exp (mlx issue #3826 "2.3-2.8x latency jump from L=8 to L=12
-// queries", third comment: the split-S + logsumexp merge of the 2-pass path).
+// queries", third comment: the two-pass kernel there merges the partial
+// results of its key splits by log-sum-exp).
 //
 // For splits s with running max m_s (log2 units), sum l_s and unnormalised
 // output O_s:  M = max_s m_s,  w_s = 2^(m_s - M),  L = sum_s w_s l_s,
