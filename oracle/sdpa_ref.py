@@ -9,8 +9,9 @@ What is computed
 
 * grouped-query attention: query head ``h`` reads key/value head
   ``h // (Hq // Hkv)``, i.e. consecutive query heads share one KV head
-  ("gqa_factor" query heads per KV head; mlx issue #3826 "2.3-2.8x latency
-  jump from L=8 to L=12 queries", first maintainer comment, item 1).  This is
+  (the grouping factor is Hq // Hkv query heads per KV head; mlx issue #3826
+  "2.3-2.8x latency jump from L=8 to L=12 queries", first maintainer comment,
+  item 1).  This is
   the same as repeating every KV head ``Hq // Hkv`` times in place.
 * causal masking aligned bottom-right: query row ``i`` sits at key position
   ``p = i + (Lk - Lq)`` and sees keys ``j <= p`` (K-relative coordinates with
@@ -20,8 +21,8 @@ What is computed
   Validation).
 * sliding window: each query sees only the last ``window`` key positions up to
   and including its own, combined with causal masking, i.e. ``p - W < j <= p``
-  (mlx PR #3552, Summary and the per-element rule "row_pos - col_pos >= W is
-  masked" in Implementation).  ``window >= 1`` is required.
+  (mlx PR #3552, Summary, and the per-element rule in Implementation that
+  removes a key once the query's position exceeds it by W or more).  ``window >= 1`` is required.
 * an optional explicit mask array broadcast over ``[B, Hq, Lq, Lk]`` (the
   ``mask_arr`` argument beside the mask mode in mlx PR #3552, Public API; the
   boolean and float mask specialisations listed in mlx PR #4185's validation
