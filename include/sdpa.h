@@ -82,7 +82,7 @@ typedef enum {
   SDPA_OK = 0,
   SDPA_E_NULL = -1,      /* a required pointer is NULL */
   SDPA_E_SHAPE = -2,     /* a size < 1, Hq not a multiple of Hkv, size overflow */
-  SDPA_E_HEAD_DIM = -3,  /* head dim outside the instantiated set (e.g. 512) */
+  SDPA_E_HEAD_DIM = -3,  /* head dim not a multiple of 8, above 512, or above 128 in float32 */
   SDPA_E_DTYPE = -4,     /* unknown element type */
   SDPA_E_MASK = -5,      /* unknown mask or mask array kind, causal/window with Lq > Lk, bad window */
   SDPA_E_STRIDE = -6,    /* stride or pointer alignment (16-byte rows) violated */
