@@ -33,8 +33,12 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a)
   __shared__ float msh[kCombineMaxSplits];
   __shared__ f32x4 part[kCombineThreads];
   __shared__ float red[kCombineThreads / 64], red_l[kCombineThreads / 64];
-  const int row = blockIdx.x;  // z * R + r
-  const int z = row / a.R, r = row % a.R;
+  // row = z * R + r; with xcd_rows the workgroups of XCD w % 8 take the
+  // rows of the KV heads z = w % 8 (mod 8), whose splits ran on that XCD
+  const int w = blockIdx.x;
+  const int z = a.xcd_rows ? 8 * (w / (8 * a.R)) + w % 8 : w / a.R;
+  const int r = a.xcd_rows ? (w / 8) % a.R : w % a.R;
+  const int row = z * a.R + r;
   const int b = z / a.Hkv, kvh = z % a.Hkv;
   const int g = r % a.G, i = r / a.G, h = kvh * a.G + g;
   if (a.q_lens && i >= min(max(a.q_lens[b], 0), a.Lq)) return;  // past the entry's queries: not written

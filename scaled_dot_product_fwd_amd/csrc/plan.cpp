@@ -262,6 +262,11 @@ int make_plan(const sdpa_desc_t* d, Plan* p, std::string* err) {
   // nor for a single round of window tiles.
   p->xcd_group = ((splits > 1 && row_tiles > 1) ||
                   (mask == MASK_WINDOW && base * splits >= 4 * (int64_t)kTargetCUs)) ? 8 : 0;
+  // One row tile per KV head and a multiple of 8 heads: all splits of a head
+  // run on one XCD, and the combine takes that head's rows on the same XCD,
+  // so the partials it reads were written through its own L2.
+  p->combine_xcd = splits > 1 && row_tiles == 1 && (B * Hkv) % 8 == 0;
+  if (p->combine_xcd) p->xcd_group = splits;
   p->combine_grid = splits > 1 ? B * Hkv * R : 0;
   p->workspace = 0;
   if (splits > 1) {
@@ -321,6 +326,7 @@ std::string describe(const sdpa_desc_t* d, const Plan& p) {
   if (p.mask == MASK_WINDOW) s << "(" << p.window << ")";
   if (p.mask_array != MA_NONE) s << " mask_array=" << (p.mask_array == MA_BOOL ? "bool" : "add");
   s << " grid=" << p.grid << " xcd_group=" << p.xcd_group << " combine_grid=" << p.combine_grid
+    << " combine_xcd=" << (p.combine_xcd ? 1 : 0)
     << " lds=" << p.lds_bytes
     << " workspace=" << p.workspace;
   return s.str();

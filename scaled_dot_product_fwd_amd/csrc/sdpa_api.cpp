@@ -221,6 +221,7 @@ int sdpa_forward_varlen(const sdpa_desc_t* d, const void* q, const void* k, cons
     c.q_lens = q_lens;
     c.kv_lens = kv_lens;
     c.kv_balance = a.kv_balance;
+    c.xcd_rows = p.combine_xcd ? 1 : 0;
     c.Lk = a.Lk;
     for (int j = 0; j < 3; ++j) c.os[j] = d->o_stride[j];
     c.B = a.B;

@@ -88,6 +88,7 @@ struct CombineArgs {
   int64_t os[3];
   int B, Hq, Hkv, Lq, Lk, dv, G, R, splits;
   int kv_balance;     // see AttnArgs::kv_balance
+  int xcd_rows;       // 1: workgroup w takes KV head row group z with z % 8 == w % 8 (B Hkv % 8 == 0)
 };
 
 // Kernel family = how the waves of a workgroup divide the work.
@@ -161,6 +162,7 @@ struct Plan {
   int mes;               // bytes per mask array element (0 without one)
   int64_t grid;          // workgroups of the attention kernel
   int xcd_group;         // see AttnArgs::xcd_group
+  bool combine_xcd;      // see CombineArgs::xcd_rows
   int64_t combine_grid;  // workgroups of the combine kernel (0 when unsplit)
   size_t workspace;      // bytes
   size_t lds_bytes;      // static LDS of the chosen attention kernel

@@ -189,8 +189,12 @@ def test_split_workspace_layout():
 def test_plan_xcd_grouping():
     p = _plan(hq=32, hkv=8, lq=96, lk=32768, dqk=128, dv=128, dtype=_lib.SDPA_F16)
     assert int(p["row_tiles"]) == 3 and int(p["splits"]) > 1 and p["xcd_group"] == "8"
+    # one row tile per KV head, 8 KV heads: each head's splits on one XCD,
+    # the combine's rows of that head on the same XCD
     p = _plan(hq=64, hkv=8, lq=1, lk=32768, dqk=192, dv=128)
-    assert p["xcd_group"] == "0"
+    assert p["xcd_group"] == p["splits"] and int(p["splits"]) > 1 and p["combine_xcd"] == "1"
+    p = _plan(hq=32, hkv=4, lq=1, lk=32768, dqk=128, dv=128)
+    assert int(p["splits"]) > 1 and p["xcd_group"] == "0" and p["combine_xcd"] == "0"
     p = _plan(hq=16, hkv=8, lq=4096, lk=4096, dqk=256, dv=256, mask="window", window_size=1024)
     assert p["splits"] == "1" and p["xcd_group"] == "0"  # two rounds of tiles only
     p = _plan(hq=16, hkv=8, lq=8192, lk=8192, dqk=256, dv=256, mask="window", window_size=1024)
