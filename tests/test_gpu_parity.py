@@ -242,6 +242,20 @@ def test_split_plan_with_several_row_tiles(lq):
     check_full(1, 32, 8, lq, 3000, 128, 128, "f16", "none", 0, seed=61)
 
 
+@pytest.mark.parametrize("b,hkv,lq", [(1, 8, 1), (2, 8, 2), (3, 8, 3)])
+def test_split_heads_grouped_by_xcd(b, hkv, lq):
+    """One row tile per KV head and B Hkv a multiple of 8: each head's splits
+    and its combine rows are dealt to one XCD (8, 16 and 24 head rows, so
+    one to three groups of eight); every row must come out exactly once."""
+    _say("split heads by XCD", b, hkv, lq)
+    d = sdpa.make_desc((b, 4 * hkv, lq, 128), (b, hkv, 2500, 128), (b, hkv, 2500, 128), sdpa.SDPA_BF16,
+                       mask="causal")
+    plan = dict(t.split("=", 1) for t in sdpa.sdpa_describe_plan(d).split())
+    assert plan["row_tiles"] == "1" and int(plan["splits"]) > 1 and plan["combine_xcd"] == "1"
+    assert plan["xcd_group"] == plan["splits"]
+    check_full(b, 4 * hkv, hkv, lq, 2500, 128, 128, "bf16", "causal", 0, seed=67 + b)
+
+
 WIDE = [
     # 128 < packed rows <= 256: the wide family (256-row tiles, eight waves)
     (1, 32, 8, 48, 2000, 128, 128, "f16", "none", 0),
