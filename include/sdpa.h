@@ -167,6 +167,24 @@ int sdpa_forward_varlen(const sdpa_desc_t* desc, const void* q, const void* k, c
                         const void* mask, const int32_t* q_lens, const int32_t* kv_lens, void* o,
                         float* lse, void* workspace, size_t workspace_bytes, sdpa_stream_t stream);
 
+/* Forward pass that allocates nothing, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments and results as
+ * sdpa_forward_varlen without the workspace: a split plan keeps its partial
+ * outputs in a fixed scratch array of 64 MiB that the library holds on each
+ * device it runs on until the process ends.  A plan whose workspace
+ * (sdpa_workspace_bytes) exceeds 64 MiB is rejected with SDPA_E_WORKSPACE
+ * before anything is launched (force fewer splits with desc->num_splits, or
+ * pass a workspace to sdpa_forward_varlen).  No part of the scratch needs to
+ * start at zero: every partial a call's combine reads is written earlier in
+ * the same call.  All calls on one device share its scratch and each leaves
+ * its partials there: calls on one stream are ordered, but calls that
+ * overlap on one device (different streams or threads) race and must not be
+ * issued.  The call makes no hipMalloc or hipFree. */
+int sdpa_forward_noalloc(const sdpa_desc_t* desc, const void* q, const void* k, const void* v,
+                         const void* mask, const int32_t* q_lens, const int32_t* kv_lens, void* o,
+                         float* lse, sdpa_stream_t stream);
+
 /* Backward pass (mlx PR #4185, Background and API: training needs the
  * log-sum-exp; mlx PR #3552, Outstanding: the VJP).  Given the forward's
  * inputs, its output o and log-sum-exp lse (contiguous float32 [B,Hq,Lq], as

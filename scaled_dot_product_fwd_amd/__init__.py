@@ -21,11 +21,11 @@ from ._lib import (SDPA_BF16, SDPA_F16, SDPA_F32, SDPA_MASK_ARRAY_ADD,  # noqa: 
                    SDPA_MASK_WINDOW, SdpaError, SdpaRuntimeError, SdpaValueError, load,
                    sdpa_desc_init, sdpa_desc_t, sdpa_describe_plan, sdpa_forward,
                    sdpa_backward, sdpa_backward_varlen, sdpa_backward_workspace_bytes, sdpa_forward_masked,
-                   sdpa_forward_varlen, sdpa_last_error, sdpa_set_profile_events,
+                   sdpa_forward_noalloc, sdpa_forward_varlen, sdpa_last_error, sdpa_set_profile_events,
                    sdpa_workspace_bytes)
 
 __all__ = ["forward", "backward", "sdpa_backward", "sdpa_backward_varlen", "sdpa_backward_workspace_bytes", "make_desc", "plan_for", "workspace_for", "pad_mask", "sdpa_forward",
-           "sdpa_forward_masked", "sdpa_forward_varlen", "sdpa_workspace_bytes", "sdpa_describe_plan", "sdpa_last_error",
+           "sdpa_forward_masked", "sdpa_forward_varlen", "sdpa_forward_noalloc", "sdpa_workspace_bytes", "sdpa_describe_plan", "sdpa_last_error",
            "sdpa_desc_init", "sdpa_set_profile_events",
            "SdpaError", "SdpaValueError", "SdpaRuntimeError"]
 

@@ -33,7 +33,7 @@ STATUS = {
 STATUS_CODE = {v: k for k, v in STATUS.items()}
 
 EXPORTED = ("sdpa_desc_init", "sdpa_workspace_bytes", "sdpa_forward", "sdpa_forward_masked",
-            "sdpa_forward_varlen", "sdpa_backward_workspace_bytes", "sdpa_backward", "sdpa_backward_varlen",
+            "sdpa_forward_varlen", "sdpa_forward_noalloc", "sdpa_backward_workspace_bytes", "sdpa_backward", "sdpa_backward_varlen",
             "sdpa_describe_plan",
             "sdpa_set_profile_events", "sdpa_last_error")
 
@@ -109,6 +109,8 @@ def load() -> ctypes.CDLL:
     lib.sdpa_forward_varlen.argtypes = [P(sdpa_desc_t)] + [ctypes.c_void_p] * 9 + [ctypes.c_size_t,
                                                                                     ctypes.c_void_p]
     lib.sdpa_forward_varlen.restype = ctypes.c_int
+    lib.sdpa_forward_noalloc.argtypes = [P(sdpa_desc_t)] + [ctypes.c_void_p] * 9
+    lib.sdpa_forward_noalloc.restype = ctypes.c_int
     lib.sdpa_backward_workspace_bytes.argtypes = [P(sdpa_desc_t), P(ctypes.c_size_t)]
     lib.sdpa_backward_workspace_bytes.restype = ctypes.c_int
     lib.sdpa_backward.argtypes = [P(sdpa_desc_t)] + [ctypes.c_void_p] * 10 + [ctypes.c_size_t, ctypes.c_void_p]
@@ -188,6 +190,15 @@ def sdpa_forward_varlen(desc: sdpa_desc_t, q: int, k: int, v: int, mask: int | N
     check(load().sdpa_forward_varlen(ctypes.byref(desc), q, k, v, mask or None, q_lens or None,
                                      kv_lens or None, o, lse or None, workspace or None,
                                      workspace_bytes, stream or None))
+
+
+def sdpa_forward_noalloc(desc: sdpa_desc_t, q: int, k: int, v: int, mask: int | None,
+                         q_lens: int | None, kv_lens: int | None, o: int, lse: int | None,
+                         stream: int | None) -> None:
+    """Raw call of the forward that allocates nothing (split partials in the
+    library's fixed per-device scratch); raises on a non-zero status."""
+    check(load().sdpa_forward_noalloc(ctypes.byref(desc), q, k, v, mask or None, q_lens or None,
+                                      kv_lens or None, o, lse or None, stream or None))
 
 
 def sdpa_backward_workspace_bytes(desc: sdpa_desc_t) -> int:

@@ -113,16 +113,21 @@ int sdpa_describe_plan(const sdpa_desc_t* d, char* buf, size_t len) {
   return ok();
 }
 
-int sdpa_forward_varlen(const sdpa_desc_t* d, const void* q, const void* k, const void* v, const void* mask,
-                        const int32_t* q_lens, const int32_t* kv_lens, void* o, float* lse, void* workspace,
-                        size_t workspace_bytes, sdpa_stream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// The forward call behind sdpa_forward_varlen and sdpa_forward_noalloc, on a
+// plan already made: argument checks, then the attention kernel and, for a
+// split plan, the combine.
+int forward_planned(const sdpa_desc_t* d, const sdpa::Plan& p, const void* q, const void* k, const void* v,
+                    const void* mask, const int32_t* q_lens, const int32_t* kv_lens, void* o, float* lse,
+                    void* workspace, size_t workspace_bytes, sdpa_stream_t stream) {
   hipEvent_t ev_start = g_prof_start, ev_stop = g_prof_stop;  // consumed by this call
   g_prof_start = g_prof_stop = nullptr;
   if (!q || !k || !v || !o) return set_error(SDPA_E_NULL, "q, k, v and o must be non-NULL device pointers");
-  sdpa::Plan p;
   std::string err;
-  int rc = sdpa::make_plan(d, &p, &err);
-  if (rc != SDPA_OK) return set_error(rc, err);
+  int rc = SDPA_OK;
   if ((p.mask_array != sdpa::MA_NONE) != (mask != nullptr))
     return set_error(SDPA_E_NULL, p.mask_array != sdpa::MA_NONE
                                       ? "desc names a mask array but mask is NULL"
@@ -236,6 +241,88 @@ int sdpa_forward_varlen(const sdpa_desc_t* d, const void* q, const void* k, cons
     if (rc != SDPA_OK) return set_error(rc, err);
   }
   return ok();
+}
+
+// Scratch of sdpa_forward_noalloc: the split partials (O, m, l) live here
+// instead of in a caller workspace.  Each device that loads the library holds
+// its own copy until the process ends.  Host code never passes the name
+// `scratch` to a kernel (on the host it is only a stand-in for the symbol):
+// it passes the device address hipGetSymbolAddress returns, taken once per
+// device with that device current.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+int scratch_ptr(void** out, std::string* err) {
+  static std::mutex mu;
+  static void* ptrs[64] = {nullptr};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    *err = "no HIP device is available";
+    return SDPA_E_DEVICE;
+  }
+  if (dev >= 64) {
+    *err = "sdpa_forward_noalloc supports device ordinals below 64";
+    return SDPA_E_DEVICE;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptrs[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      *err = std::string("hipGetSymbolAddress(scratch) failed: ") + hipGetErrorString(e);
+      return SDPA_E_HIP;
+    }
+    ptrs[dev] = ptr;
+  }
+  *out = ptrs[dev];
+  return SDPA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sdpa_forward_varlen(const sdpa_desc_t* d, const void* q, const void* k, const void* v, const void* mask,
+                        const int32_t* q_lens, const int32_t* kv_lens, void* o, float* lse, void* workspace,
+                        size_t workspace_bytes, sdpa_stream_t stream) {
+  sdpa::Plan p;
+  std::string err;
+  const int rc = sdpa::make_plan(d, &p, &err);
+  if (rc != SDPA_OK) {
+    g_prof_start = g_prof_stop = nullptr;
+    return set_error(rc, err);
+  }
+  return forward_planned(d, p, q, k, v, mask, q_lens, kv_lens, o, lse, workspace, workspace_bytes, stream);
+}
+
+int sdpa_forward_noalloc(const sdpa_desc_t* d, const void* q, const void* k, const void* v, const void* mask,
+                         const int32_t* q_lens, const int32_t* kv_lens, void* o, float* lse,
+                         sdpa_stream_t stream) {
+  sdpa::Plan p;
+  std::string err;
+  int rc = sdpa::make_plan(d, &p, &err);
+  if (rc != SDPA_OK) {
+    g_prof_start = g_prof_stop = nullptr;
+    return set_error(rc, err);
+  }
+  if (p.workspace > kScratchBytes) {
+    g_prof_start = g_prof_stop = nullptr;
+    return set_error(SDPA_E_WORKSPACE, "sdpa_forward_noalloc: the plan needs " + std::to_string(p.workspace) +
+                                           " bytes of split scratch, above its fixed " +
+                                           std::to_string(kScratchBytes) +
+                                           " bytes (force fewer splits with num_splits, or pass a workspace "
+                                           "to sdpa_forward_varlen)");
+  }
+  void* ws = nullptr;
+  if (p.workspace > 0) {
+    rc = scratch_ptr(&ws, &err);
+    if (rc != SDPA_OK) {
+      g_prof_start = g_prof_stop = nullptr;
+      return set_error(rc, err);
+    }
+  }
+  return forward_planned(d, p, q, k, v, mask, q_lens, kv_lens, o, lse, ws, p.workspace ? kScratchBytes : 0,
+                         stream);
 }
 
 int sdpa_forward_masked(const sdpa_desc_t* d, const void* q, const void* k, const void* v, const void* mask,

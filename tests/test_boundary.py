@@ -111,6 +111,20 @@ def test_forward_missing_workspace():
     assert msg.startswith("SDPA_E_WORKSPACE")
 
 
+def test_noalloc_rejects_plans_beyond_its_scratch():
+    # 8 KV heads x 64 packed rows x 1024 forced splits x (128 + 2) float32 = 272 MB > 64 MiB:
+    # rejected on the host, before any pointer or device is looked at
+    d = _desc(hq=64, hkv=8, lq=8, lk=65536, dqk=128, dv=128, num_splits=1024)
+    need = sdpa.sdpa_workspace_bytes(d)
+    assert need > 64 << 20
+    msg = _status(sdpa.sdpa_forward_noalloc, d, 16, 16, 16, None, None, None, 16, None, None)
+    assert msg.startswith("SDPA_E_WORKSPACE") and str(need) in msg and str(64 << 20) in msg
+    # invalid descriptors fail validation first, as in every other entry point
+    msg = _status(sdpa.sdpa_forward_noalloc, _desc(dqk=1024, dv=1024), 16, 16, 16, None, None, None, 16, None,
+                  None)
+    assert msg.startswith("SDPA_E_HEAD_DIM")
+
+
 def test_last_error_is_cleared_by_success():
     _status(sdpa.sdpa_workspace_bytes, _desc(dqk=1024, dv=1024))
     assert sdpa.sdpa_last_error() != ""
