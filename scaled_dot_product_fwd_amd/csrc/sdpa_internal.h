@@ -128,11 +128,16 @@ constexpr Family family_for(int kind, int elem_bytes, int dqk_pad, int dv_pad, i
   // rows read K/V once (head dims up to 128, two waves per SIMD).
   if (kind == KIND_WIDE)
     return (key_bytes + 256 * mes) * 64 * 2 <= 160 * 1024 ? Family{8, 1, 64} : Family{8, 1, 32};
-  // Prefill: 64-key blocks when two workgroups still fit per CU, or when the
-  // head dims are so large that one workgroup per CU is all the registers
-  // allow anyway (then the longer block halves the per-block overheads).
+  // Prefill: 64-key blocks when two workgroups still fit per CU.  Both head
+  // dims 192 or more and no mask array: 32-key blocks, which leave room for
+  // the software-pipelined loop (two blocks of scores beside Q and O); with
+  // an array the plain loop measures faster (it skips removed blocks whole).
+  // Otherwise 64-key blocks when the head dims are so large that one
+  // workgroup per CU is all the registers allow anyway (then the longer block
+  // halves the per-block overheads).
   const int per_key = key_bytes + 128 * mes;  // K, V and a 128-row mask column
   if (per_key * 64 * 2 <= 80 * 1024) return Family{4, 1, 64};
+  if (dqk_pad >= 192 && dv_pad >= 192 && mes == 0) return Family{4, 1, 32};
   const int dmax = dqk_pad > dv_pad ? dqk_pad : dv_pad;
   return dmax >= 192 && per_key * 64 * 2 <= 160 * 1024 ? Family{4, 1, 64} : Family{4, 1, 32};
 }

@@ -276,11 +276,14 @@ def test_mask_array_pointer_must_match_the_desc():
 
 @pytest.mark.parametrize("dtype,d,kind,family,bk", [
     # prefill: the mask tile joins K and V in LDS; 64-key blocks while two
-    # workgroups still fit a CU, else 32-key blocks (large dims keep 64)
+    # workgroups still fit a CU, else 32-key blocks (large dims keep 64 with
+    # an array; without one, both head dims from 192 take 32-key blocks for
+    # the pipelined loop)
     (_lib.SDPA_BF16, 128, _lib.SDPA_MASK_ARRAY_NONE, "prefill", "64"),
     (_lib.SDPA_BF16, 128, _lib.SDPA_MASK_ARRAY_BOOL, "prefill", "64"),
     (_lib.SDPA_BF16, 128, _lib.SDPA_MASK_ARRAY_ADD, "prefill", "32"),
     (_lib.SDPA_BF16, 256, _lib.SDPA_MASK_ARRAY_ADD, "prefill", "64"),
+    (_lib.SDPA_BF16, 256, _lib.SDPA_MASK_ARRAY_NONE, "prefill", "32"),
     (_lib.SDPA_F32, 128, _lib.SDPA_MASK_ARRAY_ADD, "prefill", "32"),
 ])
 def test_plan_masked_prefill_family(dtype, d, kind, family, bk):
