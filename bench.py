@@ -15,10 +15,16 @@ The KV set (168 MB) fits in the 256 MB Infinity Cache, so consecutive steps
 rotate over enough identical copies of K/V (> 2 x 256 MB in total) that every
 step streams its K/V from HBM, not from the cache.
 
-Printed: ONE JSON line with the metric, plus ``roofline`` (the attention
-kernel's algorithmic bytes per launch over its average duration, measured with
-HIP events recorded on the launch stream by the library's profiling hook) and
-``cpu_baseline`` (the float64 oracle timed on the host cores).
+Printed: ONE JSON line with the metric, plus ``roofline`` (the algorithmic
+bytes per call over the call's device time, attention kernel plus the split
+combine, measured with HIP events recorded on the launch stream by the
+library's profiling hook; mean, median, p10 and p90 over at least 40 calls)
+and ``cpu_baseline`` (the float64 oracle timed on the host cores).  The
+default line also carries ``prefill``, the other half of the metric: the
+causal D=256 layer at L=32768 (Hq=16, Hkv=2) timed the same way with its own
+roofline (algorithmic flops over MFMA peak) and oracle baseline, and under
+``configs`` the encoder, vision and windowed D=256 prefill workloads (10
+warm-up and 40 timed calls each, median with p10 and p90).
 
 ``--sweep`` additionally times every shape of the table below (the five
 workloads, then explicit mask arrays beside the same shapes without one) and
@@ -375,24 +381,32 @@ class Runner:
         return self.o, self.lse
 
 
-# Every EVENT_EVERY-th timed step records the kernel's HIP events: two
-# event packets around a launch cost ~3 us of queue time per step (measured:
-# decode step 37.2 us with events on every step, 33.8 us without), so
-# sampling keeps the measurement from inflating the step time it sits in.
+# Every EVENT_EVERY-th timed step records the call's HIP events: two event
+# packets around a call cost ~2 us of queue time per step (measured: decode
+# step 36.3 us with events on every step, 34.3 us without, 34.6 us with every
+# 4th), so sampling keeps the measurement from inflating the step time it
+# sits in.
 EVENT_EVERY = 4
+# Kernel-time samples per workload, as in mlx issue #3826 (report: 10 warm-up
+# calls, then 40 timed ones).
+MIN_SAMPLES = 40
 
 
-def time_steps(r, steps, warmup, event_every=EVENT_EVERY):
+def time_steps(r, steps, warmup, event_every=EVENT_EVERY, min_samples=MIN_SAMPLES):
     """Warm up, then time exactly `steps` steps; returns (ms_per_step, kernel_ms list).
 
-    The attention kernel's duration is taken with HIP events recorded on its
-    stream around the launch in steps 0, event_every, 2 event_every, ... of
-    the timed region.
+    The device time of a call (attention kernel plus the split combine, when
+    the plan splits) is taken with HIP events recorded on its stream around
+    the call in steps 0, event_every, 2 event_every, ... of the timed region.
+    When those are fewer than ``min_samples``, the calls right after the
+    timed region (same inputs, same rotation, every call sampled) add the
+    rest, outside the clock of ``ms_per_step``.
     """
     import torch
 
     sampled = list(range(0, steps, event_every))
-    ev = HipEvents(len(sampled))
+    extra = max(0, min_samples - len(sampled))
+    ev = HipEvents(len(sampled) + extra)
     for i in range(warmup):
         r.step(i)
     torch.cuda.synchronize()
@@ -404,7 +418,10 @@ def time_steps(r, steps, warmup, event_every=EVENT_EVERY):
             r.step(i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    kms = [ev.elapsed_ms(n) for n in range(len(sampled))]
+    for n in range(extra):
+        r.step(steps + n, ev, len(sampled) + n)
+    torch.cuda.synchronize()
+    kms = [ev.elapsed_ms(n) for n in range(len(sampled) + extra)]
     ev.close()
     return (t1 - t0) * 1e3 / steps, kms
 
@@ -487,7 +504,20 @@ def cpu_baseline(s, runner, budget_s=12.0):
     else:
         value, unit = flops / sec_per_step / 1e12, "TFLOP/s"
     return {"value": round(value, 6), "unit": unit, "cores": int(cores), "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"{sample} of the same workload, float64 numpy, {t_total:.1f} s"}
+
+
+def cpu_model():
+    """The host CPU's model name (as lscpu prints it), from /proc/cpuinfo."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return "unknown"
 
 
 def kernel_source_hash(name):
@@ -567,13 +597,14 @@ def summarize_pmc(fetch_dir, write_dir, name, copy_mib, commands):
         return k, v
 
     copy_bytes = 2 * copy_mib * (1 << 20)  # read once, written once
+    _, inst = instance_of(SHAPES[name])
     out = {"workload": name, "kernel_source_hash": kernel_source_hash(name), "commands": commands,
            "copy": {"kernel": "float32 dst = src * 1", "bytes_read": copy_bytes // 2,
                     "bytes_written": copy_bytes // 2}}
     total = 0.0
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         vals = per_kernel(d, counter)
-        kname, kv = pick(vals, lambda k: "attn_fwd_kernel" in k)
+        kname, kv = pick(vals, lambda k: "attn_fwd_kernel" in k and inst in k)
         cname, cv = pick(vals, lambda k: "elementwise" in k and "Mul" in k)
         cv = [x for x in cv if x > 0.25 * copy_bytes / 2 / 1024] or cv
         k_kib = sum(kv) / len(kv)
@@ -593,7 +624,142 @@ def summarize_pmc(fetch_dir, write_dir, name, copy_mib, commands):
     print(json.dumps(out, indent=1))
 
 
-def measure(s, steps, warmup, warm=False):
+def instance_of(s):
+    """(plan string, template-argument prefix of the attention kernel instance
+    the plan launches), e.g. "BF16, 192, 128, 1, 4, 32", to pick the
+    workload's own dispatches out of a trace."""
+    import scaled_dot_product_fwd_amd as sdpa
+    from scaled_dot_product_fwd_amd.synth import DTYPES
+
+    desc = sdpa.make_desc((s["b"], s["hq"], s["lq"], s["dqk"]), (s["b"], s["hkv"], s["lk"], s["dqk"]),
+                          (s["b"], s["hkv"], s["lk"], s["dv"]), sdpa._dtype_code(DTYPES[s["dtype"]]),
+                          mask=s["mask"], window_size=s["window"])
+    plan = sdpa.sdpa_describe_plan(desc)
+    pl = dict(tok.split("=", 1) for tok in plan.split())
+    nwq, nwk = (int(x) for x in pl["waves"].split("x")[:2])
+    inst = "{}, {}, {}, {}, {}, {}".format({"bf16": "BF16", "f16": "F16", "f32": "F32"}[s["dtype"]],
+                                           pl["dqk"].split("->")[1], pl["dv"].split("->")[1], nwq, nwk,
+                                           int(pl["block_keys"]) // nwk)
+    return plan, inst
+
+
+def summarize_trace(trace_dir, name, command):
+    """Reduce a ``rocprofv3 --kernel-trace --stats --output-format csv`` run of
+    ``bench.py --workload NAME`` to profiles/NAME_kernel_stats.md: calls and
+    average / min / max duration per kernel, the call's device time (the
+    attention kernel plus the combine, when the plan splits) and the roofline
+    fraction it gives."""
+    import csv
+    import glob
+
+    s = SHAPES[name]
+    files = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_stats.csv under {trace_dir}")
+    rows = []
+    with open(files[0]) as fh:
+        for r in csv.DictReader(fh):
+            rows.append((r["Name"], int(r["Calls"]), float(r["AverageNs"]), float(r["MinNs"]), float(r["MaxNs"])))
+    flops, nbytes = work(s)
+    plan, inst = instance_of(s)
+    # the workload's own instance (a default run also times the prefill workloads)
+    attn = [r for r in rows if "attn_fwd_kernel" in r[0] and inst in r[0]]
+    comb = [r for r in rows if "combine_kernel" in r[0]] if " splits=1 " not in plan else []
+    call_ns = (attn[0][2] if attn else 0.0) + (comb[0][2] if comb else 0.0)
+    if bound(s) == "hbm":
+        rate = nbytes / (call_ns * 1e-9) / 1e9
+        frac = rate / HBM_PEAK_GBS
+        work_line = f"Algorithmic bytes per call: {nbytes:,} B; by rocprof's averages {rate:.0f} GB/s = {100 * frac:.1f}% of 8 TB/s."
+    else:
+        peak = FP32_PEAK_TFLOPS if s["dtype"] == "f32" else MFMA16_PEAK_TFLOPS
+        rate = flops / (call_ns * 1e-9) / 1e12
+        frac = rate / peak
+        work_line = (f"Algorithmic flops per call: {flops:,}; by rocprof's averages {rate:.1f} TFLOP/s = "
+                     f"{100 * frac:.1f}% of {peak:.0f} TFLOP/s.")
+    out = [f"# Kernel trace: {name}", "",
+           f"B={s['b']} Hq={s['hq']} Hkv={s['hkv']} Lq={s['lq']} Lk={s['lk']} Dqk={s['dqk']} Dv={s['dv']} "
+           f"{s['dtype']} mask={s['mask']}" + (f"({s['window']})" if s["window"] else ""), "",
+           "Command (from /tmp with TMPDIR=/tmp; `$R` is the repository root):", "", "    " + command, "",
+           f"Plan: {plan}", "",
+           "| kernel | calls | avg ns | min ns | max ns |", "|---|---|---|---|---|"]
+    for n, c, a, mn, mx in sorted(rows, key=lambda r: -r[1] * r[2]):
+        out.append(f"| `{n}` | {c} | {a:.0f} | {mn:.0f} | {mx:.0f} |")
+    out += ["", f"One call = `{attn[0][0] if attn else '?'}`" + (" + combine kernel" if comb else "") +
+            f": {call_ns:.0f} ns by the averages above.", work_line, ""]
+    path = os.path.join(ROOT, "profiles", f"{name}_kernel_stats.md")
+    with open(path, "w") as f:
+        f.write("\n".join(out))
+    print("\n".join(out))
+
+
+# SQ counters of the counter summaries, and what they show.
+COUNTER_NOTES = {
+    "SQ_WAVES": "waves launched",
+    "SQ_INSTS_VALU": "vector ALU instructions (MFMA included)",
+    "SQ_INSTS_MFMA": "MFMA instructions",
+    "SQ_INSTS_LDS": "LDS instructions",
+    "SQ_INSTS_SALU": "scalar ALU instructions",
+    "SQ_INSTS_VALU_TRANS_F32": "transcendental float32 instructions (v_exp_f32 ...)",
+    "SQ_VALU_MFMA_BUSY_CYCLES": "cycles the matrix cores are busy, summed over SIMDs",
+    "SQ_BUSY_CYCLES": "cycles the SQs are busy",
+    "SQ_WAVE_CYCLES": "wave-resident cycles (quad-cycle units)",
+    "SQ_WAIT_INST_ANY": "wave cycles waiting for any instruction's dependencies (quad-cycles)",
+    "SQ_ACTIVE_INST_VALU": "wave cycles issuing VALU (quad-cycles)",
+    "SQ_ACTIVE_INST_LDS": "wave cycles issuing LDS (quad-cycles)",
+    "SQ_WAIT_INST_LDS": "wave cycles waiting on LDS (quad-cycles)",
+    "SQ_LDS_BANK_CONFLICT": "LDS bank-conflict cycles",
+    "SQ_INSTS_LDS_LOAD_BANDWIDTH": "LDS read bandwidth (64-byte units)",
+    "GRBM_GUI_ACTIVE": "GPU busy cycles (summed over the 8 XCDs)",
+}
+
+
+def summarize_counters(dirs, name, commands, kernel_us):
+    """Reduce ``rocprofv3 --pmc ... --output-format csv`` runs of ``bench.py
+    --workload NAME`` to profiles/NAME_counters.md: each counter averaged over
+    the attention dispatches, per-wave instruction counts, and the matrix
+    cores' busy fraction of the elapsed cycles."""
+    import csv
+    import glob
+
+    vals = {}
+    for d in dirs:
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(f) as fh:
+                for r in csv.DictReader(fh):
+                    if "attn_fwd_kernel" not in r["Kernel_Name"]:
+                        continue
+                    vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    avg = {k: sum(v) / len(v) for k, v in vals.items()}
+    waves = avg.get("SQ_WAVES", 1.0)
+    out = [f"# SQ counters: {name} (attention kernel)", "", "Commands (from /tmp with TMPDIR=/tmp; `$R` is the repository root):", ""]
+    out += ["    " + c for c in commands]
+    out += ["", "| counter | per dispatch | per wave | meaning |", "|---|---|---|---|"]
+    for k in sorted(avg):
+        out.append(f"| {k} | {avg[k]:,.0f} | {avg[k] / waves:,.1f} | {COUNTER_NOTES.get(k, '')} |")
+    out.append("")
+    if "SQ_INSTS_MFMA" in avg and "SQ_INSTS_VALU" in avg:
+        out.append(f"VALU instructions per MFMA: {(avg['SQ_INSTS_VALU'] - avg['SQ_INSTS_MFMA']) / avg['SQ_INSTS_MFMA']:.2f}"
+                   " (MFMA itself counts as VALU, so it is taken out).")
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in avg and "GRBM_GUI_ACTIVE" in avg:
+        clk = avg["GRBM_GUI_ACTIVE"] / 8  # per XCD
+        simd = 256 * 4
+        busy = avg["SQ_VALU_MFMA_BUSY_CYCLES"] / simd / clk
+        out.append(f"Matrix cores busy: {100 * busy:.1f}% of the elapsed cycles per SIMD "
+                   f"({clk:,.0f} busy cycles per XCD per dispatch under the counters; the bench times "
+                   f"{kernel_us:.1f} us per call without them).")
+    for a, b, what in (("SQ_ACTIVE_INST_VALU", "SQ_WAVE_CYCLES", "issuing VALU"),
+                       ("SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES", "waiting on dependencies"),
+                       ("SQ_WAIT_INST_LDS", "SQ_WAVE_CYCLES", "waiting on LDS")):
+        if a in avg and b in avg and avg[b]:
+            out.append(f"Share of wave cycles {what}: {100 * avg[a] / avg[b]:.1f}%.")
+    out.append("")
+    path = os.path.join(ROOT, "profiles", f"{name}_counters.md")
+    with open(path, "w") as f:
+        f.write("\n".join(out))
+    print("\n".join(out))
+
+
+def measure(s, steps, warmup, warm=False, event_every=EVENT_EVERY):
     """Time one workload.  HBM-bound workloads rotate over K/V copies that
     together exceed three times the Infinity Cache, so every step streams from
     HBM (cold, the graded number); ``warm`` keeps one copy, which the caches
@@ -602,7 +768,7 @@ def measure(s, steps, warmup, warm=False):
 
     floor = 3 * INFINITY_CACHE if bound(s) == "hbm" and not warm else 0
     r = BwdRunner(s) if s.get("bwd") else Runner(s, floor)
-    ms, kms = time_steps(r, steps, warmup)
+    ms, kms = time_steps(r, steps, warmup, event_every=event_every)
     flops, nbytes = work(s)
     kmean = sum(kms) / len(kms)
     kms_sorted = sorted(kms)
@@ -625,11 +791,75 @@ def measure(s, steps, warmup, warm=False):
     return res, r
 
 
+# The prefill half of the metric: the long causal D=256 layer (L = 32768,
+# 16 query / 2 KV heads), then the other prefill workloads in brief (the
+# encoder and vision layers, the windowed D=256 layers).
+PREFILL = "causal_l32768_d256"
+PREFILL_CONFIGS = ("encoder_h20_l1500_d64", "vision_h16_l1024_d72", "vision_h16_l4096_d72",
+                   "window_l2048_d256", "window_l4096_d256", "window_l8192_d256")
+
+
+def roofline_of(res, name):
+    """The roofline object of a measured workload: algorithmic work per call
+    over the call's device time (attention kernel plus the split combine)."""
+    return {"bound": res["bound"], "achieved": round(res["achieved"], 3), "peak": res["peak"],
+            "unit": res["unit"], "frac": round(res["frac"], 4), "traffic": traffic_from_profiles(name),
+            "kernels": "attention + combine" if "splits=1 " not in res["plan"] else "attention",
+            "kernel_us_mean": round(res["kernel_ms_mean"] * 1e3, 3),
+            "kernel_us_median": round(res["kernel_ms_p50"] * 1e3, 3),
+            "kernel_us_p10": round(res["kernel_ms_p10"] * 1e3, 3),
+            "kernel_us_p90": round(res["kernel_ms_p90"] * 1e3, 3),
+            "kernel_samples": res["kernel_samples"]}
+
+
+def shape_config(s, res):
+    return {"workload": s["name"], "B": s["b"], "Hq": s["hq"], "Hkv": s["hkv"], "Lq": s["lq"], "Lk": s["lk"],
+            "Dqk": s["dqk"], "Dv": s["dv"], "mask": s["mask"], "window": s["window"],
+            "mask_array": s["arr"], "kv_lens": kv_lengths(s) if s.get("varlen") else None,
+            "pass": "backward" if s.get("bwd") else "forward", "kv_sets": res["kv_sets"], "plan": res["plan"]}
+
+
+def prefill_report(steps, warmup, cpu):
+    """The prefill half of the line: the long causal layer timed like the
+    headline workload, then each other prefill workload with 10 warm-up and 40
+    timed calls, every call sampled."""
+    import torch
+
+    s = SHAPES[PREFILL]
+    print(f"prefill {PREFILL}", file=sys.stderr, flush=True)
+    res, run = measure(s, steps, warmup)
+    out = {"workload": PREFILL, "metric": "prefill TFLOP/s", "value": round(res["step_value"], 3),
+           "unit": res["unit"], "ms_per_step": round(res["ms_per_step"], 5), "dtype": s["dtype"],
+           "config": shape_config(s, res), "roofline": roofline_of(res, PREFILL),
+           "cpu_baseline": cpu_baseline(s, run) if cpu else None}
+    del run
+    torch.cuda.empty_cache()
+    rows = []
+    for name in PREFILL_CONFIGS:
+        sh = SHAPES[name]
+        print(f"prefill {name}", file=sys.stderr, flush=True)
+        r, run = measure(sh, MIN_SAMPLES, 10, event_every=1)
+        rows.append({"workload": name, "plan": r["plan"],
+                     "kernel_us_median": round(r["kernel_ms_p50"] * 1e3, 3),
+                     "kernel_us_p10": round(r["kernel_ms_p10"] * 1e3, 3),
+                     "kernel_us_p90": round(r["kernel_ms_p90"] * 1e3, 3),
+                     "kernel_samples": r["kernel_samples"],
+                     "tflops": round(r["flops"] / (r["kernel_ms_p50"] * 1e-3) / 1e12, 3),
+                     "frac": round(r["flops"] / (r["kernel_ms_p50"] * 1e-3) / 1e12 / r["peak"], 4),
+                     "cpu_baseline": cpu_baseline(sh, run, budget_s=4.0) if cpu else None})
+        del run
+        torch.cuda.empty_cache()
+    out["configs"] = rows
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=160)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="with the default workload: leave out the prefill half of the line")
     ap.add_argument("--workload", default=DEFAULT, choices=sorted(SHAPES))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true", help="also time every shape of the table")
@@ -643,8 +873,21 @@ def main():
                     help="host only: reduce FETCH_SIZE / WRITE_SIZE counter runs of --workload "
                          "into profiles/traffic_<workload>.json")
     ap.add_argument("--pmc-command", action="append", default=[],
-                    help="with --summarize-pmc: the profiling commands, recorded in the summary")
+                    help="with --summarize-pmc / --summarize-counters: the profiling commands, recorded in the summary")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="host only: reduce a rocprofv3 kernel-trace stats run of --workload into "
+                         "profiles/<workload>_kernel_stats.md (--pmc-command gives the command)")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="DIR",
+                    help="host only: reduce rocprofv3 SQ counter runs of --workload into profiles/<workload>_counters.md")
+    ap.add_argument("--kernel-us", type=float, default=0.0,
+                    help="with --summarize-counters: the bench's device time per call, for the clock estimate")
     args = ap.parse_args()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.workload, " ".join(args.pmc_command))
+        return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters, args.workload, args.pmc_command, args.kernel_us)
+        return
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload,
                       args.calibrate_copy_mib, args.pmc_command)
@@ -683,18 +926,12 @@ def main():
         "vs_baseline": None if vs is None else round(vs, 3),
         "dtype": s["dtype"],
         "data": "synthetic",
-        "config": {"workload": s["name"], "B": s["b"], "Hq": s["hq"], "Hkv": s["hkv"], "Lq": s["lq"],
-                   "Lk": s["lk"], "Dqk": s["dqk"], "Dv": s["dv"], "mask": s["mask"], "window": s["window"],
-                   "mask_array": s["arr"], "kv_lens": kv_lengths(s) if s.get("varlen") else None,
-                   "pass": "backward" if s.get("bwd") else "forward",
-                   "kv_sets": res["kv_sets"], "plan": res["plan"]},
-        "roofline": {"bound": res["bound"], "achieved": round(res["achieved"], 3), "peak": res["peak"],
-                     "unit": res["unit"], "frac": round(res["frac"], 4),
-                     "traffic": traffic_from_profiles(s["name"]),
-                     "kernel_us_mean": round(res["kernel_ms_mean"] * 1e3, 3),
-                     "kernel_samples": res["kernel_samples"]},
+        "config": shape_config(s, res),
+        "roofline": roofline_of(res, s["name"]),
         "cpu_baseline": cpu,
     }
+    if args.workload == DEFAULT and not args.no_prefill:
+        line["prefill"] = prefill_report(args.steps, args.warmup, not args.no_cpu_baseline)
     if args.sweep:
         rows = []
         prefixes = [p for p in args.sweep_only.split(",") if p]
@@ -702,7 +939,7 @@ def main():
             if prefixes and not any(sh["name"].startswith(p) for p in prefixes):
                 continue
             print(f"sweep {sh['name']}", file=sys.stderr, flush=True)
-            r, rr = measure(sh, 20, 5, warm=args.warm)
+            r, rr = measure(sh, MIN_SAMPLES, 10, warm=args.warm, event_every=1)
             del rr
             torch.cuda.empty_cache()
             rows.append({k: r[k] for k in ("name", "plan", "kv_sets", "ms_per_step", "kernel_ms_mean",

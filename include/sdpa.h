@@ -121,17 +121,28 @@ typedef struct {
 } sdpa_desc_t;
 
 /* Fills *desc with contiguous [B,H,L,D] strides for the given sizes, no mask,
- * scale = 1/sqrt(dim_qk), no overrides.  Returns SDPA_OK or SDPA_E_NULL. */
+ * scale = 1/sqrt(dim_qk), no overrides.  Returns SDPA_OK or SDPA_E_NULL.
+ * The descriptor carries the operation's arguments (mlx PR #4185, API: q, k,
+ * v, scale and the mask; mlx PR #3552, Public API: the mask mode and
+ * window_size); 1/sqrt(D) is the scale the workloads on the pages use. */
 int sdpa_desc_init(sdpa_desc_t* desc, int64_t batch, int64_t heads_q, int64_t heads_kv,
                    int64_t len_q, int64_t len_k, int64_t dim_qk, int64_t dim_v,
                    int32_t dtype);
 
 /* Workspace bytes the plan for *desc needs (0 when the plan does not split
- * the key range).  Validates *desc; host only, launches nothing. */
+ * the key range).  Validates *desc; host only, launches nothing.  A split
+ * plan keeps one partial output with its running max and sum per key split
+ * until the log-sum-exp merge combines them (mlx issue #3826, second and
+ * third comments: the key range is split and the splits are merged by
+ * log-sum-exp); this is their size: [B*Hkv][G*Lq][splits] x (Dv + 2) float32,
+ * 256-byte aligned. */
 int sdpa_workspace_bytes(const sdpa_desc_t* desc, size_t* bytes);
 
-/* Forward pass.  q, k, v, o: device pointers, 16-byte aligned, laid out as
- * described above.  lse: NULL or a contiguous [B,Hq,Lq] float32 buffer.
+/* Forward pass (mlx PR #4185, API: the fused forward, which always runs a
+ * fused kernel and raises with the violated constraint when none covers the
+ * shape; mlx PR #3552, Public API and Implementation: the mask mode, the
+ * window and the bottom-right query alignment).  q, k, v, o: device
+ * pointers, 16-byte aligned, laid out as described above.  lse: NULL or a contiguous [B,Hq,Lq] float32 buffer.
  * workspace: at least sdpa_workspace_bytes() bytes (may be NULL when that is
  * 0).  Enqueues one kernel (unsplit) or a split kernel plus a combine kernel
  * on `stream` and returns without synchronising. */
@@ -220,17 +231,28 @@ int sdpa_backward_varlen(const sdpa_desc_t* desc, const void* q, const void* k, 
                          sdpa_stream_t stream);
 
 /* Writes a one-line, NUL-terminated description of the plan (kernel family,
- * tile, splits, grid, workspace) into buf.  Host only. */
+ * tile, splits, grid, workspace) into buf.  Host only.  The kernel choice is
+ * shown to the caller rather than hidden behind a heuristic (mlx PR #4185,
+ * Proposed changes and Background: the caller, not a fixed dispatch
+ * threshold, decides, and the follow-up hardening adds capability
+ * diagnostics).  Validates as sdpa_forward does;
+ * on error buf is left untouched. */
 int sdpa_describe_plan(const sdpa_desc_t* desc, char* buf, size_t len);
 
-/* Measurement hook: the next sdpa_forward call on this thread records the
- * two hipEvent_t `start` and `stop` on its stream immediately before and
- * after the launch of its attention kernel (the split combine, when present,
- * comes after `stop`), then forgets them.  Passing NULL for both cancels a
- * pending pair.  The events stay owned by the caller. */
+/* Measurement hook (per-call timing as in mlx issue #3826, report: ten
+ * warm-up calls, then forty timed ones): the next
+ * forward call on this thread records the two
+ * hipEvent_t `start` and `stop` on its stream immediately before the launch
+ * of its attention kernel and after its last kernel (the split combine, when
+ * the plan splits), then forgets them, so the pair brackets the device time
+ * of the whole call.  Passing NULL for both cancels a pending pair.  The
+ * events stay owned by the caller. */
 int sdpa_set_profile_events(void* start, void* stop);
 
-/* Message of the last failed call on this thread ("" if none). */
+/* Message of the last failed call on this thread ("" if none): it names the
+ * violated constraint, e.g. the unsupported head dim or causal with Lq > Lk
+ * (mlx PR #4185, API and Validation: an unsupported shape raises with the
+ * specific constraint named).  A successful call clears it. */
 const char* sdpa_last_error(void);
 
 #ifdef __cplusplus

@@ -215,8 +215,6 @@ int forward_planned(const sdpa_desc_t* d, const sdpa::Plan& p, const void* q, co
     return set_error(SDPA_E_HIP, "hipEventRecord(start) failed");
   rc = launch(p, a, stream, &err);
   if (rc != SDPA_OK) return set_error(rc, err);
-  if (ev_stop && hipEventRecord(ev_stop, (hipStream_t)stream) != hipSuccess)
-    return set_error(SDPA_E_HIP, "hipEventRecord(stop) failed");
   if (p.splits > 1) {
     sdpa::CombineArgs c;
     c.ws_o = a.ws_o;
@@ -240,6 +238,8 @@ int forward_planned(const sdpa_desc_t* d, const sdpa::Plan& p, const void* q, co
     rc = sdpa::launch_combine(p, c, stream, &err);
     if (rc != SDPA_OK) return set_error(rc, err);
   }
+  if (ev_stop && hipEventRecord(ev_stop, (hipStream_t)stream) != hipSuccess)
+    return set_error(SDPA_E_HIP, "hipEventRecord(stop) failed");
   return ok();
 }
 
