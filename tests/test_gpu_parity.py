@@ -263,6 +263,14 @@ WIDE = [
     (2, 2, 1, 200, 333, 64, 64, "bf16", "causal", 0),
     (1, 4, 2, 90, 300, 96, 96, "f32", "window", 40),
     (1, 2, 2, 129, 129, 72, 72, "bf16", "none", 0),
+    # tiles of five or six 32-row groups (one key block, two, ragged groups,
+    # causal, window)
+    (1, 32, 8, 48, 20, 128, 128, "bf16", "none", 0),
+    (1, 32, 8, 48, 70, 128, 128, "f16", "causal", 0),
+    (1, 4, 1, 40, 300, 128, 128, "bf16", "none", 0),
+    (1, 4, 1, 37, 333, 128, 128, "f16", "causal", 0),
+    (1, 8, 2, 45, 500, 128, 128, "bf16", "window", 100),
+    (1, 8, 2, 50, 333, 64, 64, "bf16", "window", 37),
 ]
 
 
@@ -271,6 +279,15 @@ def test_wide_family(case):
     b, hq, hkv, lq, lk, dqk, dv, dt, mask, w = case
     _say("wide", case)
     check_full(b, hq, hkv, lq, lk, dqk, dv, dt, mask, w, seed=zlib.crc32(repr(case).encode()) % 10000)
+
+
+def test_wide_family_more_splits_than_blocks():
+    # 200 keys in 64-key blocks, 16 splits: some workgroups get one block, some none
+    _say("wide, 16 splits over 4 blocks")
+    check_full(1, 32, 8, 48, 200, 128, 128, "f16", "none", 0, seed=91, num_splits=16)
+    # five row groups with a split key range
+    _say("wide, five row groups, 5 splits")
+    check_full(1, 4, 1, 40, 900, 128, 128, "bf16", "none", 0, seed=92, num_splits=5)
 
 
 def test_forced_256_row_tiles_on_a_long_prefill():
