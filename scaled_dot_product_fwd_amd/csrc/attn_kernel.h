@@ -896,8 +896,9 @@ void attn_fwd_kernel(AttnArgs a) {
   } else {
     // Software-pipelined loop: the QK products of block j + 1 are issued
     // between the exponentials of block j and its PV products, so the
-    // matrix cores work while the vector unit computes probabilities (one
-    // wave per SIMD cannot overlap them otherwise).  K runs two blocks
+    // matrix cores work while the vector unit computes probabilities (inside
+    // one block the products wait for the probabilities, so only a
+    // neighbouring block's products can run beside them).  K runs two blocks
     // ahead of V: K(j + 1) and V(j) are consumed in step j, after which
     // their buffers take K(j + 3) and V(j + 2).  Step j waits for K(j + 1)
     // and V(j); what may still be in flight is K(j + 2) and V(j + 1).

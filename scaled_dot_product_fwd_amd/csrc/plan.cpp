@@ -217,8 +217,9 @@ int make_plan(const sdpa_desc_t* d, Plan* p, std::string* err) {
   } else {
     // Split the key range when the row tiles alone leave the chip idle: aim
     // for one workgroup per CU.  A second resident workgroup does not raise a
-    // CU's throughput for these kernels (MFMA and the softmax's VALU work
-    // share each SIMD's issue), while every extra split adds partial-result
+    // CU's throughput for these kernels (measured: their waves stall on
+    // their own dependency chains, and two workgroups' waves compete for the
+    // same matrix cores and vector units), while every extra split adds partial-result
     // traffic and combine work: speculative verify at Lk = 16384, Lq = 32 runs
     // 39.2 us with 64 splits and 29.3 us with 32.  A full-size prefill tile
     // (128 rows) is only split when very few tiles exist: its partial outputs

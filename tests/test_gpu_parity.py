@@ -290,6 +290,17 @@ def test_wide_family_more_splits_than_blocks():
     check_full(1, 4, 1, 40, 900, 128, 128, "bf16", "none", 0, seed=92, num_splits=5)
 
 
+def test_window_tiles_grouped_by_xcd_full_parity():
+    # 2 x 32 KV heads x 16 row tiles = 1024 window workgroups: the plan groups
+    # neighbouring tiles on one XCD (xcd_group = 8); every element is checked
+    desc = sdpa.make_desc((2, 32, 2048, 32), (2, 32, 2048, 32), (2, 32, 2048, 32), sdpa.SDPA_BF16,
+                          mask="window", window_size=300)
+    plan = dict(tok.split("=", 1) for tok in sdpa.sdpa_describe_plan(desc).split())
+    assert plan["xcd_group"] == "8" and plan["grid"] == "1024", plan
+    _say("window tiles grouped by XCD, full parity")
+    check_full(2, 32, 32, 2048, 2048, 32, 32, "bf16", "window", 300, seed=93)
+
+
 def test_forced_256_row_tiles_on_a_long_prefill():
     _say("row_tile 256 prefill")
     check_full(1, 4, 2, 300, 300, 128, 128, "bf16", "causal", 0, seed=3, row_tile=256)
