@@ -351,7 +351,8 @@ class Runner:
             self.mask = sdpa.pad_mask(self.mask_cpu.to(dev))
             kind, mstr = sdpa._mask_layout(self.mask, self.q, s["b"], s["hq"], s["lq"], s["lk"])
         self.desc = sdpa.make_desc(self.q.shape, kd.shape, vd.shape, sdpa._dtype_code(dt), scale=self.scale,
-                                   mask=s["mask"], window_size=s["window"], mask_array=kind, mask_stride=mstr)
+                                   mask=s["mask"], window_size=s["window"], mask_array=kind, mask_stride=mstr,
+                                   num_splits=s.get("num_splits", 0), row_tile=s.get("row_tile", 0))
         self.plan = sdpa.sdpa_describe_plan(self.desc)
         self.ws_bytes = sdpa.sdpa_workspace_bytes(self.desc)
         self.ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=dev)

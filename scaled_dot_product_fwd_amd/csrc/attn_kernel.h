@@ -62,6 +62,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "sdpa_internal.h"
 
 namespace sdpa {
@@ -709,9 +711,57 @@ void attn_fwd_kernel(AttnArgs a) {
     }
   };
 
+  // ---- edge blocks: the diagonal, a window edge, the Lk tail ----
+  // (wave-uniform: decided from this wave's first and last row)
+  auto edge_of = [&](int j) __attribute__((always_inline)) -> bool {
+    const int kw = blk(j) * S::BK + wk * BKW;  // first key of this wave's slice
+    return (kw + BKW > Lk) || (a.mask != MASK_NONE && kw + BKW - 1 > pmin_w) ||
+           (a.mask == MASK_WINDOW && kw <= pmax_w - a.window);
+  };
+  // Per-element mask of an edge block: keys outside this row's visible range
+  // [lo, hi] go to -inf.  The key of register e in tile kt is
+  // kw + 32 kt + 4 hl + off(e) with off(e) = 8 (e / 4) + e % 4.
+  auto mask_edge = [&](int j, f32x16 (&sacc)[S::NKT]) __attribute__((always_inline)) {
+    const int kw = blk(j) * S::BK + wk * BKW;
+    int hi = Lk - 1, lo = 0;
+    if (a.mask != MASK_NONE) hi = min(hi, pos);
+    if (a.mask == MASK_WINDOW) lo = max(lo, pos - a.window + 1);
+#pragma unroll
+    for (int kt = 0; kt < S::NKT; ++kt) {
+      const int base = kw + kt * 32 + 4 * hl;
+      const unsigned span = (unsigned)(hi - lo);  // visible iff 0 <= key - lo <= span
+      const int first = lo - base;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int off = 8 * (e >> 2) + (e & 3);
+        if ((unsigned)(off - first) > span || hi < lo) sacc[kt][e] = kNegInf;
+      }
+    }
+  };
+  // Fold the block max into the running max: online softmax with lazy
+  // rescaling (scale c > 0); the reference max moves only when the block max
+  // exceeds it by more than kRescale.
+  auto fold_max = [&](f32x16 (&sacc)[S::NKT]) __attribute__((always_inline)) {
+    float mx = kNegInf;
+#pragma unroll
+    for (int kt = 0; kt < S::NKT; ++kt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kt][e]);
+    mx = wave_max32(mx);
+    const float mxs = mx * cs;  // block max in log2 units (-inf if all masked)
+    const bool need = mxs > m_ref + kRescale;
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(need) != 0, 0)) [[unlikely]] {
+      const float m_new = need ? mxs : m_ref;
+      const float alpha = need ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.0f;
+      l_run *= alpha;
+#pragma unroll
+      for (int t = 0; t < S::NDTW; ++t) oacc[t] *= alpha;
+      m_ref = m_new;
+    }
+  };
+
   // ---- mask edge blocks and fold the block max into the running max ----
   auto mask_max = [&](int j, f32x16 (&sacc)[S::NKT]) __attribute__((always_inline)) {
-    const int kw = blk(j) * S::BK + wk * BKW;  // first key of this wave's slice
     if constexpr (MA != MA_NONE) {
       // This lane's row of the block's mask tile: register e of tile kt is
       // key wk BKW + 32 kt + 8 (e / 4) + 4 hl + e % 4 of the block, so each
@@ -757,44 +807,8 @@ void attn_fwd_kernel(AttnArgs a) {
         }
       }
     }
-    // edge blocks: the diagonal, a window edge, the Lk tail
-    const bool edge = (kw + BKW > Lk) || (a.mask != MASK_NONE && kw + BKW - 1 > pmin_w) ||
-                      (a.mask == MASK_WINDOW && kw <= pmax_w - a.window);
-    if (edge) {
-      // Visible keys of this row form [lo, hi]; key of register e in tile kt
-      // is kw + 32 kt + 4 hl + off(e) with off(e) = 8 (e / 4) + e % 4.
-      int hi = Lk - 1, lo = 0;
-      if (a.mask != MASK_NONE) hi = min(hi, pos);
-      if (a.mask == MASK_WINDOW) lo = max(lo, pos - a.window + 1);
-#pragma unroll
-      for (int kt = 0; kt < S::NKT; ++kt) {
-        const int base = kw + kt * 32 + 4 * hl;
-        const unsigned span = (unsigned)(hi - lo);  // visible iff 0 <= key - lo <= span
-        const int first = lo - base;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int off = 8 * (e >> 2) + (e & 3);
-          if ((unsigned)(off - first) > span || hi < lo) sacc[kt][e] = kNegInf;
-        }
-      }
-    }
-    // online softmax with lazy rescaling (scale c > 0)
-    float mx = kNegInf;
-#pragma unroll
-    for (int kt = 0; kt < S::NKT; ++kt)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kt][e]);
-    mx = wave_max32(mx);
-    const float mxs = mx * cs;  // block max in log2 units (-inf if all masked)
-    const bool need = mxs > m_ref + kRescale;
-    if (__builtin_expect(__builtin_amdgcn_ballot_w64(need) != 0, 0)) [[unlikely]] {
-      const float m_new = need ? mxs : m_ref;
-      const float alpha = need ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.0f;
-      l_run *= alpha;
-#pragma unroll
-      for (int t = 0; t < S::NDTW; ++t) oacc[t] *= alpha;
-      m_ref = m_new;
-    }
+    if (edge_of(j)) mask_edge(j, sacc);
+    fold_max(sacc);
   };
 
   // ---- probabilities of a block against the reference max ----
@@ -931,7 +945,27 @@ void attn_fwd_kernel(AttnArgs a) {
       // (checked as in the plain loop: every 4th block, or after a removed one)
       bool ln = true;
       if (MA == MA_BOOL && more && (!live_cur || ((j + 1) & 3) == 0)) ln = mask_live(j + 1);
-      if (MA != MA_BOOL || live_cur) {
+      if constexpr (MA == MA_NONE && DQK <= 64 && DV <= 64) {
+        // Small head dims without a mask array: the step is one straight
+        // stretch of code, so the scheduler can put the next block's max and
+        // the row sums beside the matrix products.  Whether block j + 1 needs
+        // the per-element mask is decided first, and each case has its own
+        // copy of the step (at larger head dims the two copies no longer fit
+        // the register file).
+        auto body = [&](auto EDGE) __attribute__((always_inline)) {
+          vfrag_t vf;
+          vhoist(j, vf);
+          expo(cur);
+          if (more) qk(j + 1, nxt);
+          pv(j, cur, vf);
+          if (more) {
+            if constexpr (decltype(EDGE)::value) mask_edge(j + 1, nxt);
+            fold_max(nxt);
+          }
+        };
+        if (more && edge_of(j + 1)) body(std::true_type{});
+        else body(std::false_type{});
+      } else if (MA != MA_BOOL || live_cur) {
         // Large head dims: ask the scheduler to interleave the exponentials
         // with the matrix products (one of LLVM's fixed interleaving
         // strategies for exponential-plus-MFMA code; measured 5-12% faster
