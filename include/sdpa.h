@@ -36,6 +36,8 @@
  *   o [B, Hq,  Lq, Dv]    lse [B, Hq, Lq] contiguous float32 (optional)
  *   mask [B, Hq, Lq, Lk]  element strides mask_stride[] for (batch, query
  *                         head, query); 0 broadcasts a dim; key stride 1
+ * Every row stride is a multiple of 16 bytes; the k and v position strides
+ * (k_stride[2], v_stride[2]) are at most 16 MiB.
  * q, k, v and o share one element type (float32, float16 or bfloat16).
  * Accumulation is float32; o is rounded once, to nearest even.
  *

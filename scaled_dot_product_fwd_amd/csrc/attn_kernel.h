@@ -280,6 +280,23 @@ __device__ __forceinline__ void lds_dma16(const void* src, unsigned lds) {
                  : "memory", "m0");
 }
 
+// The same with a wave-uniform base address in scalar registers and a 32-bit
+// per-lane byte offset (the instruction's scalar-base form: no 64-bit address
+// arithmetic per lane and load).
+template <bool STREAM>
+__device__ __forceinline__ void lds_dma16_s(const char* base, unsigned off, unsigned lds) {
+  if constexpr (STREAM)
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+                 :
+                 : "v"(off), "s"(base), "s"(lds)
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(off), "s"(base), "s"(lds)
+                 : "memory", "m0");
+}
+
 // Wait until at most N vector-memory operations of this wave are in flight.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -445,43 +462,50 @@ void attn_fwd_kernel(AttnArgs a) {
   // LDS: K tiles in two buffers, then V tiles in two buffers.  Block j's K
   // sits in K buffer j % 2 and its V in V buffer j % 2.
   const unsigned lds_base = (unsigned)(uintptr_t)smem;
-  auto dma_k = [&](int blk, int buf) __attribute__((always_inline)) {
-    const int k0 = blk * S::BK;
+  // Block jj of this split starts at key blk(jj) * BK: its K and V rows
+  // begin at a wave-uniform address (scalar registers), and each lane adds
+  // its fixed 32-bit offset (the planner bounds a block's rows below 2 GiB).
+  const char* const kblk0 = kbase + (int64_t)(kb_first + split) * S::BK * kstr;
+  const char* const vblk0 = vbase + (int64_t)(kb_first + split) * S::BK * vstr;
+  const int64_t kstep = (int64_t)nsp * S::BK * kstr;
+  const int64_t vstep = (int64_t)nsp * S::BK * vstr;
+  auto dma_k = [&](int jj, int buf) __attribute__((always_inline)) {
+    const int k0 = blk(jj) * S::BK;
     const unsigned kl = lds_base + buf * S::KBYTES;
+    const char* kb = kblk0 + jj * kstep;
     if (k0 + S::BK <= Lk) {
-      const char* kb = kbase + (int64_t)k0 * kstr;
 #pragma unroll
       for (int ii = 0; ii < KPW; ++ii)
         if ((ii + 1) * S::NW <= S::KDMA || ii * S::NW + wave_u < S::KDMA)
-          lds_dma16<S::STREAM>(kb + koff[ii], kl + (ii * S::NW + wave_u) * 1024);
+          lds_dma16_s<S::STREAM>(kb, koff[ii], kl + (ii * S::NW + wave_u) * 1024);
     } else {
 #pragma unroll
       for (int ii = 0; ii < KPW; ++ii) {
         if ((ii + 1) * S::NW > S::KDMA && ii * S::NW + wave_u >= S::KDMA) continue;
         int row, colb;
         kslot((ii * S::NW + wave_u) * 64 + lane, row, colb);
-        const int grow = min(k0 + row, Lk - 1);
-        lds_dma16<S::STREAM>(kbase + (int64_t)grow * kstr + colb, kl + (ii * S::NW + wave_u) * 1024);
+        const int lrow = min(row, Lk - 1 - k0);
+        lds_dma16_s<S::STREAM>(kb, (unsigned)(lrow * kstr) + colb, kl + (ii * S::NW + wave_u) * 1024);
       }
     }
   };
-  auto dma_v = [&](int blk, int buf) __attribute__((always_inline)) {
-    const int k0 = blk * S::BK;
+  auto dma_v = [&](int jj, int buf) __attribute__((always_inline)) {
+    const int k0 = blk(jj) * S::BK;
     const unsigned vl = lds_base + 2 * S::KBYTES + buf * S::VBYTES;
+    const char* vb = vblk0 + jj * vstep;
     if (k0 + S::BK <= Lk) {
-      const char* vb = vbase + (int64_t)k0 * vstr;
 #pragma unroll
       for (int ii = 0; ii < VPW; ++ii)
         if ((ii + 1) * S::NW <= S::VDMA || ii * S::NW + wave_u < S::VDMA)
-          lds_dma16<S::STREAM>(vb + voff[ii], vl + (ii * S::NW + wave_u) * 1024);
+          lds_dma16_s<S::STREAM>(vb, voff[ii], vl + (ii * S::NW + wave_u) * 1024);
     } else {
 #pragma unroll
       for (int ii = 0; ii < VPW; ++ii) {
         if ((ii + 1) * S::NW > S::VDMA && ii * S::NW + wave_u >= S::VDMA) continue;
         int row, colb;
         vslot((ii * S::NW + wave_u) * 64 + lane, row, colb);
-        const int grow = min(k0 + row, Lk - 1);
-        lds_dma16<S::STREAM>(vbase + (int64_t)grow * vstr + colb, vl + (ii * S::NW + wave_u) * 1024);
+        const int lrow = min(row, Lk - 1 - k0);
+        lds_dma16_s<S::STREAM>(vb, (unsigned)(lrow * vstr) + colb, vl + (ii * S::NW + wave_u) * 1024);
       }
     }
   };
@@ -527,9 +551,9 @@ void attn_fwd_kernel(AttnArgs a) {
   // Prologue: block 0 goes in flight ahead of the Q loads; block 1 follows
   // once both have landed (see below).
   if (nblk > 0) {
-    dma_k(blk(0), 0);
+    dma_k(0, 0);
     dma_m(blk(0), 0);
-    dma_v(blk(0), 0);
+    dma_v(0, 0);
   }
 
   // ---- Q fragments (B operand of S^T = K Q^T), kept in registers ----
@@ -611,9 +635,9 @@ void attn_fwd_kernel(AttnArgs a) {
   // flight there).  Block 1 then goes in flight.
   wait_vmcnt<0>();
   if (nblk > 1) {
-    dma_k(blk(1), 1);
+    dma_k(1, 1);
     dma_m(blk(1), 1);
-    dma_v(blk(1), 1);
+    dma_v(1, 1);
   }
 
   // ---- S^T = K Q^T of one block (this wave's BKW keys) ----
@@ -889,7 +913,7 @@ void attn_fwd_kernel(AttnArgs a) {
       if constexpr (KEARLY) {
         if (j + 2 < nblk) {
           __syncthreads();  // every wave is done with K(j)
-          dma_k(blk(j + 2), j & 1);
+          dma_k(j + 2, j & 1);
         }
       }
       if (live) {
@@ -902,9 +926,9 @@ void attn_fwd_kernel(AttnArgs a) {
       if (j + 2 < nblk) {
         if constexpr (!KEARLY) wait_vmcnt<63 - S::DMA_MAX>();
         __syncthreads();  // every wave is done with V(j) and the mask tile of j
-        if constexpr (!KEARLY) dma_k(blk(j + 2), j & 1);
+        if constexpr (!KEARLY) dma_k(j + 2, j & 1);
         dma_m(blk(j + 2), j & 1);
-        dma_v(blk(j + 2), j & 1);
+        dma_v(j + 2, j & 1);
       }
     }
   } else {
@@ -925,7 +949,7 @@ void attn_fwd_kernel(AttnArgs a) {
       mask_max(0, sa);
       if (nblk > 2) {
         __syncthreads();  // every wave is done with K(0) and the mask tile of 0
-        dma_k(blk(2), 0);
+        dma_k(2, 0);
         dma_m(blk(2), 0);
       }
     }
@@ -987,10 +1011,10 @@ void attn_fwd_kernel(AttnArgs a) {
       if (j + 2 < nblk) {
         __syncthreads();  // every wave is done with K(j + 1), its mask tile and V(j)
         if (j + 3 < nblk) {
-          dma_k(blk(j + 3), (j + 1) & 1);
+          dma_k(j + 3, (j + 1) & 1);
           dma_m(blk(j + 3), (j + 1) & 1);
         }
-        dma_v(blk(j + 2), j & 1);
+        dma_v(j + 2, j & 1);
       }
     };
     int j = 0;

@@ -144,6 +144,16 @@ int make_plan(const sdpa_desc_t* d, Plan* p, std::string* err) {
       }
     }
   }
+  // A key block's rows (at most 128) are addressed by 32-bit byte offsets
+  // from the block's first row.
+  for (int t = 1; t <= 2; ++t) {
+    if (strides[t][2] * es > kMaxRowStrideBytes) {
+      std::ostringstream s;
+      s << names[t] << "_stride[2] = " << strides[t][2] << " elements is more than "
+        << (kMaxRowStrideBytes >> 20) << " MiB per row (a key block's rows are addressed with 32-bit offsets)";
+      return fail(err, SDPA_E_STRIDE, s.str());
+    }
+  }
   if (d->mask_array != SDPA_MASK_ARRAY_NONE && d->mask_array != SDPA_MASK_ARRAY_BOOL &&
       d->mask_array != SDPA_MASK_ARRAY_ADD) {
     return fail(err, SDPA_E_MASK, "mask_array must be SDPA_MASK_ARRAY_NONE, _BOOL or _ADD (got " +

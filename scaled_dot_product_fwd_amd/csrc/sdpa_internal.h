@@ -114,6 +114,10 @@ constexpr int mask_elem_bytes(int ma, int elem_bytes) {
 // array is given) fit: prefill keeps two workgroups per CU (<= 80 KB), decode
 // takes the largest key block that fits one workgroup's 160 KB.  Shared by
 // the planner and the kernel instantiation units.
+// Largest K / V row (position) stride in bytes: a key block spans at most 128
+// rows, addressed with 32-bit offsets from its first row.
+constexpr int64_t kMaxRowStrideBytes = (int64_t)16 << 20;
+
 constexpr Family family_for(int kind, int elem_bytes, int dqk_pad, int dv_pad, int mes = 0) {
   const int key_bytes = (dqk_pad + dv_pad) * elem_bytes;  // one key of K plus V
   // Head dims above 256 (512): a 32-row wave cannot hold Q and the whole O

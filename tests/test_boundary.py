@@ -71,6 +71,8 @@ def _status(fn, *args):
     (dict(scale=float("inf")), "SDPA_E_SCALE", "finite"),
     (dict(scale=float("nan")), "SDPA_E_SCALE", "finite"),
     (dict(q_stride=(8 * 8 * 64, 8 * 64, 60)), "SDPA_E_STRIDE", "q_stride[2]"),
+    (dict(k_stride=(1 << 30, 1 << 26, (16 << 20) // 2 + 8)), "SDPA_E_STRIDE", "k_stride[2]"),
+    (dict(v_stride=(1 << 30, 1 << 26, (16 << 20) // 2 + 8)), "SDPA_E_STRIDE", "v_stride[2]"),
     (dict(num_splits=-1), "SDPA_E_PLAN", "num_splits"),
     (dict(row_tile=48), "SDPA_E_PLAN", "row_tile"),
 ])
