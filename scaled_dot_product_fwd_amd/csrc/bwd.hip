@@ -212,9 +212,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int col = lane & 31, hl = lane >> 5;
+  // Tile-major order, heaviest first: under a causal mask the last row tiles
+  // see the most keys, so they go out first, every head's before any lighter
+  // tile, and the short tiles fill in behind them (in-order dispatch onto
+  // free CUs then balances like longest-processing-time-first).
   const int row_tiles = (a.R + 127) / 128;
-  const int rt = blockIdx.x % row_tiles;
-  const int z = blockIdx.x / row_tiles;
+  const int Z = (int)(gridDim.x / row_tiles);
+  const int rt = row_tiles - 1 - (int)(blockIdx.x / Z);
+  const int z = blockIdx.x % Z;
   const int b = z / a.Hkv, kvh = z % a.Hkv;
   const EntryLens en = entry_lens(a, b);
   const int r_wg = rt * 128;
@@ -430,9 +435,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int col = lane & 31, hl = lane >> 5;
+  // Tile-major order, heaviest first: under a causal mask the first key
+  // tiles are seen by the most queries, so every head's tile 0 goes out
+  // before any tile 1, and so on (see the dq kernel).
   const int key_tiles = (a.Lk + 127) / 128;
-  const int kti = blockIdx.x % key_tiles;
-  const int z = blockIdx.x / key_tiles;
+  const int Z = (int)(gridDim.x / key_tiles);
+  const int kti = (int)(blockIdx.x / Z);
+  const int z = blockIdx.x % Z;
   const int b = z / a.Hkv, kvh = z % a.Hkv;
   const EntryLens en = entry_lens(a, b);
   const int k_wg = kti * 128;
