@@ -342,11 +342,24 @@ void attn_fwd_kernel(AttnArgs a) {
       id = ((slot / a.xcd_group) * 8 + x) * a.xcd_group + slot % a.xcd_group;
     }
   }
-  int rt = id % a.row_tiles;
-  id /= a.row_tiles;
-  int split = id % a.splits;
-  int z = id / a.splits;
-  if (a.heavy_first) rt = a.row_tiles - 1 - rt;
+  int rt, split, z;
+  if (a.heavy_first == 2) {
+    // Tile-major, heaviest first (causal or window, one split, no XCD
+    // grouping): every KV head's longest row tile goes out before any
+    // shorter one, so in-order dispatch onto free CUs balances like
+    // longest-processing-time-first instead of finishing one head's short
+    // tiles while later heads' long tiles still queue.
+    const int Z = (int)(gridDim.x / a.row_tiles);
+    rt = a.row_tiles - 1 - id / Z;
+    split = 0;
+    z = id % Z;
+  } else {
+    rt = id % a.row_tiles;
+    id /= a.row_tiles;
+    split = id % a.splits;
+    z = id / a.splits;
+    if (a.heavy_first) rt = a.row_tiles - 1 - rt;
+  }
   // Splits of this row tile's key range, and (balanced lengths) the first
   // partial row of its batch entry's workspace segment, in units of R rows.
   int nsp = a.splits;

@@ -181,7 +181,9 @@ int forward_planned(const sdpa_desc_t* d, const sdpa::Plan& p, const void* q, co
   a.scale = d->scale;
   a.splits = p.splits;
   a.row_tiles = p.row_tiles;
-  a.heavy_first = p.mask != sdpa::MASK_NONE && p.row_tiles > 1;
+  // Masked prefill visits its longest row tiles first: tile-major across
+  // heads when nothing else orders the grid, else within each head.
+  a.heavy_first = p.mask != sdpa::MASK_NONE && p.row_tiles > 1 ? (p.splits == 1 && p.xcd_group == 0 ? 2 : 1) : 0;
   a.xcd_group = p.xcd_group;
   // Per-batch key lengths on a split plan: deal the workgroups by the
   // entries' key blocks (a window's tiles see about W keys whatever the

@@ -35,7 +35,7 @@ struct AttnArgs {
   float scale;         // scale itself (an additive mask is added in natural-log units)
   int splits;          // key splits per row tile (1: normalise in place)
   int row_tiles;       // ceil(R / rows per workgroup)
-  int heavy_first;     // causal/window prefill: visit the longest row tiles first
+  int heavy_first;     // causal/window prefill: longest row tiles first (1: within each head, 2: across heads)
   int xcd_group;       // > 0: consecutive work items run in groups of this many on one XCD
   int kv_balance;      // > 0 (split plans with kv_lens): deal each KV head's B * splits
                        // workgroups to the batch entries by their blocks of this many keys
