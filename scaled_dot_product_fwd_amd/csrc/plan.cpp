@@ -209,6 +209,17 @@ int make_plan(const sdpa_desc_t* d, Plan* p, std::string* err) {
   int rows = xl ? 64
              : d->row_tile ? d->row_tile
                            : (R <= 32 || R == 64 ? 32 : (R <= 64 ? 64 : (R <= 128 || !wide_ok || R > 256 ? 128 : 256)));
+  // A long prefill whose 128-row tiles would fill at most half of the CUs
+  // (few heads, about a thousand queries) takes 64-row tiles instead (two
+  // waves per SIMD up to head dim 128): every CU then gets a tile.  Measured:
+  // H=16, L=1024, D=72 (128 -> 256 workgroups) 20.5 -> 19.1 us; with more
+  // tiles than that the 128-row tile stays faster (H=20, L=1500, D=64:
+  // 240 -> 480 workgroups, 26.9 -> 28.9 us).  Fewer tiles than a quarter of
+  // the CUs split the keys instead (below); mask arrays keep their tiles.
+  const int64_t tiles128 = B * Hkv * ceil_div(R, 128);
+  if (!d->row_tile && rows == 128 && R > 128 && std::max(dqk_pad, dv_pad) <= 128 && ma == MA_NONE &&
+      tiles128 >= kTargetCUs / 4 && tiles128 <= kTargetCUs / 2)
+    rows = 64;
   const int64_t row_tiles = ceil_div(R, rows);
   const int64_t base = B * Hkv * row_tiles;
   const int kind = xl ? KIND_PREFILL

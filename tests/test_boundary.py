@@ -162,6 +162,20 @@ def test_plan_verify_window_family(lq, fam, tiles):
     assert int(p["grid"]) >= 256
 
 
+def test_plan_small_prefill_grid_takes_64_row_tiles():
+    # 16 heads x 8 tiles of 128 rows would leave half of the 256 CUs idle
+    p = _plan(hq=16, hkv=16, lq=1024, lk=1024, dqk=72, dv=72)
+    assert p["family"] == "short" and p["rows_per_wg"] == "64" and p["grid"] == "256" and p["splits"] == "1"
+    # 240 tiles of 128 rows: kept
+    p = _plan(hq=20, hkv=20, lq=1500, lk=1500, dqk=64, dv=64)
+    assert p["family"] == "prefill" and p["rows_per_wg"] == "128"
+    # head dims above 128 and forced tiles: kept
+    p = _plan(hq=4, hkv=4, lq=1024, lk=1024, dqk=256, dv=256)
+    assert p["family"] == "prefill" and p["rows_per_wg"] == "128"
+    p = _plan(hq=16, hkv=16, lq=1024, lk=1024, dqk=72, dv=72, row_tile=128)
+    assert p["rows_per_wg"] == "128"
+
+
 def test_plan_prefill_configs_do_not_split():
     p = _plan(hq=20, hkv=20, lq=1500, lk=1500, dqk=64, dv=64)
     assert p["family"] == "prefill" and p["splits"] == "1" and p["workspace"] == "0"
@@ -289,7 +303,8 @@ def test_mask_array_pointer_must_match_the_desc():
     (_lib.SDPA_F32, 128, _lib.SDPA_MASK_ARRAY_ADD, "prefill", "32"),
 ])
 def test_plan_masked_prefill_family(dtype, d, kind, family, bk):
-    p = _plan(b=1, hq=8, hkv=8, lq=2048, lk=2048, dqk=d, dv=d, dtype=dtype, mask_array=kind,
+    # (16 heads: enough 128-row tiles that no shape here moves to 64-row tiles)
+    p = _plan(b=1, hq=16, hkv=16, lq=2048, lk=2048, dqk=d, dv=d, dtype=dtype, mask_array=kind,
               mask_stride=(0, 0, 2048))
     assert p["family"] == family and p["block_keys"] == bk
     if kind != _lib.SDPA_MASK_ARRAY_NONE:

@@ -146,6 +146,42 @@ def test_monotone_scores_running_max_changes_every_block():
         assert float(np.abs(lse - rl).max()) <= 1e-4
 
 
+@pytest.mark.parametrize("d", [192, 224, 256])
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_large_head_dims_every_block_count(d, dt):
+    """Prefill tiles at head dims 192-256 run 32-key blocks through a fixed
+    product order, two blocks per loop turn: one to six blocks (either parity
+    of the pair loop, a ragged last block), unmasked, causal and windowed,
+    three 128-row tiles with a ragged last one."""
+    for lk in (20, 64, 90, 128, 150, 190):
+        _say("large dims", d, dt, lk)
+        check_full(1, 2, 1, 130, lk, d, d, dt, "none", 0, seed=lk + d)
+        lq = min(lk, 130)
+        check_full(1, 2, 1, lq, lk, d, d, dt, "causal", 0, seed=lk + d + 1)
+        check_full(1, 2, 1, lq, lk, d, d, dt, "window", 40, seed=lk + d + 2)
+
+
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16])
+def test_monotone_scores_large_head_dim_prefill(dt):
+    """The running max rises (then falls) block after block in 128-row tiles
+    at head dim 256, so the rescale of O between the matrix products runs."""
+    _say("monotone scores D256", dt)
+    from oracle import sdpa_ref
+    lk, d = 700, 256
+    q = torch.ones(1, 1, 130, d)
+    # scores -40 .. 40: the block max climbs by more than the lazy-rescale
+    # threshold block after block
+    ramp = torch.linspace(-40, 40, lk)[:, None].repeat(1, d) / d
+    for sign in (1.0, -1.0):
+        k = (sign * ramp)[None, None].to(dt)
+        v = torch.randn(1, 1, lk, d, generator=torch.Generator().manual_seed(2)).to(dt)
+        qq = q.to(dt)
+        o, lse = run_gpu(qq, k, v, 1.0, "none", 0)
+        ro, rl = sdpa_ref(qq, k, v, 1.0, "none", 0)
+        assert float(np.abs(o - ro).max()) <= TOL_O[dt]
+        assert float(np.abs(lse - rl).max()) <= 1e-4
+
+
 def test_single_spike_key_in_last_split():
     _say("spike in last split")
     from oracle import sdpa_ref
