@@ -191,9 +191,12 @@ struct Shape {
   // of the 256-byte bank window.  V: a transposing read group covers 4
   // consecutive rows (32 bytes each); chunk ^ vy(row) spreads them over the
   // window.  Each swizzle permutes chunks inside aligned groups (KG, VG
-  // chunks), so it never leaves the row.
-  static constexpr int KG = (KCH % 16 == 0) ? 16 : (KCH % 8 == 0) ? 8 : 4;
-  static constexpr int KSH = (KG == 16) ? 0 : (KG == 8) ? 1 : 2;
+  // chunks), so it never leaves the row.  Rows of 10 chunks (head dim 80):
+  // 10 r mod 16 takes 8 distinct even slots for r = 0..7 and repeats for
+  // r = 8..15, so flipping the chunk's low bit on row bit 3 (pairs of
+  // chunks) moves the second eight rows onto the odd slots.
+  static constexpr int KG = (KCH % 16 == 0) ? 16 : (KCH % 8 == 0) ? 8 : (KCH % 4 == 0) ? 4 : 2;
+  static constexpr int KSH = (KG == 16) ? 0 : (KG == 8) ? 1 : (KG == 4) ? 2 : 3;
   static constexpr int VG = (VCH % 16 == 0) ? 16 : (VCH % 8 == 0) ? 8 : 4;
   static __device__ __forceinline__ int kx(int row) { return (row >> KSH) & (KG - 1); }
   static __device__ __forceinline__ int vy(int row) {

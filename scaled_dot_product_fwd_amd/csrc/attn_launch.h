@@ -60,11 +60,13 @@ int launch_one(const Plan& p, const AttnArgs& a, void* stream, std::string* err)
                       wpe_for(KIND, dev::E::ES, DQK, DV), MA, f_.nwd>(p, a, stream, err);      \
   }
 
-// Head-dim pairs of the 16-bit types: equal padded dims plus (192, 128),
-// split at 192 so that the large ones can live in units of their own.
+// Head-dim pairs of the 16-bit types: equal padded dims plus (80, 96) and
+// (192, 128), split at 192 so that the large ones can live in units of
+// their own.
 #define SDPA_PAIRS16_SMALL(E, KIND, MA) \
   SDPA_CASE(E, KIND, 32, 32, MA)         \
   SDPA_CASE(E, KIND, 64, 64, MA)         \
+  SDPA_CASE(E, KIND, 80, 96, MA)         \
   SDPA_CASE(E, KIND, 96, 96, MA)         \
   SDPA_CASE(E, KIND, 128, 128, MA)       \
   SDPA_CASE(E, KIND, 160, 160, MA)
@@ -82,6 +84,7 @@ int launch_one(const Plan& p, const AttnArgs& a, void* stream, std::string* err)
 #define SDPA_PAIRS16_UPTO128(E, KIND, MA) \
   SDPA_CASE(E, KIND, 32, 32, MA)         \
   SDPA_CASE(E, KIND, 64, 64, MA)         \
+  SDPA_CASE(E, KIND, 80, 96, MA)         \
   SDPA_CASE(E, KIND, 96, 96, MA)         \
   SDPA_CASE(E, KIND, 128, 128, MA)
 // float32 wide: head dims up to 96 (two waves per SIMD)

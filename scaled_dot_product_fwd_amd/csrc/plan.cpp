@@ -106,6 +106,11 @@ int make_plan(const sdpa_desc_t* d, Plan* p, std::string* err) {
   } else {
     const int m = dqk_pad > dv_pad ? dqk_pad : dv_pad;
     dqk_pad = dv_pad = m;  // zero padding in-kernel: no host copy
+    // The QK product steps 16 deep along the head dim, so a 16-bit Q and K of
+    // head dim 72 or 80 pad to 80, not 96 (mlx-rs issue #339, findings: pad
+    // 72 to 80 rather than to the next larger kernel); V keeps whole 32-wide
+    // dv tiles.  One MFMA in six fewer per key tile, K tiles a sixth smaller.
+    if (m == 96 && Dqk <= 80 && d->dtype != SDPA_F32) dqk_pad = 80;
   }
   if (d->dtype == SDPA_F32 && (dqk_pad > 128 || dv_pad > 128)) {
     std::ostringstream s;

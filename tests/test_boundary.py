@@ -180,9 +180,22 @@ def test_plan_prefill_configs_do_not_split():
     p = _plan(hq=20, hkv=20, lq=1500, lk=1500, dqk=64, dv=64)
     assert p["family"] == "prefill" and p["splits"] == "1" and p["workspace"] == "0"
     p = _plan(hq=16, hkv=16, lq=4096, lk=4096, dqk=72, dv=72)
-    assert p["dqk"] == "72->96" and p["dv"] == "72->96"
+    assert p["dqk"] == "72->80" and p["dv"] == "72->96"
     p = _plan(hq=16, hkv=2, lq=32768, lk=32768, dqk=256, dv=256, mask="causal")
     assert p["splits"] == "1" and p["mask"] == "causal"
+
+
+def test_plan_head_dim_padding():
+    # QK pads to the 16-deep MFMA step where an (80, 96) kernel exists; PV to
+    # whole 32-wide tiles; float32 keeps 32-wide padding on both.
+    for dqk, dv, want in ((72, 72, ("80", "96")), (80, 80, ("80", "96")), (80, 96, ("80", "96")),
+                          (72, 64, ("80", "96")), (64, 96, ("80", "96")), (88, 88, ("96", "96")),
+                          (64, 64, ("64", "64")), (40, 40, ("64", "64"))):
+        for lq in (1, 16, 200, 4096):
+            p = _plan(hq=16, hkv=4, lq=lq, lk=4096, dqk=dqk, dv=dv)
+            assert (p["dqk"], p["dv"]) == (f"{dqk}->{want[0]}", f"{dv}->{want[1]}"), (dqk, dv, lq, p)
+    p = _plan(hq=16, hkv=4, lq=200, lk=4096, dqk=72, dv=72, dtype=_lib.SDPA_F32)
+    assert (p["dqk"], p["dv"]) == ("72->96", "72->96")
 
 
 def test_plan_canonical_masks():

@@ -43,6 +43,9 @@ MASK_CASES = [
     (2, 2, 2, 140, 300, 256, 256, "bf16", "window", 70, "add", (2, 1, 1, 300)),
     (1, 2, 2, 140, 300, 256, 256, "bf16", "none", 0, "bool", (140, 300)),
     (1, 8, 2, 100, 100, 72, 72, "bf16", "none", 0, "add", (100, 100)),
+    (1, 4, 2, 200, 333, 80, 80, "f16", "causal", 0, "bool", (1, 4, 200, 333)),
+    (1, 16, 4, 1, 1200, 72, 72, "bf16", "none", 0, "bool", (1, 16, 1, 1200)),
+    (1, 32, 8, 48, 700, 72, 72, "bf16", "none", 0, "add", (48, 700)),
     (1, 2, 1, 129, 129, 160, 160, "f16", "none", 0, "bool", (1, 2, 129, 129)),
     (1, 2, 2, 96, 96, 16, 48, "f16", "causal", 0, "bool", (96, 96)),
     (1, 2, 2, 130, 200, 192, 128, "bf16", "causal", 0, "add", (130, 200)),

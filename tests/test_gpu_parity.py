@@ -292,6 +292,35 @@ def test_split_heads_grouped_by_xcd(b, hkv, lq):
     check_full(b, 4 * hkv, hkv, lq, 2500, 128, 128, "bf16", "causal", 0, seed=67 + b)
 
 
+HEAD_DIM_80 = [
+    # b, hq, hkv, lq, lk, dqk, dv, dtype, mask, window, family, forced plan
+    (1, 16, 4, 1, 777, 72, 72, "bf16", "none", 0, "decode", {}),
+    (1, 16, 2, 3, 1000, 80, 80, "f16", "causal", 0, "decode", {}),
+    (1, 8, 2, 12, 1500, 72, 72, "bf16", "causal", 0, "short", {}),
+    (1, 16, 2, 40, 900, 80, 80, "bf16", "none", 0, "prefill", {}),
+    (1, 32, 8, 48, 700, 72, 64, "f16", "window", 100, "wide", {}),
+    (2, 2, 2, 300, 300, 72, 72, "f16", "none", 0, "prefill", {}),
+    (2, 2, 2, 300, 300, 72, 72, "bf16", "causal", 0, "prefill", {"num_splits": 1}),
+    (1, 2, 1, 333, 333, 80, 96, "bf16", "causal", 0, "prefill", {}),
+    (1, 3, 1, 200, 450, 64, 96, "bf16", "window", 77, "prefill", {"num_splits": 1}),
+    (1, 4, 2, 190, 260, 72, 72, "f16", "window", 50, "short", {"row_tile": 64, "num_splits": 1}),
+]
+
+
+@pytest.mark.parametrize("case", HEAD_DIM_80, ids=lambda c: "-".join(str(x) for x in c[:11]))
+def test_qk_head_dim_80_every_family(case):
+    """Head dims 65-80 take the (80, 96) kernels: Q and K padded to 80 (a
+    K row of ten 16-byte chunks, swizzled in pairs), V to 96."""
+    b, hq, hkv, lq, lk, dqk, dv, dt, mask, w, fam, plan = case
+    _say("qk80", case)
+    code = sdpa.SDPA_BF16 if dt == "bf16" else sdpa.SDPA_F16
+    d = sdpa.make_desc((b, hq, lq, dqk), (b, hkv, lk, dqk), (b, hkv, lk, dv), code, mask=mask,
+                       window_size=w, **plan)
+    got = dict(t.split("=", 1) for t in sdpa.sdpa_describe_plan(d).split())
+    assert got["family"] == fam and got["dqk"] == f"{dqk}->80" and got["dv"] == f"{dv}->96", got
+    check_full(b, hq, hkv, lq, lk, dqk, dv, dt, mask, w, seed=zlib.crc32(repr(case).encode()) % 10000, **plan)
+
+
 WIDE = [
     # 128 < packed rows <= 256: the wide family (256-row tiles, eight waves)
     (1, 32, 8, 48, 2000, 128, 128, "f16", "none", 0),
