@@ -663,10 +663,19 @@ def summarize_trace(trace_dir, name, command):
             rows.append((r["Name"], int(r["Calls"]), float(r["AverageNs"]), float(r["MinNs"]), float(r["MaxNs"])))
     flops, nbytes = work(s)
     plan, inst = instance_of(s)
-    # the workload's own instance (a default run also times the prefill workloads)
-    attn = [r for r in rows if "attn_fwd_kernel" in r[0] and inst in r[0]]
-    comb = [r for r in rows if "combine_kernel" in r[0]] if " splits=1 " not in plan else []
-    call_ns = (attn[0][2] if attn else 0.0) + (comb[0][2] if comb else 0.0)
+    if s.get("bwd"):
+        # a backward call is the prep, dQ and dK/dV kernels (the forward that
+        # produces o and lse runs once, outside the timed calls)
+        parts = [[r for r in rows if k in r[0]] for k in ("bwd_prep_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel")]
+        call_ns = sum(p[0][2] for p in parts if p)
+        call_name = " + ".join(f"`{p[0][0]}`" for p in parts if p)
+        plan = "backward: bwd_prep, then bwd_dq (128-row tiles) and bwd_dkdv (128-key tiles)"
+    else:
+        # the workload's own instance (a default run also times the prefill workloads)
+        attn = [r for r in rows if "attn_fwd_kernel" in r[0] and inst in r[0]]
+        comb = [r for r in rows if "combine_kernel" in r[0]] if " splits=1 " not in plan else []
+        call_ns = (attn[0][2] if attn else 0.0) + (comb[0][2] if comb else 0.0)
+        call_name = f"`{attn[0][0] if attn else '?'}`" + (" + combine kernel" if comb else "")
     if bound(s) == "hbm":
         rate = nbytes / (call_ns * 1e-9) / 1e9
         frac = rate / HBM_PEAK_GBS
@@ -685,8 +694,7 @@ def summarize_trace(trace_dir, name, command):
            "| kernel | calls | avg ns | min ns | max ns |", "|---|---|---|---|---|"]
     for n, c, a, mn, mx in sorted(rows, key=lambda r: -r[1] * r[2]):
         out.append(f"| `{n}` | {c} | {a:.0f} | {mn:.0f} | {mx:.0f} |")
-    out += ["", f"One call = `{attn[0][0] if attn else '?'}`" + (" + combine kernel" if comb else "") +
-            f": {call_ns:.0f} ns by the averages above.", work_line, ""]
+    out += ["", f"One call = {call_name}: {call_ns:.0f} ns by the averages above.", work_line, ""]
     path = os.path.join(ROOT, "profiles", f"{name}_kernel_stats.md")
     with open(path, "w") as f:
         f.write("\n".join(out))

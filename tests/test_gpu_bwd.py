@@ -2,11 +2,12 @@
 
 The forward runs on the GPU first (its o and lse feed the backward, as in
 training); the oracle's gradients come from the definition alone.  Bound:
-max |g - ref| <= TOL_REL * max |ref| per gradient, with TOL_REL = 2e-2 for
-bfloat16 and 4e-3 for float16 -- about five units of the type's rounding
-(2^-8, 2^-11): P and dS are rounded to the input type before their matrix
-products and each output once more, while the float32 accumulation adds
-far less.
+max |g - ref| <= TOL_REL * max |ref| per gradient, with TOL_REL = 1e-2 for
+bfloat16 and 1.25e-3 for float16 -- two and a half units of the type's
+rounding (u = 2^-8, 2^-11): P and dS are rounded to the input type before
+their matrix products (one unit each, relative to the largest gradient
+element) and each output once more, while the float32 accumulation adds far
+less.  The cases below measure at most 1.3 units.
 """
 
 import zlib
@@ -21,7 +22,7 @@ from scaled_dot_product_fwd_amd.synth import default_scale, make_qkv, randn
 
 pytestmark = pytest.mark.gpu
 
-TOL_REL = {torch.bfloat16: 2e-2, torch.float16: 4e-3}
+TOL_REL = {torch.bfloat16: 1e-2, torch.float16: 1.25e-3}
 
 
 def _say(*a):
@@ -53,7 +54,7 @@ def check_bwd(case, scale=None):
         scale_ref = max(float(np.abs(r).max()), 1e-30)
         e = float(np.abs(g - r).max()) / scale_ref
         errs.append(e)
-        assert e <= TOL_REL[dt], f"{name}: max|g - ref| / max|ref| = {e:.3e} > {TOL_REL[dt]:.0e}"
+        assert e <= TOL_REL[dt], f"{name}: max|g - ref| / max|ref| = {e:.3e} > {TOL_REL[dt]:.2e}"
     print("  rel errors dq dk dv", " ".join(f"{e:.2e}" for e in errs), flush=True)
 
 
@@ -158,7 +159,7 @@ def test_bwd_varlen(case):
         scale_ref = max(float(np.abs(r).max()), 1e-30)
         e = float(np.abs(g - r).max()) / scale_ref
         errs.append(e)
-        assert e <= TOL_REL[dt], f"{name}: max|g - ref| / max|ref| = {e:.3e} > {TOL_REL[dt]:.0e}"
+        assert e <= TOL_REL[dt], f"{name}: max|g - ref| / max|ref| = {e:.3e} > {TOL_REL[dt]:.2e}"
     print("  rel errors dq dk dv", " ".join(f"{e:.2e}" for e in errs), flush=True)
 
 
@@ -206,5 +207,5 @@ def test_bwd_mask_array(case):
         scale_ref = max(float(np.abs(r).max()), 1e-30)
         e = float(np.abs(g - r).max()) / scale_ref
         errs.append(e)
-        assert e <= TOL_REL[dt], f"{name}: max|g - ref| / max|ref| = {e:.3e} > {TOL_REL[dt]:.0e}"
+        assert e <= TOL_REL[dt], f"{name}: max|g - ref| / max|ref| = {e:.3e} > {TOL_REL[dt]:.2e}"
     print("  rel errors dq dk dv", " ".join(f"{e:.2e}" for e in errs), flush=True)
