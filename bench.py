@@ -433,8 +433,13 @@ def cpu_baseline(s, runner, budget_s=12.0):
     Whole KV groups (all query heads sharing one KV head) are run one after
     another until the time budget is spent; when even one group would blow the
     budget, evenly spaced query rows are recomputed one by one instead.  The
-    work done is scaled to the metric's unit.
+    work done is scaled to the metric's unit.  The oracle's results for the
+    sample are also compared with the GPU's output of the same inputs (the
+    runner's last call): ``max_abs_err`` holds max |gpu - oracle| over the
+    sample (o and lse; for the backward dQ, and dK, dV where one query head
+    is its KV head's whole gradient).
     """
+    import numpy as np
     from oracle import sdpa_bwd_ref, sdpa_ref, sdpa_ref_rows, sdpa_ref_varlen
 
     try:
@@ -447,6 +452,19 @@ def cpu_baseline(s, runner, budget_s=12.0):
     flops, nbytes = work(s)
     group_flops = flops / s["hkv"]
     t_total, frac, sample = 0.0, 0.0, ""
+    err = {}
+
+    def note(key, got, ref):
+        d = np.abs(np.asarray(got, dtype=np.float64) - ref)
+        # rows that see no key: lse = -inf on both sides counts as equal
+        d = np.where(np.isinf(ref) & (np.asarray(got, dtype=np.float64) == ref), 0.0, d)
+        err[key] = max(err.get(key, 0.0), float(d.max()) if d.size else 0.0)
+
+    if s.get("bwd"):
+        gq, gk, gv = (x.float().cpu().numpy() for x in runner.g)
+    else:
+        o_gpu = runner.o.float().cpu().numpy()
+        lse_gpu = runner.lse.cpu().numpy()
     if s.get("bwd"):
         # whole query heads (with their KV head) until the budget is spent
         do = runner.cpu[3]
@@ -455,9 +473,14 @@ def cpu_baseline(s, runner, budget_s=12.0):
         while time.perf_counter() - t_start < budget_s and heads < s["b"] * s["hq"]:
             bi, h = divmod(heads, s["hq"])
             t0 = time.perf_counter()
-            sdpa_bwd_ref(q[bi:bi + 1, h:h + 1], k[bi:bi + 1, h // g:h // g + 1], v[bi:bi + 1, h // g:h // g + 1],
-                         do[bi:bi + 1, h:h + 1], runner.scale, s["mask"], s["window"])
+            rq, rk, rv = sdpa_bwd_ref(q[bi:bi + 1, h:h + 1], k[bi:bi + 1, h // g:h // g + 1],
+                                      v[bi:bi + 1, h // g:h // g + 1], do[bi:bi + 1, h:h + 1], runner.scale,
+                                      s["mask"], s["window"])
             t_total += time.perf_counter() - t0
+            note("dq", gq[bi:bi + 1, h:h + 1], rq)
+            if g == 1:
+                note("dk", gk[bi:bi + 1, h:h + 1], rk)
+                note("dv", gv[bi:bi + 1, h:h + 1], rv)
             heads += 1
         frac = heads / (s["b"] * s["hq"])
         sample = f"{heads} query heads' gradients ({frac:.3f} of one step)"
@@ -469,12 +492,14 @@ def cpu_baseline(s, runner, budget_s=12.0):
             hs = slice(kvh * g, (kvh + 1) * g)
             t0 = time.perf_counter()
             if s.get("varlen"):
-                sdpa_ref_varlen(q[:, hs], k[:, kvh:kvh + 1], v[:, kvh:kvh + 1], runner.scale, s["mask"],
-                                s["window"], kv_lens=kv_lengths(s))
+                ro, rl = sdpa_ref_varlen(q[:, hs], k[:, kvh:kvh + 1], v[:, kvh:kvh + 1], runner.scale, s["mask"],
+                                         s["window"], kv_lens=kv_lengths(s))
             else:
-                sdpa_ref(q[:, hs], k[:, kvh:kvh + 1], v[:, kvh:kvh + 1], runner.scale, s["mask"], s["window"],
-                         mask_arr=runner.mask_cpu)
+                ro, rl = sdpa_ref(q[:, hs], k[:, kvh:kvh + 1], v[:, kvh:kvh + 1], runner.scale, s["mask"],
+                                  s["window"], mask_arr=runner.mask_cpu)
             t_total += time.perf_counter() - t0
+            note("o", o_gpu[:, hs], ro)
+            note("lse", lse_gpu[:, hs], rl)
             heads += g
         frac = heads / s["hq"]
         sample = f"{heads} query heads in whole KV groups ({frac:.2f} of one step)"
@@ -489,9 +514,12 @@ def cpu_baseline(s, runner, budget_s=12.0):
         for n0 in range(0, len(picks), 64):
             chunk = picks[n0:n0 + 64]
             t0 = time.perf_counter()
-            sdpa_ref_rows(q, k, v, runner.scale, s["mask"], s["window"], chunk, mask_arr=runner.mask_cpu,
-                          kv_lens=kv_lengths(s) if s.get("varlen") else None)
+            ro, rl = sdpa_ref_rows(q, k, v, runner.scale, s["mask"], s["window"], chunk, mask_arr=runner.mask_cpu,
+                                   kv_lens=kv_lengths(s) if s.get("varlen") else None)
             t_total += time.perf_counter() - t0
+            idx = tuple(np.array(chunk).T)
+            note("o", o_gpu[idx], ro)
+            note("lse", lse_gpu[idx], rl)
             for (_, _, i) in chunk:
                 done_flops += 2 * (s["dqk"] + s["dv"]) * row_visible(i, s)
             n += len(chunk)
@@ -506,7 +534,8 @@ def cpu_baseline(s, runner, budget_s=12.0):
         value, unit = flops / sec_per_step / 1e12, "TFLOP/s"
     return {"value": round(value, 6), "unit": unit, "cores": int(cores), "kind": "oracle",
             "cpu_model": cpu_model(),
-            "sample": f"{sample} of the same workload, float64 numpy, {t_total:.1f} s"}
+            "sample": f"{sample} of the same workload, float64 numpy, {t_total:.1f} s",
+            "max_abs_err": {k_: float(f"{e:.3g}") for k_, e in err.items()}}
 
 
 def cpu_model():
@@ -554,6 +583,43 @@ def traffic_from_profiles(name):
     if t.get("kernel_source_hash") != kernel_source_hash(name):
         return None
     return t.get("hbm_bytes_per_launch")
+
+
+def context_rates():
+    """What the part delivers to plain library code, beside the quoted peaks:
+    a device-to-device copy of 1 GiB (read + written bytes over its time) and
+    a 8192^3 bfloat16 matrix product through torch (hipBLASLt), each the
+    median of 20 runs after 3 warm-up, HIP events on the current stream.
+    Context only: the roofline fractions stay against the quoted peaks."""
+    import torch
+
+    def med(fn, n=20):
+        for _ in range(3):
+            fn()
+        ts = []
+        for _ in range(n):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            b.synchronize()
+            ts.append(a.elapsed_time(b))
+        return sorted(ts)[n // 2]
+
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    copy_ms = med(lambda: dst.copy_(src))
+    del src, dst
+    n = 8192
+    a = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+    b = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+    gemm_ms = med(lambda: torch.matmul(a, b))
+    del a, b
+    torch.cuda.empty_cache()
+    return {"copy_gbs": round(2 * (1 << 30) / (copy_ms * 1e-3) / 1e9, 1),
+            "gemm_bf16_tflops": round(2 * n ** 3 / (gemm_ms * 1e-3) / 1e12, 1),
+            "what": "1 GiB device copy (read + write bytes) and an 8192^3 bf16 torch.matmul (hipBLASLt), "
+                    "median of 20; context beside the quoted 8 TB/s and 2.5 PFLOP/s"}
 
 
 def calibration_copy(mib):
@@ -941,6 +1007,8 @@ def main():
     }
     if args.workload == DEFAULT and not args.no_prefill:
         line["prefill"] = prefill_report(args.steps, args.warmup, not args.no_cpu_baseline)
+    if args.workload == DEFAULT:
+        line["context"] = context_rates()
     if args.sweep:
         rows = []
         prefixes = [p for p in args.sweep_only.split(",") if p]

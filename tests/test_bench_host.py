@@ -108,3 +108,31 @@ def test_backward_workload_counts_five_products():
     f_bwd, _ = bench.work(s)
     assert f_bwd * 4 == f_fwd * 10  # 2 (3 Dqk + 2 Dv) vs 2 (Dqk + Dv) per pair at Dqk = Dv
     assert bench.bound(s) == "mfma"
+
+
+@pytest.mark.parametrize("budget", [5.0, 1e-12])
+def test_cpu_baseline_reports_the_error_of_the_sampled_rows(budget):
+    """The oracle sample of ``cpu_baseline`` doubles as a max-abs error check
+    against the runner's output: a stand-in runner whose output is the
+    oracle's with one element moved by 0.25 (and one lse by 0.5) must report
+    exactly those, on the whole-group path (budget 5 s) and the row-sampled
+    path (a budget too small for one group)."""
+    import types
+
+    import torch
+
+    from oracle import sdpa_ref
+    from scaled_dot_product_fwd_amd.synth import default_scale, make_qkv
+
+    s = bench.shape("tiny", 1, 4, 2, 6, 40, 16, 16, "f32", "causal", 0, 5)
+    q, k, v = make_qkv(1, 4, 2, 6, 40, 16, 16, torch.float32, 5)
+    scale = default_scale(16)
+    ro, rl = sdpa_ref(q, k, v, scale, "causal", 0)
+    o = torch.tensor(ro, dtype=torch.float32)
+    lse = torch.tensor(rl, dtype=torch.float32)
+    o[0, 1, 0, 3] += 0.25  # row 0 is picked by the row sampler too
+    lse[0, 2, 0] += 0.5
+    run = types.SimpleNamespace(cpu=(q, k, v), scale=scale, o=o, lse=lse, mask_cpu=None)
+    out = bench.cpu_baseline(s, run, budget_s=budget)
+    err = out["max_abs_err"]
+    assert abs(err["o"] - 0.25) < 1e-6 and abs(err["lse"] - 0.5) < 1e-6, err
