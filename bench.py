@@ -668,7 +668,7 @@ def summarize_pmc(fetch_dir, write_dir, name, copy_mib, commands):
     out = {"workload": name, "kernel_source_hash": kernel_source_hash(name), "commands": commands,
            "copy": {"kernel": "float32 dst = src * 1", "bytes_read": copy_bytes // 2,
                     "bytes_written": copy_bytes // 2}}
-    total = 0.0
+    total, comb_total, fetch_raw = 0.0, 0.0, 0.0
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         vals = per_kernel(d, counter)
         kname, kv = pick(vals, lambda k: "attn_fwd_kernel" in k and inst in k)
@@ -679,12 +679,31 @@ def summarize_pmc(fetch_dir, write_dir, name, copy_mib, commands):
         factor = (copy_bytes / 2) / (c_kib * 1024)
         out[counter] = {"attention_kib_per_dispatch": round(k_kib, 1), "dispatches": len(kv),
                         "copy_kib_per_dispatch": round(c_kib, 1), "scale": round(factor, 4)}
+        # the split combine of the same calls (partials read, output written)
+        comb = [v for k, v in vals.items() if "combine_kernel" in k]
+        if comb:
+            cb = max(comb, key=len)
+            out[counter]["combine_kib_per_dispatch"] = round(sum(cb) / len(cb), 1)
+            comb_total += sum(cb) / len(cb) * 1024 * factor
         out["kernel"] = kname
         total += k_kib * 1024 * factor
+        if counter == "FETCH_SIZE":
+            fetch_raw = k_kib * 1024
     s = SHAPES[name]
     out["hbm_bytes_per_launch"] = int(total)
     out["algorithmic_bytes_per_launch"] = work(s)[1]
     out["ratio_to_algorithmic"] = round(total / work(s)[1], 4)
+    if comb_total:
+        out["combine_hbm_bytes_per_launch"] = int(comb_total)
+        out["call_ratio_to_algorithmic"] = round((total + comb_total) / work(s)[1], 4)
+    # The copy calibrates the scale with ordinary loads.  The attention
+    # kernel loads K and V by LDS DMA; that the same scale holds for them
+    # follows from a lower bound: every K/V byte must be read at least once,
+    # so unscaled FETCH_SIZE below the K/V bytes means the counter sees the
+    # same fraction of these loads.
+    kv_bytes = 2 * s["b"] * s["hkv"] * s["lk"] * (s["dqk"] + s["dv"])
+    out["scale_check"] = {"fetch_unscaled_bytes": int(fetch_raw), "kv_bytes_read_at_least_once": kv_bytes,
+                          "unscaled_below_minimum": bool(fetch_raw < kv_bytes)}
     path = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
