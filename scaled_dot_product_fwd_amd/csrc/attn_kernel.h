@@ -166,6 +166,10 @@ struct Shape {
   static constexpr int NDT = DV / 32;          // 32-wide dv tiles
   static constexpr int NDTW = NDT / NWD;       // dv tiles one wave accumulates
   static constexpr int NQS = DQK / E::KQK;     // QK MFMAs per key tile
+  // With the dv split each wave of a pair also takes half of the QK
+  // product's depth (its Q columns), and the pair adds its partial scores
+  // through LDS: NQSW steps per wave.
+  static constexpr int NQSW = NQS / NWD;
   static constexpr int KCH = DQK * E::ES / 16; // 16-byte chunks per K row
   static constexpr int VCH = DV * E::ES / 16;  // 16-byte chunks per V row
   static constexpr int KROW = DQK * E::ES;
@@ -207,7 +211,11 @@ struct Shape {
   // more than they hold for the smallest head dims.
   static constexpr int MSLOTS = NWQ * (NWK - 1);
   static constexpr int MLB = (MSLOTS * 32 * 8 + 15) / 16 * 16;
-  static constexpr int LDS = cmax(2 * BUF + 2 * MBYTES, MLB + MSLOTS * 32 * (32 + 4) * 4);
+  // Partial-score exchange of the dv split: one 32 x 32 float32 tile per
+  // wave, stored chunk-major (chunk c of lane l at 1024 c + 16 l).
+  static constexpr int XOFF = 2 * BUF + 2 * MBYTES;
+  static constexpr int XBYTES = NWD > 1 ? NW * 4096 : 0;
+  static constexpr int LDS = cmax(XOFF + XBYTES, MLB + MSLOTS * 32 * (32 + 4) * 4);
   // Families that split the keys over waves (decode, short queries) have one
   // row tile per KV head in practice, so each K/V byte is read once per
   // launch: stream it past the caches.  Prefill row tiles re-read the same
@@ -241,6 +249,8 @@ struct Shape {
   static constexpr int MROW = TPR * 32 + 4;  // +4 floats skew the rows across banks
   static_assert(NWK == 1 || TPR >= 1, "merge scratch must fit the tile buffers");
   static_assert(NWD == 1 || (NWK == 1 && NDT % NWD == 0), "dv split: waves on rows only, whole dv tiles");
+  static_assert(NWD == 1 || (NWD == 2 && NKT == 1 && NQSW % (KG / 2) == 0),
+                "dv split: wave pairs, one key tile, whole K swizzle groups per half");
   static_assert(DMA_MAX <= 63, "vmcnt range");
   static_assert(BKW % 32 == 0, "BKW must be a multiple of 32");
   static_assert(DQK % E::KQK == 0 && DV % 32 == 0, "bad head-dim tile");
@@ -573,13 +583,14 @@ void attn_fwd_kernel(AttnArgs a) {
   }
 
   // ---- Q fragments (B operand of S^T = K Q^T), kept in registers ----
-  frag qf[S::NQS];
+  // (with the dv split, this wave's half of the head dim only)
+  frag qf[S::NQSW];
   {
     const char* qrow = (const char*)a.q +
                        ((int64_t)b * a.qs[0] + (int64_t)hq * a.qs[1] + (int64_t)iq * a.qs[2]) * E::ES;
 #pragma unroll
-    for (int s = 0; s < S::NQS; ++s) {
-      const int d = s * E::KQK + hl * E::EPL;
+    for (int s = 0; s < S::NQSW; ++s) {
+      const int d = (wd * S::NQSW + s) * E::KQK + hl * E::EPL;
       if constexpr (E::ES == 2) {
         u32x4 v = {0u, 0u, 0u, 0u};
         if (row_ok && d < a.dqk) v = *(const u32x4*)(qrow + (int64_t)d * 2);
@@ -602,7 +613,7 @@ void attn_fwd_kernel(AttnArgs a) {
     c = -c;
     sn = -sn;
 #pragma unroll
-    for (int s = 0; s < S::NQS; ++s) {
+    for (int s = 0; s < S::NQSW; ++s) {
       if constexpr (E::ES == 2) qf[s] ^= 0x80008000u;
       else qf[s] = -qf[s];
     }
@@ -610,7 +621,7 @@ void attn_fwd_kernel(AttnArgs a) {
     c = 1.f;
     sn = 1.f;
 #pragma unroll
-    for (int s = 0; s < S::NQS; ++s) {
+    for (int s = 0; s < S::NQSW; ++s) {
       if constexpr (E::ES == 2) qf[s] = u32x4{0u, 0u, 0u, 0u};
       else qf[s] = 0.f;
     }
@@ -630,7 +641,8 @@ void attn_fwd_kernel(AttnArgs a) {
   if constexpr (E::ES == 2) {
     const int xk = S::kx(col);
 #pragma unroll
-    for (int sl = 0; sl < SPG; ++sl) koffl[sl] = col * S::KROW + 16 * ((2 * sl + hl) ^ xk);
+    for (int sl = 0; sl < SPG; ++sl)
+      koffl[sl] = col * S::KROW + 16 * ((2 * sl + hl) ^ xk) + wd * (S::NQSW / SPG) * 16 * S::KG;
     const int g = lane >> 4, t16 = lane & 15;
     const int x = 2 * (g & 1) + ((t16 & 3) >> 1);
     const int y = S::vy(t16 >> 2);
@@ -663,19 +675,19 @@ void attn_fwd_kernel(AttnArgs a) {
       // Every K fragment of the block is read before the first product, so
       // the reads overlap each other instead of each product waiting for
       // its own.
-      frag kf[S::NKT][S::NQS];
+      frag kf[S::NKT][S::NQSW];
 #pragma unroll
       for (int kt = 0; kt < S::NKT; ++kt) {
         const SDPA_LDS char* ktile = kl + (wk * BKW + kt * 32) * S::KROW;
 #pragma unroll
-        for (int s = 0; s < S::NQS; ++s)
+        for (int s = 0; s < S::NQSW; ++s)
           kf[kt][s] = *(const SDPA_LDS u32x4*)(ktile + koffl[s % SPG] + 16 * S::KG * (s / SPG));
       }
 #pragma unroll
       for (int kt = 0; kt < S::NKT; ++kt) {
         sacc[kt] = f32x16{};
 #pragma unroll
-        for (int s = 0; s < S::NQS; ++s) sacc[kt] = E::mma(kf[kt][s], qf[s], sacc[kt]);
+        for (int s = 0; s < S::NQSW; ++s) sacc[kt] = E::mma(kf[kt][s], qf[s], sacc[kt]);
       }
       return;
     }
@@ -684,7 +696,7 @@ void attn_fwd_kernel(AttnArgs a) {
       sacc[kt] = f32x16{};
       const SDPA_LDS char* ktile = kl + (wk * BKW + kt * 32) * S::KROW;
 #pragma unroll
-      for (int s = 0; s < S::NQS; ++s) {
+      for (int s = 0; s < S::NQSW; ++s) {
         frag af;
         if constexpr (E::ES == 2) {
           // chunk (2 s + hl) ^ kx(row) of row col: 8 elements
@@ -910,6 +922,7 @@ void attn_fwd_kernel(AttnArgs a) {
     // overflow the 63-entry vector-memory counter, K waits for the end too
     // and part of block j + 1 lands first.)
     constexpr bool KEARLY = 2 * S::DMA_MAX <= 63;
+    static_assert(NWD == 1 || KEARLY, "the dv split's score exchange uses the barrier after QK");
     f32x16 sacc[S::NKT];
     bool live_prev = true;
     // A wave whose 32 rows all lie past the packed rows (a short query set
@@ -926,10 +939,34 @@ void attn_fwd_kernel(AttnArgs a) {
       if (MA == MA_BOOL && wave_rows && (!live_prev || (j & 3) == 0)) live = mask_live(j);
       live_prev = live;
       if (live) qk(j, sacc);
+      if constexpr (NWD > 1) {
+        // dv split: this wave's scores cover half of the head dim; leave
+        // them for the other wave of the pair (same rows, same keys, same
+        // register layout), whose half comes back after the barrier.
+        if (live) {
+          SDPA_LDS char* xw = smem + S::XOFF + wave * 4096 + lane * 16;
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            *(SDPA_LDS f32x4*)(xw + c * 1024) =
+                f32x4{sacc[0][4 * c], sacc[0][4 * c + 1], sacc[0][4 * c + 2], sacc[0][4 * c + 3]};
+        }
+      }
       if constexpr (KEARLY) {
-        if (j + 2 < nblk) {
-          __syncthreads();  // every wave is done with K(j)
-          dma_k(j + 2, j & 1);
+        if (NWD > 1 || j + 2 < nblk) {
+          __syncthreads();  // every wave is done with K(j) (and the partial scores are in LDS)
+          if (j + 2 < nblk) dma_k(j + 2, j & 1);
+        }
+      }
+      if constexpr (NWD > 1) {
+        if (live) {
+          // the same sum in both waves of the pair: a + b = b + a exactly
+          const SDPA_LDS char* xr = smem + S::XOFF + (wave ^ (NWQ * NWK)) * 4096 + lane * 16;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const f32x4 o = *(const SDPA_LDS f32x4*)(xr + c * 1024);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sacc[0][4 * c + i] += o[i];
+          }
         }
       }
       if (live) {
