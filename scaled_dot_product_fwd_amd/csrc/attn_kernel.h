@@ -584,8 +584,55 @@ void attn_fwd_kernel(AttnArgs a) {
 
   // ---- Q fragments (B operand of S^T = K Q^T), kept in registers ----
   // (with the dv split, this wave's half of the head dim only)
+  //
+  // The key-split families without a mask array (decode, short queries:
+  // bound by the K/V stream) bring Q in by LDS DMA as well, into the V half
+  // of buffer 1, which is idle until block 1's V loads.  The compiler waits
+  // for none of these loads, so K(1) can go in flight at once, next to
+  // block 0 and Q, instead of after them: the stream's first two blocks
+  // overlap (a split of one block has nothing to overlap and loads Q
+  // straight into registers).  Q rows of the tile: row-major, 16-byte
+  // chunks; rows past the entry's re-read its last one, chunks past the real
+  // head dim the row's last real chunk (both are zeroed below).
+  constexpr int QROWB = DQK * E::ES;
+  constexpr int QBYTES = S::BM * QROWB;
+  constexpr bool QDMA_OK = S::STREAM && MA == MA_NONE && E::ES == 2 && NWD == 1 && QBYTES <= S::VBYTES &&
+                           QBYTES % 1024 == 0;
+  const bool qdma = QDMA_OK && nblk > 1;  // uniform
   frag qf[S::NQSW];
-  {
+  if constexpr (QDMA_OK) {
+    if (qdma) {
+      constexpr int QCH = QROWB / 16, QI = QBYTES / 1024, QPW = (QI + S::NW - 1) / S::NW;
+      const int qch_valid = a.dqk * E::ES / 16;
+      const unsigned ql = lds_base + 2 * S::KBYTES + S::VBYTES;
+#pragma unroll
+      for (int ii = 0; ii < QPW; ++ii) {
+        const int ins = ii * S::NW + wave_u;
+        if ((ii + 1) * S::NW > QI && ins >= QI) continue;
+        const int slot = ins * 64 + lane;
+        const int rr = min(r_wg + slot / QCH, R - 1);
+        const int hr = kvh * a.G + rr % a.G;
+        const char* src = (const char*)a.q +
+                          ((int64_t)b * a.qs[0] + (int64_t)hr * a.qs[1] + (int64_t)(rr / a.G) * a.qs[2]) * E::ES +
+                          min(slot % QCH, qch_valid - 1) * 16;
+        lds_dma16<false>(src, ql + ins * 1024);
+      }
+      dma_k(1, 1);
+      // K(0), V(0) and Q have landed once no more than this wave's K(1) loads
+      // remain (its count rounded down: waves with one more wait for it too)
+      wait_vmcnt<S::KDMA / S::NW>();
+      __syncthreads();
+      const SDPA_LDS char* qt = smem + 2 * S::KBYTES + S::VBYTES + (wq * 32 + col) * QROWB;
+#pragma unroll
+      for (int s = 0; s < S::NQSW; ++s) {
+        const int d = s * E::KQK + hl * E::EPL;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (row_ok && d < a.dqk) v = *(const SDPA_LDS u32x4*)(qt + d * 2);
+        qf[s] = v;
+      }
+    }
+  }
+  if (!qdma) {
     const char* qrow = (const char*)a.q +
                        ((int64_t)b * a.qs[0] + (int64_t)hq * a.qs[1] + (int64_t)iq * a.qs[2]) * E::ES;
 #pragma unroll
@@ -601,6 +648,11 @@ void attn_fwd_kernel(AttnArgs a) {
         qf[s] = v;
       }
     }
+    // Block 0 and the Q loads must have landed.  Waiting for everything
+    // here also tells the compiler the Q loads are complete, so it puts no
+    // load wait of its own inside the loop (which would also stall on the
+    // DMA in flight there).
+    wait_vmcnt<0>();
   }
 
   // The loop below assumes a positive scale.  A negative one is folded into
@@ -657,12 +709,13 @@ void attn_fwd_kernel(AttnArgs a) {
   float m_ref = kNegInf;  // reference max of this row, log2 units (same in both lane halves)
   float l_run = 0.f;      // this lane's share of the row sum (halves add up at the end)
 
-  // Block 0 and the Q loads must have landed.  Waiting for everything here
-  // also tells the compiler the Q loads are complete, so it puts no load
-  // wait of its own inside the loop (which would also stall on the DMA in
-  // flight there).  Block 1 then goes in flight.
-  wait_vmcnt<0>();
-  if (nblk > 1) {
+  // Block 1 goes in flight once block 0 and Q have landed (waited for
+  // above).  With Q by DMA, K(1) is in flight already and V(1) follows once
+  // every wave has read its Q.
+  if (qdma) {
+    __syncthreads();  // every wave has its Q fragments: V buffer 1 is free
+    dma_v(1, 1);
+  } else if (nblk > 1) {
     dma_k(1, 1);
     dma_m(blk(1), 1);
     dma_v(1, 1);
