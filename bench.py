@@ -115,6 +115,9 @@ def all_shapes():
     out.append(shape("decode_d512_hkv8_lk16384", 1, 32, 8, 1, 16384, 512, 512, "bf16", "causal", 0, 8001))
     # backward pass, beside the forward of the same shape (causal_l4096_d128)
     out.append(shape("bwd_causal_l4096_d128", 1, 16, 16, 4096, 4096, 128, 128, "bf16", "causal", 0, 6001, bwd=True))
+    # the same layer with grouped queries (4 query heads per KV head)
+    out.append(shape("bwd_causal_gqa_l4096_d128", 1, 32, 8, 4096, 4096, 128, 128, "bf16", "causal", 0, 6003,
+                     bwd=True))
     # per-entry key lengths, beside the same lengths as a padding mask
     out.append(shape("decode_b8_hkv8_lk8192_d128", 8, 32, 8, 1, 8192, 128, 128, "bf16", "none", 0, 7000))
     out.append(shape("maskarr_pad_decode_b8_hkv8_lk8192_d128", 8, 32, 8, 1, 8192, 128, 128, "bf16", "none", 0,

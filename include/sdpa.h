@@ -108,8 +108,9 @@ typedef struct {
   float scale;     /* finite; any sign; 0 allowed */
   /* Plan overrides (0 = let the planner choose).  They select among the same
    * kernels, never a different code path.  num_splits forces the number of
-   * key splits (>= 1); row_tile forces the query rows per workgroup (32, 64
-   * or 128). */
+   * key splits (>= 1); for the backward it forces the number of row parts
+   * each dK/dV key tile is cut into (1..64).  row_tile forces the query rows
+   * per workgroup (32, 64 or 128). */
   int32_t num_splits;
   int32_t row_tile;
   /* Explicit mask array (sdpa_forward_masked only).  mask_array is a
@@ -209,8 +210,11 @@ int sdpa_forward_noalloc(const sdpa_desc_t* desc, const void* q, const void* k, 
  * input type (float16 or bfloat16), head dims up to 128, the causal and
  * window modes (a mask array goes through sdpa_backward_varlen).
  * Deterministic (no atomics).  Needs a
- * workspace of sdpa_backward_workspace_bytes() bytes (256-byte aligned).
- * Enqueues three kernels on `stream`. */
+ * workspace of sdpa_backward_workspace_bytes() bytes (256-byte aligned):
+ * per-row terms, plus float32 partial dK/dV when the plan cuts the dK/dV key
+ * tiles into row parts (grouped queries that leave too few tiles to fill the
+ * chip or balance a causal mask).  Enqueues three kernels on `stream`, four
+ * with row parts. */
 int sdpa_backward_workspace_bytes(const sdpa_desc_t* desc, size_t* bytes);
 int sdpa_backward(const sdpa_desc_t* desc, const void* q, const void* k, const void* v, const void* o,
                   const void* dout, const float* lse, void* dq, void* dk, void* dv, void* workspace,

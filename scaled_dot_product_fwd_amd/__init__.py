@@ -236,7 +236,7 @@ def forward(q, k, v, *, scale: Optional[float] = None, mask: str = "none", windo
 
 def backward(q, k, v, o, dout, lse, *, scale: Optional[float] = None, mask: str = "none",
              window_size: int = 0, attn_mask=None, q_lens=None, kv_lens=None, dq=None, dk=None, dv=None,
-             workspace=None, stream=None):
+             workspace=None, stream=None, kv_parts: int = 0):
     """Gradients ``(dq, dk, dv)`` of the fused forward on the current HIP device.
 
     ``q, k, v`` and ``scale``, ``mask``, ``window_size``, ``attn_mask``,
@@ -245,7 +245,8 @@ def backward(q, k, v, o, dout, lse, *, scale: Optional[float] = None, mask: str 
     upstream gradient, shaped and strided like ``o``.  The mask array is a
     constant (no gradient for it).  With per-batch lengths every gradient
     position past them is 0.  float16 / bfloat16, head dims up to 128.
-    Deterministic.
+    Deterministic.  ``kv_parts`` (0: the planner's choice) forces the number
+    of row parts each dK/dV key tile is cut into (``desc.num_splits``).
     """
     import torch
 
@@ -266,7 +267,7 @@ def backward(q, k, v, o, dout, lse, *, scale: Optional[float] = None, mask: str 
         kind, mstr = _mask_layout(attn_mask, q, b, hq, lq, k.shape[2])
     desc = make_desc(q.shape, k.shape, v.shape, dt, scale=scale, mask=mask, window_size=window_size,
                      q_stride=q.stride()[:3], k_stride=k.stride()[:3], v_stride=v.stride()[:3],
-                     o_stride=o.stride()[:3], mask_array=kind, mask_stride=mstr)
+                     o_stride=o.stride()[:3], mask_array=kind, mask_stride=mstr, num_splits=kv_parts)
     outs = []
     for name, given, like in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
         if given is None:

@@ -437,10 +437,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
   const int col = lane & 31, hl = lane >> 5;
   // Tile-major order, heaviest first: under a causal mask the first key
   // tiles are seen by the most queries, so every head's tile 0 goes out
-  // before any tile 1, and so on (see the dq kernel).
+  // before any tile 1, and so on (see the dq kernel).  With kv_parts > 1
+  // each (tile, head) is kv_parts workgroups, one per part of its rows.
   const int key_tiles = (a.Lk + 127) / 128;
-  const int Z = (int)(gridDim.x / key_tiles);
-  const int kti = (int)(blockIdx.x / Z);
+  const int P = a.kv_parts;
+  const int Z = (int)(gridDim.x / (key_tiles * P));
+  const int kti = (int)(blockIdx.x / (Z * P));
+  const int part = (int)(blockIdx.x / Z) % P;
   const int z = blockIdx.x % Z;
   const int b = z / a.Hkv, kvh = z % a.Hkv;
   const EntryLens en = entry_lens(a, b);
@@ -449,7 +452,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
   if (k_wg >= en.Lk || en.R == 0) {
     // No key of the tile is valid, or the entry has no queries (uniform,
     // before any barrier): every gradient of the tile's keys is 0.
-    if (key < a.Lk) {
+    if (key < a.Lk && P > 1) {
+      float* zp = a.ws_part + (((int64_t)part * Z + z) * a.Lk + key) * (a.dqk + a.dv);
+      for (int d = 4 * hl; d < a.dqk + a.dv; d += 8) *(f32x4*)(zp + d) = f32x4{0.f, 0.f, 0.f, 0.f};
+    } else if (key < a.Lk) {
       char* zk = (char*)a.grad_k + ((int64_t)b * a.ks[0] + (int64_t)kvh * a.ks[1] + (int64_t)key * a.ks[2]) * 2;
       char* zv = (char*)a.grad_v + ((int64_t)b * a.vs[0] + (int64_t)kvh * a.vs[1] + (int64_t)key * a.vs[2]) * 2;
       for (int d = 8 * hl; d < a.dqk; d += 16) *(u32x4*)(zk + d * 2) = u32x4{0u, 0u, 0u, 0u};
@@ -466,8 +472,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
     const int64_t i_hi = (int64_t)min(en.Lk - 1, k_wg + 127) + a.window - 1 - en.off;  // last query that sees it
     r_hi = min<int64_t>(en.R, i_hi < 0 ? 0 : (i_hi + 1) * a.G);
   }
-  const int jb0 = (int)(min<int64_t>(r_lo, en.R) / BQ);
-  const int nblk = r_hi > r_lo ? (int)((r_hi + BQ - 1) / BQ) - jb0 : 0;
+  int jb0 = (int)(min<int64_t>(r_lo, en.R) / BQ);
+  int nblk = r_hi > r_lo ? (int)((r_hi + BQ - 1) / BQ) - jb0 : 0;
+  if (P > 1) {
+    // this part's share of the blocks (possibly none: it then writes zeros)
+    const int lo = (int)((int64_t)nblk * part / P), hi = (int)((int64_t)nblk * (part + 1) / P);
+    jb0 += lo;
+    nblk = hi - lo;
+  }
 
   // K / V rows past the entry's keys re-read its last key (their P is 0)
   const char* kbase = (const char*)a.k + ((int64_t)b * a.ks[0] + (int64_t)kvh * a.ks[1]) * 2;
@@ -679,6 +691,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
   }
 
   if (key >= a.Lk) return;
+  if (P > 1) {
+    // partial sums of this part's rows, float32, dK before the scale
+    float* wp = a.ws_part + (((int64_t)part * Z + z) * a.Lk + key) * (a.dqk + a.dv);
+#pragma unroll
+    for (int t = 0; t < NDT; ++t) {
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int d = t * 32 + 8 * i4 + 4 * hl;
+        if (d < a.dqk)
+          *(f32x4*)(wp + d) = f32x4{dk[t][4 * i4], dk[t][4 * i4 + 1], dk[t][4 * i4 + 2], dk[t][4 * i4 + 3]};
+        if (d < a.dv)
+          *(f32x4*)(wp + a.dqk + d) =
+              f32x4{dv[t][4 * i4], dv[t][4 * i4 + 1], dv[t][4 * i4 + 2], dv[t][4 * i4 + 3]};
+      }
+    }
+    return;
+  }
   char* krow = (char*)a.grad_k + ((int64_t)b * a.ks[0] + (int64_t)kvh * a.ks[1] + (int64_t)key * a.ks[2]) * 2;
   char* vrow = (char*)a.grad_v + ((int64_t)b * a.vs[0] + (int64_t)kvh * a.vs[1] + (int64_t)key * a.vs[2]) * 2;
 #pragma unroll
@@ -702,6 +731,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
   }
 }
 
+// ---- dK, dV from the row parts: their float32 sums in part order ----
+// One thread per 4 consecutive columns of one key's [dK | dV] row (Dqk and Dv
+// are multiples of 8, so no group straddles the two).
+template <class E>
+__global__ __launch_bounds__(256) void bwd_kvsum_kernel(BwdArgs a) {
+  const int nc = (a.dqk + a.dv) / 4;
+  const int64_t per_z = (int64_t)a.Lk * nc;
+  const int64_t zn = (int64_t)a.B * a.Hkv;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= zn * per_z) return;
+  const int z = (int)(idx / per_z);
+  const int64_t rem = idx % per_z;
+  const int key = (int)(rem / nc), d = 4 * (int)(rem % nc);
+  const int b = z / a.Hkv, kvh = z % a.Hkv;
+  const float* src = a.ws_part + ((int64_t)z * a.Lk + key) * (a.dqk + a.dv) + d;
+  const int64_t pstride = zn * a.Lk * (a.dqk + a.dv);
+  f32x4 acc = *(const f32x4*)src;
+  for (int q = 1; q < a.kv_parts; ++q) acc += *(const f32x4*)(src + q * pstride);
+  u32x2 w;
+  if (d < a.dqk) {
+    w[0] = E::pack2(acc[0] * a.scale, acc[1] * a.scale);
+    w[1] = E::pack2(acc[2] * a.scale, acc[3] * a.scale);
+    char* krow = (char*)a.grad_k + ((int64_t)b * a.ks[0] + (int64_t)kvh * a.ks[1] + (int64_t)key * a.ks[2]) * 2;
+    *(u32x2*)(krow + d * 2) = w;
+  } else {
+    w[0] = E::pack2(acc[0], acc[1]);
+    w[1] = E::pack2(acc[2], acc[3]);
+    char* vrow = (char*)a.grad_v + ((int64_t)b * a.vs[0] + (int64_t)kvh * a.vs[1] + (int64_t)key * a.vs[2]) * 2;
+    *(u32x2*)(vrow + (d - a.dqk) * 2) = w;
+  }
+}
+
 template <class E, int D>
 int launch_bwd_dims(const BwdPlan& p, const BwdArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(bwd_prep_kernel<E>, dim3((unsigned)p.prep_grid), dim3(256), 0, s, a);
@@ -714,6 +775,8 @@ int launch_bwd_dims(const BwdPlan& p, const BwdArgs& a, hipStream_t s) {
     if (masked) hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, true>), dim3((unsigned)p.dkdv_grid), dim3(256), 0, s, a);
     else hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, false>), dim3((unsigned)p.dkdv_grid), dim3(256), 0, s, a);
   }
+  if (p.kv_parts > 1 && p.sum_grid > 0)
+    hipLaunchKernelGGL(bwd_kvsum_kernel<E>, dim3((unsigned)p.sum_grid), dim3(256), 0, s, a);
   return SDPA_OK;
 }
 

@@ -331,11 +331,43 @@ int make_bwd_plan(const sdpa_desc_t* d, BwdPlan* p, std::string* err) {
   p->Rp = (int)ceil_div(R, 32) * 32;
   p->prep_grid = ceil_div(Z * p->Rp, 16);  // 16 rows per 256-thread workgroup
   p->dq_grid = Z * ceil_div(R, 128);       // 128 packed rows per workgroup
-  p->dkdv_grid = Z * ceil_div(d->len_k, 128);  // 128 keys per workgroup
-  if (p->prep_grid > 0x7fffffffLL || p->dq_grid > 0x7fffffffLL || p->dkdv_grid > 0x7fffffffLL)
+  // dK/dV takes 128 keys per workgroup and walks every packed row that can
+  // see them.  Under grouped queries a key tile's rows span all G query
+  // heads, so there are G times fewer tiles, each G times longer; under a
+  // causal mask their lengths also fall from R rows (the first tile) to one
+  // tile's worth (the last), and the longest alone can outlast everything
+  // else.  The row range of each tile is then cut into kv_parts parts, each
+  // part a workgroup that writes float32 partial dK, dV; a last kernel adds
+  // the parts in order (deterministic).  Parts are added, in powers of two,
+  // while the tiles are too few to fill the chip or (causal) while the
+  // longest tile is longer than the chip's share of the total, and while
+  // each part keeps at least 8 blocks of 32 rows.  desc->num_splits > 0
+  // forces the count (1..64).
+  const int64_t key_tiles = ceil_div(d->len_k, 128);
+  const int64_t items = Z * key_tiles;
+  int parts = 1;
+  if (d->num_splits > 0) {
+    if (d->num_splits > 64)
+      return fail(err, SDPA_E_PLAN, "num_splits for the backward (row parts of each dK/dV key tile) must be 1..64");
+    parts = d->num_splits;
+  } else {
+    int64_t want = ceil_div(kTargetCUs, items);
+    if (fp.mask == MASK_CAUSAL) want = std::max<int64_t>(want, ceil_div(2 * kTargetCUs, Z * (key_tiles + 1)));
+    const int64_t nb_max = ceil_div(R, 32);  // 32-row blocks of the longest tile
+    while (parts < want && parts < 16 && 2 * parts * 8 <= nb_max) parts *= 2;
+  }
+  p->kv_parts = parts;
+  p->dkdv_grid = items * parts;
+  const int64_t dsum = d->dim_qk + d->dim_v;
+  p->sum_grid = parts > 1 ? ceil_div(Z * d->len_k * (dsum / 4), 256) : 0;
+  if (p->prep_grid > 0x7fffffffLL || p->dq_grid > 0x7fffffffLL || p->dkdv_grid > 0x7fffffffLL ||
+      p->sum_grid > 0x7fffffffLL)
     return fail(err, SDPA_E_SHAPE, "grid too large");
-  // [lse2][D] per (batch, KV head, packed row), then the query index per row
-  p->workspace = ((size_t)(2 * Z * p->Rp + p->Rp) * 4 + 255) / 256 * 256;
+  // [lse2][D] per (batch, KV head, packed row), then the query index per
+  // row, then (kv_parts > 1) the partial dK, dV
+  p->part_offset = ((size_t)(2 * Z * p->Rp + p->Rp) * 4 + 255) / 256 * 256;
+  const size_t part_bytes = parts > 1 ? (size_t)parts * Z * d->len_k * dsum * 4 : 0;
+  p->workspace = (p->part_offset + part_bytes + 255) / 256 * 256;
   return SDPA_OK;
 }
 

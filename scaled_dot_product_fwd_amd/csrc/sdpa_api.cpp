@@ -420,6 +420,8 @@ int sdpa_backward_varlen(const sdpa_desc_t* d, const void* q, const void* k, con
   a.ws_lse2 = static_cast<float*>(workspace);
   a.ws_d = a.ws_lse2 + zrp;
   a.ws_qi = reinterpret_cast<int*>(a.ws_d + zrp);
+  a.kv_parts = p.kv_parts;
+  a.ws_part = p.kv_parts > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + p.part_offset) : nullptr;
   rc = sdpa::launch_backward(p, a, stream, &err);
   if (rc != SDPA_OK) return set_error(rc, err);
   return ok();

@@ -232,6 +232,8 @@ struct BwdArgs {
   float* ws_lse2;     // [B*Hkv][Rp] lse in log2 units per packed row (+inf: row has no gradient)
   float* ws_d;        // [B*Hkv][Rp] D = dO . O per packed row
   int* ws_qi;         // [Rp] query index of packed row r (r / G)
+  float* ws_part;     // kv_parts > 1: [kv_parts][B*Hkv][Lk][dqk + dv] float32 partial dK (unscaled), dV
+  int kv_parts;       // row parts of each dK/dV key tile (1: the kernel writes dK, dV itself)
   const int* q_lens;  // nullable [B]: valid queries per batch entry
   const int* kv_lens; // nullable [B]: valid keys per batch entry
   const void* mask_arr;  // explicit mask array of the forward (ma != MA_NONE)
@@ -251,6 +253,9 @@ struct BwdPlan {
   int mask, window;   // canonical
   int Rp;             // packed rows rounded up to 32
   int64_t prep_grid, dq_grid, dkdv_grid;
+  int kv_parts;       // row parts per dK/dV key tile; > 1 adds the partial sums' kernel
+  int64_t sum_grid;   // workgroups of that kernel (0 when kv_parts == 1)
+  size_t part_offset; // byte offset of the partial dK/dV in the workspace
   size_t workspace;
 };
 

@@ -21,7 +21,7 @@ def test_visible_pairs_closed_form_matches_oracle_count(lq, lk, mask, w):
 
 def test_workload_table_matches_the_five_workloads():
     names = [s["name"] for s in bench.all_shapes()]
-    assert len(names) == 1 + 12 + 20 + 3 + 4 + 5 + 2 + 1 + 3
+    assert len(names) == 1 + 12 + 20 + 3 + 4 + 5 + 2 + 2 + 3
     assert bench.DEFAULT in names
     s = bench.SHAPES[bench.DEFAULT]
     assert (s["hq"], s["hkv"], s["lq"], s["lk"], s["dqk"], s["dv"], s["dtype"]) == (64, 8, 1, 32768, 192, 128, "bf16")

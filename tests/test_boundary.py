@@ -440,3 +440,28 @@ def test_backward_varlen_validates_before_any_launch():
     # the plain backward refuses a descriptor with a mask array
     msg = _status(sdpa.sdpa_backward, dm, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, 1 << 20, 0)
     assert msg.startswith("SDPA_E_MASK"), msg
+
+
+def _bwd_ws(hq, hkv, l, d, mask, parts=0):
+    desc = _desc(hq=hq, hkv=hkv, lq=l, lk=l, dqk=d, dv=d, mask=mask, num_splits=parts)
+    return sdpa.sdpa_backward_workspace_bytes(desc)
+
+
+def test_bwd_plan_row_parts():
+    """The dK/dV row parts show in the workspace: [lse2][D][query index]
+    rounded to 256 bytes, then parts x B*Hkv x Lk x (Dqk + Dv) float32."""
+    def base(hq, hkv, l):
+        z, rp = hkv, -(-(hq // hkv) * l // 32) * 32
+        return ((2 * z * rp + rp) * 4 + 255) // 256 * 256
+
+    # MHA causal L=4096 (512 key tiles, balanced by heaviest-first): no parts
+    assert _bwd_ws(16, 16, 4096, 128, "causal") == base(16, 16, 4096)
+    # GQA causal L=4096, Hkv=8 (256 tiles, the first 32x longer than the last): 2 parts
+    assert _bwd_ws(32, 8, 4096, 128, "causal") == base(32, 8, 4096) + 2 * 8 * 4096 * 256 * 4
+    # forced counts, and the limit
+    assert _bwd_ws(32, 8, 4096, 128, "causal", parts=1) == base(32, 8, 4096)
+    assert _bwd_ws(4, 2, 300, 64, "none", parts=5) == base(4, 2, 300) + 5 * 2 * 300 * 128 * 4
+    with pytest.raises(sdpa.SdpaError, match="row parts"):
+        _bwd_ws(4, 2, 300, 64, "none", parts=65)
+    # small shapes keep at least 8 row blocks per part: a 16-row tile gets none
+    assert _bwd_ws(4, 2, 16, 64, "causal") == base(4, 2, 16)

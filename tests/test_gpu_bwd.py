@@ -29,7 +29,7 @@ def _say(*a):
     print("CASE", *a, flush=True)
 
 
-def run_bwd(b, hq, hkv, lq, lk, dqk, dv, dt, mask, w, seed, scale=None):
+def run_bwd(b, hq, hkv, lq, lk, dqk, dv, dt, mask, w, seed, scale=None, kv_parts=0):
     q, k, v = make_qkv(b, hq, hkv, lq, lk, dqk, dv, dt, seed)
     do = randn((b, hq, lq, dv), seed + 3, dt)
     scale = default_scale(dqk) if scale is None else scale
@@ -38,16 +38,17 @@ def run_bwd(b, hq, hkv, lq, lk, dqk, dv, dt, mask, w, seed, scale=None):
     o, lse = sdpa.forward(qd, kd, vd, scale=scale, mask=mask, window_size=w, return_lse=True)
     grads = [torch.full_like(x, float("nan")) for x in (qd, kd, vd)]
     gq, gk, gv = sdpa.backward(qd, kd, vd, o, dod, lse, scale=scale, mask=mask, window_size=w,
-                               dq=grads[0], dk=grads[1], dv=grads[2])
+                               dq=grads[0], dk=grads[1], dv=grads[2], kv_parts=kv_parts)
     torch.cuda.synchronize()
     ref = sdpa_bwd_ref(q, k, v, do, scale, mask, w)
     return [g.cpu().double().numpy() for g in (gq, gk, gv)], ref
 
 
-def check_bwd(case, scale=None):
+def check_bwd(case, scale=None, kv_parts=0):
     b, hq, hkv, lq, lk, dqk, dv, dt, mask, w = case
     dt = {"bf16": torch.bfloat16, "f16": torch.float16}[dt]
-    got, ref = run_bwd(b, hq, hkv, lq, lk, dqk, dv, dt, mask, w, zlib.crc32(repr(case).encode()) % 10000, scale)
+    got, ref = run_bwd(b, hq, hkv, lq, lk, dqk, dv, dt, mask, w, zlib.crc32(repr(case).encode()) % 10000, scale,
+                       kv_parts)
     errs = []
     for name, g, r in zip(("dq", "dk", "dv"), got, ref):
         assert not np.isnan(g).any(), f"unwritten {name} elements"
@@ -89,6 +90,41 @@ def test_bwd_is_deterministic():
     _say("bwd determinism")
     a, _ = run_bwd(1, 4, 2, 150, 150, 64, 64, torch.bfloat16, "causal", 0, 5)
     b, _ = run_bwd(1, 4, 2, 150, 150, 64, 64, torch.bfloat16, "causal", 0, 5)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+
+
+# dK/dV key tiles cut into row parts (float32 partials summed by a last
+# kernel): forced counts, including more parts than a tile has row blocks
+# (empty parts write zeros), and the planner's own choice at a grouped-query
+# causal shape that gets parts.
+PARTS = [
+    (1, 8, 2, 300, 300, 64, 64, "bf16", "causal", 0),
+    (1, 4, 1, 200, 333, 128, 128, "f16", "none", 0),
+    (1, 4, 2, 260, 260, 96, 96, "bf16", "window", 70),
+    (2, 6, 2, 130, 200, 32, 48, "f16", "causal", 0),
+]
+
+
+@pytest.mark.parametrize("parts", [1, 2, 3, 5, 16])
+@pytest.mark.parametrize("case", PARTS, ids=lambda c: "-".join(str(x) for x in c))
+def test_bwd_row_parts(case, parts):
+    _say("bwd row parts", parts, case)
+    check_bwd(case, kv_parts=parts)
+
+
+def test_bwd_row_parts_auto_and_deterministic():
+    """B=1, Hq=16, Hkv=4, L=2048, D=64, causal: the planner cuts each dK/dV
+    key tile into row parts (64 tiles for 256 CUs); two runs agree bitwise."""
+    _say("bwd row parts auto")
+    d = sdpa.make_desc((1, 16, 2048, 64), (1, 4, 2048, 64), (1, 4, 2048, 64), sdpa.SDPA_BF16, mask="causal")
+    d1 = sdpa.make_desc((1, 16, 2048, 64), (1, 4, 2048, 64), (1, 4, 2048, 64), sdpa.SDPA_BF16, mask="causal",
+                        num_splits=1)
+    assert sdpa.sdpa_backward_workspace_bytes(d) > sdpa.sdpa_backward_workspace_bytes(d1)
+    case = (1, 16, 4, 2048, 2048, 64, 64, "bf16", "causal", 0)
+    check_bwd(case)
+    a, _ = run_bwd(1, 16, 4, 2048, 2048, 64, 64, torch.bfloat16, "causal", 0, 5)
+    b, _ = run_bwd(1, 16, 4, 2048, 2048, 64, 64, torch.bfloat16, "causal", 0, 5)
     for x, y in zip(a, b):
         np.testing.assert_array_equal(x, y)
 
