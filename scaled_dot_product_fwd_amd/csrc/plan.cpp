@@ -59,9 +59,11 @@ const char* mask_name(int m) {
 size_t attn_lds_bytes(int dtype, int dqk_pad, int dv_pad, const Family& f, int mes) {
   // Mirrors Shape<> in attn_kernel.h: two K, two V and (with a mask array)
   // two mask tile buffers, which the cross-wave merge reuses (with a little
-  // more for the smallest dims).
+  // more for the smallest dims); with the dv split, a 4 KB score-exchange
+  // tile per wave after them.
   const int es = dtype == SDPA_F32 ? 4 : 2;
-  const size_t tiles = (size_t)2 * f.nwk * f.bkw * ((dqk_pad + dv_pad) * es + 32 * f.nwq * mes);
+  const size_t tiles = (size_t)2 * f.nwk * f.bkw * ((dqk_pad + dv_pad) * es + 32 * f.nwq * mes) +
+                       (f.nwd > 1 ? (size_t)f.nwq * f.nwk * f.nwd * 4096 : 0);
   const size_t slots = (size_t)f.nwq * (f.nwk - 1);
   const size_t merge = (slots * 32 * 8 + 15) / 16 * 16 + slots * 32 * (32 + 4) * 4;
   return std::max(tiles, merge);
