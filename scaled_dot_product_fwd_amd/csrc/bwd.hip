@@ -197,7 +197,12 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
 template <class E, int D, bool MASKED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void bwd_dq_kernel(BwdArgs a) {
   using T = Tile<D>;
-  constexpr int BK = D <= 64 ? 64 : 32;  // keys per block
+  // keys per block: 64 while two key tiles' scores fit the registers (head
+  // dims up to 96: 228 VGPRs at 96); at 128 they would spill into the
+  // accumulation registers (causal L=4096 backward 422 -> 433 us, grouped
+  // queries 739 -> 816 us), while at 96 the longer block saves a barrier per
+  // 32 keys (L=2048 D=96 173 -> 168 us)
+  constexpr int BK = D <= 96 ? 64 : 32;
   constexpr int NKT = BK / 32;
   constexpr int NQS = D / 16;
   constexpr int NDT = D / 32;
