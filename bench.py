@@ -800,6 +800,7 @@ COUNTER_NOTES = {
     "SQ_VALU_MFMA_BUSY_CYCLES": "cycles the matrix cores are busy, summed over SIMDs",
     "SQ_BUSY_CYCLES": "cycles the SQs are busy",
     "SQ_WAVE_CYCLES": "wave-resident cycles (quad-cycle units)",
+    "SQ_WAIT_ANY": "wave cycles waiting for anything: counters, barriers, dependencies (quad-cycles)",
     "SQ_WAIT_INST_ANY": "wave cycles waiting for any instruction's dependencies (quad-cycles)",
     "SQ_ACTIVE_INST_VALU": "wave cycles issuing VALU (quad-cycles)",
     "SQ_ACTIVE_INST_LDS": "wave cycles issuing LDS (quad-cycles)",
