@@ -291,6 +291,21 @@ int make_plan(const sdpa_desc_t* d, Plan* p, std::string* err) {
   // nor for a single round of window tiles.
   p->xcd_group = ((splits > 1 && row_tiles > 1) ||
                   (mask == MASK_WINDOW && base * splits >= 4 * (int64_t)kTargetCUs)) ? 8 : 0;
+  // Unmasked prefill without a split: every row tile of a KV head reads the
+  // whole of its K/V, so the tiles of one head go to one XCD (the largest
+  // group size that divides the head's tiles and tiles the grid exactly) and
+  // that head's K/V stays in one L2 instead of passing through all eight.
+  // Measured, interleaved on one box: H=16, L=4096, D=72 (32 tiles per head)
+  // 114-122 -> 112-114 us; H=20, L=1500, D=64 (12 tiles, groups of 6)
+  // 27.2-28.2 -> 25.8-27.7 us.
+  if (mask == MASK_NONE && ma == MA_NONE && splits == 1 && row_tiles > 1) {
+    for (int64_t g = row_tiles; g >= 1; --g) {
+      if (row_tiles % g == 0 && base % (8 * g) == 0) {
+        p->xcd_group = (int)g;
+        break;
+      }
+    }
+  }
   // One row tile per KV head and a multiple of 8 heads: all splits of a head
   // run on one XCD, and the combine takes that head's rows on the same XCD,
   // so the partials it reads were written through its own L2.

@@ -244,6 +244,14 @@ def test_plan_xcd_grouping():
     assert p["splits"] == "1" and p["xcd_group"] == "8"
     p = _plan(hq=16, hkv=2, lq=32768, lk=32768, dqk=256, dv=256, mask="causal")
     assert p["xcd_group"] == "0"
+    # unmasked prefill: the row tiles of one head in one group (the largest
+    # divisor of the tiles per head that tiles the grid in groups of 8)
+    p = _plan(hq=16, hkv=16, lq=4096, lk=4096, dqk=72, dv=72)
+    assert p["row_tiles"] == "32" and p["grid"] == "512" and p["xcd_group"] == "32"
+    p = _plan(hq=20, hkv=20, lq=1500, lk=1500, dqk=64, dv=64)
+    assert p["row_tiles"] == "12" and p["grid"] == "240" and p["xcd_group"] == "6"
+    p = _plan(hq=13, hkv=13, lq=1500, lk=1500, dqk=64, dv=64)  # 156 tiles: no group of 8 fits
+    assert p["splits"] == "1" and p["xcd_group"] == "0"
 
 
 def test_split_rows_beyond_one_grid_fall_back_to_unsplit():

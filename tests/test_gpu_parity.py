@@ -366,6 +366,21 @@ def test_window_tiles_grouped_by_xcd_full_parity():
     check_full(2, 32, 32, 2048, 2048, 32, 32, "bf16", "window", 300, seed=93)
 
 
+def test_unmasked_prefill_tiles_grouped_by_xcd_full_parity():
+    # 16 heads x 16 row tiles of 64 rows = 256 workgroups: the tiles of each
+    # head run as one group on one XCD (xcd_group = 16); every element is checked
+    desc = sdpa.make_desc((1, 16, 1024, 64), (1, 16, 1024, 64), (1, 16, 1024, 64), sdpa.SDPA_BF16)
+    plan = dict(tok.split("=", 1) for tok in sdpa.sdpa_describe_plan(desc).split())
+    assert plan["xcd_group"] == "16" and plan["grid"] == "256" and plan["splits"] == "1", plan
+    _say("unmasked prefill tiles grouped by XCD, full parity")
+    check_full(1, 16, 16, 1024, 1024, 64, 64, "bf16", "none", 0, seed=94)
+    # 12 heads x 12 tiles of 128 rows in groups of 6 (the encoder arrangement)
+    desc = sdpa.make_desc((1, 12, 1500, 64), (1, 12, 1500, 64), (1, 12, 1500, 64), sdpa.SDPA_F16)
+    plan = dict(tok.split("=", 1) for tok in sdpa.sdpa_describe_plan(desc).split())
+    assert plan["row_tiles"] == "12" and plan["xcd_group"] == "6" and plan["splits"] == "1", plan
+    check_full(1, 12, 12, 1500, 1500, 64, 64, "f16", "none", 0, seed=95)
+
+
 def test_forced_256_row_tiles_on_a_long_prefill():
     _say("row_tile 256 prefill")
     check_full(1, 4, 2, 300, 300, 128, 128, "bf16", "causal", 0, seed=3, row_tile=256)
