@@ -13,9 +13,11 @@ t is the median device time of one call (attention kernel plus the split
 combine, HIP events on the launch stream) over 40 calls after 10 warm-up
 calls, the K/V set rotating over copies that together exceed three times the
 256 MB Infinity Cache, so every call streams K/V from HBM as in the bench.
-The sweep runs twice and each length keeps the smaller median, so a
-transient slowdown of the device during one pass does not decide a ratio.
-Collected after the parity tests: a timing failure cannot hide them.
+The lengths are interleaved (each round calls every length once), so a drift
+of the device's clock or memory state over the run shifts every length
+alike instead of deciding a ratio between two lengths timed minutes apart.
+The sweep runs twice and each length keeps the smaller median.  Collected
+after the parity tests: a timing failure cannot hide them.
 """
 
 import math
@@ -39,20 +41,24 @@ def _verify_times(lk):
     nsets = math.ceil(3 * bench.INFINITY_CACHE / (2 * k.numel() * k.element_size()))
     ks = [k] + [k.clone() for _ in range(nsets - 1)]
     vs = [v] + [v.clone() for _ in range(nsets - 1)]
-    ev = bench.HipEvents(40)
+    qs = {lq: randn((1, 32, lq, 128), 3102 + lq, torch.float16).to(dev) for lq in LQS}
+    os_ = {lq: torch.empty((1, 32, lq, 128), dtype=torch.float16, device=dev) for lq in LQS}
+    ev = bench.HipEvents(40 * len(LQS))
     times = {}
     try:
-        for _ in range(2):
-            for lq in LQS:
-                print("CASE nocliff", lk, lq, flush=True)
-                q = randn((1, 32, lq, 128), 3102 + lq, torch.float16).to(dev)
-                o = torch.empty((1, 32, lq, 128), dtype=torch.float16, device=dev)
-                for i in range(50):
+        for p in range(2):
+            print("CASE nocliff", lk, "pass", p, flush=True)
+            n = 0
+            for i in range(50):
+                for j, lq in enumerate(LQS):
                     if i >= 10:
-                        sdpa.sdpa_set_profile_events(ev.start[i - 10], ev.stop[i - 10])
-                    sdpa.forward(q, ks[i % nsets], vs[i % nsets], scale=default_scale(128), out=o)
-                torch.cuda.synchronize()
-                t = sorted(ev.elapsed_ms(n) * 1e3 for n in range(40))
+                        e = (i - 10) * len(LQS) + j
+                        sdpa.sdpa_set_profile_events(ev.start[e], ev.stop[e])
+                    sdpa.forward(qs[lq], ks[n % nsets], vs[n % nsets], scale=default_scale(128), out=os_[lq])
+                    n += 1
+            torch.cuda.synchronize()
+            for j, lq in enumerate(LQS):
+                t = sorted(ev.elapsed_ms(r * len(LQS) + j) * 1e3 for r in range(40))
                 times[lq] = min(times.get(lq, float("inf")), t[20])
     finally:
         ev.close()
