@@ -24,8 +24,15 @@
 //              the Q and dO tiles.  Packed rows cover all G query heads of
 //              the KV head, so grouped-query sums come out of the loop.
 // Tiles move by the same 16-byte LDS DMA as the forward (counted waits).
+//
+// bwd_dq and bwd_dkdv only read what bwd_prep wrote and write disjoint
+// outputs, so dQ runs on a second stream of the library's own beside dK/dV
+// (fork after the prep, join before the call returns to the caller's
+// stream).  One dK/dV workgroup (99 KB of LDS) and one dQ workgroup (32 KB)
+// then share a CU, two waves per SIMD where each kernel alone leaves one.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
 #include <string>
 
 #include "attn_kernel.h"
@@ -768,40 +775,101 @@ __global__ __launch_bounds__(256) void bwd_kvsum_kernel(BwdArgs a) {
   }
 }
 
+// The dQ kernel's stream: `s2` with the fork and join events, or s2 = null
+// for one stream (the caller's) throughout.
+struct DqStream {
+  hipStream_t s2 = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+
 template <class E, int D>
-int launch_bwd_dims(const BwdPlan& p, const BwdArgs& a, hipStream_t s) {
+int launch_bwd_dims(const BwdPlan& p, const BwdArgs& a, hipStream_t s, const DqStream& ds) {
   hipLaunchKernelGGL(bwd_prep_kernel<E>, dim3((unsigned)p.prep_grid), dim3(256), 0, s, a);
   const bool masked = a.ma != MA_NONE;
-  if (p.dq_grid > 0) {
-    if (masked) hipLaunchKernelGGL((bwd_dq_kernel<E, D, true>), dim3((unsigned)p.dq_grid), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((bwd_dq_kernel<E, D, false>), dim3((unsigned)p.dq_grid), dim3(256), 0, s, a);
+  hipStream_t sq = s;
+  if (ds.s2 && p.dq_grid > 0 && p.dkdv_grid > 0) {
+    if (hipEventRecord(ds.fork, s) != hipSuccess || hipStreamWaitEvent(ds.s2, ds.fork, 0) != hipSuccess)
+      return SDPA_E_HIP;
+    sq = ds.s2;
   }
+  if (p.dq_grid > 0) {
+    if (masked) hipLaunchKernelGGL((bwd_dq_kernel<E, D, true>), dim3((unsigned)p.dq_grid), dim3(256), 0, sq, a);
+    else hipLaunchKernelGGL((bwd_dq_kernel<E, D, false>), dim3((unsigned)p.dq_grid), dim3(256), 0, sq, a);
+  }
+  if (sq != s && hipEventRecord(ds.join, sq) != hipSuccess) return SDPA_E_HIP;
   if (p.dkdv_grid > 0) {
     if (masked) hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, true>), dim3((unsigned)p.dkdv_grid), dim3(256), 0, s, a);
     else hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, false>), dim3((unsigned)p.dkdv_grid), dim3(256), 0, s, a);
   }
   if (p.kv_parts > 1 && p.sum_grid > 0)
     hipLaunchKernelGGL(bwd_kvsum_kernel<E>, dim3((unsigned)p.sum_grid), dim3(256), 0, s, a);
+  if (sq != s && hipStreamWaitEvent(s, ds.join, 0) != hipSuccess) return SDPA_E_HIP;
   return SDPA_OK;
 }
 
 template <class E>
-int launch_bwd_type(const BwdPlan& p, const BwdArgs& a, hipStream_t s) {
+int launch_bwd_type(const BwdPlan& p, const BwdArgs& a, hipStream_t s, const DqStream& ds) {
   switch (p.d_pad) {
-    case 32: return launch_bwd_dims<E, 32>(p, a, s);
-    case 64: return launch_bwd_dims<E, 64>(p, a, s);
-    case 96: return launch_bwd_dims<E, 96>(p, a, s);
-    case 128: return launch_bwd_dims<E, 128>(p, a, s);
+    case 32: return launch_bwd_dims<E, 32>(p, a, s, ds);
+    case 64: return launch_bwd_dims<E, 64>(p, a, s, ds);
+    case 96: return launch_bwd_dims<E, 96>(p, a, s, ds);
+    case 128: return launch_bwd_dims<E, 128>(p, a, s, ds);
     default: return SDPA_E_HEAD_DIM;
   }
 }
 
 }  // namespace dev
 
+namespace {
+
+// One dQ stream (default priority, non-blocking) and its two events per
+// device, made on the first backward call on that device outside a graph
+// capture and kept until the process ends.  Where they cannot be made, or
+// the first call comes under capture, the call runs on the caller's stream
+// alone.  The mutex spans the enqueue of a whole call, so concurrent callers
+// cannot interleave their records and waits on the shared events.
+constexpr int kMaxDevices = 64;
+std::mutex g_dq_mu;
+int g_dq_state[kMaxDevices] = {0};  // 0 not made yet, 1 ready, -1 unavailable
+dev::DqStream g_dq[kMaxDevices];
+
+void make_dq_stream(int d) {
+  dev::DqStream ds;
+  if (hipStreamCreateWithFlags(&ds.s2, hipStreamNonBlocking) == hipSuccess &&
+      hipEventCreateWithFlags(&ds.fork, hipEventDisableTiming) == hipSuccess &&
+      hipEventCreateWithFlags(&ds.join, hipEventDisableTiming) == hipSuccess) {
+    g_dq[d] = ds;
+    g_dq_state[d] = 1;
+    return;
+  }
+  if (ds.join) (void)hipEventDestroy(ds.join);
+  if (ds.fork) (void)hipEventDestroy(ds.fork);
+  if (ds.s2) (void)hipStreamDestroy(ds.s2);
+  (void)hipGetLastError();  // the failure is handled: one stream
+  g_dq_state[d] = -1;
+}
+
+}  // namespace
+
 int launch_backward(const BwdPlan& p, const BwdArgs& a, void* stream, std::string* err) {
   const hipStream_t s = (hipStream_t)stream;
-  const int rc = p.dtype == SDPA_BF16 ? dev::launch_bwd_type<dev::BF16>(p, a, s)
-                                      : dev::launch_bwd_type<dev::F16>(p, a, s);
+  int d = -1;
+  std::lock_guard<std::mutex> lock(g_dq_mu);
+  dev::DqStream ds;
+  if (hipGetDevice(&d) == hipSuccess && d >= 0 && d < kMaxDevices) {
+    if (g_dq_state[d] == 0) {
+      hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+      if (hipStreamIsCapturing(s, &cs) == hipSuccess && cs == hipStreamCaptureStatusNone) make_dq_stream(d);
+      (void)hipGetLastError();
+    }
+    if (g_dq_state[d] == 1) ds = g_dq[d];
+  }
+  const int rc = p.dtype == SDPA_BF16 ? dev::launch_bwd_type<dev::BF16>(p, a, s, ds)
+                                      : dev::launch_bwd_type<dev::F16>(p, a, s, ds);
+  if (rc == SDPA_E_HIP) {
+    *err = std::string("backward stream fork/join failed: ") + hipGetErrorString(hipGetLastError());
+    return rc;
+  }
   if (rc != SDPA_OK) {
     *err = "no backward kernel for padded head dim " + std::to_string(p.d_pad);
     return rc;
