@@ -751,13 +751,21 @@ def summarize_trace(trace_dir, name, command):
             rows.append((r["Name"], int(r["Calls"]), float(r["AverageNs"]), float(r["MinNs"]), float(r["MaxNs"])))
     flops, nbytes = work(s)
     plan, inst = instance_of(s)
+    span_line = ""
     if s.get("bwd"):
         # a backward call is the prep, dQ and dK/dV kernels (the forward that
-        # produces o and lse runs once, outside the timed calls)
+        # produces o and lse runs once, outside the timed calls); dQ and dK/dV
+        # overlap on two streams, so the call is the span from the prep's
+        # start to the last of the call's kernels to end, per call in the trace
         parts = [[r for r in rows if k in r[0]] for k in ("bwd_prep_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel")]
-        call_ns = sum(p[0][2] for p in parts if p)
         call_name = " + ".join(f"`{p[0][0]}`" for p in parts if p)
-        plan = "backward: bwd_prep, then bwd_dq (128-row tiles) and bwd_dkdv (128-key tiles)"
+        spans = bwd_call_spans(trace_dir)
+        call_ns = sum(spans) / len(spans) if spans else sum(p[0][2] for p in parts if p)
+        span_line = (f"Call spans (prep start to the last kernel's end, {len(spans)} calls): mean {call_ns:.0f} ns, "
+                     f"min {min(spans):.0f} ns; the kernels' averages add up to "
+                     f"{sum(p[0][2] for p in parts if p):.0f} ns because dQ and dK/dV overlap.") if spans else ""
+        plan = ("backward: bwd_prep, then bwd_dq (128-row tiles, second stream) beside bwd_dkdv "
+                "(128-key tiles)")
     else:
         # the workload's own instance (a default run also times the prefill workloads)
         attn = [r for r in rows if "attn_fwd_kernel" in r[0] and inst in r[0]]
@@ -782,11 +790,42 @@ def summarize_trace(trace_dir, name, command):
            "| kernel | calls | avg ns | min ns | max ns |", "|---|---|---|---|---|"]
     for n, c, a, mn, mx in sorted(rows, key=lambda r: -r[1] * r[2]):
         out.append(f"| `{n}` | {c} | {a:.0f} | {mn:.0f} | {mx:.0f} |")
-    out += ["", f"One call = {call_name}: {call_ns:.0f} ns by the averages above.", work_line, ""]
+    how = "by the call spans below" if span_line else "by the averages above"
+    out += ["", f"One call = {call_name}: {call_ns:.0f} ns {how}.", work_line]
+    out += ([span_line, ""] if span_line else [""])
     path = os.path.join(ROOT, "profiles", f"{name}_kernel_stats.md")
     with open(path, "w") as f:
         f.write("\n".join(out))
     print("\n".join(out))
+
+
+def bwd_call_spans(trace_dir):
+    """Per backward call in a ``--kernel-trace`` run: the time from the start
+    of its bwd_prep kernel to the end of the last bwd_* kernel dispatched
+    before the next call's prep (ns)."""
+    import csv
+    import glob
+
+    files = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        return []
+    ev = []
+    with open(files[0]) as fh:
+        for r in csv.DictReader(fh):
+            if "sdpa::dev::bwd_" in r["Kernel_Name"]:
+                ev.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), "bwd_prep_kernel" in r["Kernel_Name"]))
+    ev.sort()
+    spans, start, end = [], None, None
+    for t0, t1, is_prep in ev:
+        if is_prep:
+            if start is not None:
+                spans.append(end - start)
+            start, end = t0, t1
+        elif start is not None:
+            end = max(end, t1)
+    if start is not None:
+        spans.append(end - start)
+    return spans
 
 
 # SQ counters of the counter summaries, and what they show.

@@ -136,3 +136,19 @@ def test_cpu_baseline_reports_the_error_of_the_sampled_rows(budget):
     out = bench.cpu_baseline(s, run, budget_s=budget)
     err = out["max_abs_err"]
     assert abs(err["o"] - 0.25) < 1e-6 and abs(err["lse"] - 0.5) < 1e-6, err
+
+
+def test_backward_call_spans_from_a_kernel_trace(tmp_path):
+    # two calls whose dQ and dK/dV kernels overlap; a forward kernel between
+    # them is not part of either call
+    rows = [("void sdpa::dev::bwd_prep_kernel<sdpa::dev::BF16>(sdpa::BwdArgs)", 100, 110),
+            ("void sdpa::dev::bwd_dkdv_kernel<sdpa::dev::BF16, 128, false>(sdpa::BwdArgs)", 112, 400),
+            ("void sdpa::dev::bwd_dq_kernel<sdpa::dev::BF16, 128, false>(sdpa::BwdArgs)", 111, 350),
+            ("void sdpa::dev::attn_fwd_kernel<sdpa::dev::BF16, 128, 128, 4, 1, 64, 2, 0, 1>(sdpa::AttnArgs)", 401, 900),
+            ("void sdpa::dev::bwd_prep_kernel<sdpa::dev::BF16>(sdpa::BwdArgs)", 1000, 1010),
+            ("void sdpa::dev::bwd_dq_kernel<sdpa::dev::BF16, 128, false>(sdpa::BwdArgs)", 1011, 1500),
+            ("void sdpa::dev::bwd_dkdv_kernel<sdpa::dev::BF16, 128, false>(sdpa::BwdArgs)", 1012, 1300)]
+    lines = ['"Kind","Kernel_Name","Start_Timestamp","End_Timestamp"']
+    lines += [f'"KERNEL_DISPATCH","{n}",{a},{b}' for n, a, b in rows]
+    (tmp_path / "run_kernel_trace.csv").write_text("\n".join(lines) + "\n")
+    assert bench.bwd_call_spans(str(tmp_path)) == [300, 500]
