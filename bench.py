@@ -757,7 +757,8 @@ def summarize_trace(trace_dir, name, command):
         # produces o and lse runs once, outside the timed calls); dQ and dK/dV
         # overlap on two streams, so the call is the span from the prep's
         # start to the last of the call's kernels to end, per call in the trace
-        parts = [[r for r in rows if k in r[0]] for k in ("bwd_prep_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel")]
+        parts = [[r for r in rows if k in r[0]]
+                 for k in ("bwd_prep_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel", "bwd_kvsum_kernel")]
         call_name = " + ".join(f"`{p[0][0]}`" for p in parts if p)
         spans = bwd_call_spans(trace_dir)
         call_ns = sum(spans) / len(spans) if spans else sum(p[0][2] for p in parts if p)
@@ -775,12 +776,12 @@ def summarize_trace(trace_dir, name, command):
     if bound(s) == "hbm":
         rate = nbytes / (call_ns * 1e-9) / 1e9
         frac = rate / HBM_PEAK_GBS
-        work_line = f"Algorithmic bytes per call: {nbytes:,} B; by rocprof's averages {rate:.0f} GB/s = {100 * frac:.1f}% of 8 TB/s."
+        work_line = f"Algorithmic bytes per call: {nbytes:,} B; by rocprof {rate:.0f} GB/s = {100 * frac:.1f}% of 8 TB/s."
     else:
         peak = FP32_PEAK_TFLOPS if s["dtype"] == "f32" else MFMA16_PEAK_TFLOPS
         rate = flops / (call_ns * 1e-9) / 1e12
         frac = rate / peak
-        work_line = (f"Algorithmic flops per call: {flops:,}; by rocprof's averages {rate:.1f} TFLOP/s = "
+        work_line = (f"Algorithmic flops per call: {flops:,}; by rocprof {rate:.1f} TFLOP/s = "
                      f"{100 * frac:.1f}% of {peak:.0f} TFLOP/s.")
     out = [f"# Kernel trace: {name}", "",
            f"B={s['b']} Hq={s['hq']} Hkv={s['hkv']} Lq={s['lq']} Lk={s['lk']} Dqk={s['dqk']} Dv={s['dv']} "
