@@ -213,8 +213,14 @@ int sdpa_forward_noalloc(const sdpa_desc_t* desc, const void* q, const void* k, 
  * workspace of sdpa_backward_workspace_bytes() bytes (256-byte aligned):
  * per-row terms, plus float32 partial dK/dV when the plan cuts the dK/dV key
  * tiles into row parts (grouped queries that leave too few tiles to fill the
- * chip or balance a causal mask).  Enqueues three kernels on `stream`, four
- * with row parts. */
+ * chip or balance a causal mask).  Enqueues three kernels, four with row
+ * parts: the prep and dK/dV kernels on `stream`, the dQ kernel on a stream
+ * the library keeps per device (made on the first backward call on that
+ * device outside a graph capture), forked from `stream` after the prep and
+ * joined back into it before the call returns, so work enqueued on `stream`
+ * afterwards sees all three gradients.  `stream` must belong to the current
+ * device.  Concurrent calls serialize their enqueue on a lock; the dQ
+ * kernels of calls on different streams of one device run in turn. */
 int sdpa_backward_workspace_bytes(const sdpa_desc_t* desc, size_t* bytes);
 int sdpa_backward(const sdpa_desc_t* desc, const void* q, const void* k, const void* v, const void* o,
                   const void* dout, const float* lse, void* dq, void* dk, void* dv, void* workspace,
