@@ -2,7 +2,9 @@
 
 The HIP path runs each workload at its real shape in the launch configuration
 the bench times; the oracle recomputes sampled rows one by one (first and last
-rows, window edges and random rows) from the same seeded inputs.  Seeds follow
+rows, window edges and random rows; 256 per shape, every row of the decode
+shapes and of speculative verify up to Lq = 8) from the same seeded inputs.
+The NaN-filled outputs show that every element was written.  Seeds follow
 1000 * workload + shape index.
 """
 
@@ -41,27 +43,27 @@ VERIFY_LQ = [1, 2, 4, 8, 12, 16, 24, 32, 48, 64]
 def test_speculative_verify(lk, lq):
     _say("verify", lk, lq)
     idx = VERIFY_LQ.index(lq) + (0 if lk == 16384 else len(VERIFY_LQ))
-    check_sampled(1, 32, 8, lq, lk, 128, 128, "f16", "none", 0, seed=3000 + idx, nrows=64)
+    check_sampled(1, 32, 8, lq, lk, 128, 128, "f16", "none", 0, seed=3000 + idx, nrows=256)
 
 
 def test_encoder_prefill_d64():
     _say("encoder H20 L1500 D64")
-    check_sampled(1, 20, 20, 1500, 1500, 64, 64, "bf16", "none", 0, seed=4000)
+    check_sampled(1, 20, 20, 1500, 1500, 64, 64, "bf16", "none", 0, seed=4000, nrows=256)
 
 
 @pytest.mark.parametrize("L", [1024, 4096])
 def test_vision_prefill_d72(L):
     _say("vision H16 D72", L)
-    check_sampled(1, 16, 16, L, L, 72, 72, "bf16", "none", 0, seed=4001 + (L == 4096))
+    check_sampled(1, 16, 16, L, L, 72, 72, "bf16", "none", 0, seed=4001 + (L == 4096), nrows=256)
 
 
 @pytest.mark.parametrize("L", [2048, 4096, 8192])
 def test_window_prefill_d256(L):
     _say("window prefill D256", L)
     idx = [2048, 4096, 8192].index(L)
-    check_sampled(1, 16, 8, L, L, 256, 256, "bf16", "window", 1024, seed=5000 + idx, nrows=64)
+    check_sampled(1, 16, 8, L, L, 256, 256, "bf16", "window", 1024, seed=5000 + idx, nrows=256)
 
 
 def test_full_causal_32k_d256():
     _say("causal 32k D256")
-    check_sampled(1, 16, 2, 32768, 32768, 256, 256, "bf16", "causal", 0, seed=5003, nrows=64)
+    check_sampled(1, 16, 2, 32768, 32768, 256, 256, "bf16", "causal", 0, seed=5003, nrows=256)
