@@ -16,7 +16,7 @@ calls, the K/V set rotating over copies that together exceed three times the
 The lengths are interleaved (each round calls every length once), so a drift
 of the device's clock or memory state over the run shifts every length
 alike instead of deciding a ratio between two lengths timed minutes apart.
-The sweep runs twice and each length keeps the smaller median.  Collected
+The sweep runs three times and each length keeps the smallest median.  Collected
 after the parity tests: a timing failure cannot hide them.
 """
 
@@ -46,7 +46,7 @@ def _verify_times(lk):
     ev = bench.HipEvents(40 * len(LQS))
     times = {}
     try:
-        for p in range(2):
+        for p in range(3):
             print("CASE nocliff", lk, "pass", p, flush=True)
             n = 0
             for i in range(50):
@@ -100,9 +100,9 @@ def test_no_step_above_125_percent(lk):
 
 
 @pytest.mark.xfail(strict=False, reason=(
-    "32 -> 48 queries (128 -> 192 packed rows) measures 1.25-1.37x on MI355X boxes: the four-wave "
-    "128-row tile gives way to the eight-wave tile, whose per-block barriers and load waits do not "
-    "shrink with the rows; the per-row cost still falls (criterion ii holds)"))
+    "32 -> 48 queries (128 -> 192 packed rows) measures 1.15-1.37x on MI355X boxes: the call is bound by "
+    "the matrix and softmax work of the rows there (the K/V stream alone takes ~22 us at Lk=32768), so "
+    "1.5x the rows cost about that much more; the per-row cost still falls (criterion ii holds)"))
 @pytest.mark.parametrize("lk", [16384, 32768])
 def test_no_step_above_125_percent_32_to_48(lk):
     times = _times(lk)
